@@ -1,0 +1,170 @@
+"""fp64 CPU oracle of the Hybrid Forcing hybrid attention step -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, the smoke check and the CPU-baseline leg of the benchmark use
+this package.  It loads ``liboracle.so`` (plain C, built by :func:`build`) through
+ctypes and wraps its functions for numpy arrays.  It imports nothing from the HIP
+library and the HIP library imports nothing from it.
+
+Every wrapper takes and returns fp64 arrays shaped [B, H, N, D] (planes = B*H).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+LIB_PATH = _HERE / "liboracle.so"
+_SOURCES = [_HERE / "hf_oracle.c"]
+
+
+def build(verbose: bool = False) -> Path:
+    """Compile liboracle.so with gcc (fp64, -O2, OpenMP, no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-Wall", "-Wextra", "-o", str(LIB_PATH) + ".tmp", *map(str, _SOURCES), "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(str(LIB_PATH) + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I32 = ctypes.POINTER(ctypes.c_int32)
+_I64 = ctypes.POINTER(ctypes.c_int64)
+_i64 = ctypes.c_int64
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            build()
+        L = ctypes.CDLL(str(LIB_PATH))
+        L.hfo_phi.argtypes = [ctypes.c_double]
+        L.hfo_phi.restype = ctypes.c_double
+        L.hfo_pool.argtypes = [_i64, _i64, _i64, _i64, _D, _D]
+        L.hfo_block_scores.argtypes = [_i64, _i64, _i64, _i64, _D, _D, _D]
+        L.hfo_select.argtypes = [_i64, _i64, _i64, _i64, _D, _I32]
+        L.hfo_sparse_attn.argtypes = [_i64] * 7 + [_D, _D, _D, _I32, _I64, _i64, _D]
+        L.hfo_linear_readout.argtypes = [_i64, _i64, _i64, _i64, _D, _D, _D, ctypes.c_double, _I64, _i64, _D]
+        L.hfo_absorb.argtypes = [_i64, _i64, _i64, _D, _D, _D, _D]
+        L.hfo_hybrid_step.argtypes = ([_i64] * 7 + [ctypes.c_double, _D, _D, _D, _D, _D, _I64, _i64, _I32, _D, _D])
+        L.hfo_num_threads.restype = ctypes.c_int
+        L.hfo_set_num_threads.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _p(a, t=_D):
+    return None if a is None else a.ctypes.data_as(t)
+
+
+def _blocks(blocks):
+    """[(plane, query_block), ...] -> (int64 array [n,2] or None, n)."""
+    if blocks is None:
+        return None, 0
+    b = np.ascontiguousarray(np.asarray(blocks, dtype=np.int64).reshape(-1, 2))
+    return b, b.shape[0]
+
+
+def n_blocks(n: int, blk: int) -> int:
+    return -(-n // blk)
+
+
+def phi(x: float) -> float:
+    return lib().hfo_phi(float(x))
+
+
+def num_threads() -> int:
+    return lib().hfo_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().hfo_set_num_threads(int(n))
+
+
+def pool(X, blk):
+    X = _f64(X)
+    B, H, N, D = X.shape
+    out = np.empty((B, H, n_blocks(N, blk), D))
+    lib().hfo_pool(B * H, N, D, blk, _p(X), _p(out))
+    return out
+
+
+def block_scores(qbar, kbar):
+    qbar, kbar = _f64(qbar), _f64(kbar)
+    B, H, nqb, D = qbar.shape
+    nkb = kbar.shape[2]
+    s = np.empty((B, H, nqb, nkb))
+    lib().hfo_block_scores(B * H, nqb, nkb, D, _p(qbar), _p(kbar), _p(s))
+    return s
+
+
+def select(s, k):
+    s = _f64(s)
+    B, H, nqb, nkb = s.shape
+    if not 1 <= k <= nkb:
+        raise ValueError("need 1 <= k <= n_kb")
+    idx = np.empty((B, H, nqb, k), dtype=np.int32)
+    lib().hfo_select(B * H, nqb, nkb, k, _p(s), _p(idx, _I32))
+    return idx
+
+
+def sparse_attn(Q, K, V, idx, bq, bk, blocks=None, out=None):
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    B, H, Nq, D = Q.shape
+    Nk = K.shape[2]
+    k = idx.shape[-1]
+    out = np.zeros_like(Q) if out is None else out
+    bl, nb = _blocks(blocks)
+    lib().hfo_sparse_attn(B * H, Nq, Nk, D, bq, bk, k, _p(Q), _p(K), _p(V), _p(idx, _I32), _p(bl, _I64), nb,
+                          _p(out))
+    return out
+
+
+def linear_readout(Q, S, z, bq=64, eps=1e-6, blocks=None, out=None):
+    Q, S, z = _f64(Q), _f64(S), _f64(z)
+    B, H, Nq, D = Q.shape
+    out = np.zeros_like(Q) if out is None else out
+    bl, nb = _blocks(blocks)
+    lib().hfo_linear_readout(B * H, Nq, D, bq, _p(Q), _p(S), _p(z), eps, _p(bl, _I64), nb, _p(out))
+    return out
+
+
+def absorb(K, V, S=None, z=None):
+    """Return (S + sum phi(K)^T V, z + sum phi(K)) -- inputs are not modified."""
+    K, V = _f64(K), _f64(V)
+    B, H, n, D = K.shape
+    S = np.zeros((B, H, D, D)) if S is None else _f64(S).copy()
+    z = np.zeros((B, H, D)) if z is None else _f64(z).copy()
+    lib().hfo_absorb(B * H, n, D, _p(K), _p(V), _p(S), _p(z))
+    return S, z
+
+
+def hybrid_step(Q, K, V, S, z, bq, bk, k, eps=1e-6, blocks=None, want_scores=False):
+    """Whole step -> (out [B,H,Nq,D], idx [B,H,nqb,k], scores or None)."""
+    Q, K, V, S, z = _f64(Q), _f64(K), _f64(V), _f64(S), _f64(z)
+    B, H, Nq, D = Q.shape
+    Nk = K.shape[2]
+    nqb, nkb = n_blocks(Nq, bq), n_blocks(Nk, bk)
+    if not 1 <= k <= nkb:
+        raise ValueError("need 1 <= k <= n_kb")
+    out = np.zeros_like(Q)
+    idx = np.empty((B, H, nqb, k), dtype=np.int32)
+    sc = np.empty((B, H, nqb, nkb)) if want_scores else None
+    bl, nb = _blocks(blocks)
+    lib().hfo_hybrid_step(B * H, Nq, Nk, D, bq, bk, k, eps, _p(Q), _p(K), _p(V), _p(S), _p(z), _p(bl, _I64), nb,
+                          _p(idx, _I32), _p(sc), _p(out))
+    return out, idx, sc

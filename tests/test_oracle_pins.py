@@ -1,0 +1,301 @@
+"""Pins of the fp64 oracle to facts outside itself.
+
+Each test checks the oracle against brute force, a textbook routine the method
+reduces to in a special case, a closed form, or an invariant, so that a dropped
+term, a wrong sign or index, or a transposed operand anywhere in it fails here.
+No GPU is needed.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from hybrid_sparse_linear_hf_amd import synth
+
+EPS = 1e-6
+
+
+def dense_attention(Q, K, V):
+    """Textbook softmax(Q K^T / sqrt(D)) V per plane, numpy fp64."""
+    D = Q.shape[-1]
+    L = np.einsum("bhtd,bhud->bhtu", Q, K) / math.sqrt(D)
+    L = L - L.max(axis=-1, keepdims=True)
+    P = np.exp(L)
+    P /= P.sum(axis=-1, keepdims=True)
+    return np.einsum("bhtu,bhud->bhtd", P, V)
+
+
+def masked_attention(Q, K, V, keep_mask):
+    """Dense attention where logits of masked-out keys are -inf; keep_mask [B,H,Nq,Nk] bool."""
+    D = Q.shape[-1]
+    L = np.einsum("bhtd,bhud->bhtu", Q, K) / math.sqrt(D)
+    L = np.where(keep_mask, L, -np.inf)
+    L = L - L.max(axis=-1, keepdims=True)
+    P = np.exp(L)
+    P /= P.sum(axis=-1, keepdims=True)
+    return np.einsum("bhtu,bhud->bhtd", P, V)
+
+
+def lexsort_select(s, k):
+    """Brute-force selection: numpy lexsort on (index, -score), first k, ascending."""
+    B, H, nqb, nkb = s.shape
+    out = np.empty((B, H, nqb, k), dtype=np.int32)
+    j = np.arange(nkb)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nqb):
+                order = np.lexsort((j, -s[b, h, i]))
+                out[b, h, i] = np.sort(order[:k])
+    return out
+
+
+def block_mask(idx, Nq, Nk, bq, bk):
+    B, H, nqb, k = idx.shape
+    m = np.zeros((B, H, Nq, Nk), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nqb):
+                for j in idx[b, h, i]:
+                    m[b, h, i * bq:min((i + 1) * bq, Nq), j * bk:min((j + 1) * bk, Nk)] = True
+    return m
+
+
+def rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# ------------------------------------------------------------------ feature map
+
+def test_phi_closed_forms():
+    assert oracle.phi(0.0) == 1.0
+    assert oracle.phi(1.5) == 2.5
+    assert oracle.phi(-1.0) == pytest.approx(math.exp(-1.0), rel=1e-15)
+    assert oracle.phi(-30.0) == pytest.approx(math.exp(-30.0), rel=1e-15)
+    # continuous at 0 from both sides, increasing and positive
+    assert oracle.phi(1e-12) == pytest.approx(1.0, abs=2e-12)
+    assert oracle.phi(-1e-12) == pytest.approx(1.0, abs=2e-12)
+    xs = np.linspace(-20, 20, 2001)
+    ys = np.array([oracle.phi(x) for x in xs])
+    assert np.all(ys > 0) and np.all(np.diff(ys) > 0)
+
+
+# ------------------------------------------------------------------ pooling
+
+@pytest.mark.parametrize("N,blk", [(64, 16), (70, 16), (1560 * 2, 64), (5, 8)])
+def test_pool_invariants(N, blk):
+    X = rand((2, 3, N, 8), 1)
+    P = oracle.pool(X, blk)
+    nb = -(-N // blk)
+    assert P.shape == (2, 3, nb, 8)
+    sizes = np.array([min(blk, N - j * blk) for j in range(nb)], dtype=np.float64)
+    # size-weighted block means add up to the total sum: catches a wrong count in a short block
+    np.testing.assert_allclose((P * sizes[None, None, :, None]).sum(axis=2), X.sum(axis=2), rtol=1e-12, atol=1e-12)
+    # one block covering everything is the global mean; block size 1 is the identity
+    np.testing.assert_allclose(oracle.pool(X, N + 3)[:, :, 0], X.mean(axis=2), rtol=1e-13)
+    np.testing.assert_array_equal(oracle.pool(X, 1), X)
+    # constant rows pool to the constant
+    Cst = np.full((1, 1, N, 8), 0.75)
+    np.testing.assert_array_equal(oracle.pool(Cst, blk), 0.75)
+
+
+# ------------------------------------------------------------------ scores + selection
+
+def test_block_scores_special_case():
+    qbar = rand((1, 2, 3, 16), 2)
+    kbar = rand((1, 2, 5, 16), 3)
+    s = oracle.block_scores(qbar, kbar)
+    np.testing.assert_allclose(s, np.matmul(qbar, np.swapaxes(kbar, -1, -2)) / 4.0, rtol=1e-14)
+
+
+@pytest.mark.parametrize("nkb,k", [(16, 2), (16, 16), (147, 37), (7, 1)])
+def test_select_matches_lexsort(nkb, k):
+    s = rand((2, 2, 9, nkb), 4)
+    s[0, 0, 0, 3] = s[0, 0, 0, 5]  # an exact tie
+    idx = oracle.select(s, k)
+    np.testing.assert_array_equal(idx, lexsort_select(s, k))
+    # every kept score >= every dropped score
+    for b in range(2):
+        for h in range(2):
+            for i in range(9):
+                kept = np.zeros(nkb, bool)
+                kept[idx[b, h, i]] = True
+                if not kept.all():
+                    assert s[b, h, i][kept].min() >= s[b, h, i][~kept].max()
+
+
+def test_select_exact_ties_prefer_lower_index():
+    s = np.zeros((1, 1, 1, 10))
+    s[..., [2, 4, 7, 9]] = 1.0
+    np.testing.assert_array_equal(oracle.select(s, 2)[0, 0, 0], [2, 4])
+    np.testing.assert_array_equal(oracle.select(s, 5)[0, 0, 0], [0, 2, 4, 7, 9])
+    np.testing.assert_array_equal(oracle.select(s, 10)[0, 0, 0], np.arange(10))
+
+
+def test_select_ties_from_duplicated_key_blocks():
+    # duplicated key blocks give bit-identical pooled scores; the lower block must win
+    K = rand((1, 1, 8 * 16, 32), 5)
+    K[0, 0, 5 * 16:6 * 16] = K[0, 0, 2 * 16:3 * 16]
+    Q = np.broadcast_to(K[0, 0, 2 * 16:3 * 16].mean(axis=0), (1, 1, 16, 32)).copy()
+    s = oracle.block_scores(oracle.pool(Q, 16), oracle.pool(K, 16))
+    assert s[0, 0, 0, 2] == s[0, 0, 0, 5]
+    assert s[0, 0, 0, 2] == s[0, 0, 0].max()
+    np.testing.assert_array_equal(oracle.select(s, 1)[0, 0, 0], [2])
+
+
+# ------------------------------------------------------------------ sparse attention
+
+@pytest.mark.parametrize("Nq,Nk,D,bq,bk", [(64, 256, 64, 16, 16), (50, 130, 16, 16, 32), (7, 9, 4, 4, 4),
+                                          (128, 200, 32, 64, 64)])
+def test_keep_all_equals_dense(Nq, Nk, D, bq, bk):
+    Q, K, V = rand((1, 2, Nq, D), 6), rand((1, 2, Nk, D), 7), rand((1, 2, Nk, D), 8)
+    nqb, nkb = -(-Nq // bq), -(-Nk // bk)
+    idx = np.broadcast_to(np.arange(nkb, dtype=np.int32), (1, 2, nqb, nkb)).copy()
+    out = oracle.sparse_attn(Q, K, V, idx, bq, bk)
+    np.testing.assert_allclose(out, dense_attention(Q, K, V), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("Nq,Nk,D,bq,bk,k", [(64, 256, 64, 16, 16, 2), (50, 130, 16, 16, 32, 3),
+                                            (100, 300, 32, 32, 64, 1)])
+def test_sparse_equals_masked_dense(Nq, Nk, D, bq, bk, k):
+    Q, K, V = rand((2, 1, Nq, D), 9), rand((2, 1, Nk, D), 10), rand((2, 1, Nk, D), 11)
+    nqb, nkb = -(-Nq // bq), -(-Nk // bk)
+    rng = np.random.default_rng(12)
+    idx = np.stack([np.sort(rng.choice(nkb, k, replace=False)) for _ in range(2 * nqb)]).astype(np.int32)
+    idx = idx.reshape(2, 1, nqb, k)
+    out = oracle.sparse_attn(Q, K, V, idx, bq, bk)
+    ref = masked_attention(Q, K, V, block_mask(idx, Nq, Nk, bq, bk))
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_sparse_closed_forms():
+    Nq, Nk, D, bq, bk, k = 32, 96, 8, 16, 16, 2
+    Q, K = rand((1, 1, Nq, D), 13), rand((1, 1, Nk, D), 14)
+    idx = np.array([[[[1, 4], [0, 5]]]], dtype=np.int32)
+    # constant value rows -> that constant
+    Vc = np.full((1, 1, Nk, D), -0.375)
+    np.testing.assert_allclose(oracle.sparse_attn(Q, K, Vc, idx, bq, bk), -0.375, rtol=1e-14)
+    # identical keys -> uniform weights -> mean of the kept value rows
+    V = rand((1, 1, Nk, D), 15)
+    Ksame = np.broadcast_to(K[:, :, :1], K.shape).copy()
+    out = oracle.sparse_attn(Q, Ksame, V, idx, bq, bk)
+    want0 = np.concatenate([V[0, 0, 16:32], V[0, 0, 64:80]]).mean(axis=0)
+    np.testing.assert_allclose(out[0, 0, :16], np.broadcast_to(want0, (16, D)), rtol=1e-12)
+    # one kept block of one key (bk=1) -> exactly that value row
+    out1 = oracle.sparse_attn(Q, K, V, np.full((1, 1, 2, 1), 17, np.int32), bq, 1)
+    np.testing.assert_allclose(out1[0, 0], np.broadcast_to(V[0, 0, 17], (Nq, D)), rtol=1e-15)
+
+
+def test_softmax_shift_invariance_whole_step():
+    Nq, Nk, D, bq, bk, k = 48, 160, 16, 16, 16, 3
+    Q, K, V = rand((1, 1, Nq, D), 16), rand((1, 1, Nk, D), 17), rand((1, 1, Nk, D), 18)
+    S, z = np.zeros((1, 1, D, D)), np.zeros((1, 1, D))
+    o1, i1, _ = oracle.hybrid_step(Q, K, V, S, z, bq, bk, k)
+    o2, i2, _ = oracle.hybrid_step(Q, K + rand((D,), 19), V, S, z, bq, bk, k)
+    np.testing.assert_array_equal(i1, i2)
+    np.testing.assert_allclose(o1, o2, rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------------------------------ linear branch
+
+def _phi_np(x):
+    return np.vectorize(oracle.phi)(x)
+
+
+def test_readout_empty_state_is_zero():
+    Q = rand((1, 2, 20, 8), 20)
+    out = oracle.linear_readout(Q, np.zeros((1, 2, 8, 8)), np.zeros((1, 2, 8)), bq=16)
+    assert np.all(out == 0.0)
+
+
+def test_readout_one_token_closed_form():
+    D = 8
+    Q, k1, v1 = rand((1, 1, 5, D), 21), rand((D,), 22), rand((D,), 23)
+    S, z = oracle.absorb(k1.reshape(1, 1, 1, D), v1.reshape(1, 1, 1, D))
+    out = oracle.linear_readout(Q, S, z, bq=4, eps=EPS)
+    for t in range(5):
+        w = float(_phi_np(Q[0, 0, t]) @ _phi_np(k1))
+        np.testing.assert_allclose(out[0, 0, t], v1 * w / (w + EPS), rtol=1e-13)
+
+
+def test_readout_constant_values():
+    D, n = 8, 40
+    K, Q = rand((1, 1, n, D), 24), rand((1, 1, 6, D), 25)
+    S, z = oracle.absorb(K, np.full((1, 1, n, D), 2.5))
+    out = oracle.linear_readout(Q, S, z, bq=8, eps=EPS)
+    den = _phi_np(Q[0, 0]) @ z[0, 0]
+    np.testing.assert_allclose(out[0, 0], 2.5 * (den / (den + EPS))[:, None] * np.ones(D), rtol=1e-13)
+
+
+def test_absorb_recurrent_equals_direct():
+    D, n = 16, 300
+    K, V = rand((2, 2, n, D), 26), rand((2, 2, n, D), 27)
+    S_direct = np.einsum("bhua,bhuc->bhac", _phi_np(K), V)
+    z_direct = _phi_np(K).sum(axis=2)
+    S, z = oracle.absorb(K, V)
+    np.testing.assert_allclose(S, S_direct, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(z, z_direct, rtol=1e-13)
+    # chunk by chunk, in reverse order, gives the same state
+    S2, z2 = None, None
+    for c0 in reversed(range(0, n, 64)):
+        S2, z2 = oracle.absorb(K[:, :, c0:c0 + 64], V[:, :, c0:c0 + 64], S2, z2)
+    np.testing.assert_allclose(S2, S_direct, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(z2, z_direct, rtol=1e-13)
+
+
+# ------------------------------------------------------------------ the whole step
+
+def test_step_is_sparse_plus_linear():
+    Nq, Nk, D, bq, bk, k = 64, 256, 32, 16, 16, 4
+    Q, K, V = rand((1, 2, Nq, D), 28), rand((1, 2, Nk, D), 29), rand((1, 2, Nk, D), 30)
+    S, z = oracle.absorb(rand((1, 2, 100, D), 31), rand((1, 2, 100, D), 32))
+    out, idx, s = oracle.hybrid_step(Q, K, V, S, z, bq, bk, k, want_scores=True)
+    np.testing.assert_array_equal(idx, lexsort_select(s, k))
+    sp = masked_attention(Q, K, V, block_mask(idx, Nq, Nk, bq, bk))
+    lin = oracle.linear_readout(Q, S, z, bq=bq)
+    np.testing.assert_allclose(out, sp + lin, rtol=1e-11, atol=1e-12)
+    # restricted to a subset of blocks: same rows, other rows untouched (zero)
+    sub = [(0, 1), (1, 3)]
+    out_s, _, _ = oracle.hybrid_step(Q, K, V, S, z, bq, bk, k, blocks=sub)
+    np.testing.assert_array_equal(out_s[0, 0, 16:32], out[0, 0, 16:32])
+    np.testing.assert_array_equal(out_s[0, 1, 48:64], out[0, 1, 48:64])
+    assert np.all(out_s[0, 0, :16] == 0)
+
+
+def test_tiny_config_brute_force():
+    """The tiny configuration (1 head, D=64, 64 tokens/frame, window 4, block 16, top-2,
+    3 frames absorbed), checked end to end against brute force."""
+    cfg = synth.TINY
+    st = synth.tiny_stream(seed=0)
+    T, ev = cfg.T, cfg.n_evicted
+    Q = st.q.astype(np.float64)
+    K = st.k_all[:, :, ev * T:].astype(np.float64)
+    V = st.v_all[:, :, ev * T:].astype(np.float64)
+    Kev, Vev = st.k_all[:, :, :ev * T].astype(np.float64), st.v_all[:, :, :ev * T].astype(np.float64)
+    S, z = oracle.absorb(Kev, Vev)
+    k = cfg.top_k()
+    assert (k, cfg.n_qb, cfg.n_kb) == (2, 4, 16)
+    out, idx, s = oracle.hybrid_step(Q, K, V, S, z, cfg.bq, cfg.bk, k, want_scores=True)
+    qbar = Q.reshape(1, 1, 4, 16, 64).mean(axis=3)
+    kbar = K.reshape(1, 1, 16, 16, 64).mean(axis=3)
+    np.testing.assert_allclose(s, qbar @ np.swapaxes(kbar, -1, -2) / 8.0, rtol=1e-12, atol=1e-15)
+    np.testing.assert_array_equal(idx, lexsort_select(s, k))
+    # the keep-all case is plain dense attention over the window
+    dense = oracle.sparse_attn(Q, K, V, np.broadcast_to(np.arange(16, dtype=np.int32), (1, 1, 4, 16)).copy(), 16, 16)
+    np.testing.assert_allclose(dense, dense_attention(Q, K, V), rtol=1e-11, atol=1e-12)
+    phiK = _phi_np(Kev)
+    lin = np.einsum("bhta,bhac->bhtc", _phi_np(Q), np.einsum("bhua,bhuc->bhac", phiK, Vev))
+    lin /= (np.einsum("bhta,bha->bht", _phi_np(Q), phiK.sum(axis=2)) + EPS)[..., None]
+    sp = masked_attention(Q, K, V, block_mask(idx, 64, 256, 16, 16))
+    np.testing.assert_allclose(out, sp + lin, rtol=1e-11, atol=1e-12)
+
+
+def test_sparse_large_logits_stay_finite():
+    # logits of several hundred overflow exp() unless the row maximum is subtracted first
+    Nq, Nk, D, bq, bk = 16, 64, 16, 16, 16
+    Q, K, V = rand((1, 1, Nq, D), 33, 60.0), rand((1, 1, Nk, D), 34, 60.0), rand((1, 1, Nk, D), 35)
+    idx = np.array([[[[0, 1, 2, 3]]]], dtype=np.int32)
+    out = oracle.sparse_attn(Q, K, V, idx, bq, bk)
+    assert np.all(np.isfinite(out))
+    np.testing.assert_allclose(out, dense_attention(Q, K, V), rtol=1e-10, atol=1e-12)

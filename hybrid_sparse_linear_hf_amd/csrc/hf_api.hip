@@ -1,0 +1,355 @@
+// C ABI of libhf: argument validation, workspace layout and kernel launches.
+// Every entry point validates all of its arguments before enqueuing anything, so a
+// failing call has no side effect; the reason is kept per thread for hf_last_error().
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "hf_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hf_status fail(hf_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+hf_status ok() {
+    g_last_error.clear();
+    return HF_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kMaxKeyBlocks = 1536;
+constexpr int64_t kMaxElems = (int64_t)1 << 31;
+
+hf_status check_dims(const hf_dims *d) {
+    if (!d) return fail(HF_ERR_NULL, "dims is NULL");
+    if (d->B < 1 || d->H < 1) return fail(HF_ERR_SHAPE, "B=%d H=%d must be >= 1", d->B, d->H);
+    if (d->D != 64 && d->D != 128) return fail(HF_ERR_UNSUPPORTED, "D=%d (supported: 64, 128)", d->D);
+    if (d->T < 8 || d->T % 8) return fail(HF_ERR_UNSUPPORTED, "T=%d must be a positive multiple of 8", d->T);
+    if (d->C < 1 || d->W < d->C) return fail(HF_ERR_SHAPE, "need 1 <= C <= W (C=%d W=%d)", d->C, d->W);
+    if (d->bq != 16 && d->bq != 32 && d->bq != 64)
+        return fail(HF_ERR_UNSUPPORTED, "bq=%d (supported: 16, 32, 64)", d->bq);
+    if (d->bk != 16 && d->bk != 32 && d->bk != 64 && d->bk != 128)
+        return fail(HF_ERR_UNSUPPORTED, "bk=%d (supported: 16, 32, 64, 128)", d->bk);
+    const int64_t ring = (int64_t)d->B * d->H * d->W * d->T * d->D;
+    if (ring >= kMaxElems) return fail(HF_ERR_UNSUPPORTED, "ring of %lld elements exceeds 2^31", (long long)ring);
+    if (cdiv((int64_t)d->W * d->T, d->bk) > kMaxKeyBlocks)
+        return fail(HF_ERR_UNSUPPORTED, "window of %lld key blocks exceeds %d", (long long)cdiv((int64_t)d->W * d->T, d->bk),
+                    kMaxKeyBlocks);
+    return HF_OK;
+}
+
+hf_status check_ring(const hf_dims *d, const hf_kv_ring *r) {
+    if (!r) return fail(HF_ERR_NULL, "ring is NULL");
+    if (!r->k_dev || !r->vt_dev) return fail(HF_ERR_NULL, "ring storage pointer is NULL");
+    if (r->head < 0 || r->head >= d->W) return fail(HF_ERR_RING_STATE, "ring head=%d outside [0, W=%d)", r->head, d->W);
+    if (r->n_committed < 0 || r->n_committed > d->W - d->C)
+        return fail(HF_ERR_RING_STATE, "ring n_committed=%d outside [0, W-C=%d]", r->n_committed, d->W - d->C);
+    return HF_OK;
+}
+
+struct Geometry {
+    int BH, Nq, Nk, nqb, nkb;
+};
+
+Geometry geometry(const hf_dims *d, const hf_kv_ring *r) {
+    Geometry g;
+    g.BH = d->B * d->H;
+    g.Nq = d->C * d->T;
+    g.Nk = (r->n_committed + d->C) * d->T;
+    g.nqb = (int)cdiv(g.Nq, d->bq);
+    g.nkb = (int)cdiv(g.Nk, d->bk);
+    return g;
+}
+
+// Workspace layout (offsets 256-byte aligned):
+//   [absorb counters | absorb partials]  [qbar fp64]  [kbar fp64]  [S^T bf16]
+struct WsLayout {
+    size_t absorb, qbar, kbar, st, total;
+};
+
+size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const hf_dims *d) {
+    const int BH = d->B * d->H;
+    const int64_t nqb = cdiv((int64_t)d->C * d->T, d->bq);
+    const int64_t nkb = cdiv((int64_t)d->W * d->T, d->bk);
+    WsLayout w;
+    w.absorb = 0;
+    w.qbar = al(hf_absorb_workspace_bytes(BH, d->D));
+    w.kbar = w.qbar + al((size_t)BH * nqb * d->D * sizeof(double));
+    w.st = w.kbar + al((size_t)BH * nkb * d->D * sizeof(double));
+    w.total = w.st + al((size_t)BH * d->D * d->D * sizeof(uint16_t));
+    return w;
+}
+
+hf_status check_ws(const hf_dims *d, void *ws, size_t bytes) {
+    const size_t need = ws_layout(d).total;
+    if (!ws) return fail(HF_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (bytes < need) return fail(HF_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", bytes, need);
+    return HF_OK;
+}
+
+char *wsp(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
+
+// absorb counters + partials live at the start of the workspace
+void absorb_ws(void *ws, int BH, int D, float **part, uint32_t **counters) {
+    const size_t nctr = (size_t)BH * (D / 64) * (D / 64);
+    *counters = reinterpret_cast<uint32_t *>(ws);
+    *part = reinterpret_cast<float *>(wsp(ws, al(nctr * sizeof(uint32_t))));
+}
+
+hf_status hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(HF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return HF_OK;
+}
+
+// --- enqueue helpers (arguments already validated)
+
+hipError_t enqueue_append(const hf_dims *d, const hf_kv_ring *r, const void *kc, const void *vc, hipStream_t s) {
+    hf_append_args a{};
+    a.BH = d->B * d->H;
+    a.D = d->D;
+    a.T = d->T;
+    a.W = d->W;
+    a.head = r->head;
+    a.first_frame = r->n_committed;
+    a.C = d->C;
+    a.k_cur = static_cast<const uint16_t *>(kc);
+    a.v_cur = static_cast<const uint16_t *>(vc);
+    a.ring_k = static_cast<uint16_t *>(r->k_dev);
+    a.ring_vt = static_cast<uint16_t *>(r->vt_dev);
+    return hf_launch_ring_append(a, s);
+}
+
+hipError_t enqueue_select(const hf_dims *d, const void *q, const hf_kv_ring *r, int top_k, int32_t *idx,
+                          double *scores, void *ws, hipStream_t s) {
+    const Geometry g = geometry(d, r);
+    const WsLayout L = ws_layout(d);
+    hf_select_args a{};
+    a.BH = g.BH;
+    a.D = d->D;
+    a.T = d->T;
+    a.W = d->W;
+    a.head = r->head;
+    a.Nq = g.Nq;
+    a.Nk = g.Nk;
+    a.bq = d->bq;
+    a.bk = d->bk;
+    a.nqb = g.nqb;
+    a.nkb = g.nkb;
+    a.top_k = top_k;
+    a.q = static_cast<const uint16_t *>(q);
+    a.ring_k = static_cast<const uint16_t *>(r->k_dev);
+    a.qbar = reinterpret_cast<double *>(wsp(ws, L.qbar));
+    a.kbar = reinterpret_cast<double *>(wsp(ws, L.kbar));
+    a.idx = idx;
+    a.scores = scores;
+    return hf_launch_block_select(a, s);
+}
+
+hipError_t enqueue_attn(const hf_dims *d, const void *q, const hf_kv_ring *r, const int32_t *idx, int top_k,
+                        const float *S, const float *z, float eps, float *out, void *ws, hipStream_t s) {
+    const Geometry g = geometry(d, r);
+    const WsLayout L = ws_layout(d);
+    hf_attn_args a{};
+    a.BH = g.BH;
+    a.D = d->D;
+    a.T = d->T;
+    a.W = d->W;
+    a.head = r->head;
+    a.Nq = g.Nq;
+    a.Nk = g.Nk;
+    a.bq = d->bq;
+    a.bk = d->bk;
+    a.nqb = g.nqb;
+    a.nkb = g.nkb;
+    a.top_k = top_k;
+    a.q = static_cast<const uint16_t *>(q);
+    a.ring_k = static_cast<const uint16_t *>(r->k_dev);
+    a.ring_vt = static_cast<const uint16_t *>(r->vt_dev);
+    a.idx = idx;
+    a.S = S;
+    a.z = z;
+    a.st = reinterpret_cast<uint16_t *>(wsp(ws, L.st));
+    a.eps = eps;
+    a.out = out;
+    return hf_launch_sparse_attn(a, s);
+}
+
+hipError_t enqueue_absorb_plain(const hf_dims *d, const void *k, const void *v, int64_t n_tok, float *S, float *z,
+                                void *ws, hipStream_t s) {
+    hf_absorb_args a{};
+    a.BH = d->B * d->H;
+    a.D = d->D;
+    a.n_tok = n_tok;
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.S = S;
+    a.z = z;
+    absorb_ws(ws, a.BH, d->D, &a.part, &a.counters);
+    if (hf_absorb_required_bytes(a.BH, a.D, n_tok) > hf_absorb_workspace_bytes(a.BH, a.D)) return hipErrorInvalidValue;
+    return hf_launch_absorb(a, s);
+}
+
+hipError_t enqueue_absorb_ring(const hf_dims *d, const hf_kv_ring *r, int e_frames, float *S, float *z, void *ws,
+                               hipStream_t s) {
+    hf_absorb_args a{};
+    a.BH = d->B * d->H;
+    a.D = d->D;
+    a.n_tok = (int64_t)e_frames * d->T;
+    a.ring_k = static_cast<const uint16_t *>(r->k_dev);
+    a.ring_vt = static_cast<const uint16_t *>(r->vt_dev);
+    a.W = d->W;
+    a.T = d->T;
+    a.head = r->head;
+    a.S = S;
+    a.z = z;
+    absorb_ws(ws, a.BH, d->D, &a.part, &a.counters);
+    if (hf_absorb_required_bytes(a.BH, a.D, a.n_tok) > hf_absorb_workspace_bytes(a.BH, a.D)) return hipErrorInvalidValue;
+    return hf_launch_absorb(a, s);
+}
+
+hipError_t record(const hf_step_events *ev, int i, hipStream_t s) {
+    if (ev && ev->ev[i]) return hipEventRecord(ev->ev[i], s);
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hf_abi_version(void) { return HF_ABI_VERSION; }
+
+const char *hf_status_str(hf_status s) {
+    switch (s) {
+        case HF_OK: return "HF_OK";
+        case HF_ERR_NULL: return "HF_ERR_NULL";
+        case HF_ERR_SHAPE: return "HF_ERR_SHAPE";
+        case HF_ERR_UNSUPPORTED: return "HF_ERR_UNSUPPORTED";
+        case HF_ERR_RING_STATE: return "HF_ERR_RING_STATE";
+        case HF_ERR_WORKSPACE: return "HF_ERR_WORKSPACE";
+        case HF_ERR_HIP: return "HF_ERR_HIP";
+    }
+    return "HF_ERR_UNKNOWN";
+}
+
+const char *hf_last_error(void) { return g_last_error.c_str(); }
+
+hf_status hf_workspace_size(const hf_dims *d, int32_t top_k, size_t *bytes) {
+    hf_status st = check_dims(d);
+    if (st != HF_OK) return st;
+    if (!bytes) return fail(HF_ERR_NULL, "bytes is NULL");
+    (void)top_k;
+    *bytes = ws_layout(d).total;
+    return ok();
+}
+
+hf_status hf_ring_append(const hf_dims *d, const hf_kv_ring *ring, const void *k_cur, const void *v_cur,
+                         hipStream_t stream) {
+    hf_status st = check_dims(d);
+    if (st == HF_OK) st = check_ring(d, ring);
+    if (st != HF_OK) return st;
+    if (!k_cur || !v_cur) return fail(HF_ERR_NULL, "k_cur/v_cur is NULL");
+    st = hip_status(enqueue_append(d, ring, k_cur, v_cur, stream), "ring append launch");
+    return st == HF_OK ? ok() : st;
+}
+
+hf_status hf_block_select(const hf_dims *d, const void *q, const hf_kv_ring *ring, int32_t top_k, int32_t *idx,
+                          double *scores, void *ws, size_t ws_bytes, hipStream_t stream) {
+    hf_status st = check_dims(d);
+    if (st == HF_OK) st = check_ring(d, ring);
+    if (st != HF_OK) return st;
+    if (!q || !idx) return fail(HF_ERR_NULL, "q/idx is NULL");
+    const Geometry g = geometry(d, ring);
+    if (top_k < 1 || top_k > g.nkb) return fail(HF_ERR_SHAPE, "top_k=%d outside [1, n_kb=%d]", top_k, g.nkb);
+    st = check_ws(d, ws, ws_bytes);
+    if (st != HF_OK) return st;
+    st = hip_status(enqueue_select(d, q, ring, top_k, idx, scores, ws, stream), "block select launch");
+    return st == HF_OK ? ok() : st;
+}
+
+hf_status hf_sparse_window_attn(const hf_dims *d, const void *q, const hf_kv_ring *ring, const int32_t *idx,
+                                int32_t top_k, const float *S, const float *z, float eps, float *out, void *ws,
+                                size_t ws_bytes, hipStream_t stream) {
+    hf_status st = check_dims(d);
+    if (st == HF_OK) st = check_ring(d, ring);
+    if (st != HF_OK) return st;
+    if (!q || !idx || !out) return fail(HF_ERR_NULL, "q/idx/out is NULL");
+    if ((S == nullptr) != (z == nullptr)) return fail(HF_ERR_NULL, "S and z must both be given or both be NULL");
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(HF_ERR_SHAPE, "eps must be finite and >= 0");
+    const Geometry g = geometry(d, ring);
+    if (top_k < 1 || top_k > g.nkb) return fail(HF_ERR_SHAPE, "top_k=%d outside [1, n_kb=%d]", top_k, g.nkb);
+    st = check_ws(d, ws, ws_bytes);
+    if (st != HF_OK) return st;
+    st = hip_status(enqueue_attn(d, q, ring, idx, top_k, S, z, eps, out, ws, stream), "sparse attention launch");
+    return st == HF_OK ? ok() : st;
+}
+
+hf_status hf_linear_absorb(const hf_dims *d, const void *k_ev, const void *v_ev, int64_t n_tok, float *S, float *z,
+                           void *ws, size_t ws_bytes, hipStream_t stream) {
+    hf_status st = check_dims(d);
+    if (st != HF_OK) return st;
+    if (n_tok < 0) return fail(HF_ERR_SHAPE, "n_tok=%lld < 0", (long long)n_tok);
+    if (!S || !z) return fail(HF_ERR_NULL, "S/z is NULL");
+    if (n_tok > 0 && (!k_ev || !v_ev)) return fail(HF_ERR_NULL, "k_ev/v_ev is NULL");
+    if ((int64_t)d->B * d->H * n_tok * d->D >= kMaxElems)
+        return fail(HF_ERR_UNSUPPORTED, "evicted tensors exceed 2^31 elements");
+    st = check_ws(d, ws, ws_bytes);
+    if (st != HF_OK) return st;
+    st = hip_status(enqueue_absorb_plain(d, k_ev, v_ev, n_tok, S, z, ws, stream), "absorb launch");
+    return st == HF_OK ? ok() : st;
+}
+
+hf_status hf_hybrid_step(const hf_dims *d, const void *q, const void *k_cur, const void *v_cur, hf_kv_ring *ring,
+                         int32_t top_k, uint32_t flags, float *S, float *z, float eps, int32_t *idx, float *out,
+                         void *ws, size_t ws_bytes, const hf_step_events *events, hipStream_t stream) {
+    hf_status st = check_dims(d);
+    if (st == HF_OK) st = check_ring(d, ring);
+    if (st != HF_OK) return st;
+    if (!q || !idx || !out) return fail(HF_ERR_NULL, "q/idx/out is NULL");
+    if ((k_cur == nullptr) != (v_cur == nullptr)) return fail(HF_ERR_NULL, "give both k_cur and v_cur or neither");
+    if ((S == nullptr) != (z == nullptr)) return fail(HF_ERR_NULL, "S and z must both be given or both be NULL");
+    if ((flags & HF_STEP_COMMIT) && !S) return fail(HF_ERR_NULL, "HF_STEP_COMMIT needs S and z");
+    if (flags & ~HF_STEP_COMMIT) return fail(HF_ERR_SHAPE, "unknown flags 0x%x", flags);
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(HF_ERR_SHAPE, "eps must be finite and >= 0");
+    const Geometry g = geometry(d, ring);
+    if (top_k < 1 || top_k > g.nkb) return fail(HF_ERR_SHAPE, "top_k=%d outside [1, n_kb=%d]", top_k, g.nkb);
+    st = check_ws(d, ws, ws_bytes);
+    if (st != HF_OK) return st;
+
+    hipError_t e = record(events, 0, stream);
+    if (e == hipSuccess && k_cur) e = enqueue_append(d, ring, k_cur, v_cur, stream);
+    if (e == hipSuccess) e = record(events, 1, stream);
+    if (e == hipSuccess) e = enqueue_select(d, q, ring, top_k, idx, nullptr, ws, stream);
+    if (e == hipSuccess) e = record(events, 2, stream);
+    if (e == hipSuccess) e = enqueue_attn(d, q, ring, idx, top_k, S, z, eps, out, ws, stream);
+    if (e == hipSuccess) e = record(events, 3, stream);
+    hf_kv_ring next = *ring;
+    if (e == hipSuccess && (flags & HF_STEP_COMMIT)) {
+        next.n_committed += d->C;
+        const int evict = next.n_committed - (d->W - d->C);
+        if (evict > 0) {
+            e = enqueue_absorb_ring(d, ring, evict, S, z, ws, stream);
+            next.head = (next.head + evict) % d->W;
+            next.n_committed -= evict;
+        }
+    }
+    if (e == hipSuccess) e = record(events, 4, stream);
+    if (e != hipSuccess) return hip_status(e, "hybrid step launch");
+    *ring = next;
+    return ok();
+}
+
+}  // extern "C"

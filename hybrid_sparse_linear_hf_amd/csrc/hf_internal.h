@@ -1,0 +1,110 @@
+// Internal declarations shared by the HIP sources of libhf (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/hf.h"
+
+namespace hf {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// ------------------------------------------------------------------ bf16 helpers
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// elu(x) + 1
+__device__ __forceinline__ float phi_f32(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+// ------------------------------------------------------------------ matrix cores
+// D = A * B + C on a 32x32x16 bf16 tile.  Lane l supplies A row (l % 32) and B column
+// (l % 32), 8 contraction elements each (the same 8 for A and B); the accumulator of
+// lane l holds rows 8*(i/4) + 4*(l/32) + (i%4), i = 0..15, of column l % 32.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Accumulator rows held by a lane are {8*(i/4) + 4*g + i%4}.  Feeding operand row
+// perm32(m) from lane m makes lane group g hold the 16 CONSECUTIVE logical rows
+// 16*g + i, i = 0..15, in accumulator slot i.
+__device__ __forceinline__ int perm32(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
+
+// ------------------------------------------------------------------ ring addressing
+
+struct RingView {
+    const uint16_t *k;   // [BH][W][T][D]
+    const uint16_t *vt;  // [BH][W][D][T]
+    int W, T, D, head;
+};
+
+// Slot of logical window frame f.
+__device__ __forceinline__ int ring_slot(const RingView &r, int f) {
+    int s = r.head + f;
+    return s >= r.W ? s - r.W : s;
+}
+
+}  // namespace hf
+
+// ------------------------------------------------------------------ host-side launch API
+// (implemented in the .hip files, called from hf_api.cpp)
+
+struct hf_select_args {
+    int BH, D, T, W, head, Nq, Nk, bq, bk, nqb, nkb, top_k;
+    const uint16_t *q, *ring_k;
+    double *qbar, *kbar;       // workspace
+    int32_t *idx;
+    double *scores;            // may be null
+};
+hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s);
+
+struct hf_attn_args {
+    int BH, D, T, W, head, Nq, Nk, bq, bk, nqb, nkb, top_k;
+    const uint16_t *q, *ring_k, *ring_vt;
+    const int32_t *idx;
+    const float *S, *z;        // may be null (sparse part only)
+    uint16_t *st;              // workspace: S^T in bf16 [BH][D][D]
+    float eps;
+    float *out;
+};
+hipError_t hf_launch_sparse_attn(const hf_attn_args &a, hipStream_t s);
+
+struct hf_absorb_args {
+    int BH, D;
+    int64_t n_tok;
+    // source: either plain row-major buffers (k, v) or ring frames (ring_k, ring_vt, W, T, head)
+    const uint16_t *k, *v;
+    const uint16_t *ring_k, *ring_vt;
+    int W, T, head;
+    float *S, *z;
+    float *part;               // workspace partials
+    uint32_t *counters;        // workspace counters (zero between calls)
+};
+size_t hf_absorb_required_bytes(int BH, int D, int64_t n_tok);
+size_t hf_absorb_workspace_bytes(int BH, int D);
+hipError_t hf_launch_absorb(const hf_absorb_args &a, hipStream_t s);
+
+struct hf_append_args {
+    int BH, D, T, W, head, first_frame, C;
+    const uint16_t *k_cur, *v_cur;
+    uint16_t *ring_k, *ring_vt;
+};
+hipError_t hf_launch_ring_append(const hf_append_args &a, hipStream_t s);

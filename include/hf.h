@@ -1,0 +1,194 @@
+/*
+ * hf.h -- C ABI of the MI355X (gfx950) hybrid attention step of Hybrid Forcing.
+ *
+ * The method (pages, cited by title and section):
+ *   [HF-de]  gist.science (German) summary of "Long-Horizon Streaming Video Generation
+ *            via Hybrid Attention with Decoupled Distillation", §2.A "Hybride
+ *            Aufmerksamkeitsmechanismen".
+ *   [HF-pt]  gist.science (Portuguese) summary of the same paper, §2.A "Mecanismo de
+ *            Atenção Híbrida" (2.A.1 linear temporal attention, 2.A.2 sparse window
+ *            attention, "Resultado").
+ *   [HF-abs] the paper's English abstract (arxivdaily.com page of the same paper).
+ *   [LF-de]  gist.science (German) summary of "Light Forcing: Accelerating Autoregressive
+ *            Video Diffusion via Sparse Attention", §2.2 "Hierarchische Spärliche
+ *            Attention" (mean-pooled block tokens).
+ *
+ * Each chunk of latent frames attends to a sliding window of recent frames kept in a
+ * KV cache.  Its output is the sum of (a) block-sparse softmax attention over the
+ * window, computed only on the top-k key blocks of each query block, and (b) a linear
+ * attention readout from a compact state (S, z) that absorbs the tokens evicted from
+ * the window ([HF-de] §2.A, [HF-pt] §2.A, [HF-abs]).
+ *
+ * Readings where the pages are silent (the same ones the fp64 oracle takes):
+ *   feature map phi(x) = elu(x) + 1; readout phi(q)^T S / (phi(q) . z + eps), eps as
+ *   passed (1e-6 by default); softmax and block scores scaled by 1/sqrt(D); block score
+ *   = mean-pooled query block . mean-pooled key block; top-k ties go to the lower key
+ *   block index; no causal mask inside the window; the two branches are summed with no
+ *   weight; a step reads (S, z) as they were before its own evictions.
+ *
+ * ---------------------------------------------------------------------------------
+ * Conventions shared by every entry point
+ *
+ *  * Memory: every pointer argument named *_dev is DEVICE memory owned by the caller;
+ *    hf_dims / hf_kv_ring structs and `bytes` out-parameters are HOST memory.  The
+ *    library never allocates, frees, or keeps a pointer after returning.
+ *  * Asynchrony: work is enqueued on `stream` (0 = the null stream) and the call
+ *    returns without waiting.  A device fault surfaces at the caller's next
+ *    synchronisation.
+ *  * Validation happens before anything is enqueued.  A call that returns an error has
+ *    enqueued nothing and changed nothing (buffers and ring descriptor untouched); the
+ *    reason is kept in a thread-local string read by hf_last_error().
+ *  * Dtypes: Q/K/V are bfloat16 (raw 16-bit storage); S, z and the output are fp32;
+ *    block indices int32.
+ *  * Supported shapes: D in {64, 128}; bq in {16, 32, 64}; bk in {16, 32, 64, 128};
+ *    T a positive multiple of 8; 1 <= C <= W; B, H >= 1; total sizes below 2^31
+ *    elements per tensor.  Anything else -> HF_ERR_UNSUPPORTED or HF_ERR_SHAPE.
+ *  * Determinism: no floating-point atomics; the same inputs give bit-identical
+ *    outputs, independent of the ring's physical head position.
+ *  * Overlap: calls on different streams must not share an output or workspace buffer.
+ * ---------------------------------------------------------------------------------
+ */
+#ifndef HF_H
+#define HF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HF_ABI_VERSION 1
+
+typedef enum {
+    HF_OK = 0,
+    HF_ERR_NULL = 1,         /* a required pointer is NULL */
+    HF_ERR_SHAPE = 2,        /* inconsistent sizes (e.g. top_k > number of key blocks) */
+    HF_ERR_UNSUPPORTED = 3,  /* valid but not supported (D, block sizes, T % 8 != 0) */
+    HF_ERR_RING_STATE = 4,   /* ring descriptor out of range (head, n_committed) */
+    HF_ERR_WORKSPACE = 5,    /* workspace missing or smaller than hf_workspace_size() */
+    HF_ERR_HIP = 6           /* a HIP launch failed (message holds hipGetErrorString) */
+} hf_status;
+
+/* Problem geometry (host struct).
+ *   B  independent streams (batch)         H  heads            D  head dim (64 | 128)
+ *   T  tokens per latent frame             C  frames per chunk (the current chunk)
+ *   W  window frames incl. the current chunk (the sliding window of [HF-de] §1)
+ *   bq, bk  query / key block sizes of the block-sparse attention ([HF-de] §2.A). */
+typedef struct {
+    int32_t B, H, D;
+    int32_t T, C, W;
+    int32_t bq, bk;
+} hf_dims;
+
+/* KV cache as a ring of W frame slots (the windowed KV cache with eviction of
+ * [HF-de] §1 / [HF-pt] §1).
+ *   k_dev   bf16 [B][H][W][T][D]  key frames, row-major (D contiguous)
+ *   vt_dev  bf16 [B][H][W][D][T]  value frames stored TRANSPOSED per frame (T contiguous),
+ *                                 the layout the matrix cores read them in
+ *   head         slot holding the oldest frame of the window, 0 <= head < W
+ *   n_committed  frames already committed to the window, 0 <= n_committed <= W - C
+ * Logical window frame f (0 = oldest) lives in slot (head + f) % W.  A step's window
+ * is the n_committed committed frames followed by the C frames of the current chunk
+ * (logical frames n_committed .. n_committed+C-1), so it holds
+ * Nk = (n_committed + C) * T keys; key j is token j % T of logical frame j / T.
+ * Query blocks cut the current chunk's Nq = C*T queries; key blocks cut the window,
+ * across frame boundaries; a short last block is allowed. */
+typedef struct {
+    void *k_dev;
+    void *vt_dev;
+    int32_t head;
+    int32_t n_committed;
+} hf_kv_ring;
+
+/* hf_hybrid_step flag: after attending, commit the current chunk to the window and
+ * evict (absorb into S, z) the oldest frames beyond W - C committed frames. */
+#define HF_STEP_COMMIT 1u
+
+/* Optional timing hooks for hf_hybrid_step: any non-NULL event is recorded on the
+ * step's stream at that point (begin, after append, after select, after attention,
+ * after absorb).  Events must have been created by the caller with hipEventCreate. */
+typedef struct {
+    hipEvent_t ev[5];
+} hf_step_events;
+
+int hf_abi_version(void);
+const char *hf_status_str(hf_status s);
+/* Detail of the last failed call on this thread ("" if none). */
+const char *hf_last_error(void);
+
+/* Bytes of device workspace the entry points need for these dims and top_k, for a
+ * window of up to W frames (host call, no GPU work).  The same workspace serves every
+ * entry point; it holds transient per-call data only and needs no initialisation. */
+hf_status hf_workspace_size(const hf_dims *d, int32_t top_k, size_t *bytes);
+
+/* Copy the current chunk into the ring: k_cur_dev, v_cur_dev are bf16 [B][H][C*T][D]
+ * (row-major).  Frame c of the chunk goes to logical frame n_committed + c; values are
+ * written transposed (see hf_kv_ring).  The descriptor is not changed. */
+hf_status hf_ring_append(const hf_dims *d, const hf_kv_ring *ring, const void *k_cur_dev,
+                         const void *v_cur_dev, hipStream_t stream);
+
+/* Block selection ([HF-de] §2.A "nur die wichtigsten Blöcke (Top-K)", [HF-pt] §2.A.2
+ * "blocos mais ativos"; pooling as [LF-de] §2.2 token compression).
+ * For each (b, h, query block i): qbar_i = mean of Q over block i, kbar_j = mean of the
+ * window keys over key block j, score s_ij = qbar_i . kbar_j / sqrt(D) (pooled and
+ * scored in fp64); keep the top_k largest, ties to the lower j, written in ASCENDING
+ * order.
+ *   q_dev          bf16 [B][H][C*T][D] current chunk queries
+ *   idx_dev        int32 [B][H][n_qb][top_k] out, n_qb = ceil(C*T/bq)
+ *   scores_dev     fp64 [B][H][n_qb][n_kb] out (may be NULL), n_kb = ceil(Nk/bk)
+ * Requires 1 <= top_k <= n_kb <= 4096 (HF_ERR_SHAPE otherwise). */
+hf_status hf_block_select(const hf_dims *d, const void *q_dev, const hf_kv_ring *ring, int32_t top_k,
+                          int32_t *idx_dev, double *scores_dev, void *workspace_dev,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* Block-sparse window attention plus linear readout ([HF-de] §2.A, [HF-pt] §2.A.1,
+ * 2.A.2 and "Resultado"; [HF-abs]).
+ * out[b,h,t,:] = sum_{u in kept blocks of t's block} softmax_u(q_t.k_u / sqrt(D)) v_u
+ *              + phi(q_t)^T S[b,h] / (phi(q_t) . z[b,h] + eps)
+ *   q_dev    bf16 [B][H][C*T][D]
+ *   idx_dev  int32 [B][H][n_qb][top_k]: kept key blocks, each in [0, n_kb); duplicates
+ *            are not allowed (hf_block_select's output qualifies)
+ *   S_dev    fp32 [B][H][D][D] (S[a][c]) and z_dev fp32 [B][H][D]: the linear state;
+ *            both NULL -> the linear branch is skipped (sparse part only)
+ *   out_dev  fp32 [B][H][C*T][D] out
+ * Numerics: bf16 matrix-core products with fp32 accumulation and fp32 online softmax;
+ * the readout multiplies bf16-rounded phi(q) and S with fp32 accumulation. */
+hf_status hf_sparse_window_attn(const hf_dims *d, const void *q_dev, const hf_kv_ring *ring,
+                                const int32_t *idx_dev, int32_t top_k, const float *S_dev,
+                                const float *z_dev, float eps, float *out_dev, void *workspace_dev,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* Absorb evicted tokens into the state ([HF-abs]: a compact key-value state that
+ * incrementally absorbs evicted tokens; [HF-de] §2.A; [HF-pt] §2.A.1):
+ *   S[a][c] += sum_u phi(K_u[a]) V_u[c],   z[a] += sum_u phi(K_u[a])
+ *   k_ev_dev, v_ev_dev  bf16 [B][H][n_tok][D] row-major evicted tokens
+ *   S_dev, z_dev        fp32 state, updated in place
+ * n_tok >= 0 (0 is a no-op).  Products use bf16 hi+lo halves of phi(K) so S keeps
+ * fp32-grade accuracy; the token sum is split over workgroups and reduced in a fixed
+ * order. */
+hf_status hf_linear_absorb(const hf_dims *d, const void *k_ev_dev, const void *v_ev_dev, int64_t n_tok,
+                           float *S_dev, float *z_dev, void *workspace_dev, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* One hybrid attention step on the ring:
+ *   1. if k_cur_dev and v_cur_dev are given: hf_ring_append (else the caller has
+ *      already written the current chunk into its slots);
+ *   2. hf_block_select -> idx_dev ([B][H][n_qb][top_k], also an output);
+ *   3. hf_sparse_window_attn with (S, z) as they are -> out_dev;
+ *   4. if flags & HF_STEP_COMMIT: n_committed += C; if that exceeds W - C, the
+ *      e = n_committed - (W - C) oldest frames are absorbed into (S, z) as by
+ *      hf_linear_absorb, then head = (head + e) % W and n_committed -= e.
+ * `ring` is updated on success only.  S_dev/z_dev may be NULL only without
+ * HF_STEP_COMMIT (sparse part only).  `events` may be NULL. */
+hf_status hf_hybrid_step(const hf_dims *d, const void *q_dev, const void *k_cur_dev, const void *v_cur_dev,
+                         hf_kv_ring *ring, int32_t top_k, uint32_t flags, float *S_dev, float *z_dev,
+                         float eps, int32_t *idx_dev, float *out_dev, void *workspace_dev,
+                         size_t workspace_bytes, const hf_step_events *events, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HF_H */

@@ -1,0 +1,148 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, and rejects
+bad arguments before enqueuing anything (so these calls never reach the device)."""
+
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import hybrid_sparse_linear_hf_amd as hf
+from hybrid_sparse_linear_hf_amd import _lib
+
+ROOT = Path(__file__).resolve().parents[1]
+FAKE = 0x10000  # never dereferenced: validation fails before any device work
+
+
+def declared_symbols():
+    text = (ROOT / "include" / "hf.h").read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hf_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for s in ("hf_block_select", "hf_sparse_window_attn", "hf_linear_absorb", "hf_hybrid_step", "hf_ring_append",
+              "hf_workspace_size", "hf_last_error", "hf_status_str", "hf_abi_version"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    missing = [s for s in declared_symbols() if not hasattr(L, s)]
+    assert not missing, missing
+    assert hf.abi_version() == 1
+    assert L.hf_status_str(2) == b"HF_ERR_SHAPE"
+
+
+def geom(**kw):
+    base = dict(B=1, H=12, D=128, T=1560, C=3, W=6, bq=64, bk=64)
+    base.update(kw)
+    return _lib.Geometry(**base)
+
+
+def ring_desc(head=0, n_committed=3):
+    return _lib.KVRing(FAKE, FAKE, head, n_committed)
+
+
+def call_select(g, ring, top_k=37, ws_bytes=None, q=FAKE, idx=FAKE):
+    L = _lib.lib()
+    ws_bytes = hf.workspace_size(g) if ws_bytes is None else ws_bytes
+    return L.hf_block_select(ctypes.byref(g.dims()), q, ctypes.byref(ring), top_k, idx, None, FAKE, ws_bytes, None)
+
+
+def last_error():
+    return _lib.lib().hf_last_error().decode()
+
+
+def test_workspace_size_scales():
+    small = hf.workspace_size(geom(H=1))
+    big = hf.workspace_size(geom(H=12))
+    assert 0 < small < big
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), 3), (dict(D=256), 3), (dict(T=1561), 3), (dict(T=0), 3), (dict(C=7), 2), (dict(C=0), 2),
+    (dict(bq=48), 3), (dict(bk=8), 3), (dict(B=0), 2), (dict(W=21, bk=16), 3),
+])
+def test_bad_dims_rejected(kw, status):
+    g = geom(**kw)
+    st = call_select(g, ring_desc(n_committed=0), top_k=1, ws_bytes=1 << 30)
+    assert st == status, last_error()
+    assert last_error()
+
+
+def test_top_k_bounds():
+    g = geom()
+    assert call_select(g, ring_desc(), top_k=0) == 2
+    assert call_select(g, ring_desc(), top_k=148) == 2  # n_kb = 147 for a full window
+    assert "top_k" in last_error()
+    # a window that is not yet full has fewer key blocks
+    assert call_select(g, ring_desc(n_committed=0), top_k=75) == 2  # n_kb = 74 with only the chunk
+
+
+def test_ring_state_rejected():
+    g = geom()
+    assert call_select(g, ring_desc(head=6)) == 4
+    assert call_select(g, ring_desc(head=-1)) == 4
+    assert call_select(g, ring_desc(n_committed=4)) == 4
+    assert call_select(g, _lib.KVRing(None, FAKE, 0, 3)) == 1
+
+
+def test_null_and_workspace_rejected():
+    g = geom()
+    assert call_select(g, ring_desc(), q=None) == 1
+    assert call_select(g, ring_desc(), idx=None) == 1
+    assert call_select(g, ring_desc(), ws_bytes=100) == 5
+    assert "workspace" in last_error()
+
+
+def test_attn_and_step_validation():
+    L = _lib.lib()
+    g = geom()
+    d, r = g.dims(), ring_desc()
+    ws = hf.workspace_size(g)
+    # S without z
+    assert L.hf_sparse_window_attn(ctypes.byref(d), FAKE, ctypes.byref(r), FAKE, 37, FAKE, None, 1e-6, FAKE, FAKE,
+                                   ws, None) == 1
+    # negative eps
+    assert L.hf_sparse_window_attn(ctypes.byref(d), FAKE, ctypes.byref(r), FAKE, 37, FAKE, FAKE, -1.0, FAKE, FAKE,
+                                   ws, None) == 2
+    # commit without a state
+    assert L.hf_hybrid_step(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(r), 37, 1, None, None, 1e-6, FAKE, FAKE,
+                            FAKE, ws, None, None) == 1
+    # only one of k_cur / v_cur
+    assert L.hf_hybrid_step(ctypes.byref(d), FAKE, FAKE, None, ctypes.byref(r), 37, 0, None, None, 1e-6, FAKE, FAKE,
+                            FAKE, ws, None, None) == 1
+    # unknown flag
+    assert L.hf_hybrid_step(ctypes.byref(d), FAKE, None, None, ctypes.byref(r), 37, 4, FAKE, FAKE, 1e-6, FAKE, FAKE,
+                            FAKE, ws, None, None) == 2
+    # a failed call leaves the ring descriptor untouched
+    assert (r.head, r.n_committed) == (0, 3)
+
+
+def test_absorb_validation():
+    L = _lib.lib()
+    g = geom()
+    ws = hf.workspace_size(g)
+    assert L.hf_linear_absorb(ctypes.byref(g.dims()), FAKE, FAKE, -1, FAKE, FAKE, FAKE, ws, None) == 2
+    assert L.hf_linear_absorb(ctypes.byref(g.dims()), None, FAKE, 10, FAKE, FAKE, FAKE, ws, None) == 1
+    assert L.hf_linear_absorb(ctypes.byref(g.dims()), FAKE, FAKE, 10, None, FAKE, FAKE, ws, None) == 1
+    assert L.hf_linear_absorb(ctypes.byref(g.dims()), FAKE, FAKE, 10, FAKE, FAKE, FAKE, 10, None) == 5
+
+
+@pytest.mark.parametrize("B,H,D", [(1, 1, 64), (1, 3, 128), (1, 12, 128), (4, 12, 128), (2, 5, 64)])
+def test_workspace_covers_absorb_partials(B, H, D):
+    """Regression: the absorb splits each 64x64 state tile's token range over
+    P = min(#64-token chunks, max(1, round(256 / #tiles))) workgroups and stores P partial
+    tiles (16 KiB each) plus P partial z slices per 64 rows; the workspace must hold them for
+    every token count, including counts whose chunk number exceeds 2^31 / 64 in the sizing."""
+    g = geom(B=B, H=H, D=D, T=1560, W=6)
+    ws = hf.workspace_size(g)
+    tiles = B * H * (D // 64) ** 2
+    pmax = max(1, (256 + tiles // 2) // tiles)
+    for n_tok in (1, 64, 200, 4680, 28080, 1 << 20):
+        nch = -(-n_tok // 64)
+        P = min(nch, pmax)
+        need = tiles * P * 64 * 64 * 4 + B * H * (D // 64) * P * 64 * 4 + tiles * 4
+        assert ws >= need, (n_tok, ws, need)

@@ -39,7 +39,7 @@ class KVRing(ctypes.Structure):
 
 
 class StepEvents(ctypes.Structure):
-    _fields_ = [("ev", ctypes.c_void_p * 5)]
+    _fields_ = [("ev", ctypes.c_void_p * 6)]
 
 
 _lib = None
@@ -148,7 +148,7 @@ def workspace_size(g: Geometry, top_k: int = 1) -> int:
 
 
 def new_workspace(g: Geometry, device="cuda") -> torch.Tensor:
-    """Zero-filled workspace (the absorb reduction keeps its counters zero between calls)."""
+    """Device workspace for every entry point (contents need no initialisation)."""
     return torch.zeros(workspace_size(g), dtype=torch.uint8, device=device)
 
 
@@ -180,7 +180,7 @@ def hf_linear_absorb(g: Geometry, k_ev, v_ev, n_tok: int, S, z, ws, stream=None)
 
 def hf_hybrid_step(g: Geometry, q, k_cur, v_cur, ring: Ring, top_k: int, flags: int, S, z, idx, out, ws,
                    eps=1e-6, events=None, stream=None) -> None:
-    """`events`: None or a sequence of 5 raw hipEvent_t handles (ints or None)."""
+    """`events`: None or a sequence of 6 raw hipEvent_t handles (ints or None)."""
     ev = None
     if events is not None:
         ev = StepEvents()

@@ -44,9 +44,14 @@ hf_status check_dims(const hf_dims *d) {
         return fail(HF_ERR_UNSUPPORTED, "bk=%d (supported: 16, 32, 64, 128)", d->bk);
     const int64_t ring = (int64_t)d->B * d->H * d->W * d->T * d->D;
     if (ring >= kMaxElems) return fail(HF_ERR_UNSUPPORTED, "ring of %lld elements exceeds 2^31", (long long)ring);
-    if (cdiv((int64_t)d->W * d->T, d->bk) > kMaxKeyBlocks)
-        return fail(HF_ERR_UNSUPPORTED, "window of %lld key blocks exceeds %d", (long long)cdiv((int64_t)d->W * d->T, d->bk),
-                    kMaxKeyBlocks);
+    const int64_t nkb = cdiv((int64_t)d->W * d->T, d->bk);
+    if (nkb > kMaxKeyBlocks)
+        return fail(HF_ERR_UNSUPPORTED, "window of %lld key blocks exceeds %d", (long long)nkb, kMaxKeyBlocks);
+    // the attention workgroup keeps its list of kept 32-key subtiles in LDS
+    const int64_t list_bytes = nkb * cdiv(d->bk, 32) * 8 + 2 * nkb;
+    if (list_bytes > 24576)
+        return fail(HF_ERR_UNSUPPORTED, "window of %lld keys in blocks of %d needs a %lld-byte subtile list (max 24576)",
+                    (long long)d->W * d->T, d->bk, (long long)list_bytes);
     return HF_OK;
 }
 
@@ -74,9 +79,9 @@ Geometry geometry(const hf_dims *d, const hf_kv_ring *r) {
 }
 
 // Workspace layout (offsets 256-byte aligned):
-//   [absorb counters | absorb partials]  [qbar fp64]  [kbar fp64]  [S^T bf16]
+//   [absorb partials]  [qbar fp64]  [kbar fp64]  [scores fp64]  [S^T bf16]  [z copy fp32]
 struct WsLayout {
-    size_t absorb, qbar, kbar, st, total;
+    size_t absorb, qbar, kbar, sc, st, zc, total;
 };
 
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -89,8 +94,10 @@ WsLayout ws_layout(const hf_dims *d) {
     w.absorb = 0;
     w.qbar = al(hf_absorb_workspace_bytes(BH, d->D));
     w.kbar = w.qbar + al((size_t)BH * nqb * d->D * sizeof(double));
-    w.st = w.kbar + al((size_t)BH * nkb * d->D * sizeof(double));
-    w.total = w.st + al((size_t)BH * d->D * d->D * sizeof(uint16_t));
+    w.sc = w.kbar + al((size_t)BH * nkb * d->D * sizeof(double));
+    w.st = w.sc + al((size_t)BH * nqb * nkb * sizeof(double));
+    w.zc = w.st + al((size_t)BH * d->D * d->D * sizeof(uint16_t));
+    w.total = w.zc + al((size_t)BH * d->D * sizeof(float));
     return w;
 }
 
@@ -102,13 +109,6 @@ hf_status check_ws(const hf_dims *d, void *ws, size_t bytes) {
 }
 
 char *wsp(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
-
-// absorb counters + partials live at the start of the workspace
-void absorb_ws(void *ws, int BH, int D, float **part, uint32_t **counters) {
-    const size_t nctr = (size_t)BH * (D / 64) * (D / 64);
-    *counters = reinterpret_cast<uint32_t *>(ws);
-    *part = reinterpret_cast<float *>(wsp(ws, al(nctr * sizeof(uint32_t))));
-}
 
 hf_status hip_status(hipError_t e, const char *what) {
     if (e != hipSuccess) return fail(HF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -154,13 +154,32 @@ hipError_t enqueue_select(const hf_dims *d, const void *q, const hf_kv_ring *r, 
     a.ring_k = static_cast<const uint16_t *>(r->k_dev);
     a.qbar = reinterpret_cast<double *>(wsp(ws, L.qbar));
     a.kbar = reinterpret_cast<double *>(wsp(ws, L.kbar));
+    a.sc = reinterpret_cast<double *>(wsp(ws, L.sc));
     a.idx = idx;
     a.scores = scores;
     return hf_launch_block_select(a, s);
 }
 
+// The state pass of a step: readout operands (S^T bf16, z copy) from the state as it is,
+// and, when `absorb_tokens` > 0, the absorb partials already in the workspace added in.
+hipError_t enqueue_state(const hf_dims *d, float *S, float *z, bool readout, int64_t absorb_tokens, void *ws,
+                         hipStream_t s) {
+    const WsLayout L = ws_layout(d);
+    hf_state_args a{};
+    a.BH = d->B * d->H;
+    a.D = d->D;
+    a.S = S;
+    a.z = z;
+    a.part = absorb_tokens > 0 ? reinterpret_cast<const float *>(wsp(ws, L.absorb)) : nullptr;
+    a.P = absorb_tokens > 0 ? hf_absorb_splits(a.BH, d->D, absorb_tokens) : 0;
+    a.st = readout ? reinterpret_cast<uint16_t *>(wsp(ws, L.st)) : nullptr;
+    a.zc = readout ? reinterpret_cast<float *>(wsp(ws, L.zc)) : nullptr;
+    return hf_launch_state(a, s);
+}
+
+// Attention (+ readout from the prepared S^T / z copy when `readout`).
 hipError_t enqueue_attn(const hf_dims *d, const void *q, const hf_kv_ring *r, const int32_t *idx, int top_k,
-                        const float *S, const float *z, float eps, float *out, void *ws, hipStream_t s) {
+                        bool readout, float eps, float *out, void *ws, hipStream_t s) {
     const Geometry g = geometry(d, r);
     const WsLayout L = ws_layout(d);
     hf_attn_args a{};
@@ -180,45 +199,36 @@ hipError_t enqueue_attn(const hf_dims *d, const void *q, const hf_kv_ring *r, co
     a.ring_k = static_cast<const uint16_t *>(r->k_dev);
     a.ring_vt = static_cast<const uint16_t *>(r->vt_dev);
     a.idx = idx;
-    a.S = S;
-    a.z = z;
-    a.st = reinterpret_cast<uint16_t *>(wsp(ws, L.st));
+    a.st = readout ? reinterpret_cast<const uint16_t *>(wsp(ws, L.st)) : nullptr;
+    a.zc = readout ? reinterpret_cast<const float *>(wsp(ws, L.zc)) : nullptr;
     a.eps = eps;
     a.out = out;
     return hf_launch_sparse_attn(a, s);
 }
 
-hipError_t enqueue_absorb_plain(const hf_dims *d, const void *k, const void *v, int64_t n_tok, float *S, float *z,
-                                void *ws, hipStream_t s) {
+// Absorb partial sums into the workspace: from row-major buffers (k, v) or from the e
+// oldest frames of the ring (ring != null).
+hipError_t enqueue_absorb_partial(const hf_dims *d, const void *k, const void *v, int64_t n_tok,
+                                  const hf_kv_ring *ring, void *ws, hipStream_t s) {
     hf_absorb_args a{};
     a.BH = d->B * d->H;
     a.D = d->D;
     a.n_tok = n_tok;
-    a.k = static_cast<const uint16_t *>(k);
-    a.v = static_cast<const uint16_t *>(v);
-    a.S = S;
-    a.z = z;
-    absorb_ws(ws, a.BH, d->D, &a.part, &a.counters);
-    if (hf_absorb_required_bytes(a.BH, a.D, n_tok) > hf_absorb_workspace_bytes(a.BH, a.D)) return hipErrorInvalidValue;
-    return hf_launch_absorb(a, s);
-}
-
-hipError_t enqueue_absorb_ring(const hf_dims *d, const hf_kv_ring *r, int e_frames, float *S, float *z, void *ws,
-                               hipStream_t s) {
-    hf_absorb_args a{};
-    a.BH = d->B * d->H;
-    a.D = d->D;
-    a.n_tok = (int64_t)e_frames * d->T;
-    a.ring_k = static_cast<const uint16_t *>(r->k_dev);
-    a.ring_vt = static_cast<const uint16_t *>(r->vt_dev);
-    a.W = d->W;
-    a.T = d->T;
-    a.head = r->head;
-    a.S = S;
-    a.z = z;
-    absorb_ws(ws, a.BH, d->D, &a.part, &a.counters);
-    if (hf_absorb_required_bytes(a.BH, a.D, a.n_tok) > hf_absorb_workspace_bytes(a.BH, a.D)) return hipErrorInvalidValue;
-    return hf_launch_absorb(a, s);
+    if (ring) {
+        a.ring_k = static_cast<const uint16_t *>(ring->k_dev);
+        a.ring_vt = static_cast<const uint16_t *>(ring->vt_dev);
+        a.W = d->W;
+        a.T = d->T;
+        a.head = ring->head;
+    } else {
+        a.k = static_cast<const uint16_t *>(k);
+        a.v = static_cast<const uint16_t *>(v);
+    }
+    a.part = reinterpret_cast<float *>(wsp(ws, ws_layout(d).absorb));
+    if (hf_absorb_partial_floats(a.BH, a.D, hf_absorb_splits(a.BH, a.D, n_tok)) * sizeof(float) >
+        hf_absorb_workspace_bytes(a.BH, a.D))
+        return hipErrorInvalidValue;
+    return hf_launch_absorb_partial(a, s);
 }
 
 hipError_t record(const hf_step_events *ev, int i, hipStream_t s) {
@@ -293,7 +303,9 @@ hf_status hf_sparse_window_attn(const hf_dims *d, const void *q, const hf_kv_rin
     if (top_k < 1 || top_k > g.nkb) return fail(HF_ERR_SHAPE, "top_k=%d outside [1, n_kb=%d]", top_k, g.nkb);
     st = check_ws(d, ws, ws_bytes);
     if (st != HF_OK) return st;
-    st = hip_status(enqueue_attn(d, q, ring, idx, top_k, S, z, eps, out, ws, stream), "sparse attention launch");
+    hipError_t e = S ? enqueue_state(d, const_cast<float *>(S), const_cast<float *>(z), true, 0, ws, stream) : hipSuccess;
+    if (e == hipSuccess) e = enqueue_attn(d, q, ring, idx, top_k, S != nullptr, eps, out, ws, stream);
+    st = hip_status(e, "sparse attention launch");
     return st == HF_OK ? ok() : st;
 }
 
@@ -308,7 +320,10 @@ hf_status hf_linear_absorb(const hf_dims *d, const void *k_ev, const void *v_ev,
         return fail(HF_ERR_UNSUPPORTED, "evicted tensors exceed 2^31 elements");
     st = check_ws(d, ws, ws_bytes);
     if (st != HF_OK) return st;
-    st = hip_status(enqueue_absorb_plain(d, k_ev, v_ev, n_tok, S, z, ws, stream), "absorb launch");
+    if (n_tok == 0) return ok();
+    hipError_t e = enqueue_absorb_partial(d, k_ev, v_ev, n_tok, nullptr, ws, stream);
+    if (e == hipSuccess) e = enqueue_state(d, S, z, false, n_tok, ws, stream);
+    st = hip_status(e, "absorb launch");
     return st == HF_OK ? ok() : st;
 }
 
@@ -329,24 +344,30 @@ hf_status hf_hybrid_step(const hf_dims *d, const void *q, const void *k_cur, con
     st = check_ws(d, ws, ws_bytes);
     if (st != HF_OK) return st;
 
+    // Order: append; absorb partials of the frames this step will evict (they stay in the
+    // ring until the next append); select; state pass (readout operands from the state as
+    // it is, then the partials added in); attention with the fused readout.
+    hf_kv_ring next = *ring;
+    int evict = 0;
+    if (flags & HF_STEP_COMMIT) {
+        next.n_committed += d->C;
+        evict = next.n_committed - (d->W - d->C);
+        if (evict < 0) evict = 0;
+        next.head = (next.head + evict) % d->W;
+        next.n_committed -= evict;
+    }
+    const int64_t evict_tok = (int64_t)evict * d->T;
     hipError_t e = record(events, 0, stream);
     if (e == hipSuccess && k_cur) e = enqueue_append(d, ring, k_cur, v_cur, stream);
     if (e == hipSuccess) e = record(events, 1, stream);
-    if (e == hipSuccess) e = enqueue_select(d, q, ring, top_k, idx, nullptr, ws, stream);
+    if (e == hipSuccess && evict_tok > 0) e = enqueue_absorb_partial(d, nullptr, nullptr, evict_tok, ring, ws, stream);
     if (e == hipSuccess) e = record(events, 2, stream);
-    if (e == hipSuccess) e = enqueue_attn(d, q, ring, idx, top_k, S, z, eps, out, ws, stream);
+    if (e == hipSuccess) e = enqueue_select(d, q, ring, top_k, idx, nullptr, ws, stream);
     if (e == hipSuccess) e = record(events, 3, stream);
-    hf_kv_ring next = *ring;
-    if (e == hipSuccess && (flags & HF_STEP_COMMIT)) {
-        next.n_committed += d->C;
-        const int evict = next.n_committed - (d->W - d->C);
-        if (evict > 0) {
-            e = enqueue_absorb_ring(d, ring, evict, S, z, ws, stream);
-            next.head = (next.head + evict) % d->W;
-            next.n_committed -= evict;
-        }
-    }
+    if (e == hipSuccess && S) e = enqueue_state(d, S, z, true, evict_tok, ws, stream);
     if (e == hipSuccess) e = record(events, 4, stream);
+    if (e == hipSuccess) e = enqueue_attn(d, q, ring, idx, top_k, S != nullptr, eps, out, ws, stream);
+    if (e == hipSuccess) e = record(events, 5, stream);
     if (e != hipSuccess) return hip_status(e, "hybrid step launch");
     *ring = next;
     return ok();

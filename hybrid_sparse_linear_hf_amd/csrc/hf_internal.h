@@ -19,21 +19,32 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Two fp32 -> packed bf16 pair (round to nearest even; one v_cvt_pk_bf16_f32), lo in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
+// fp32 -> bf16 bits (round to nearest even).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.f) & 0xFFFFu; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // elu(x) + 1
 __device__ __forceinline__ float phi_f32(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+// n / d for 0 <= n < 2^31 with magic = ceil(2^32 / d) (one correction step suffices).
+__host__ __device__ inline uint32_t div_magic(uint32_t d) {
+    return (uint32_t)((0x100000000ull + (uint64_t)d - 1) / (uint64_t)d);
+}
+__device__ __forceinline__ int fast_div(int n, uint32_t magic, int d) {
+    int q = (int)__umulhi((uint32_t)n, magic);
+    q -= (q * d > n);
+    return q;
+}
 
 // ------------------------------------------------------------------ matrix cores
 // D = A * B + C on a 32x32x16 bf16 tile.  Lane l supplies A row (l % 32) and B column
@@ -70,7 +81,8 @@ __device__ __forceinline__ int ring_slot(const RingView &r, int f) {
 struct hf_select_args {
     int BH, D, T, W, head, Nq, Nk, bq, bk, nqb, nkb, top_k;
     const uint16_t *q, *ring_k;
-    double *qbar, *kbar;       // workspace
+    double *qbar, *kbar;       // workspace: pooled blocks
+    double *sc;                // workspace: scores [BH][nqb][nkb]
     int32_t *idx;
     double *scores;            // may be null
 };
@@ -80,8 +92,8 @@ struct hf_attn_args {
     int BH, D, T, W, head, Nq, Nk, bq, bk, nqb, nkb, top_k;
     const uint16_t *q, *ring_k, *ring_vt;
     const int32_t *idx;
-    const float *S, *z;        // may be null (sparse part only)
-    uint16_t *st;              // workspace: S^T in bf16 [BH][D][D]
+    const uint16_t *st;        // S^T in bf16 [BH][D][D] (null: sparse part only)
+    const float *zc;           // z [BH][D] as read by this step
     float eps;
     float *out;
 };
@@ -94,13 +106,23 @@ struct hf_absorb_args {
     const uint16_t *k, *v;
     const uint16_t *ring_k, *ring_vt;
     int W, T, head;
-    float *S, *z;
-    float *part;               // workspace partials
-    uint32_t *counters;        // workspace counters (zero between calls)
+    uint32_t magicT;           // div_magic(T), set by the launcher
+    float *part;               // workspace: partial sums (hf_absorb_partial_floats floats)
 };
-size_t hf_absorb_required_bytes(int BH, int D, int64_t n_tok);
+int hf_absorb_splits(int BH, int D, int64_t n_tok);
+size_t hf_absorb_partial_floats(int BH, int D, int P);
 size_t hf_absorb_workspace_bytes(int BH, int D);
-hipError_t hf_launch_absorb(const hf_absorb_args &a, hipStream_t s);
+hipError_t hf_launch_absorb_partial(const hf_absorb_args &a, hipStream_t s);
+
+struct hf_state_args {
+    int BH, D;
+    float *S, *z;              // state, read (and updated when part != null)
+    const float *part;         // absorb partials to add (null: none), P splits
+    int P;
+    uint16_t *st;              // out: S^T bf16 of the state as read (null: skip)
+    float *zc;                 // out: copy of z as read (null: skip)
+};
+hipError_t hf_launch_state(const hf_state_args &a, hipStream_t s);
 
 struct hf_append_args {
     int BH, D, T, W, head, first_frame, C;

@@ -5,19 +5,18 @@
 // mean-pooled query block and the mean-pooled key block ([LF-de] §2.2 token
 // compression by mean pooling), scaled by 1/sqrt(D).  Ties go to the lower key block.
 //
-// Two launches:
+// Three launches:
 //   pool_kernel   HBM-bound: one workgroup per query or key block sums its rows in fp64
 //                 (sums of bf16 values are exact in fp64) and stores the block mean.
-//   score_topk    one workgroup per (plane, 4 query blocks): fp64 scores against every
-//                 key block, evaluated as sum_d (qbar_d * kbar_d) in index order with
-//                 separately rounded products and sums, then a wavefront radix select
-//                 of the k-th largest (score, -index) key and an ascending emit.
+//   score_kernel  16 x 16 tiles of fp64 scores, each evaluated as sum_d (qbar_d * kbar_d) in
+//                 index order with separately rounded products and sums (the pooled
+//                 tiles are staged in LDS by one coalesced load).
+//   topk_kernel   one wave per query block: radix select of the k-th largest
+//                 (score, -index) key and an ascending emit of the kept indices.
 #include "hf_internal.h"
 
 namespace hf {
 namespace {
-
-constexpr int kQPerWG = 4;  // query blocks per score_topk workgroup (one wave each)
 
 __device__ __forceinline__ double bf16_to_f64(uint32_t bits) { return (double)__uint_as_float(bits << 16); }
 
@@ -48,6 +47,7 @@ __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
     double acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+#pragma unroll 4
     for (int r = r0 + ro; r < r1; r += kRowsPerPass) {
         const uint16_t *row = is_q ? a.q + ((size_t)bh * a.Nq + r) * D : key_row(a, bh, r);
         const u32x4 w = *reinterpret_cast<const u32x4 *>(row + v * 8);
@@ -74,83 +74,79 @@ __device__ __forceinline__ uint64_t order_key(double s) {
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
+constexpr int kTile = 16;   // score tile: 16 query blocks x 16 key blocks per workgroup
+
+// Scores of a 16 x 16 tile of (query block, key block) pairs: both pooled tiles are staged
+// in LDS with one coalesced load, then each thread forms one dot product in index order.
 template <int D>
-__global__ __launch_bounds__(256) void score_topk_kernel(hf_select_args a, double scale) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    double *qb = reinterpret_cast<double *>(smem);                 // [kQPerWG][D]
-    uint64_t *keys = reinterpret_cast<uint64_t *>(qb + kQPerWG * D);  // [kQPerWG][nkb]
-
-    const int groups = (a.nqb + kQPerWG - 1) / kQPerWG;
-    const int bh = blockIdx.x / groups;
-    const int i0 = (blockIdx.x % groups) * kQPerWG;
-    const int nq = min(kQPerWG, a.nqb - i0);
-
-    for (int e = threadIdx.x; e < kQPerWG * D; e += 256) {
-        const int g = e / D;
-        qb[e] = g < nq ? a.qbar[((size_t)bh * a.nqb + i0 + g) * D + e % D] : 0.0;
+__global__ __launch_bounds__(256) void score_kernel(hf_select_args a, double scale) {
+    __shared__ double qs[kTile][D + 1];
+    __shared__ double ks[kTile][D + 1];
+    const int ti_n = (a.nqb + kTile - 1) / kTile, tj_n = (a.nkb + kTile - 1) / kTile;
+    const int bh = blockIdx.x / (ti_n * tj_n);
+    const int i0 = ((blockIdx.x / tj_n) % ti_n) * kTile, j0 = (blockIdx.x % tj_n) * kTile;
+    for (int e = threadIdx.x; e < kTile * D; e += 256) {
+        const int r = e / D, d = e % D;
+        qs[r][d] = i0 + r < a.nqb ? a.qbar[((size_t)bh * a.nqb + i0 + r) * D + d] : 0.0;
+        ks[r][d] = j0 + r < a.nkb ? a.kbar[((size_t)bh * a.nkb + j0 + r) * D + d] : 0.0;
     }
     __syncthreads();
-
-    // scores: thread per key block, all query blocks of the group at once
-    for (int j = threadIdx.x; j < a.nkb; j += 256) {
-        // products and sums rounded separately (no fused multiply-add), as in the definition
+    const int ti = threadIdx.x / kTile, tj = threadIdx.x % kTile;
+    const int i = i0 + ti, j = j0 + tj;
+    if (i >= a.nqb || j >= a.nkb) return;
+    double acc = 0.0;
+    {
+        // products and sums rounded separately (no fused multiply-add), in index order
 #pragma clang fp contract(off)
-        const double *kb = a.kbar + ((size_t)bh * a.nkb + j) * D;
-        double acc[kQPerWG];
-#pragma unroll
-        for (int g = 0; g < kQPerWG; ++g) acc[g] = 0.0;
-#pragma unroll 1
-        for (int d0 = 0; d0 < D; d0 += 8) {
-            double kv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) kv[e] = kb[d0 + e];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-#pragma unroll
-                for (int g = 0; g < kQPerWG; ++g) acc[g] = acc[g] + qb[g * D + d0 + e] * kv[e];
-        }
-#pragma unroll
-        for (int g = 0; g < kQPerWG; ++g) {
-            if (g < nq) {
-                const double s = acc[g] * scale;
-                if (a.scores) a.scores[((size_t)bh * a.nqb + i0 + g) * a.nkb + j] = s;
-                keys[g * a.nkb + j] = order_key(s);
-            }
-        }
+#pragma unroll 8
+        for (int d = 0; d < D; ++d) acc = acc + qs[ti][d] * ks[tj][d];
+        acc = acc * scale;
     }
-    __syncthreads();
+    a.sc[((size_t)bh * a.nqb + i) * a.nkb + j] = acc;
+    if (a.scores) a.scores[((size_t)bh * a.nqb + i) * a.nkb + j] = acc;
+}
 
+// One wave per (plane, query block): radix select of the k-th largest (score, -index)
+// key, then an ascending emit of the kept block indices.  Lane l holds keys of blocks
+// l, l + 64, ... in registers (KPL of them).
+template <int KPL>
+__global__ __launch_bounds__(256) void topk_kernel(hf_select_args a) {
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    if (wave >= nq) return;
-    const uint64_t *K = keys + wave * a.nkb;
+    const int row = blockIdx.x * 4 + wave;                    // (bh, i) flattened
+    if (row >= a.BH * a.nqb) return;
+    const double *src = a.sc + (size_t)row * a.nkb;
+    uint64_t key[KPL];
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) {
+        const int j = lane + 64 * e;
+        key[e] = j < a.nkb ? order_key(src[j]) : 0;          // 0 is below every real key
+    }
     const int k = a.top_k;
 
-    // radix select: largest v with #{key >= v} >= k, i.e. the k-th largest key
+    // largest v with #{key >= v} >= k, i.e. the k-th largest key (padding keys are 0 and
+    // never counted once v > 0; v = 0 is only reached if fewer than k real keys exist,
+    // which the caller's 1 <= k <= n_kb rules out)
     uint64_t prefix = 0;
     for (int bit = 63; bit >= 0; --bit) {
         const uint64_t cand = prefix | (1ull << bit);
         int cnt = 0;
-        for (int j0 = 0; j0 < a.nkb; j0 += 64) {
-            const int j = j0 + lane;
-            cnt += __popcll(__ballot(j < a.nkb && K[j] >= cand));
-        }
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) cnt += __popcll(__ballot(key[e] >= cand));
         if (cnt >= k) prefix = cand;
     }
     int gt = 0;
-    for (int j0 = 0; j0 < a.nkb; j0 += 64) {
-        const int j = j0 + lane;
-        gt += __popcll(__ballot(j < a.nkb && K[j] > prefix));
-    }
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) gt += __popcll(__ballot(key[e] > prefix));
     const int need_eq = k - gt;  // >= 1 by construction
-    int32_t *out = a.idx + ((size_t)bh * a.nqb + i0 + wave) * k;
+    int32_t *out = a.idx + (size_t)row * k;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int written = 0, eq_seen = 0;
-    for (int j0 = 0; j0 < a.nkb; j0 += 64) {
-        const int j = j0 + lane;
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) {
+        const int j = lane + 64 * e;
         const bool valid = j < a.nkb;
-        const uint64_t key = valid ? K[j] : 0;
-        const bool is_gt = valid && key > prefix;
-        const bool is_eq = valid && key == prefix;
+        const bool is_gt = valid && key[e] > prefix;
+        const bool is_eq = valid && key[e] == prefix;
         const uint64_t eq_b = __ballot(is_eq);
         const int eq_rank = eq_seen + __popcll(eq_b & lt_mask);
         const bool sel = is_gt || (is_eq && eq_rank < need_eq);
@@ -166,16 +162,24 @@ __global__ __launch_bounds__(256) void score_topk_kernel(hf_select_args a, doubl
 
 hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s) {
     const dim3 grid_pool((unsigned)(a.BH * (a.nqb + a.nkb)));
-    const int groups = (a.nqb + hf::kQPerWG - 1) / hf::kQPerWG;
-    const dim3 grid_sel((unsigned)(a.BH * groups));
-    const size_t smem = (size_t)hf::kQPerWG * a.D * sizeof(double) + (size_t)hf::kQPerWG * a.nkb * sizeof(uint64_t);
+    const int ti_n = (a.nqb + hf::kTile - 1) / hf::kTile, tj_n = (a.nkb + hf::kTile - 1) / hf::kTile;
+    const dim3 grid_score((unsigned)(a.BH * ti_n * tj_n));
+    const dim3 grid_topk((unsigned)((a.BH * a.nqb + 3) / 4));
     const double scale = 1.0 / sqrt((double)a.D);
     if (a.D == 64) {
         hipLaunchKernelGGL(hf::pool_kernel<64>, grid_pool, dim3(256), 0, s, a);
-        hipLaunchKernelGGL(hf::score_topk_kernel<64>, grid_sel, dim3(256), smem, s, a, scale);
+        hipLaunchKernelGGL(hf::score_kernel<64>, grid_score, dim3(256), 0, s, a, scale);
     } else {
         hipLaunchKernelGGL(hf::pool_kernel<128>, grid_pool, dim3(256), 0, s, a);
-        hipLaunchKernelGGL(hf::score_topk_kernel<128>, grid_sel, dim3(256), smem, s, a, scale);
+        hipLaunchKernelGGL(hf::score_kernel<128>, grid_score, dim3(256), 0, s, a, scale);
     }
+    const int kpl = (a.nkb + 63) / 64;
+    if (kpl <= 1) hipLaunchKernelGGL(hf::topk_kernel<1>, grid_topk, dim3(256), 0, s, a);
+    else if (kpl <= 2) hipLaunchKernelGGL(hf::topk_kernel<2>, grid_topk, dim3(256), 0, s, a);
+    else if (kpl <= 3) hipLaunchKernelGGL(hf::topk_kernel<3>, grid_topk, dim3(256), 0, s, a);
+    else if (kpl <= 4) hipLaunchKernelGGL(hf::topk_kernel<4>, grid_topk, dim3(256), 0, s, a);
+    else if (kpl <= 8) hipLaunchKernelGGL(hf::topk_kernel<8>, grid_topk, dim3(256), 0, s, a);
+    else if (kpl <= 16) hipLaunchKernelGGL(hf::topk_kernel<16>, grid_topk, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(hf::topk_kernel<24>, grid_topk, dim3(256), 0, s, a);
     return hipGetLastError();
 }

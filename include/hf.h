@@ -108,10 +108,12 @@ typedef struct {
 #define HF_STEP_COMMIT 1u
 
 /* Optional timing hooks for hf_hybrid_step: any non-NULL event is recorded on the
- * step's stream at that point (begin, after append, after select, after attention,
- * after absorb).  Events must have been created by the caller with hipEventCreate. */
+ * step's stream at that point: ev[0] begin, ev[1] after the ring append, ev[2] after the
+ * absorb partial sums, ev[3] after block selection, ev[4] after the state pass, ev[5]
+ * after the attention kernel.  Events must have been created by the caller with
+ * hipEventCreate. */
 typedef struct {
-    hipEvent_t ev[5];
+    hipEvent_t ev[6];
 } hf_step_events;
 
 int hf_abi_version(void);
@@ -167,8 +169,9 @@ hf_status hf_sparse_window_attn(const hf_dims *d, const void *q_dev, const hf_kv
  *   k_ev_dev, v_ev_dev  bf16 [B][H][n_tok][D] row-major evicted tokens
  *   S_dev, z_dev        fp32 state, updated in place
  * n_tok >= 0 (0 is a no-op).  Products use bf16 hi+lo halves of phi(K) so S keeps
- * fp32-grade accuracy; the token sum is split over workgroups and reduced in a fixed
- * order. */
+ * fp32-grade accuracy.  The token range is cut into a fixed number of splits (set by
+ * B, H, D and n_tok only); each split's partial sum goes to the workspace and a second
+ * kernel adds them to (S, z) in split order, so the result is deterministic. */
 hf_status hf_linear_absorb(const hf_dims *d, const void *k_ev_dev, const void *v_ev_dev, int64_t n_tok,
                            float *S_dev, float *z_dev, void *workspace_dev, size_t workspace_bytes,
                            hipStream_t stream);
@@ -176,13 +179,17 @@ hf_status hf_linear_absorb(const hf_dims *d, const void *k_ev_dev, const void *v
 /* One hybrid attention step on the ring:
  *   1. if k_cur_dev and v_cur_dev are given: hf_ring_append (else the caller has
  *      already written the current chunk into its slots);
- *   2. hf_block_select -> idx_dev ([B][H][n_qb][top_k], also an output);
- *   3. hf_sparse_window_attn with (S, z) as they are -> out_dev;
- *   4. if flags & HF_STEP_COMMIT: n_committed += C; if that exceeds W - C, the
- *      e = n_committed - (W - C) oldest frames are absorbed into (S, z) as by
- *      hf_linear_absorb, then head = (head + e) % W and n_committed -= e.
- * `ring` is updated on success only.  S_dev/z_dev may be NULL only without
- * HF_STEP_COMMIT (sparse part only).  `events` may be NULL. */
+ *   2. with HF_STEP_COMMIT, when committing the chunk leaves more than W - C committed
+ *      frames, the e oldest window frames are the evicted ones: their absorb partial sums
+ *      are computed now (those frames stay in the ring until the next append);
+ *   3. block selection as hf_block_select -> idx_dev ([B][H][n_qb][top_k], an output);
+ *   4. state pass: the readout operands are taken from (S, z) as they are, then the
+ *      partial sums of step 2 are added into (S, z) (as hf_linear_absorb would);
+ *   5. block-sparse attention with the fused readout, as hf_sparse_window_attn -> out_dev;
+ *   6. with HF_STEP_COMMIT: n_committed += C - e and head = (head + e) % W.
+ * The output therefore reads the state before this step's evictions, and on return the
+ * state includes them.  `ring` is updated on success only.  S_dev/z_dev may be NULL only
+ * without HF_STEP_COMMIT (sparse part only).  `events` may be NULL. */
 hf_status hf_hybrid_step(const hf_dims *d, const void *q_dev, const void *k_cur_dev, const void *v_cur_dev,
                          hf_kv_ring *ring, int32_t top_k, uint32_t flags, float *S_dev, float *z_dev,
                          float eps, int32_t *idx_dev, float *out_dev, void *workspace_dev,

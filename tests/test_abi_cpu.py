@@ -133,16 +133,16 @@ def test_absorb_validation():
 
 @pytest.mark.parametrize("B,H,D", [(1, 1, 64), (1, 3, 128), (1, 12, 128), (4, 12, 128), (2, 5, 64)])
 def test_workspace_covers_absorb_partials(B, H, D):
-    """Regression: the absorb splits each 64x64 state tile's token range over
-    P = min(#64-token chunks, max(1, round(256 / #tiles))) workgroups and stores P partial
-    tiles (16 KiB each) plus P partial z slices per 64 rows; the workspace must hold them for
-    every token count, including counts whose chunk number exceeds 2^31 / 64 in the sizing."""
+    """Regression: absorb splits each 64-row block of S over P = min(#64-token chunks,
+    max(1, 256 // #blocks)) workgroups, each storing a 64 x D partial plus 64 partial z
+    values; the workspace must hold them for every token count, including counts whose
+    chunk number would overflow a 32-bit count in the sizing."""
     g = geom(B=B, H=H, D=D, T=1560, W=6)
     ws = hf.workspace_size(g)
-    tiles = B * H * (D // 64) ** 2
-    pmax = max(1, (256 + tiles // 2) // tiles)
-    for n_tok in (1, 64, 200, 4680, 28080, 1 << 20):
+    blocks = B * H * (D // 64)
+    pmax = max(1, 256 // blocks)
+    for n_tok in (1, 64, 200, 4680, 28080, 1 << 20, 1 << 37):
         nch = -(-n_tok // 64)
         P = min(nch, pmax)
-        need = tiles * P * 64 * 64 * 4 + B * H * (D // 64) * P * 64 * 4 + tiles * 4
+        need = blocks * P * 64 * D * 4 + blocks * P * 64 * 4
         assert ws >= need, (n_tok, ws, need)

@@ -9,7 +9,7 @@ with commit: append the chunk to the KV ring, block select, block-sparse attenti
 the fused linear readout, and absorption of the 3 evicted frames into the state.
 
 Inputs are seeded synthetic bf16 activations (rank-8 smooth spatial field + noise per
-head, see hybrid_sparse_linear_hf_amd/synth.py); 8 distinct chunks (~345 MB of Q/K/V)
+head, see hybrid_sparse_linear_hf_amd/synth.py); 12 distinct chunks (~518 MB of Q/K/V)
 rotate through the steps so that the 256 MB last-level cache cannot hold them.
 
 Prints ONE JSON line.  value = effective TFLOP/s on kept blocks over the whole step
@@ -20,15 +20,20 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
 import time
+from pathlib import Path
 
 import numpy as np
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 matrix-core peak (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak
+ROOT = Path(__file__).resolve().parent
+ATTN_SOURCES = [ROOT / "hybrid_sparse_linear_hf_amd" / "csrc" / n for n in ("sparse_attn.hip", "hf_internal.h")]
+ATTN_PMC_SUMMARY = ROOT / "profiles" / "hybrid_step_832x480_layer_hbm_traffic.md"
 METRIC = "hybrid-attn chunk step ms + TFLOP/s on kept blocks (832x480 shape, 1 GPU)"
 
 
@@ -64,8 +69,10 @@ def kept_flops(idx: np.ndarray, Nq: int, Nk: int, bq: int, bk: int, D: int) -> f
     return float(4.0 * D * np.sum(qsz[None, None, :] * ksz.sum(axis=-1)))
 
 
-def cpu_baseline(cfg, sample_heads: int):
-    """The fp64 oracle (test infrastructure) timed on the host on a bounded sample."""
+def cpu_baseline(cfg, sample_heads: int, min_seconds: float):
+    """The fp64 oracle (test infrastructure) timed on the host on a bounded sample: the full
+    step (select, sparse attention, readout, absorb of the evicted frames) on `sample_heads`
+    heads of the same workload, repeated until `min_seconds` of wall time have passed."""
     import oracle
     from hybrid_sparse_linear_hf_amd import synth
 
@@ -73,18 +80,46 @@ def cpu_baseline(cfg, sample_heads: int):
     inp = synth.field_step_inputs(cfg, heads=heads)
     f64 = synth.f64_from_bf16_bits
     Q, K, V = f64(inp["q"]), f64(inp["k_win"]), f64(inp["v_win"])
-    S, z = oracle.absorb(f64(inp["k_ev"]), f64(inp["v_ev"]))
-    Kev, Vev = K[:, :, :cfg.C * cfg.T], V[:, :, :cfg.C * cfg.T]   # the 3 frames this step evicts
+    S0, z0 = oracle.absorb(f64(inp["k_ev"]), f64(inp["v_ev"]))
+    Kev, Vev = K[:, :, :cfg.C * cfg.T], V[:, :, :cfg.C * cfg.T]   # the frames this step evicts
     k = cfg.top_k()
+    reps, fl = 0, 0.0
     t0 = time.perf_counter()
-    out, idx, _ = oracle.hybrid_step(Q, K, V, S, z, cfg.bq, cfg.bk, k)
-    oracle.absorb(Kev, Vev, S, z)
-    dt = time.perf_counter() - t0
-    fl = kept_flops(idx, cfg.Nq, cfg.Nk, cfg.bq, cfg.bk, cfg.D)
+    while True:
+        S, z = S0.copy(), z0.copy()
+        out, idx, _ = oracle.hybrid_step(Q, K, V, S, z, cfg.bq, cfg.bk, k)
+        oracle.absorb(Kev, Vev, S, z)
+        fl += kept_flops(idx, cfg.Nq, cfg.Nk, cfg.bq, cfg.bk, cfg.D)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"one full step (select + sparse attention + readout + absorb of 3 frames) on {sample_heads} of "
-                      f"{cfg.H} heads of the 832x480 layer, fp64, {dt:.2f} s wall",
-            "seconds": dt}
+            "sample": f"{reps} full steps (select + sparse attention + readout + absorb of {cfg.C} "
+                      f"frames) on {sample_heads} of {cfg.H} heads of the {cfg.name} workload, fp64, "
+                      f"{dt:.1f} s wall, {dt / reps * 1e3:.0f} ms per step",
+            "ms_per_step": dt / reps * 1e3}
+
+
+def pmc_traffic(profile: Path, sources: list[Path]):
+    """HBM bytes per launch of the attention kernel from a committed rocprofv3 --pmc summary,
+    or None when the kernel's sources have changed since the counters were taken."""
+    if not profile.exists():
+        return None, "no counter summary"
+    fields = {}
+    for line in profile.read_text().splitlines():
+        if line.startswith("- ") and ": " in line:
+            key, val = line[2:].split(": ", 1)
+            fields[key.strip()] = val.strip().strip("`")
+    h = hashlib.sha256()
+    for src in sources:
+        h.update(src.read_bytes())
+    if fields.get("source_sha256") != h.hexdigest():
+        return None, "kernel changed since the counters were taken"
+    try:
+        return int(fields["traffic_bytes_per_launch"]), profile.name
+    except (KeyError, ValueError):
+        return None, "summary has no traffic_bytes_per_launch"
 
 
 def main():
@@ -92,8 +127,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--chunks", type=int, default=8, help="distinct input chunks rotated through the steps")
+    ap.add_argument("--chunks", type=int, default=12, help="distinct input chunks rotated through the steps")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the oracle CPU sample (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle CPU sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after timing, run a plain 256 MiB elementwise copy (for counter calibration)")
     ap.add_argument("--keep", type=float, default=None, help="override the kept fraction of key blocks")
     ap.add_argument("--window", type=int, default=None, help="override the window length in frames")
     args = ap.parse_args()
@@ -172,6 +210,15 @@ def main():
 
     # [steps, 5] ms: append | absorb partial sums | select | state pass | attention + readout
     phases = np.array([[hip.elapsed_ms(e[p], e[p + 1]) for p in range(5)] for e in evs])
+    step_ms = np.array([hip.elapsed_ms(e[0], e[5]) for e in evs])
+    if args.calib_copy:
+        # plain copy kernel of known size: reads and writes 256 MiB each
+        src = torch.randn(64 << 20, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     flops = np.array([kept_flops(b.cpu().numpy(), cfg.Nq, cfg.Nk, cfg.bq, cfg.bk, cfg.D) for b in idx_bufs])
     ms_step = wall * 1e3 / args.steps
     value = flops.sum() / wall / 1e12
@@ -182,6 +229,7 @@ def main():
     t_attn = phases[:, 4].mean() * 1e-3
     t_abs = t_abs_part + t_state      # the state pass also finishes the absorb
     attn_tflops = flops.mean() / t_attn / 1e12
+    traffic, traffic_src = pmc_traffic(ATTN_PMC_SUMMARY, ATTN_SOURCES)
     BH, T, D = cfg.B * cfg.H, cfg.T, cfg.D
     absorb_bytes = BH * (cfg.C * T * D * 2 * 2 + 2 * (D * D + D) * 4)
     select_bytes = BH * (cfg.Nq * D * 2 + cfg.Nk * D * 2 + g.n_qb * top_k * 4)
@@ -204,8 +252,10 @@ def main():
                    "chunk_frames": cfg.C, "window_frames": cfg.W, "block": [cfg.bq, cfg.bk], "top_k": top_k,
                    "n_kb": g.n_kb(cfg.W - cfg.C), "state_frames_at_start": cfg.n_evicted,
                    "parallelism": "single GPU", "rotating_chunks": args.chunks},
+        "step_ms_median": round(float(np.median(step_ms)), 4),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "traffic_source": traffic_src,
                      "kernel": "sparse_attn_kernel<128>",
                      "flops_per_launch": round(flops.mean()), "launch_us": round(t_attn * 1e6, 2)},
         "phases_us": {"append": round(t_app * 1e6, 2), "absorb_partial": round(t_abs_part * 1e6, 2),
@@ -223,8 +273,8 @@ def main():
         "cpu_baseline": None,
     }
     if args.cpu_heads > 0:
-        cb = cpu_baseline(cfg, args.cpu_heads)
-        cb.pop("seconds")
+        cb = cpu_baseline(cfg, min(args.cpu_heads, cfg.H), args.cpu_seconds)
+        res["cpu_baseline_ms_per_step"] = round(cb.pop("ms_per_step"), 1)
         res["cpu_baseline"] = cb
     print(json.dumps(res), flush=True)
 

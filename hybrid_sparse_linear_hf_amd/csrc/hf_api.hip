@@ -47,11 +47,6 @@ hf_status check_dims(const hf_dims *d) {
     const int64_t nkb = cdiv((int64_t)d->W * d->T, d->bk);
     if (nkb > kMaxKeyBlocks)
         return fail(HF_ERR_UNSUPPORTED, "window of %lld key blocks exceeds %d", (long long)nkb, kMaxKeyBlocks);
-    // the attention workgroup keeps its list of kept 32-key subtiles in LDS
-    const int64_t list_bytes = nkb * cdiv(d->bk, 32) * 8 + 2 * nkb;
-    if (list_bytes > 24576)
-        return fail(HF_ERR_UNSUPPORTED, "window of %lld keys in blocks of %d needs a %lld-byte subtile list (max 24576)",
-                    (long long)d->W * d->T, d->bk, (long long)list_bytes);
     return HF_OK;
 }
 

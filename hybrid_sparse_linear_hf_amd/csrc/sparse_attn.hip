@@ -7,362 +7,406 @@
 // is their sum ([HF-de] §2.A "Kombination", [HF-pt] §2.A "Resultado").
 //
 // gfx950 design
-//   * A workgroup of 4 waves owns two adjacent query blocks of one plane (two 32-query
-//     tiles each).  Adjacent query blocks keep largely the same key blocks, so the
-//     workgroup walks the UNION of their two kept lists and loads every 32-key K/V subtile
-//     once for both: fewer bytes per matrix-core flop than one block per workgroup.
-//   * Subtiles are staged cooperatively (coalesced 16-byte loads) through registers four
-//     subtiles ahead, into a double-buffered LDS stage, with rows stored in the lane order
-//     the matrix-core operands read them (conflict-free 16-byte LDS reads).
-//   * Each wave computes S^T = K Q^T and O^T += V^T P^T on 32x32x16 bf16 matrix cores, so
-//     the probabilities leave the first product already in the register layout the second
-//     consumes.  Feeding key rows in the order perm32(m) makes each lane hold 16
-//     consecutive keys of its query; value frames are stored transposed ([D][T]) in the
-//     ring, so the V operand needs no transpose either.
-//   * fp32 online softmax in base 2 with the 1/sqrt(D) scale folded into one FMA; the
-//     running maximum is only raised when a tile exceeds it by more than 2^8, so the
-//     accumulator rescale is rare.
-//   * At most 256 registers per wave, so two workgroups share a CU and one wave's memory
-//     waits overlap the other's matrix-core work.
-//   * Workgroup ids are remapped so that the query blocks of one plane run on one XCD
-//     and share its L2 for the window's K/V.
+//   * A workgroup owns one query block; each of its wavefronts owns one 32-query tile
+//     (two waves for 64-query blocks).  At most 256 registers per wave, so two waves share
+//     a SIMD and the hardware overlaps one wave's softmax with the other's matrix-core
+//     work.  Workgroup ids are remapped so that the query blocks of one plane run on one
+//     XCD and share its L2 for the window's K/V.
+//   * The kept key blocks are walked in 32-key subtiles.  Each subtile's K rows and V^T
+//     columns are fetched with direct-to-LDS buffer loads (16 bytes per lane, whole 256-byte
+//     K rows and 64-byte V^T row segments per instruction, so every load is coalesced) into
+//     a double-buffered LDS stage, one subtile ahead of the compute; the two waves share
+//     the fetch.  Chunk positions are XOR-swizzled per row, so that the 16-byte reads in
+//     matrix-core operand order hit distinct LDS banks.
+//   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16: the probabilities leave
+//     the first product in the register layout the second consumes.  Key rows are read in
+//     the order perm32(m), so each lane holds 16 consecutive keys of its query column, and
+//     value rows (features) likewise, so each lane holds 16 consecutive output features.
+//   * Softmax in base 2 with the 1/sqrt(D) scale folded into one FMA.  Full subtiles use a
+//     FIXED reference per query row -- the exact row maximum of the first subtile -- so
+//     nothing is ever rescaled; should a later score exceed it by so much that the row sum
+//     reaches 2^32, the block is recomputed with an online (rescaling) softmax.  Short
+//     subtiles (the tail of a short last key block; every subtile when bk < 32) use the
+//     online softmax with masking.
 #include "hf_internal.h"
 
 namespace hf {
 namespace {
 
+constexpr int kSub = 32;                      // keys per subtile
+constexpr int kBufDword3 = 0x00020000;        // raw buffer resource word 3 (gfx9 family)
 constexpr float kLazyRescaleLog2 = 8.0f;
-constexpr int kSub = 32;          // keys per subtile
+constexpr float kFixedRefLimit = 4294967296.0f;   // 2^32
 
-// Inverse of perm32: LDS row that holds logical row k.
-__device__ __forceinline__ int inv_perm32(int k) { return (((k >> 2) & 3) << 3) | ((k >> 4) << 2) | (k & 3); }
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef __attribute__((address_space(3))) void *LdsPtr;
 
-template <int D>
-struct Stage {
-    uint16_t k[kSub][D + 8];      // row m holds key perm32(m) of the subtile
-    uint16_t vt[D][kSub + 8];     // row 32*dt + m holds feature 32*dt + perm32(m), keys in order
-};
-
-// Per-thread share of one subtile: D/64 K vectors and D/64 V^T vectors of 16 bytes.
-template <int D>
-struct Regs {
-    u32x4 k[D / 64];
-    u32x4 v[D / 64];
-};
-
-struct SubInfo {
-    int key0, nval, flags;
-};
-
-__device__ __forceinline__ SubInfo sub_info(const int2 *ulist, int us) {
-    const int2 e = ulist[us];
-    return SubInfo{e.x, e.y & 0xFF, e.y >> 8};
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufDword3);
 }
 
-// Frame geometry of a subtile, uniform across the workgroup: the subtile's 32 keys lie in
-// frame f0 (from token t0 on) and, past the frame end, in frame f0 + 1.
-struct SubGeom {
-    uint32_t krow0, krow1;     // ring row (in units of D) of token 0 of frames f0, f0 + 1
-    uint32_t vcol0, vcol1;     // element offset of V^T frame f0, f0 + 1
-    int t0, nval;
-};
-
-__device__ __forceinline__ SubGeom sub_geom(const hf_attn_args &a, uint32_t magicT, int bh, SubInfo si) {
-    const int key0 = __builtin_amdgcn_readfirstlane(si.key0);
-    const int f0 = fast_div(key0, magicT, a.T);
-    int s0 = a.head + f0;
-    s0 -= (s0 >= a.W) ? a.W : 0;
-    int s1 = s0 + 1;
-    s1 -= (s1 >= a.W) ? a.W : 0;
-    SubGeom g;
-    g.t0 = key0 - f0 * a.T;
-    g.krow0 = (uint32_t)((bh * a.W + s0) * a.T);
-    g.krow1 = (uint32_t)((bh * a.W + s1) * a.T) - (uint32_t)a.T;   // + t with t >= T
-    g.vcol0 = g.krow0 * (uint32_t)a.D;
-    g.vcol1 = (uint32_t)((bh * a.W + s1) * a.T) * (uint32_t)a.D - (uint32_t)a.T;
-    g.nval = __builtin_amdgcn_readfirstlane(si.nval);
-    return g;
+// 16 bytes per lane from the buffer into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(Rsrc r, unsigned char *lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 16, (int)voff, 0, 0, 0);
 }
 
-// Per-thread constants of the cooperative subtile load (see load_sub).
+// Reductions over the lane pair (l, l ^ 32) that holds the two key halves of one query.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// LDS chunk swizzles (16-byte chunks).  K rows hold D/8 chunks; V^T rows (one feature,
+// the subtile's 32 keys) hold 4.  Chosen so that the operand reads below touch 16 distinct
+// bank groups per 16 lanes.
 template <int D>
-struct LoadPlan {
-    int kr[D / 64];            // subtile key row of the thread's K vector
-    uint32_t kcol[D / 64];     // byte offset of its 8 features in the row
-    int kg8[D / 64];           // first key (0, 8, 16, 24) of the thread's V^T vector
-    uint32_t dT[D / 64];       // feature row d of the V^T vector, times T
+__device__ __forceinline__ int swz_k(int r) {
+    if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | ((r >> 1) & 8);
+    else return ((r >> 1) & 3) | ((r >> 2) & 4);
+}
+__device__ __forceinline__ int swz_v(int f) { return ((f >> 4) & 1) | (((f >> 2) & 1) << 1); }
+
+struct SmState {
+    float m;     // reference maximum of s * c_log2 (base-2 logits)
+    float l;     // this lane's partial row sum
 };
 
-template <int D>
-__device__ __forceinline__ LoadPlan<D> load_plan(int tid, int T) {
-    LoadPlan<D> p;
+__device__ __forceinline__ float tile_max_log2(const f32x16 &s, float c_log2) {
+    float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) {
-        const int v = tid + 256 * e;
-        p.kr[e] = v / (D / 8);
-        p.kcol[e] = (uint32_t)(v % (D / 8)) * 16u;
-        p.kg8[e] = 8 * (v % 4);
-        p.dT[e] = (uint32_t)(v / 4) * (uint32_t)T;
-    }
-    return p;
+    for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
+    mx = fmaxf(mx, s[15]);
+    return pair_max(mx) * c_log2;
 }
 
-// Global -> registers for one subtile.  Rows past the subtile's valid keys re-read its
-// first key (finite data; their scores are masked).  Byte offsets stay below 2^32 (the
-// ring holds fewer than 2^31 elements), so each load is a 32-bit offset from the ring base.
-template <int D>
-__device__ __forceinline__ void load_sub(const hf_attn_args &a, const SubGeom &g, const LoadPlan<D> &p,
-                                         Regs<D> &r) {
-    const char *kbase = reinterpret_cast<const char *>(a.ring_k);
-    const char *vbase = reinterpret_cast<const char *>(a.ring_vt);
+__device__ __forceinline__ void pack_p(const float (&p)[16], u32x4 (&pf)[2]) {
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) {
-        const int t = g.t0 + (p.kr[e] < g.nval ? p.kr[e] : 0);
-        const uint32_t row = (t >= a.T ? g.krow1 : g.krow0) + (uint32_t)t;
-        r.k[e] = *reinterpret_cast<const u32x4 *>(kbase + (row * (uint32_t)(D * 2) + p.kcol[e]));
-        const int tv = g.t0 + (p.kg8[e] < g.nval ? p.kg8[e] : 0);
-        const uint32_t col = (tv >= a.T ? g.vcol1 : g.vcol0) + p.dT[e] + (uint32_t)tv;
-        r.v[e] = *reinterpret_cast<const u32x4 *>(vbase + col * 2u);
+    for (int ks = 0; ks < 2; ++ks) {
+        pf[ks].x = pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]);
+        pf[ks].y = pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]);
+        pf[ks].z = pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]);
+        pf[ks].w = pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7]);
     }
 }
 
-template <int D>
-__device__ __forceinline__ void store_sub(const Regs<D> &r, Stage<D> &st, int tid) {
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) {
-        const int v = tid + 256 * e;
-        const int kr = v / (D / 8), col8 = v % (D / 8);
-        *reinterpret_cast<u32x4 *>(&st.k[inv_perm32(kr)][8 * col8]) = r.k[e];
-        const int d = v / 4, kg = v % 4;
-        *reinterpret_cast<u32x4 *>(&st.vt[32 * (d / 32) + inv_perm32(d % 32)][8 * kg]) = r.v[e];
-    }
+__device__ __forceinline__ float sum16(const float (&p)[16]) {
+    return (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]))) +
+           (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2,
-                                                             int per_xcd, int npairs) {
-    __shared__ Stage<D> stage[2];
-    extern __shared__ __align__(16) unsigned char dyn[];
-    const int nsub = (a.bk + kSub - 1) / kSub;
-    int2 *ulist = reinterpret_cast<int2 *>(dyn);                                   // [nkb * nsub]
-    unsigned char *fa = dyn + (size_t)a.nkb * nsub * sizeof(int2);                 // [nkb]
-    unsigned char *fb = fa + a.nkb;                                                // [nkb]
-    __shared__ int s_usub;
+// Full tile against the fixed reference: p = 2^(s c - m).
+__device__ __forceinline__ void softmax_fixed(const f32x16 &s, float c_log2, float moff, float &l, u32x4 (&pf)[2]) {
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c_log2, moff));
+    l += sum16(p);
+    pack_p(p, pf);
+}
 
+// Masked online softmax (keys 16g + i >= nval excluded); returns the factor the output
+// accumulator must be scaled by (1 when unchanged).
+__device__ __forceinline__ float softmax_online(f32x16 s, int nval, int g, float c_log2, SmState &st, u32x4 (&pf)[2]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        if (16 * g + i >= nval) s[i] = -INFINITY;
+    const float mx = tile_max_log2(s, c_log2);
+    const float mnew = (mx > st.m + kLazyRescaleLog2) ? mx : st.m;
+    const float alpha = (mnew == st.m) ? 1.f : __builtin_amdgcn_exp2f(st.m - mnew);
+    st.m = mnew;
+    const float moff = -fmaxf(mnew, -3.0e38f);   // finite even while every key so far was masked
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c_log2, moff));
+    st.l = __builtin_fmaf(st.l, alpha, sum16(p));
+    pack_p(p, pf);
+    return alpha;
+}
+
+constexpr int kWaitVm0 = 0x0F70;   // s_waitcnt vmcnt(0), other counters untouched
+
+// D = head dim; NW = waves per workgroup = 32-query tiles per query block (2 when bq == 64).
+template <int D, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2))) void
+sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, int lsh) {
+    constexpr int LPR = D / 8;            // 16-byte chunks per K row
+    constexpr int RPI = 64 / LPR;         // K rows per load instruction
+    constexpr int NK = kSub / RPI;        // K load instructions per subtile
+    constexpr int NV = D / 16;            // V^T load instructions per subtile (16 feature rows each)
+    constexpr int KW = NK / NW, VW = NV / NW;
+    constexpr int KBYTES = kSub * D * 2, SLOT = KBYTES + D * 64;
+
+    extern __shared__ __align__(16) unsigned char dyn[];   // [2 slots][kept list][NW flags]
     const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-    if (item >= a.BH * npairs) return;
-    const int bh = item / npairs, pair = item - bh * npairs;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 31, g = lane >> 5;
-    const int qbA = 2 * pair, qbB = 2 * pair + 1;
-    const bool hasB = qbB < a.nqb;
-
-    // ---- union of the two kept lists, as a list of non-empty 32-key subtiles in key order
-    for (int j = tid; j < a.nkb; j += 256) fa[j] = fb[j] = 0;
-    __syncthreads();
-    {
-        const int32_t *selA = a.idx + ((size_t)bh * a.nqb + qbA) * a.top_k;
-        const int32_t *selB = a.idx + ((size_t)bh * a.nqb + (hasB ? qbB : qbA)) * a.top_k;
-        for (int t = tid; t < a.top_k; t += 256) {
-            // out-of-range indices (a caller error) are clamped so that no load leaves the window
-            fa[min(max(selA[t], 0), a.nkb - 1)] = 1;
-            if (hasB) fb[min(max(selB[t], 0), a.nkb - 1)] = 1;
-        }
-    }
-    __syncthreads();
-    if (w == 0) {
-        const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        int base = 0;
-        for (int j0 = 0; j0 < a.nkb; j0 += 64) {
-            const int j = j0 + lane;
-            const int flags = j < a.nkb ? (fa[j] | (fb[j] << 1)) : 0;
-            const int kb0 = j * a.bk, kb1 = min(kb0 + a.bk, a.Nk);
-            const int cnt = flags ? min(nsub, (kb1 - kb0 + kSub - 1) / kSub) : 0;
-            int before = 0, total = 0;
-            for (int s = 0; s < nsub; ++s) {
-                const uint64_t b = __ballot(cnt > s);
-                before += __popcll(b & lt_mask);
-                total += __popcll(b);
-            }
-            for (int s = 0; s < cnt; ++s) {
-                const int key0 = kb0 + kSub * s;
-                ulist[base + before + s] = int2{key0, min(kSub, kb1 - key0) | (flags << 8)};
-            }
-            base += total;
-        }
-        if (lane == 0) s_usub = base;
-    }
-    __syncthreads();
-    const int usub = s_usub;
-
-    // ---- this wave's 32 queries: query block (w >> 1), tile (w & 1)
-    const int myblk = w >> 1;
-    const int qb = myblk ? qbB : qbA;
+    if (item >= a.BH * a.nqb) return;   // uniform per workgroup
+    const int bh = item / a.nqb, qb = item - bh * a.nqb;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
     const int q0 = qb * a.bq, qend = min(q0 + a.bq, a.Nq);
-    const int qrow0 = q0 + 32 * (w & 1);
-    const bool active = (myblk == 0 || hasB) && qrow0 < qend;
-    const int myflag = 1 << myblk;
+    int32_t *s_blist = reinterpret_cast<int32_t *>(dyn + 2 * SLOT);
+    int *s_flag = reinterpret_cast<int *>(s_blist + a.top_k);
 
+    // kept blocks -> LDS (out-of-range entries, a caller error, are clamped so that no load
+    // leaves the window)
+    const int32_t *sel = a.idx + ((size_t)bh * a.nqb + qb) * a.top_k;
+    for (int t = threadIdx.x; t < a.top_k; t += 64 * NW) s_blist[t] = min(max(sel[t], 0), a.nkb - 1);
+
+    // this wave's Q^T B fragments: query q0 + 32w + n (clamped into the block), features
+    // 16ks + 8g .. + 8
     u32x4 qf[D / 16];
     {
-        int row = qrow0 + n;
-        if (!active || row >= qend) row = min(q0, a.Nq - 1);
+        int row = q0 + 32 * w + n;
+        row = row < qend ? row : q0;
         const uint16_t *qp = a.q + ((size_t)bh * a.Nq + row) * D + 8 * g;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) qf[s] = *reinterpret_cast<const u32x4 *>(qp + 16 * s);
+        for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const u32x4 *>(qp + 16 * ks);
     }
+    __syncthreads();
+
+    const size_t plane = (size_t)bh * a.W * a.T * D;
+    const uint32_t plane_bytes = (uint32_t)((size_t)a.W * a.T * D * 2);
+    const Rsrc rk = make_rsrc(a.ring_k + plane, plane_bytes);
+    const Rsrc rv = make_rsrc(a.ring_vt + plane, plane_bytes);
+    const int T = a.T, W = a.W, head = a.head;
+
+    // ---- subtile list: 2^lsh subtiles per kept block, minus the empty tail of a short last
+    // block (the list is ascending, so that block can only be the final entry)
+    const int nsub_blk = 1 << lsh;
+    int nsubt = a.top_k << lsh;
+    int nfull = (a.bk >= kSub && T >= kSub) ? nsubt : 0;
+    {
+        const int lastb = s_blist[a.top_k - 1];
+        if (lastb == a.nkb - 1 && a.bk >= kSub) {
+            const int len = a.Nk - lastb * a.bk;
+            nsubt -= nsub_blk - (len + kSub - 1) / kSub;
+            if (nfull) nfull = nsubt - ((len & (kSub - 1)) ? 1 : 0);
+        }
+    }
+    auto key0_of = [&](int u) -> int {
+        const int b = __builtin_amdgcn_readfirstlane(s_blist[u >> lsh]);
+        return b * a.bk + ((u & (nsub_blk - 1)) << 5);
+    };
+    auto nval_of = [&](int k0) -> int {
+        const int b = k0 / a.bk;
+        return min(min(kSub, b * a.bk + a.bk - k0), a.Nk - k0);
+    };
+    auto slot_of = [&](int f) -> int {
+        const int s = head + f;
+        return s >= W ? s - W : s;
+    };
+
+    // ---- per-lane load plan: this wave issues K instructions w*KW .. and V instructions w*VW ..
+    uint32_t kofs[KW], vofs[VW];
+    int krow[KW], vkr[VW];
+#pragma unroll
+    for (int jj = 0; jj < KW; ++jj) {
+        const int r = RPI * (w * KW + jj) + lane / LPR;
+        const int c = (lane % LPR) ^ swz_k<D>(r);
+        krow[jj] = r;
+        kofs[jj] = (uint32_t)(r * D * 2 + c * 16);
+    }
+#pragma unroll
+    for (int jj = 0; jj < VW; ++jj) {
+        const int f = 16 * (w * VW + jj) + (lane >> 2);
+        const int c = (lane & 3) ^ swz_v(f);
+        vkr[jj] = 8 * c;
+        vofs[jj] = (uint32_t)(f * T * 2 + c * 16);
+    }
+    // Fast plan for a full subtile (T >= 32: its keys lie in frame f0 from token t0 on and,
+    // from row `split` on, in frame f0 + 1).
+    auto dma_full = [&](int k0, int slot) {
+        const int f0 = fast_div(k0, magicT, T);
+        const int t0 = k0 - f0 * T;
+        const int s0 = slot_of(f0), s1 = slot_of(f0 + 1);
+        const int split = T - t0;
+        const uint32_t sb0 = (uint32_t)((s0 * T + t0) * D * 2), sb1 = (uint32_t)((s1 * T - split) * D * 2);
+        const uint32_t sv0 = (uint32_t)(s0 * D * T * 2 + t0 * 2), sv1 = (uint32_t)(s1 * D * T * 2 - split * 2);
+        unsigned char *base = dyn + slot * SLOT;
+#pragma unroll
+        for (int jj = 0; jj < KW; ++jj)
+            dma16(rk, base + (w * KW + jj) * 1024, (krow[jj] < split ? sb0 : sb1) + kofs[jj]);
+#pragma unroll
+        for (int jj = 0; jj < VW; ++jj)
+            dma16(rv, base + KBYTES + (w * VW + jj) * 1024, (vkr[jj] < split ? sv0 : sv1) + vofs[jj]);
+    };
+    // General plan (short subtiles, any T): rows past the valid keys re-read the last one.
+    auto dma_any = [&](int k0, int slot) {
+        const int nv = nval_of(k0);
+        unsigned char *base = dyn + slot * SLOT;
+#pragma unroll
+        for (int jj = 0; jj < KW; ++jj) {
+            const int j = k0 + min(krow[jj], nv - 1);
+            const int f = fast_div(j, magicT, T);
+            const uint32_t off = (uint32_t)((slot_of(f) * T + (j - f * T)) * D * 2) + (kofs[jj] - (uint32_t)(krow[jj] * D * 2));
+            dma16(rk, base + (w * KW + jj) * 1024, off);
+        }
+#pragma unroll
+        for (int jj = 0; jj < VW; ++jj) {
+            const int j = k0 + min(vkr[jj], (nv - 1) & ~7);
+            const int f = fast_div(j, magicT, T);
+            const uint32_t off = (uint32_t)(slot_of(f) * D * T * 2 + (j - f * T) * 2) + (vofs[jj] - (uint32_t)(vkr[jj] * 2));
+            dma16(rv, base + KBYTES + (w * VW + jj) * 1024, off);
+        }
+    };
+
+    // ---- per-lane operand reads (swizzled chunk positions)
+    const int rk_row = perm32(n);
+    const int rk_swz = swz_k<D>(rk_row);
+    const int vr_swz = swz_v(rk_row);
+    auto qk_tile = [&](int slot) -> f32x16 {
+        const unsigned char *kb = dyn + slot * SLOT + rk_row * D * 2;
+        u32x4 kfr[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            kfr[ks] = *reinterpret_cast<const u32x4 *>(kb + (((2 * ks + g) ^ rk_swz) << 4));
+        f32x16 s = {};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) s = mfma32(as_bf16x8(kfr[ks]), as_bf16x8(qf[ks]), s);
+        return s;
+    };
     f32x16 acc[D / 32];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
-    float m = -INFINITY, l = 0.f;
-
-    auto compute = [&](int us, const Stage<D> &st) {
-        const SubInfo si = sub_info(ulist, us);
-        if (!active || !(si.flags & myflag)) return;
-        f32x16 sc = {};
+    for (int ft = 0; ft < D / 32; ++ft) acc[ft] = f32x16{};
+    auto pv_tile = [&](int slot, const u32x4 (&pf)[2]) {
+        const unsigned char *vb = dyn + slot * SLOT + KBYTES + rk_row * 64;
+        u32x4 vfr[D / 32][2];
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-            sc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&st.k[n][16 * s + 8 * g])), as_bf16x8(qf[s]), sc);
-        if (si.nval < kSub) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (16 * g + i >= si.nval) sc[i] = -INFINITY;
-        }
-        float mx = sc[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (__any((mx - m) * c_log2 > kLazyRescaleLog2)) {
-            const float mn = fmaxf(m, mx);
-            const float alpha = __builtin_amdgcn_exp2f((m - mn) * c_log2);
-            m = mn;
-            l *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
-        }
-        const float mc = m * c_log2;
-        float p[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c_log2, -mc));
-            l += p[i];
-        }
-        u32x4 pf[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            pf[ks].x = pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]);
-            pf[ks].y = pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]);
-            pf[ks].z = pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]);
-            pf[ks].w = pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7]);
-        }
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+        for (int ft = 0; ft < D / 32; ++ft)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                acc[dt] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&st.vt[32 * dt + n][16 * g + 8 * ks])),
-                                 as_bf16x8(pf[ks]), acc[dt]);
+                vfr[ft][ks] = *reinterpret_cast<const u32x4 *>(vb + ft * 2048 + (((2 * g + ks) ^ vr_swz) << 4));
+#pragma unroll
+        for (int ft = 0; ft < D / 32; ++ft)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) acc[ft] = mfma32(as_bf16x8(vfr[ft][ks]), as_bf16x8(pf[ks]), acc[ft]);
     };
-
-    // ---- main loop.  LDS stage (us & 1) holds subtile us; four register buffers carry the
-    // loads of subtiles us+1 .. us+4, so a load has three steps to land before it is staged.
-    // Loads are issued unconditionally (past the end they repeat the last subtile) so that
-    // the wait for a staged subtile never covers the younger prefetches behind it.
-    const int last = usub - 1;   // >= 0: every kept block holds at least one key
-    const LoadPlan<D> plan = load_plan<D>(tid, a.T);
-    auto fetch = [&](int us, Regs<D> &r) {
-        load_sub<D>(a, sub_geom(a, magicT, bh, sub_info(ulist, min(us, last))), plan, r);
+    auto rescale = [&](float alpha) {
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+            for (int ft = 0; ft < D / 32; ++ft)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[ft][i] *= alpha;
+        }
     };
-    Regs<D> r0, r1, r2, r3;
-    fetch(0, r0);
-    fetch(1, r1);
-    fetch(2, r2);
-    fetch(3, r3);
-    store_sub<D>(r0, stage[0], tid);
-    // Drain every load issued so far (the Q fragments included) once, so that inside the
-    // loop only the prefetch of later subtiles is outstanding.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // one step: prefetch subtile us+4 into `ld` (free: its subtile us is already staged),
-    // compute subtile us, stage subtile us+1 from `nx`
-    // (the scheduling barriers keep the prefetch ahead of the compute: the memory counter is
-    // in order, so a prefetch sunk below the staging store would be waited for there)
-    auto step = [&](int us, Regs<D> &ld, const Stage<D> &cs, const Regs<D> &nx, Stage<D> &ns) {
-        fetch(us + 4, ld);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(us, cs);
-        __builtin_amdgcn_sched_barrier(0);
-        store_sub<D>(nx, ns, tid);
+    // wait for this wave's loads, then for the other wave's (and for both to be done with
+    // the stage about to be refilled)
+    auto stage_ready = [&]() {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __syncthreads();
     };
-    for (int us = 0; us < usub; us += 4) {
-        step(us, r0, stage[0], r1, stage[1]);
-        if (us + 1 >= usub) break;
-        step(us + 1, r1, stage[1], r2, stage[0]);
-        if (us + 2 >= usub) break;
-        step(us + 2, r2, stage[0], r3, stage[1]);
-        if (us + 3 >= usub) break;
-        step(us + 3, r3, stage[1], r0, stage[0]);
+
+    SmState sm{-INFINITY, 0.f};
+    int ustart = 0;            // first subtile of the online loop
+    bool first_issued = false; // its load is already in flight
+    if (nfull > 0) {
+        // ---- fast path over the full subtiles
+        dma_full(key0_of(0), 0);
+        stage_ready();
+        if (1 < nfull) dma_full(key0_of(1), 1);
+        else if (1 < nsubt) dma_any(key0_of(1), 1);
+        f32x16 s = qk_tile(0);
+        sm.m = tile_max_log2(s, c_log2);
+        const float moff = -sm.m;
+        u32x4 pf[2];
+        softmax_fixed(s, c_log2, moff, sm.l, pf);
+        pv_tile(0, pf);
+        for (int u = 1; u < nfull; ++u) {
+            stage_ready();
+            if (u + 1 < nfull) dma_full(key0_of(u + 1), (u + 1) & 1);
+            else if (u + 1 < nsubt) dma_any(key0_of(u + 1), (u + 1) & 1);
+            s = qk_tile(u & 1);
+            softmax_fixed(s, c_log2, moff, sm.l, pf);
+            pv_tile(u & 1, pf);
+        }
+        // a score far above its reference (row sum >= 2^32): recompute the block online
+        const int bad = __builtin_amdgcn_ballot_w64(!(sm.l < kFixedRefLimit)) != 0;
+        if (lane == 0) s_flag[w] = bad;
+        __syncthreads();
+        int any_bad = 0;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) any_bad |= s_flag[i];
+        if (any_bad) {
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the load of subtile nfull may be in flight
+            __syncthreads();
+            sm = SmState{-INFINITY, 0.f};
+#pragma unroll
+            for (int ft = 0; ft < D / 32; ++ft) acc[ft] = f32x16{};
+            ustart = 0;
+        } else {
+            ustart = nfull;
+            first_issued = true;
+        }
     }
-    if (!active) return;
+
+    // ---- online path: short subtiles, or every subtile after a fallback
+    if (ustart < nsubt) {
+        if (!first_issued) dma_any(key0_of(ustart), ustart & 1);
+        for (int u = ustart; u < nsubt; ++u) {
+            stage_ready();
+            if (u + 1 < nsubt) dma_any(key0_of(u + 1), (u + 1) & 1);
+            const int nv = nval_of(key0_of(u));
+            const f32x16 s = qk_tile(u & 1);
+            u32x4 pf[2];
+            const float al = softmax_online(s, nv, g, c_log2, sm, pf);
+            rescale(al);
+            pv_tile(u & 1, pf);
+        }
+    }
 
     // ---- epilogue: normalise, add the linear readout, store fp32
-    const float inv_l = 1.f / (l + __shfl_xor(l, 32));
-    const int row = qrow0 + n;
-    const bool row_ok = row < qend;
-    float *op = a.out + ((size_t)bh * a.Nq + (row_ok ? row : q0)) * D + 16 * g;
-    if (a.st) {
-        // phi(q) as the B operand (same fragment layout as Q^T) and the normaliser
-        u32x4 pq[D / 16];
-        float den = 0.f;
-        const float *zp = a.zc + (size_t)bh * D + 8 * g;
+    const float inv_l = 1.f / pair_sum(sm.l);
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            const uint32_t wv[4] = {qf[s].x, qf[s].y, qf[s].z, qf[s].w};
-            const f32x4 z0 = *reinterpret_cast<const f32x4 *>(zp + 16 * s);
-            const f32x4 z1 = *reinterpret_cast<const f32x4 *>(zp + 16 * s + 4);
+    for (int ft = 0; ft < D / 32; ++ft)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[ft][i] *= inv_l;
+    if (a.st) {
+        // B operand phi(q) / (phi(q) . z + eps) in the Q^T fragment layout, so that the
+        // readout accumulates straight onto the normalised sparse output
+        const float *zp = a.zc + (size_t)bh * D + 8 * g;
+        float den = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const uint32_t wv[4] = {qf[ks].x, qf[ks].y, qf[ks].z, qf[ks].w};
+            const f32x4 z0 = *reinterpret_cast<const f32x4 *>(zp + 16 * ks);
+            const f32x4 z1 = *reinterpret_cast<const f32x4 *>(zp + 16 * ks + 4);
             const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-            float ph[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                ph[2 * e] = phi_f32(bf16_lo_to_f32(wv[e]));
-                ph[2 * e + 1] = phi_f32(bf16_hi_to_f32(wv[e]));
+                den = __builtin_fmaf(phi_f32(bf16_lo_to_f32(wv[e])), zz[2 * e], den);
+                den = __builtin_fmaf(phi_f32(bf16_hi_to_f32(wv[e])), zz[2 * e + 1], den);
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) den += ph[e] * zz[e];
-            pq[s].x = pack_bf16x2(ph[0], ph[1]);
-            pq[s].y = pack_bf16x2(ph[2], ph[3]);
-            pq[s].z = pack_bf16x2(ph[4], ph[5]);
-            pq[s].w = pack_bf16x2(ph[6], ph[7]);
         }
-        den += __shfl_xor(den, 32);
-        const float inv_den = 1.f / (den + a.eps);
+        const float inv_den = 1.f / (pair_sum(den) + a.eps);
+        u32x4 pq[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const uint32_t wv[4] = {qf[ks].x, qf[ks].y, qf[ks].z, qf[ks].w};
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = pack_bf16x2(phi_f32(bf16_lo_to_f32(wv[e])) * inv_den, phi_f32(bf16_hi_to_f32(wv[e])) * inv_den);
+            pq[ks] = u32x4{o[0], o[1], o[2], o[3]};
+        }
         const uint16_t *stp = a.st + (size_t)bh * D * D + 8 * g;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-            f32x16 lin = {};
-            const uint16_t *srow = stp + (size_t)(32 * dt + perm32(n)) * D;
+        for (int ft = 0; ft < D / 32; ++ft) {
+            const uint16_t *srow = stp + (size_t)(32 * ft + perm32(n)) * D;
 #pragma unroll
-            for (int s = 0; s < D / 16; ++s)
-                lin = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(srow + 16 * s)), as_bf16x8(pq[s]), lin);
-            if (row_ok) {
-                f32x4 *o4 = reinterpret_cast<f32x4 *>(op + 32 * dt);
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    o4[v] = f32x4{acc[dt][4 * v] * inv_l + lin[4 * v] * inv_den,
-                                  acc[dt][4 * v + 1] * inv_l + lin[4 * v + 1] * inv_den,
-                                  acc[dt][4 * v + 2] * inv_l + lin[4 * v + 2] * inv_den,
-                                  acc[dt][4 * v + 3] * inv_l + lin[4 * v + 3] * inv_den};
-            }
+            for (int ks = 0; ks < D / 16; ++ks)
+                acc[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(srow + 16 * ks)), as_bf16x8(pq[ks]), acc[ft]);
         }
-    } else if (row_ok) {
+    }
+    const int row = q0 + 32 * w + n;
+    if (row < qend) {
+        float *op = a.out + ((size_t)bh * a.Nq + row) * D + 16 * g;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-            f32x4 *o4 = reinterpret_cast<f32x4 *>(op + 32 * dt);
+        for (int ft = 0; ft < D / 32; ++ft) {
+            f32x4 *o4 = reinterpret_cast<f32x4 *>(op + 32 * ft);
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                o4[v] = f32x4{acc[dt][4 * v] * inv_l, acc[dt][4 * v + 1] * inv_l, acc[dt][4 * v + 2] * inv_l,
-                              acc[dt][4 * v + 3] * inv_l};
+                o4[v] = f32x4{acc[ft][4 * v], acc[ft][4 * v + 1], acc[ft][4 * v + 2], acc[ft][4 * v + 3]};
         }
     }
 }
@@ -371,17 +415,24 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(hf_attn_args a, uin
 }  // namespace hf
 
 hipError_t hf_launch_sparse_attn(const hf_attn_args &a, hipStream_t s) {
-    const int npairs = (a.nqb + 1) / 2;
-    const int items = a.BH * npairs;
+    const int items = a.BH * a.nqb;
     const int per_xcd = (items + 7) / 8;
     const dim3 grid((unsigned)(per_xcd * 8));
     const uint32_t magicT = hf::div_magic((uint32_t)a.T);
     const float c_log2 = (float)(1.4426950408889634 / sqrt((double)a.D));
-    const int nsub = (a.bk + hf::kSub - 1) / hf::kSub;
-    const size_t dyn = (size_t)a.nkb * nsub * sizeof(int2) + 2 * (size_t)a.nkb;
-    if (a.D == 64)
-        hipLaunchKernelGGL((hf::sparse_attn_kernel<64>), grid, dim3(256), dyn, s, a, magicT, c_log2, per_xcd, npairs);
-    else
-        hipLaunchKernelGGL((hf::sparse_attn_kernel<128>), grid, dim3(256), dyn, s, a, magicT, c_log2, per_xcd, npairs);
+    const int lsh = a.bk >= 128 ? 2 : (a.bk >= 64 ? 1 : 0);     // 32-key subtiles per key block = 2^lsh
+    const int nw = a.bq > 32 ? 2 : 1;
+    const size_t dyn = 2 * (size_t)128 * a.D + (size_t)a.top_k * sizeof(int32_t) + nw * sizeof(int);
+    if (a.D == 64) {
+        if (nw == 2)
+            hipLaunchKernelGGL((hf::sparse_attn_kernel<64, 2>), grid, dim3(128), dyn, s, a, magicT, c_log2, per_xcd, lsh);
+        else
+            hipLaunchKernelGGL((hf::sparse_attn_kernel<64, 1>), grid, dim3(64), dyn, s, a, magicT, c_log2, per_xcd, lsh);
+    } else {
+        if (nw == 2)
+            hipLaunchKernelGGL((hf::sparse_attn_kernel<128, 2>), grid, dim3(128), dyn, s, a, magicT, c_log2, per_xcd, lsh);
+        else
+            hipLaunchKernelGGL((hf::sparse_attn_kernel<128, 1>), grid, dim3(64), dyn, s, a, magicT, c_log2, per_xcd, lsh);
+    }
     return hipGetLastError();
 }

@@ -141,7 +141,8 @@ hf_status hf_ring_append(const hf_dims *d, const hf_kv_ring *ring, const void *k
  *   q_dev          bf16 [B][H][C*T][D] current chunk queries
  *   idx_dev        int32 [B][H][n_qb][top_k] out, n_qb = ceil(C*T/bq)
  *   scores_dev     fp64 [B][H][n_qb][n_kb] out (may be NULL), n_kb = ceil(Nk/bk)
- * Requires 1 <= top_k <= n_kb <= 4096 (HF_ERR_SHAPE otherwise). */
+ * Requires 1 <= top_k <= n_kb (HF_ERR_SHAPE otherwise); n_kb of a full window must not exceed
+ * 1536 (HF_ERR_UNSUPPORTED). */
 hf_status hf_block_select(const hf_dims *d, const void *q_dev, const hf_kv_ring *ring, int32_t top_k,
                           int32_t *idx_dev, double *scores_dev, void *workspace_dev,
                           size_t workspace_bytes, hipStream_t stream);
@@ -151,8 +152,9 @@ hf_status hf_block_select(const hf_dims *d, const void *q_dev, const hf_kv_ring 
  * out[b,h,t,:] = sum_{u in kept blocks of t's block} softmax_u(q_t.k_u / sqrt(D)) v_u
  *              + phi(q_t)^T S[b,h] / (phi(q_t) . z[b,h] + eps)
  *   q_dev    bf16 [B][H][C*T][D]
- *   idx_dev  int32 [B][H][n_qb][top_k]: kept key blocks, each in [0, n_kb); duplicates
- *            are not allowed (hf_block_select's output qualifies)
+ *   idx_dev  int32 [B][H][n_qb][top_k]: kept key blocks, each in [0, n_kb), STRICTLY
+ *            ASCENDING per query block (hf_block_select's output qualifies).  Other lists
+ *            give unspecified values, but every access stays inside the window.
  *   S_dev    fp32 [B][H][D][D] (S[a][c]) and z_dev fp32 [B][H][D]: the linear state;
  *            both NULL -> the linear branch is skipped (sparse part only)
  *   out_dev  fp32 [B][H][C*T][D] out

@@ -28,6 +28,8 @@
 //     reaches 2^32, the block is recomputed with an online (rescaling) softmax.  Short
 //     subtiles (the tail of a short last key block; every subtile when bk < 32) use the
 //     online softmax with masking.
+#include <type_traits>
+
 #include "hf_internal.h"
 
 namespace hf {
@@ -137,15 +139,18 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
     constexpr int NK = kSub / RPI;        // K load instructions per subtile
     constexpr int NV = D / 16;            // V^T load instructions per subtile (16 feature rows each)
     constexpr int KW = NK / NW, VW = NV / NW;
-    constexpr int KBYTES = kSub * D * 2, SLOT = KBYTES + D * 64;
+    constexpr int KBYTES = kSub * D * 2, VBYTES = D * 64;
 
-    extern __shared__ __align__(16) unsigned char dyn[];   // [2 slots][kept list][NW flags]
+    // dynamic LDS: [K stage 0][K stage 1][V stage 0][V stage 1][kept list][NW flags]
+    extern __shared__ __align__(16) unsigned char dyn[];
     const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (item >= a.BH * a.nqb) return;   // uniform per workgroup
     const int bh = item / a.nqb, qb = item - bh * a.nqb;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
     const int q0 = qb * a.bq, qend = min(q0 + a.bq, a.Nq);
-    int32_t *s_blist = reinterpret_cast<int32_t *>(dyn + 2 * SLOT);
+    unsigned char *const kst = dyn, *const vst = dyn + 2 * KBYTES;
+    int32_t *s_blist = reinterpret_cast<int32_t *>(dyn + 2 * (KBYTES + VBYTES));
     int *s_flag = reinterpret_cast<int *>(s_blist + a.top_k);
 
     // kept blocks -> LDS (out-of-range entries, a caller error, are clamped so that no load
@@ -197,70 +202,99 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
         return s >= W ? s - W : s;
     };
 
-    // ---- per-lane load plan: this wave issues K instructions w*KW .. and V instructions w*VW ..
-    uint32_t kofs[KW], vofs[VW];
+    // ---- per-lane load plan; this wave issues K instructions w*KW .. and V instructions w*VW ..
+    // Both stages are row-major with chunk positions swizzled per row: K row r (key r of the
+    // subtile) holds D/8 chunks, V^T row f (feature f) the subtile's 4 eight-key chunks.
+    // One instruction fetches RPI whole K rows, or 16 whole V^T row segments.
+    // Subtiles start at multiples of 32 keys and T is a multiple of 8, so a frame boundary
+    // inside a subtile falls on a multiple of 8 keys and never inside a K instruction's rows:
+    // the K frame choice is a scalar offset.  A V^T instruction spans all 32 keys, so a
+    // subtile that crosses a frame boundary takes a per-lane path.
+    uint32_t kvo[KW], vvo[VW];
     int krow[KW], vkr[VW];
 #pragma unroll
     for (int jj = 0; jj < KW; ++jj) {
-        const int r = RPI * (w * KW + jj) + lane / LPR;
+        const int j = w * KW + jj;
+        const int r = RPI * j + lane / LPR;
         const int c = (lane % LPR) ^ swz_k<D>(r);
         krow[jj] = r;
-        kofs[jj] = (uint32_t)(r * D * 2 + c * 16);
+        kvo[jj] = (uint32_t)((lane / LPR) * D * 2 + c * 16);      // within the instruction's rows
     }
 #pragma unroll
     for (int jj = 0; jj < VW; ++jj) {
         const int f = 16 * (w * VW + jj) + (lane >> 2);
         const int c = (lane & 3) ^ swz_v(f);
         vkr[jj] = 8 * c;
-        vofs[jj] = (uint32_t)(f * T * 2 + c * 16);
+        vvo[jj] = (uint32_t)(f * T * 2 + c * 16);
     }
-    // Fast plan for a full subtile (T >= 32: its keys lie in frame f0 from token t0 on and,
-    // from row `split` on, in frame f0 + 1).
-    auto dma_full = [&](int k0, int slot) {
+    // Frame geometry of a full subtile (T >= 32): its keys lie in frame f0 from token t0 on
+    // and, from key `split` (a multiple of 8) on, in frame f0 + 1.  Wave-uniform scalars.
+    struct Geo {
+        uint32_t kb0, kb1, vb0, vb1;
+        int split;
+    };
+    auto geo_of = [&](int k0) -> Geo {
         const int f0 = fast_div(k0, magicT, T);
         const int t0 = k0 - f0 * T;
-        const int s0 = slot_of(f0), s1 = slot_of(f0 + 1);
         const int split = T - t0;
-        const uint32_t sb0 = (uint32_t)((s0 * T + t0) * D * 2), sb1 = (uint32_t)((s1 * T - split) * D * 2);
-        const uint32_t sv0 = (uint32_t)(s0 * D * T * 2 + t0 * 2), sv1 = (uint32_t)(s1 * D * T * 2 - split * 2);
-        unsigned char *base = dyn + slot * SLOT;
+        const int s0 = slot_of(f0), s1 = slot_of(f0 + 1);
+        return Geo{(uint32_t)((s0 * T + t0) * D * 2), (uint32_t)((s1 * T - split) * D * 2),
+                   (uint32_t)(s0 * D * T * 2 + t0 * 2), (uint32_t)(s1 * D * T * 2 - split * 2), split};
+    };
+    auto dma_full_k = [&](const Geo &ge, int st) {
 #pragma unroll
-        for (int jj = 0; jj < KW; ++jj)
-            dma16(rk, base + (w * KW + jj) * 1024, (krow[jj] < split ? sb0 : sb1) + kofs[jj]);
+        for (int jj = 0; jj < KW; ++jj) {
+            const int j = w * KW + jj;
+            const uint32_t so = (RPI * j < ge.split ? ge.kb0 : ge.kb1) + (uint32_t)(RPI * j * D * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LdsPtr)(kst + st * KBYTES + j * 1024), 16, (int)kvo[jj], (int)so, 0, 0);
+        }
+    };
+    auto dma_full_v = [&](const Geo &ge, int st) {
+        if (ge.split >= kSub) {
 #pragma unroll
-        for (int jj = 0; jj < VW; ++jj)
-            dma16(rv, base + KBYTES + (w * VW + jj) * 1024, (vkr[jj] < split ? sv0 : sv1) + vofs[jj]);
+            for (int jj = 0; jj < VW; ++jj)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LdsPtr)(vst + st * VBYTES + (w * VW + jj) * 1024), 16, (int)vvo[jj],
+                                                         (int)ge.vb0, 0, 0);
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < VW; ++jj)
+                dma16(rv, vst + st * VBYTES + (w * VW + jj) * 1024, (vkr[jj] < ge.split ? ge.vb0 : ge.vb1) + vvo[jj]);
+        }
     };
     // General plan (short subtiles, any T): rows past the valid keys re-read the last one.
-    auto dma_any = [&](int k0, int slot) {
+    auto dma_any = [&](int k0, int st) {
         const int nv = nval_of(k0);
-        unsigned char *base = dyn + slot * SLOT;
 #pragma unroll
         for (int jj = 0; jj < KW; ++jj) {
             const int j = k0 + min(krow[jj], nv - 1);
             const int f = fast_div(j, magicT, T);
-            const uint32_t off = (uint32_t)((slot_of(f) * T + (j - f * T)) * D * 2) + (kofs[jj] - (uint32_t)(krow[jj] * D * 2));
-            dma16(rk, base + (w * KW + jj) * 1024, off);
+            const uint32_t off = (uint32_t)((slot_of(f) * T + (j - f * T)) * D * 2) + (kvo[jj] - (uint32_t)((lane / LPR) * D * 2));
+            dma16(rk, kst + st * KBYTES + (w * KW + jj) * 1024, off);
         }
 #pragma unroll
         for (int jj = 0; jj < VW; ++jj) {
             const int j = k0 + min(vkr[jj], (nv - 1) & ~7);
             const int f = fast_div(j, magicT, T);
-            const uint32_t off = (uint32_t)(slot_of(f) * D * T * 2 + (j - f * T) * 2) + (vofs[jj] - (uint32_t)(vkr[jj] * 2));
-            dma16(rv, base + KBYTES + (w * VW + jj) * 1024, off);
+            const uint32_t off = (uint32_t)(slot_of(f) * D * T * 2 + (j - f * T) * 2) + (vvo[jj] - (uint32_t)(vkr[jj] * 2));
+            dma16(rv, vst + st * VBYTES + (w * VW + jj) * 1024, off);
         }
     };
 
     // ---- per-lane operand reads (swizzled chunk positions)
     const int rk_row = perm32(n);
     const int rk_swz = swz_k<D>(rk_row);
-    const int vr_swz = swz_v(rk_row);
-    auto qk_tile = [&](int slot) -> f32x16 {
-        const unsigned char *kb = dyn + slot * SLOT + rk_row * D * 2;
+    // per-lane byte offsets of the operand fragments within a stage (stage offsets are
+    // added as instruction immediates where the stage is known at compile time)
+    uint32_t koff[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) koff[ks] = (uint32_t)(rk_row * D * 2 + (((2 * ks + g) ^ rk_swz) << 4));
+    uint32_t voff[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) voff[ks] = (uint32_t)(rk_row * 64 + (((2 * g + ks) ^ swz_v(rk_row)) << 4));
+    auto qk_from = [&](const unsigned char *kb) -> f32x16 {
         u32x4 kfr[D / 16];
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            kfr[ks] = *reinterpret_cast<const u32x4 *>(kb + (((2 * ks + g) ^ rk_swz) << 4));
+        for (int ks = 0; ks < D / 16; ++ks) kfr[ks] = *reinterpret_cast<const u32x4 *>(kb + koff[ks]);
         f32x16 s = {};
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) s = mfma32(as_bf16x8(kfr[ks]), as_bf16x8(qf[ks]), s);
@@ -269,19 +303,20 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
     f32x16 acc[D / 32];
 #pragma unroll
     for (int ft = 0; ft < D / 32; ++ft) acc[ft] = f32x16{};
-    auto pv_tile = [&](int slot, const u32x4 (&pf)[2]) {
-        const unsigned char *vb = dyn + slot * SLOT + KBYTES + rk_row * 64;
+    auto pv_from = [&](const unsigned char *vb, const u32x4 (&pf)[2]) {
         u32x4 vfr[D / 32][2];
 #pragma unroll
         for (int ft = 0; ft < D / 32; ++ft)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                vfr[ft][ks] = *reinterpret_cast<const u32x4 *>(vb + ft * 2048 + (((2 * g + ks) ^ vr_swz) << 4));
+                vfr[ft][ks] = *reinterpret_cast<const u32x4 *>(vb + ft * 2048 + voff[ks]);
 #pragma unroll
         for (int ft = 0; ft < D / 32; ++ft)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) acc[ft] = mfma32(as_bf16x8(vfr[ft][ks]), as_bf16x8(pf[ks]), acc[ft]);
     };
+    auto qk_tile = [&](int st) -> f32x16 { return qk_from(kst + st * KBYTES); };
+    auto pv_tile = [&](int st, const u32x4 (&pf)[2]) { pv_from(vst + st * VBYTES, pf); };
     auto rescale = [&](float alpha) {
         if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
@@ -299,27 +334,42 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
 
     SmState sm{-INFINITY, 0.f};
     int ustart = 0;            // first subtile of the online loop
-    bool first_issued = false; // its load is already in flight
     if (nfull > 0) {
-        // ---- fast path over the full subtiles
-        dma_full(key0_of(0), 0);
+        // ---- fast path over the full subtiles, software-pipelined: step u computes
+        // S_{u+1} = K_{u+1} Q^T while the softmax of S_u runs, then O += V_u P_u.  K runs one
+        // subtile ahead of V, so K_{u+2} and V_{u+1} are fetched during step u into the K / V
+        // stages that step u-1 finished with (the barrier closing each step orders this).
+        // Past the last subtile the fetches repeat it and the extra product is discarded.
+        const int last = nfull - 1;
+        const Geo g0 = geo_of(key0_of(0));
+        Geo g1 = geo_of(key0_of(min(1, last)));
+        dma_full_k(g0, 0);
+        dma_full_v(g0, 0);
+        dma_full_k(g1, 1);
         stage_ready();
-        if (1 < nfull) dma_full(key0_of(1), 1);
-        else if (1 < nsubt) dma_any(key0_of(1), 1);
-        f32x16 s = qk_tile(0);
-        sm.m = tile_max_log2(s, c_log2);
+        f32x16 s_a = qk_tile(0), s_b;
+        sm.m = tile_max_log2(s_a, c_log2);
         const float moff = -sm.m;
-        u32x4 pf[2];
-        softmax_fixed(s, c_log2, moff, sm.l, pf);
-        pv_tile(0, pf);
-        for (int u = 1; u < nfull; ++u) {
+        __syncthreads();            // K stage 0 is refilled in step 0
+        // one step with stage parity P (compile-time): S_u in s_cur, S_{u+1} -> s_nxt
+        auto step = [&](int u, auto par, const f32x16 &s_cur, f32x16 &s_nxt) {
+            constexpr int P = decltype(par)::value;
+            const Geo g2 = geo_of(key0_of(min(u + 2, last)));
+            dma_full_k(g2, P);
+            dma_full_v(g1, 1 - P);
+            g1 = g2;
+            s_nxt = qk_from(kst + (1 - P) * KBYTES);
+            u32x4 pf[2];
+            softmax_fixed(s_cur, c_log2, moff, sm.l, pf);
+            pv_from(vst + P * VBYTES, pf);
             stage_ready();
-            if (u + 1 < nfull) dma_full(key0_of(u + 1), (u + 1) & 1);
-            else if (u + 1 < nsubt) dma_any(key0_of(u + 1), (u + 1) & 1);
-            s = qk_tile(u & 1);
-            softmax_fixed(s, c_log2, moff, sm.l, pf);
-            pv_tile(u & 1, pf);
+        };
+        int u = 0;
+        for (; u + 1 < nfull; u += 2) {
+            step(u, std::integral_constant<int, 0>{}, s_a, s_b);
+            step(u + 1, std::integral_constant<int, 1>{}, s_b, s_a);
         }
+        if (u < nfull) step(u, std::integral_constant<int, 0>{}, s_a, s_b);
         // a score far above its reference (row sum >= 2^32): recompute the block online
         const int bad = __builtin_amdgcn_ballot_w64(!(sm.l < kFixedRefLimit)) != 0;
         if (lane == 0) s_flag[w] = bad;
@@ -328,21 +378,18 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
 #pragma unroll
         for (int i = 0; i < NW; ++i) any_bad |= s_flag[i];
         if (any_bad) {
-            __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the load of subtile nfull may be in flight
-            __syncthreads();
             sm = SmState{-INFINITY, 0.f};
 #pragma unroll
             for (int ft = 0; ft < D / 32; ++ft) acc[ft] = f32x16{};
             ustart = 0;
         } else {
             ustart = nfull;
-            first_issued = true;
         }
     }
 
     // ---- online path: short subtiles, or every subtile after a fallback
     if (ustart < nsubt) {
-        if (!first_issued) dma_any(key0_of(ustart), ustart & 1);
+        dma_any(key0_of(ustart), ustart & 1);
         for (int u = ustart; u < nsubt; ++u) {
             stage_ready();
             if (u + 1 < nsubt) dma_any(key0_of(u + 1), (u + 1) & 1);
@@ -422,7 +469,7 @@ hipError_t hf_launch_sparse_attn(const hf_attn_args &a, hipStream_t s) {
     const float c_log2 = (float)(1.4426950408889634 / sqrt((double)a.D));
     const int lsh = a.bk >= 128 ? 2 : (a.bk >= 64 ? 1 : 0);     // 32-key subtiles per key block = 2^lsh
     const int nw = a.bq > 32 ? 2 : 1;
-    const size_t dyn = 2 * (size_t)128 * a.D + (size_t)a.top_k * sizeof(int32_t) + nw * sizeof(int);
+    const size_t dyn = 2 * (size_t)128 * a.D + (size_t)a.top_k * sizeof(int32_t) + nw * sizeof(int);   // 2 K + 2 V stages
     if (a.D == 64) {
         if (nw == 2)
             hipLaunchKernelGGL((hf::sparse_attn_kernel<64, 2>), grid, dim3(128), dyn, s, a, magicT, c_log2, per_xcd, lsh);

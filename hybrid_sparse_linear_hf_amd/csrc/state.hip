@@ -19,36 +19,50 @@ __global__ __launch_bounds__(256) void state_kernel(hf_state_args a) {
     constexpr int tiles = D / 32;
     const int bh = blockIdx.x / (tiles * tiles);
     const int ta = (blockIdx.x / tiles) % tiles, tc = blockIdx.x % tiles;
-    float *S = a.S + (size_t)bh * D * D;
-    const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
-    const size_t items = (size_t)a.BH * (D / 64) * a.P;        // partial blocks
-    for (int r = ty; r < 32; r += 8) {
-        const int row = 32 * ta + r, col = 32 * tc + tx;
-        const float old = S[(size_t)row * D + col];
-        tile[r][tx] = old;
-        if (a.part) {
-            const float *pp = a.part + ((size_t)(bh * (D / 64) + row / 64) * a.P) * 64 * D + (size_t)(row % 64) * D + col;
-            float sum = pp[0];
-            for (int q = 1; q < a.P; ++q) sum += pp[(size_t)q * 64 * D];
-            S[(size_t)row * D + col] = old + sum;
+    // one float4 of the tile per thread: row r, columns c4 .. c4 + 3
+    const int r = threadIdx.x >> 3, c4 = (threadIdx.x & 7) * 4;
+    const int row = 32 * ta + r, col = 32 * tc + c4;
+    float *Sp = a.S + ((size_t)bh * D + row) * D + col;
+    const f32x4 old = *reinterpret_cast<const f32x4 *>(Sp);
+    if (a.part) {
+        // every split's partial is loaded before the first add; the sum runs in split order
+        const float *pp = a.part + ((size_t)(bh * (D / 64) + row / 64) * a.P) * 64 * D + (size_t)(row % 64) * D + col;
+        f32x4 sum = *reinterpret_cast<const f32x4 *>(pp);
+        int q = 1;
+        for (; q + 4 <= a.P; q += 4) {
+            f32x4 v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const f32x4 *>(pp + (size_t)(q + i) * 64 * D);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sum += v[i];
         }
+        for (; q < a.P; ++q) sum += *reinterpret_cast<const f32x4 *>(pp + (size_t)q * 64 * D);
+        *reinterpret_cast<f32x4 *>(Sp) = old + sum;
     }
+    tile[r][c4] = old.x;
+    tile[r][c4 + 1] = old.y;
+    tile[r][c4 + 2] = old.z;
+    tile[r][c4 + 3] = old.w;
     if (tc == 0 && threadIdx.x < 32) {
-        const int row = 32 * ta + threadIdx.x;
-        const float old = a.z[(size_t)bh * D + row];
-        if (a.zc) a.zc[(size_t)bh * D + row] = old;
+        const int zr = 32 * ta + threadIdx.x;
+        const float zold = a.z[(size_t)bh * D + zr];
+        if (a.zc) a.zc[(size_t)bh * D + zr] = zold;
         if (a.part) {
-            const float *zp = a.part + items * 64 * D + ((size_t)(bh * (D / 64) + row / 64) * a.P) * 64 + row % 64;
+            const size_t items = (size_t)a.BH * (D / 64) * a.P;        // partial blocks
+            const float *zp = a.part + items * 64 * D + ((size_t)(bh * (D / 64) + zr / 64) * a.P) * 64 + zr % 64;
             float sum = zp[0];
             for (int q = 1; q < a.P; ++q) sum += zp[(size_t)q * 64];
-            a.z[(size_t)bh * D + row] = old + sum;
+            a.z[(size_t)bh * D + zr] = zold + sum;
         }
     }
     if (!a.st) return;
     __syncthreads();
-    uint16_t *dst = a.st + (size_t)bh * D * D;
-    for (int r = ty; r < 32; r += 8)
-        dst[(size_t)(32 * tc + r) * D + 32 * ta + tx] = (uint16_t)f32_to_bf16_bits(tile[tx][r]);
+    // S^T in bf16: output row 32 tc + cc (a column of the tile), 4 consecutive tile rows
+    const int cc = threadIdx.x >> 3, rr = (threadIdx.x & 7) * 4;
+    uint16_t *dst = a.st + ((size_t)bh * D + 32 * tc + cc) * D + 32 * ta + rr;
+    const uint32_t w0 = pack_bf16x2(tile[rr][cc], tile[rr + 1][cc]);
+    const uint32_t w1 = pack_bf16x2(tile[rr + 2][cc], tile[rr + 3][cc]);
+    *reinterpret_cast<u32x2 *>(dst) = u32x2{w0, w1};
 }
 
 }  // namespace

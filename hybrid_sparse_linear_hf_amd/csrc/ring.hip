@@ -9,47 +9,65 @@ namespace {
 
 constexpr int kTileTok = 64;
 
-// One workgroup per (plane, chunk frame, 64-token tile): K rows copied, V tile transposed
-// through LDS.
+// One workgroup per (plane, chunk frame, 64-token tile).  Threads 0..127 transpose V: each
+// owns an 8-token x 8-feature block, loads its 8 rows (16 bytes each), transposes the 8x8
+// block of 16-bit values in registers (byte permutes) and stores 8 rows of V^T.  Threads
+// 128..255 copy the tile's K rows, 8 16-byte vectors each.  Every load of a thread is issued
+// before its first store.
 template <int D>
 __global__ __launch_bounds__(256) void ring_append_kernel(hf_append_args a) {
-    __shared__ uint16_t tile[kTileTok][D + 8];
     const int tiles_per_frame = (a.T + kTileTok - 1) / kTileTok;
     const int tile_id = blockIdx.x % tiles_per_frame;
     const int fc = (blockIdx.x / tiles_per_frame) % a.C;   // frame within the chunk
     const int bh = blockIdx.x / (tiles_per_frame * a.C);
     const int t0 = tile_id * kTileTok;
-    const int ntok = min(kTileTok, a.T - t0);
+    const int ntok = min(kTileTok, a.T - t0);               // a multiple of 8 (T % 8 == 0)
     int slot = a.head + a.first_frame + fc;
     slot %= a.W;
 
     const size_t src_row0 = ((size_t)bh * a.C + fc) * a.T + t0;           // in rows of D
-    const size_t dst_k_row0 = ((size_t)bh * a.W + slot) * a.T + t0;
-    const uint16_t *ksrc = a.k_cur + src_row0 * D;
-    const uint16_t *vsrc = a.v_cur + src_row0 * D;
-    uint16_t *kdst = a.ring_k + dst_k_row0 * D;
-
-    constexpr int kVecPerRow = D / 8;                                     // 16-byte vectors per row
-    for (int e = threadIdx.x; e < ntok * kVecPerRow; e += 256) {
-        const int r = e / kVecPerRow, c8 = (e % kVecPerRow) * 8;
-        const u32x4 kv = *reinterpret_cast<const u32x4 *>(ksrc + (size_t)r * D + c8);
-        *reinterpret_cast<u32x4 *>(kdst + (size_t)r * D + c8) = kv;
-        const u32x4 vv = *reinterpret_cast<const u32x4 *>(vsrc + (size_t)r * D + c8);
-        *reinterpret_cast<u32x4 *>(&tile[r][c8]) = vv;
-    }
-    __syncthreads();
-
-    // V^T[d][t0 .. t0+ntok): each thread writes 8 consecutive tokens of one d row.
-    uint16_t *vdst = a.ring_vt + ((size_t)bh * a.W + slot) * (size_t)D * a.T + t0;
-    const int groups = ntok / 8;                                          // T % 8 == 0
-    for (int e = threadIdx.x; e < D * groups; e += 256) {
-        const int d = e / groups, g8 = (e % groups) * 8;
-        u32x4 w;
-        w.x = (uint32_t)tile[g8 + 0][d] | ((uint32_t)tile[g8 + 1][d] << 16);
-        w.y = (uint32_t)tile[g8 + 2][d] | ((uint32_t)tile[g8 + 3][d] << 16);
-        w.z = (uint32_t)tile[g8 + 4][d] | ((uint32_t)tile[g8 + 5][d] << 16);
-        w.w = (uint32_t)tile[g8 + 6][d] | ((uint32_t)tile[g8 + 7][d] << 16);
-        *reinterpret_cast<u32x4 *>(vdst + (size_t)d * a.T + g8) = w;
+    const int tid = threadIdx.x;
+    if (tid < 128) {
+        constexpr int kFg = D / 8;                          // feature groups of 8
+        const int fg = tid % kFg, tg = tid / kFg;
+        for (int tgo = tg; tgo < kTileTok / 8; tgo += 128 / kFg) {
+            if (8 * tgo >= ntok) break;
+            const uint16_t *src = a.v_cur + (src_row0 + 8 * tgo) * D + 8 * fg;
+            u32x4 in[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) in[r] = *reinterpret_cast<const u32x4 *>(src + (size_t)r * D);
+            // out[i] = feature 8fg + i over tokens 8tgo .. 8tgo + 7
+            uint16_t *dst = a.ring_vt + (((size_t)bh * a.W + slot) * D + 8 * fg) * a.T + t0 + 8 * tgo;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+                uint32_t o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t wa = in[2 * j][i >> 1], wb = in[2 * j + 1][i >> 1];
+                    o[j] = __builtin_amdgcn_perm(wb, wa, sel);
+                }
+                *reinterpret_cast<u32x4 *>(dst + (size_t)i * a.T) = u32x4{o[0], o[1], o[2], o[3]};
+            }
+        }
+    } else {
+        constexpr int kVecPerRow = D / 8;
+        constexpr int kIters = kTileTok * kVecPerRow / 128;
+        const uint16_t *ksrc = a.k_cur + src_row0 * D;
+        uint16_t *kdst = a.ring_k + (((size_t)bh * a.W + slot) * a.T + t0) * D;
+        u32x4 kv[kIters];
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int e = tid - 128 + 128 * it;
+            const int r = min(e / kVecPerRow, ntok - 1), c8 = (e % kVecPerRow) * 8;
+            kv[it] = *reinterpret_cast<const u32x4 *>(ksrc + (size_t)r * D + c8);
+        }
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int e = tid - 128 + 128 * it;
+            const int r = e / kVecPerRow, c8 = (e % kVecPerRow) * 8;
+            if (r < ntok) *reinterpret_cast<u32x4 *>(kdst + (size_t)r * D + c8) = kv[it];
+        }
     }
 }
 

@@ -8,9 +8,9 @@
 // Three launches:
 //   pool_kernel   HBM-bound: one workgroup per query or key block sums its rows in fp64
 //                 (sums of bf16 values are exact in fp64) and stores the block mean.
-//   score_kernel  16 x 16 tiles of fp64 scores, one wavefront each; every score is
-//                 sum_d (qbar_d * kbar_d) in index order with separately rounded products
-//                 and sums, four independent sums per lane.
+//   score_kernel  16 x 16 tiles of fp64 scores, each evaluated as sum_d (qbar_d * kbar_d) in
+//                 index order with separately rounded products and sums (the pooled
+//                 tiles are staged in LDS, every load issued up front).
 //   topk_kernel   one wave per query block: radix select of the k-th largest
 //                 (score, -index) key and an ascending emit of the kept indices.
 #include "hf_internal.h"
@@ -76,54 +76,52 @@ __device__ __forceinline__ uint64_t order_key(double s) {
 
 constexpr int kTile = 16;   // score tile: 16 query blocks x 16 key blocks per workgroup
 
-// Scores of a 16 x 16 tile of (query block, key block) pairs, one wavefront per tile: both
-// pooled tiles are staged in LDS by 16-byte loads, then each lane forms four dot products
-// (key blocks j0 + (lane & 3) + 4r), each a sequential sum in index order; the four
-// independent chains hide the fp64 add latency.
+// Scores of a 16 x 16 tile of (query block, key block) pairs: both pooled tiles are staged
+// in LDS (every staging load issued before the first LDS write), then each thread forms one
+// dot product as a sequential sum in index order.
 template <int D>
-__global__ __launch_bounds__(64) void score_kernel(hf_select_args a, double scale) {
+__global__ __launch_bounds__(256) void score_kernel(hf_select_args a, double scale) {
     __shared__ double qs[kTile][D + 1];
     __shared__ double ks[kTile][D + 1];
     const int ti_n = (a.nqb + kTile - 1) / kTile, tj_n = (a.nkb + kTile - 1) / kTile;
     const int bh = blockIdx.x / (ti_n * tj_n);
     const int i0 = ((blockIdx.x / tj_n) % ti_n) * kTile, j0 = (blockIdx.x % tj_n) * kTile;
     const int tid = threadIdx.x;
-    for (int e = tid; e < kTile * D / 2; e += 64) {
-        const int r = e / (D / 2), d = 2 * (e % (D / 2));
+    {
+        // rows past the end re-read the last row and are zeroed
         typedef __attribute__((ext_vector_type(2))) double f64x2;
-        const f64x2 zero = {0.0, 0.0};
-        const f64x2 qv = i0 + r < a.nqb ? *reinterpret_cast<const f64x2 *>(a.qbar + ((size_t)bh * a.nqb + i0 + r) * D + d) : zero;
-        const f64x2 kv = j0 + r < a.nkb ? *reinterpret_cast<const f64x2 *>(a.kbar + ((size_t)bh * a.nkb + j0 + r) * D + d) : zero;
-        qs[r][d] = qv.x;
-        qs[r][d + 1] = qv.y;
-        ks[r][d] = kv.x;
-        ks[r][d + 1] = kv.y;
+        constexpr int kPer = kTile * D / 2 / 256;       // 16-byte loads per thread per matrix
+        f64x2 qv[kPer], kv[kPer];
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const int idx = tid + 256 * e, r = idx / (D / 2), d = 2 * (idx % (D / 2));
+            qv[e] = *reinterpret_cast<const f64x2 *>(a.qbar + ((size_t)bh * a.nqb + min(i0 + r, a.nqb - 1)) * D + d);
+            kv[e] = *reinterpret_cast<const f64x2 *>(a.kbar + ((size_t)bh * a.nkb + min(j0 + r, a.nkb - 1)) * D + d);
+        }
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const int idx = tid + 256 * e, r = idx / (D / 2), d = 2 * (idx % (D / 2));
+            const bool qok = i0 + r < a.nqb, kok = j0 + r < a.nkb;
+            qs[r][d] = qok ? qv[e].x : 0.0;
+            qs[r][d + 1] = qok ? qv[e].y : 0.0;
+            ks[r][d] = kok ? kv[e].x : 0.0;
+            ks[r][d + 1] = kok ? kv[e].y : 0.0;
+        }
     }
     __syncthreads();
-    const int ti = tid >> 2, tj = tid & 3;
-    const int i = i0 + ti;
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    const int ti = tid / kTile, tj = tid % kTile;
+    const int i = i0 + ti, j = j0 + tj;
+    if (i >= a.nqb || j >= a.nkb) return;
+    double acc = 0.0;
     {
         // products and sums rounded separately (no fused multiply-add), in index order
 #pragma clang fp contract(off)
-#pragma unroll 4
-        for (int d = 0; d < D; ++d) {
-            const double qd = qs[ti][d];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = acc[r] + qd * ks[tj + 4 * r][d];
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = acc[r] * scale;
+#pragma unroll 8
+        for (int d = 0; d < D; ++d) acc = acc + qs[ti][d] * ks[tj][d];
+        acc = acc * scale;
     }
-    if (i >= a.nqb) return;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int j = j0 + tj + 4 * r;
-        if (j < a.nkb) {
-            a.sc[((size_t)bh * a.nqb + i) * a.nkb + j] = acc[r];
-            if (a.scores) a.scores[((size_t)bh * a.nqb + i) * a.nkb + j] = acc[r];
-        }
-    }
+    a.sc[((size_t)bh * a.nqb + i) * a.nkb + j] = acc;
+    if (a.scores) a.scores[((size_t)bh * a.nqb + i) * a.nkb + j] = acc;
 }
 
 // One wave per (plane, query block): radix select of the k-th largest (score, -index)
@@ -188,10 +186,10 @@ hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s) {
     const double scale = 1.0 / sqrt((double)a.D);
     if (a.D == 64) {
         hipLaunchKernelGGL(hf::pool_kernel<64>, grid_pool, dim3(256), 0, s, a);
-        hipLaunchKernelGGL(hf::score_kernel<64>, grid_score, dim3(64), 0, s, a, scale);
+        hipLaunchKernelGGL(hf::score_kernel<64>, grid_score, dim3(256), 0, s, a, scale);
     } else {
         hipLaunchKernelGGL(hf::pool_kernel<128>, grid_pool, dim3(256), 0, s, a);
-        hipLaunchKernelGGL(hf::score_kernel<128>, grid_score, dim3(64), 0, s, a, scale);
+        hipLaunchKernelGGL(hf::score_kernel<128>, grid_score, dim3(256), 0, s, a, scale);
     }
     const int kpl = (a.nkb + 63) / 64;
     if (kpl <= 1) hipLaunchKernelGGL(hf::topk_kernel<1>, grid_topk, dim3(256), 0, s, a);

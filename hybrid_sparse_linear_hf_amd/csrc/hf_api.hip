@@ -339,9 +339,10 @@ hf_status hf_hybrid_step(const hf_dims *d, const void *q, const void *k_cur, con
     st = check_ws(d, ws, ws_bytes);
     if (st != HF_OK) return st;
 
-    // Order: append; absorb partials of the frames this step will evict (they stay in the
-    // ring until the next append); select; state pass (readout operands from the state as
-    // it is, then the partials added in); attention with the fused readout.
+    // Order: append; select; readout operands from the state as it is; attention with the
+    // fused readout; then the absorb of the frames this step evicts (still in the ring
+    // until the next append, and just streamed through the caches by the attention) and
+    // the state update.
     hf_kv_ring next = *ring;
     int evict = 0;
     if (flags & HF_STEP_COMMIT) {
@@ -355,13 +356,14 @@ hf_status hf_hybrid_step(const hf_dims *d, const void *q, const void *k_cur, con
     hipError_t e = record(events, 0, stream);
     if (e == hipSuccess && k_cur) e = enqueue_append(d, ring, k_cur, v_cur, stream);
     if (e == hipSuccess) e = record(events, 1, stream);
-    if (e == hipSuccess && evict_tok > 0) e = enqueue_absorb_partial(d, nullptr, nullptr, evict_tok, ring, ws, stream);
-    if (e == hipSuccess) e = record(events, 2, stream);
     if (e == hipSuccess) e = enqueue_select(d, q, ring, top_k, idx, nullptr, ws, stream);
+    if (e == hipSuccess) e = record(events, 2, stream);
+    if (e == hipSuccess && S) e = enqueue_state(d, S, z, true, 0, ws, stream);
     if (e == hipSuccess) e = record(events, 3, stream);
-    if (e == hipSuccess && S) e = enqueue_state(d, S, z, true, evict_tok, ws, stream);
-    if (e == hipSuccess) e = record(events, 4, stream);
     if (e == hipSuccess) e = enqueue_attn(d, q, ring, idx, top_k, S != nullptr, eps, out, ws, stream);
+    if (e == hipSuccess) e = record(events, 4, stream);
+    if (e == hipSuccess && evict_tok > 0) e = enqueue_absorb_partial(d, nullptr, nullptr, evict_tok, ring, ws, stream);
+    if (e == hipSuccess && evict_tok > 0) e = enqueue_state(d, S, z, false, evict_tok, ws, stream);
     if (e == hipSuccess) e = record(events, 5, stream);
     if (e != hipSuccess) return hip_status(e, "hybrid step launch");
     *ring = next;

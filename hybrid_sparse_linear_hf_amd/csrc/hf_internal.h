@@ -33,8 +33,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// elu(x) + 1
-__device__ __forceinline__ float phi_f32(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+// elu(x) + 1, branch-free: exp(x) as exp2(x log2 e) on the transcendental unit, selected
+// for x <= 0.
+__device__ __forceinline__ float phi_f32(float x) {
+    const float e = __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+    return x > 0.f ? x + 1.f : e;
+}
 
 // n / d for 0 <= n < 2^31 with magic = ceil(2^32 / d) (one correction step suffices).
 __host__ __device__ inline uint32_t div_magic(uint32_t d) {

@@ -13,6 +13,8 @@
 namespace hf {
 namespace {
 
+constexpr int kGroup = 16;   // partial loads in flight per thread
+
 template <int D>
 __global__ __launch_bounds__(256) void state_kernel(hf_state_args a) {
     __shared__ float tile[32][33];
@@ -25,18 +27,19 @@ __global__ __launch_bounds__(256) void state_kernel(hf_state_args a) {
     float *Sp = a.S + ((size_t)bh * D + row) * D + col;
     const f32x4 old = *reinterpret_cast<const f32x4 *>(Sp);
     if (a.part) {
-        // every split's partial is loaded before the first add; the sum runs in split order
+        // the partials are loaded 16 splits at a time, all before the first add; the sum
+        // runs in split order
         const float *pp = a.part + ((size_t)(bh * (D / 64) + row / 64) * a.P) * 64 * D + (size_t)(row % 64) * D + col;
-        f32x4 sum = *reinterpret_cast<const f32x4 *>(pp);
-        int q = 1;
-        for (; q + 4 <= a.P; q += 4) {
-            f32x4 v[4];
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+        for (int q0 = 0; q0 < a.P; q0 += kGroup) {
+            f32x4 v[kGroup];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const f32x4 *>(pp + (size_t)(q + i) * 64 * D);
+            for (int i = 0; i < kGroup; ++i)
+                v[i] = q0 + i < a.P ? *reinterpret_cast<const f32x4 *>(pp + (size_t)(q0 + i) * 64 * D) : f32x4{};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sum += v[i];
+            for (int i = 0; i < kGroup; ++i)
+                if (q0 + i < a.P) sum += v[i];
         }
-        for (; q < a.P; ++q) sum += *reinterpret_cast<const f32x4 *>(pp + (size_t)q * 64 * D);
         *reinterpret_cast<f32x4 *>(Sp) = old + sum;
     }
     tile[r][c4] = old.x;
@@ -50,8 +53,15 @@ __global__ __launch_bounds__(256) void state_kernel(hf_state_args a) {
         if (a.part) {
             const size_t items = (size_t)a.BH * (D / 64) * a.P;        // partial blocks
             const float *zp = a.part + items * 64 * D + ((size_t)(bh * (D / 64) + zr / 64) * a.P) * 64 + zr % 64;
-            float sum = zp[0];
-            for (int q = 1; q < a.P; ++q) sum += zp[(size_t)q * 64];
+            float sum = 0.f;
+            for (int q0 = 0; q0 < a.P; q0 += kGroup) {
+                float v[kGroup];
+#pragma unroll
+                for (int i = 0; i < kGroup; ++i) v[i] = q0 + i < a.P ? zp[(size_t)(q0 + i) * 64] : 0.f;
+#pragma unroll
+                for (int i = 0; i < kGroup; ++i)
+                    if (q0 + i < a.P) sum += v[i];
+            }
             a.z[(size_t)bh * D + zr] = zold + sum;
         }
     }

@@ -108,9 +108,10 @@ typedef struct {
 #define HF_STEP_COMMIT 1u
 
 /* Optional timing hooks for hf_hybrid_step: any non-NULL event is recorded on the
- * step's stream at that point: ev[0] begin, ev[1] after the ring append, ev[2] after the
- * absorb partial sums, ev[3] after block selection, ev[4] after the state pass, ev[5]
- * after the attention kernel.  Events must have been created by the caller with
+ * step's stream at that point: ev[0] begin, ev[1] after the ring append, ev[2] after
+ * block selection, ev[3] after the readout operands are prepared, ev[4] after the
+ * attention kernel, ev[5] after the absorb of the evicted frames and the state update
+ * (the end of the step).  Events must have been created by the caller with
  * hipEventCreate. */
 typedef struct {
     hipEvent_t ev[6];
@@ -181,13 +182,13 @@ hf_status hf_linear_absorb(const hf_dims *d, const void *k_ev_dev, const void *v
 /* One hybrid attention step on the ring:
  *   1. if k_cur_dev and v_cur_dev are given: hf_ring_append (else the caller has
  *      already written the current chunk into its slots);
- *   2. with HF_STEP_COMMIT, when committing the chunk leaves more than W - C committed
- *      frames, the e oldest window frames are the evicted ones: their absorb partial sums
- *      are computed now (those frames stay in the ring until the next append);
- *   3. block selection as hf_block_select -> idx_dev ([B][H][n_qb][top_k], an output);
- *   4. state pass: the readout operands are taken from (S, z) as they are, then the
- *      partial sums of step 2 are added into (S, z) (as hf_linear_absorb would);
- *   5. block-sparse attention with the fused readout, as hf_sparse_window_attn -> out_dev;
+ *   2. block selection as hf_block_select -> idx_dev ([B][H][n_qb][top_k], an output);
+ *   3. the readout operands are taken from (S, z) as they are;
+ *   4. block-sparse attention with the fused readout, as hf_sparse_window_attn -> out_dev;
+ *   5. with HF_STEP_COMMIT, when committing the chunk leaves more than W - C committed
+ *      frames, the e oldest window frames are the evicted ones: they are absorbed into
+ *      (S, z) as hf_linear_absorb would (those frames stay in the ring until the next
+ *      append, so they are read right after the attention has streamed them);
  *   6. with HF_STEP_COMMIT: n_committed += C - e and head = (head + e) % W.
  * The output therefore reads the state before this step's evictions, and on return the
  * state includes them.  `ring` is updated on success only.  S_dev/z_dev may be NULL only

@@ -119,6 +119,57 @@ def test_layer_832x480_parity():
     print(f"832x480: {len(blocks)} blocks checked, max-abs {mx:.2e} mean-rel {mr:.2e}")
 
 
+
+@pytest.mark.parametrize("keep", [1.0, 0.5, 0.25, 0.125])
+def test_window21_keep_sweep(keep):
+    """832x480 shapes with a 21-frame window (32760 keys, 512 key blocks), keep ratio swept
+    from keep-all down to 1/8; heads 0 and 5, sampled query blocks."""
+    cfg = synth.LAYER_832x480_W21
+    heads = [0, 5]
+    k = int(np.ceil(keep * cfg.n_kb))
+    print(f"case: 21-frame window, heads {heads}, top-{k} of {cfg.n_kb}", flush=True)
+    g = hf.Geometry(cfg.B, len(heads), cfg.D, cfg.T, cfg.C, cfg.W, cfg.bq, cfg.bk)
+    inp = layer_inputs(cfg, heads=heads)
+    idx, sc, out, S, z = run_select_attn(g, inp, cfg.W - cfg.C, k, head=4)
+    So, zo = oracle.absorb(inp.Kev, inp.Vev)
+    blocks = sample_blocks(len(heads), cfg.n_qb, stride=17)
+    ref, idx_o, sc_o = oracle.hybrid_step(inp.Q, inp.K, inp.V, So, zo, cfg.bq, cfg.bk, k, blocks=blocks,
+                                          want_scores=True)
+    np.testing.assert_array_equal(sc, sc_o)
+    np.testing.assert_array_equal(idx, idx_o)
+    if k == cfg.n_kb:
+        np.testing.assert_array_equal(idx[0, 0, 0], np.arange(cfg.n_kb))
+    rows = rows_of_blocks(blocks, cfg.Nq, cfg.bq, (len(heads), cfg.Nq))
+    mx, mr = assert_close(out.reshape(-1, cfg.Nq, cfg.D)[rows], ref.reshape(-1, cfg.Nq, cfg.D)[rows], "W=21")
+    print(f"W=21 top-{k}: {len(blocks)} blocks checked, max-abs {mx:.2e} mean-rel {mr:.2e}")
+
+
+def test_four_streams_per_layer_seeds():
+    """Four independent streams batched (B=4) at 832x480 shapes on heads 3 and 11, for layers
+    0 and 29 of a stack (each layer seeds its own Q/K/V and state); sampled query blocks."""
+    base = synth.LAYER_832x480
+    cfg = synth.StepConfig("832x480_4streams", B=4, H=base.H, D=base.D, T=base.T, C=base.C, W=base.W,
+                           bq=base.bq, bk=base.bk, keep=base.keep, n_evicted=base.n_evicted)
+    heads = [3, 11]
+    k = cfg.top_k()
+    g = hf.Geometry(cfg.B, len(heads), cfg.D, cfg.T, cfg.C, cfg.W, cfg.bq, cfg.bk)
+    for layer in (0, 29):
+        print(f"case: 4 streams, layer {layer}, heads {heads}, top-{k}", flush=True)
+        d = synth.field_step_inputs(cfg, layer=layer, heads=heads)
+        inp = StepInputs(d["q"], d["k_win"], d["v_win"], d["k_ev"], d["v_ev"])
+        idx, sc, out, S, z = run_select_attn(g, inp, cfg.W - cfg.C, k, head=layer % cfg.W)
+        So, zo = oracle.absorb(inp.Kev, inp.Vev)
+        assert np.linalg.norm(S - So) / np.linalg.norm(So) < 2e-3
+        blocks = sample_blocks(cfg.B * len(heads), cfg.n_qb, stride=23)
+        ref, idx_o, sc_o = oracle.hybrid_step(inp.Q, inp.K, inp.V, So, zo, cfg.bq, cfg.bk, k, blocks=blocks,
+                                              want_scores=True)
+        np.testing.assert_array_equal(sc, sc_o)
+        np.testing.assert_array_equal(idx, idx_o)
+        rows = rows_of_blocks(blocks, cfg.Nq, cfg.bq, (cfg.B * len(heads), cfg.Nq))
+        mx, mr = assert_close(out.reshape(-1, cfg.Nq, cfg.D)[rows], ref.reshape(-1, cfg.Nq, cfg.D)[rows],
+                              f"layer {layer}")
+        print(f"layer {layer}: {len(blocks)} blocks checked, max-abs {mx:.2e} mean-rel {mr:.2e}")
+
 EDGE = [
     # B, H, D, T, C, W, bq, bk, n_committed, top_k
     (1, 2, 128, 200, 1, 3, 64, 64, 2, 3),     # ragged query block (200 = 3*64 + 8), ragged key block

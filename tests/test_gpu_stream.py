@@ -70,10 +70,20 @@ def run_gpu_stream(g, chunks, keep, head0=0):
 SMALL = hf.Geometry(B=1, H=2, D=128, T=96, C=2, W=5, bq=64, bk=32)
 
 
-def test_stream_commit_matches_oracle():
-    print("case: 7-step stream, T=96 C=2 W=5 bk=32, empty window at start", flush=True)
-    g, keep = SMALL, 0.3
-    chunks = random_chunks(g, 7, seed=11)
+STREAMS = [
+    # geometry, steps, keep: frames of 96 tokens (chunks cross frames), D=64 (the four-wave
+    # absorb), frames shorter than a 64-token absorb chunk (several frames per chunk)
+    (SMALL, 7, 0.3),
+    (hf.Geometry(B=2, H=1, D=64, T=64, C=1, W=4, bq=16, bk=16), 6, 0.25),
+    (hf.Geometry(B=1, H=3, D=128, T=40, C=3, W=7, bq=32, bk=16), 5, 0.4),
+]
+
+
+@pytest.mark.parametrize("g,n_steps,keep", STREAMS)
+def test_stream_commit_matches_oracle(g, n_steps, keep):
+    print(f"case: {n_steps}-step stream, B={g.B} H={g.H} D={g.D} T={g.T} C={g.C} W={g.W} bq={g.bq} bk={g.bk}, "
+          "empty window at start", flush=True)
+    chunks = random_chunks(g, n_steps, seed=11)
     outs, idxs, S, z, ring = run_gpu_stream(g, chunks, keep)
     ref = OracleStream(g.B, g.H, g.D, g.T, g.C, g.W)
     n_committed = 0
@@ -85,8 +95,9 @@ def test_stream_commit_matches_oracle():
         n_committed = min(n_committed + g.C, g.W - g.C)
     assert np.linalg.norm(S - ref.S) / np.linalg.norm(ref.S) < 1e-5
     assert np.linalg.norm(z - ref.z) / np.linalg.norm(ref.z) < 1e-6
-    # 7 chunks of 2 frames, W - C = 3 committed frames kept -> head advanced by 11 mod 5
-    assert (ring.head, ring.n_committed) == ((7 * 2 - 3) % 5, 3)
+    # every step commits C frames and W - C committed frames are kept
+    total = n_steps * g.C
+    assert (ring.head, ring.n_committed) == ((total - (g.W - g.C)) % g.W, g.W - g.C)
 
 
 def test_ring_offset_invariance_and_determinism():

@@ -263,7 +263,7 @@ def main():
         "absorb_roofline": {"bound": "hbm", "achieved": round(absorb_bytes / t_abs / 1e9, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(absorb_bytes / t_abs / 1e9 / PEAK_HBM_GBS, 4),
                             "bytes_per_launch": absorb_bytes,
-                            "note": "absorb partial sums + the state pass that adds them (and prepares the readout)"},
+                            "note": "absorb kernel + the state update that adds its partial sums (ev4 -> ev5)"},
         "select_roofline": {"bound": "hbm", "achieved": round(select_bytes / t_sel / 1e9, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "bytes_per_launch": select_bytes},
         "append_roofline": {"bound": "hbm", "achieved": round(append_bytes / t_app / 1e9, 1), "peak": PEAK_HBM_GBS,

@@ -66,8 +66,11 @@ def lib():
         L.hf_linear_absorb.argtypes = [pd, _P, _P, i64, _P, _P, _P, sz, _P]
         L.hf_hybrid_step.argtypes = [pd, _P, _P, _P, pr, i32, u32, _P, _P, f32, _P, _P, _P, sz,
                                      ctypes.POINTER(StepEvents), _P]
+        f64 = ctypes.c_double
+        L.hf_cag_schedule.argtypes = [i32, ctypes.POINTER(i32), f64, f64, f64, ctypes.POINTER(i32),
+                                      ctypes.POINTER(f64), ctypes.POINTER(f64)]
         for fn in ("hf_workspace_size", "hf_ring_append", "hf_block_select", "hf_sparse_window_attn",
-                   "hf_linear_absorb", "hf_hybrid_step"):
+                   "hf_linear_absorb", "hf_hybrid_step", "hf_cag_schedule"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -191,3 +194,15 @@ def hf_hybrid_step(g: Geometry, q, k_cur, v_cur, ring: Ring, top_k: int, flags: 
                                 int(top_k), int(flags), _ptr(S), _ptr(z), float(eps), _ptr(idx), _ptr(out), _ptr(ws),
                                 ws.numel() if ws is not None else 0, ctypes.byref(ev) if ev is not None else None,
                                 _stream(stream)))
+
+
+def hf_cag_schedule(n_kb, s_base: float, s_target: float, s_max: float):
+    """Chunk-aware growth schedule (host call).  Returns (top_k list, sparsity list, beta)."""
+    n = len(n_kb)
+    nkb = (ctypes.c_int32 * n)(*[int(x) for x in n_kb])
+    k = (ctypes.c_int32 * n)()
+    s = (ctypes.c_double * n)()
+    beta = ctypes.c_double(0.0)
+    _check("hf_cag_schedule", lib().hf_cag_schedule(n, nkb, float(s_base), float(s_target), float(s_max), k, s,
+                                                    ctypes.byref(beta)))
+    return list(k), list(s), beta.value

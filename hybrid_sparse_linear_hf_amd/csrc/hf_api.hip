@@ -237,6 +237,19 @@ extern "C" {
 
 int hf_abi_version(void) { return HF_ABI_VERSION; }
 
+hf_status hf_cag_schedule(int32_t n_chunks, const int32_t *n_kb, double s_base, double s_target, double s_max,
+                          int32_t *top_k, double *sparsity, double *beta) {
+    if (!n_kb || !top_k) return fail(HF_ERR_NULL, "n_kb/top_k is NULL");
+    if (n_chunks < 1) return fail(HF_ERR_SHAPE, "n_chunks=%d must be >= 1", n_chunks);
+    auto unit = [](double x) { return x >= 0.0 && x < 1.0; };   // also rejects NaN
+    if (!unit(s_base) || !unit(s_target) || !unit(s_max))
+        return fail(HF_ERR_SHAPE, "s_base, s_target and s_max must lie in [0, 1)");
+    for (int i = 0; i < n_chunks; ++i)
+        if (n_kb[i] < 1) return fail(HF_ERR_SHAPE, "n_kb[%d]=%d must be >= 1", i, n_kb[i]);
+    hf_status st = hf_cag_schedule_impl(n_chunks, n_kb, s_base, s_target, s_max, top_k, sparsity, beta);
+    return st == HF_OK ? ok() : st;
+}
+
 const char *hf_status_str(hf_status s) {
     switch (s) {
         case HF_OK: return "HF_OK";

@@ -128,6 +128,10 @@ struct hf_state_args {
 };
 hipError_t hf_launch_state(const hf_state_args &a, hipStream_t s);
 
+// Chunk-aware growth schedule (schedule.hip); arguments validated by the caller.
+hf_status hf_cag_schedule_impl(int32_t n, const int32_t *nkb, double s_base, double s_target, double s_max,
+                               int32_t *top_k, double *sparsity, double *beta_out);
+
 struct hf_append_args {
     int BH, D, T, W, head, first_frame, C;
     const uint16_t *k_cur, *v_cur;

@@ -179,6 +179,25 @@ hf_status hf_linear_absorb(const hf_dims *d, const void *k_ev_dev, const void *v
                            float *S_dev, float *z_dev, void *workspace_dev, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* Chunk-aware growth sparsity schedule ([LF-de] §2.1 "Chunk-bewusstes Wachstum"): the
+ * keep counts of a stream of n_chunks chunks, the first dense and later ones sparser.
+ * Host call, no GPU work; every pointer is HOST memory.
+ *   n_kb[i]      key blocks in chunk i's window (>= 1)
+ *   s_base       base sparsity, s_target the sparsity the whole stream must meet, s_max
+ *                the cap of any chunk's sparsity; each in [0, 1)
+ *   top_k[i]     out: kept key blocks per query block for chunk i (pass to hf_block_select
+ *                or hf_hybrid_step)
+ *   sparsity[i]  out (may be NULL): s_i;  beta out (may be NULL): the fitted beta
+ * Schedule: s_0 = 0; s_i = min(max(s_base - beta / sqrt(i + 1), 0), s_max) for i >= 1;
+ * top_k[i] = ceil((1 - s_i) n_kb[i]) clamped to [1, n_kb[i]]; beta >= 0 is the smallest
+ * value (to double precision, by bisection) with sum_i top_k[i] >= (1 - s_target) sum_i
+ * n_kb[i].  Readings: the page's alpha_i "proportional to 1/sqrt(T)" is taken as
+ * 1/sqrt(i + 1) of the chunk's position, and "total FLOPs" as the kept key blocks summed
+ * over the chunks (every chunk has the same query blocks).  Errors: HF_ERR_NULL,
+ * HF_ERR_SHAPE (n_chunks < 1, n_kb[i] < 1, a ratio outside [0, 1) or NaN). */
+hf_status hf_cag_schedule(int32_t n_chunks, const int32_t *n_kb, double s_base, double s_target, double s_max,
+                          int32_t *top_k, double *sparsity, double *beta);
+
 /* One hybrid attention step on the ring:
  *   1. if k_cur_dev and v_cur_dev are given: hf_ring_append (else the caller has
  *      already written the current chunk into its slots);

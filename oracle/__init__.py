@@ -168,3 +168,43 @@ def hybrid_step(Q, K, V, S, z, bq, bk, k, eps=1e-6, blocks=None, want_scores=Fal
     lib().hfo_hybrid_step(B * H, Nq, Nk, D, bq, bk, k, eps, _p(Q), _p(K), _p(V), _p(S), _p(z), _p(bl, _I64), nb,
                           _p(idx, _I32), _p(sc), _p(out))
     return out, idx, sc
+
+
+def cag_schedule(n_kb, s_base, s_target, s_max):
+    """Chunk-aware growth schedule ([LF-de] §2.1 "Chunk-bewusstes Wachstum"), written out
+    plainly: chunk 0 is dense; chunk i >= 1 has sparsity s_base - alpha_i * beta with
+    alpha_i = 1 / sqrt(i + 1) (the page's alpha proportional to one over a square root,
+    read against the chunk's position), clipped to [0, s_max]; its keep count is
+    ceil((1 - s_i) * n_kb[i]) within [1, n_kb[i]]; beta is the smallest value for which
+    the kept key blocks of all chunks reach (1 - s_target) of the dense total.  beta is
+    located by halving an interval that starts at [0, s_base * sqrt(n) + 1] (the upper
+    end makes every chunk dense).  Returns (keep counts, sparsities, beta)."""
+    import math
+    n = len(n_kb)
+
+    def sparsity(i, beta):
+        if i == 0:
+            return 0.0
+        return min(max(s_base - (1.0 / math.sqrt(i + 1)) * beta, 0.0), s_max)
+
+    def keep(s, nkb):
+        return int(min(max(math.ceil((1.0 - s) * nkb), 1), nkb))
+
+    def work(beta):
+        return sum(keep(sparsity(i, beta), n_kb[i]) for i in range(n))
+
+    goal = (1.0 - s_target) * float(sum(n_kb))
+    beta = 0.0
+    if work(0.0) < goal:
+        lo, hi = 0.0, s_base * math.sqrt(n) + 1.0
+        for _ in range(200):
+            mid = 0.5 * (lo + hi)
+            if mid <= lo or mid >= hi:
+                break
+            if work(mid) >= goal:
+                hi = mid
+            else:
+                lo = mid
+        beta = hi
+    ss = [sparsity(i, beta) for i in range(n)]
+    return [keep(ss[i], n_kb[i]) for i in range(n)], ss, beta

@@ -23,7 +23,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ("hf_block_select", "hf_sparse_window_attn", "hf_linear_absorb", "hf_hybrid_step", "hf_ring_append",
-              "hf_workspace_size", "hf_last_error", "hf_status_str", "hf_abi_version"):
+              "hf_workspace_size", "hf_last_error", "hf_status_str", "hf_abi_version", "hf_cag_schedule"):
         assert s in syms
 
 

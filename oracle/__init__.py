@@ -208,3 +208,46 @@ def cag_schedule(n_kb, s_base, s_target, s_max):
         beta = hi
     ss = [sparsity(i, beta) for i in range(n)]
     return [keep(ss[i], n_kb[i]) for i in range(n)], ss, beta
+
+
+def frames_of_block(j, bk, Nk, T):
+    """Window frames (first, last) that key block j = keys [j bk, min((j+1) bk, Nk)) touches."""
+    return (j * bk) // T, (min((j + 1) * bk, Nk) - 1) // T
+
+
+def hier_select(Q, K, bq, bk, T, k_frames, k):
+    """Hierarchical coarse-to-fine block selection ([LF-de] §2.2 "Hierarchische Spärliche
+    Attention"), in the pages' order:
+      token compression -- queries pooled per query block, keys per key block and per
+          window frame (T keys), all by the mean;
+      frame selection -- per query block, score every window frame by the pooled query
+          block . the frame-pooled keys / sqrt(D) and keep the k_frames best (ties to the
+          lower frame);
+      block selection -- among the key blocks that touch a kept frame, keep the k best by
+          the usual block score (ties to the lower block), listed ascending.
+    Q [B,H,Nq,D], K [B,H,Nk,D] with Nk a whole number of frames.  Returns
+    (idx [B,H,nqb,k] int32, frames [B,H,nqb,k_frames] int32, block scores, frame scores)."""
+    Q, K = _f64(Q), _f64(K)
+    B, H, Nk, D = K.shape
+    if Nk % T:
+        raise ValueError("the window must hold whole frames")
+    qbar, kbar, fbar = pool(Q, bq), pool(K, bk), pool(K, T)
+    s = block_scores(qbar, kbar)
+    sf = block_scores(qbar, fbar)
+    frames = select(sf, k_frames)
+    nqb, nkb = s.shape[2], s.shape[3]
+    idx = np.empty((B, H, nqb, k), dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nqb):
+                kept = set(int(f) for f in frames[b, h, i])
+                cand = []
+                for j in range(nkb):
+                    f0, f1 = frames_of_block(j, bk, Nk, T)
+                    if any(f in kept for f in range(f0, f1 + 1)):
+                        cand.append((-s[b, h, i, j], j))
+                if len(cand) < k:
+                    raise ValueError("fewer key blocks in the kept frames than k")
+                cand.sort()
+                idx[b, h, i] = sorted(j for _, j in cand[:k])
+    return idx, frames, s, sf

@@ -299,3 +299,59 @@ def test_sparse_large_logits_stay_finite():
     out = oracle.sparse_attn(Q, K, V, idx, bq, bk)
     assert np.all(np.isfinite(out))
     np.testing.assert_allclose(out, dense_attention(Q, K, V), rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- hierarchical selection
+# [LF-de] §2.2: frames first (frame-pooled keys), then blocks inside the kept frames.
+
+def _brute_hier(Q, K, bq, bk, T, kf, k):
+    """Independent loops: means, dot products, sorted() with explicit keys."""
+    Nq, D, Nk = len(Q), len(Q[0]), len(K)
+    mean = lambda X, a, b: [sum(X[t][d] for t in range(a, b)) / (b - a) for d in range(D)]
+    dot = lambda x, y: sum(x[d] * y[d] for d in range(D)) / math.sqrt(D)
+    qb = [mean(Q, i, min(i + bq, Nq)) for i in range(0, Nq, bq)]
+    kb = [mean(K, j, min(j + bk, Nk)) for j in range(0, Nk, bk)]
+    fb = [mean(K, f, f + T) for f in range(0, Nk, T)]
+    out = []
+    for q in qb:
+        fr = sorted(range(len(fb)), key=lambda f: (-dot(q, fb[f]), f))[:kf]
+        ok = [j for j in range(len(kb)) if any(t // T in fr for t in range(j * bk, min((j + 1) * bk, Nk)))]
+        out.append(sorted(sorted(ok, key=lambda j: (-dot(q, kb[j]), j))[:k]))
+    return out
+
+
+@pytest.mark.parametrize("Nq,T,nfr,D,bq,bk,kf,k", [(32, 24, 5, 8, 16, 16, 2, 3), (20, 40, 4, 4, 8, 16, 1, 2),
+                                                    (16, 16, 6, 6, 16, 32, 3, 2)])
+def test_hier_select_brute_force(Nq, T, nfr, D, bq, bk, kf, k):
+    rng = np.random.default_rng(Nq * 7 + T)
+    Q = rng.standard_normal((1, 1, Nq, D))
+    K = rng.standard_normal((1, 1, nfr * T, D))
+    idx, frames, _, _ = oracle.hier_select(Q, K, bq, bk, T, kf, k)
+    ref = _brute_hier(Q[0, 0].tolist(), K[0, 0].tolist(), bq, bk, T, kf, k)
+    assert idx[0, 0].tolist() == ref
+
+
+def test_hier_select_all_frames_is_flat_select():
+    rng = np.random.default_rng(5)
+    Q = rng.standard_normal((2, 2, 100, 16))
+    K = rng.standard_normal((2, 2, 6 * 40, 16))
+    idx, _, s, _ = oracle.hier_select(Q, K, 32, 16, 40, 6, 5)
+    np.testing.assert_array_equal(idx, oracle.select(s, 5))
+
+
+def test_hier_select_constructed_frames():
+    # four frames of constant, orthogonal keys; every query points at frame 2, so frame 2
+    # and (tie-broken by index) frame 0 among the equal rest are kept for k_frames = 2 and
+    # only blocks touching those frames can be chosen
+    T, D = 16, 4
+    K = np.zeros((1, 1, 4 * T, D))
+    for f in range(4):
+        K[0, 0, f * T:(f + 1) * T, f] = 1.0
+    Q = np.zeros((1, 1, 8, D))
+    Q[..., 2] = 1.0
+    idx, frames, _, sf = oracle.hier_select(Q, K, 8, 8, T, 2, 4)
+    assert frames[0, 0, 0].tolist() == [0, 2]
+    assert sf[0, 0, 0, 2] > sf[0, 0, 0, 0] == sf[0, 0, 0, 1] == sf[0, 0, 0, 3] == 0.0
+    assert idx[0, 0, 0].tolist() == [0, 1, 4, 5]
+    # a key block straddling a kept and a dropped frame is eligible
+    assert oracle.frames_of_block(1, 24, 64, 16) == (1, 2)

@@ -4,6 +4,7 @@ The compute lives in libhf.so (HIP kernels behind the C ABI of include/hf.h);
 `_lib` is its ctypes binding and `synth` draws seeded synthetic inputs.
 """
 
-from ._lib import (HF_STEP_COMMIT, Geometry, HFError, Ring, abi_version, hf_block_select, hf_cag_schedule,  # noqa: F401
+from ._lib import (HF_STEP_COMMIT, Geometry, HFError, Ring, abi_version, hf_block_select,  # noqa: F401
+                   hf_block_select_hier, hf_cag_schedule,
                    hf_hybrid_step, hf_linear_absorb, hf_ring_append, hf_sparse_window_attn, new_workspace,
                    workspace_size)

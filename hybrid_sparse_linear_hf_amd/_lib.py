@@ -66,11 +66,12 @@ def lib():
         L.hf_linear_absorb.argtypes = [pd, _P, _P, i64, _P, _P, _P, sz, _P]
         L.hf_hybrid_step.argtypes = [pd, _P, _P, _P, pr, i32, u32, _P, _P, f32, _P, _P, _P, sz,
                                      ctypes.POINTER(StepEvents), _P]
+        L.hf_block_select_hier.argtypes = [pd, _P, pr, i32, i32, _P, _P, _P, _P, _P, sz, _P]
         f64 = ctypes.c_double
         L.hf_cag_schedule.argtypes = [i32, ctypes.POINTER(i32), f64, f64, f64, ctypes.POINTER(i32),
                                       ctypes.POINTER(f64), ctypes.POINTER(f64)]
         for fn in ("hf_workspace_size", "hf_ring_append", "hf_block_select", "hf_sparse_window_attn",
-                   "hf_linear_absorb", "hf_hybrid_step", "hf_cag_schedule"):
+                   "hf_linear_absorb", "hf_hybrid_step", "hf_cag_schedule", "hf_block_select_hier"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -166,6 +167,14 @@ def hf_block_select(g: Geometry, q, ring: Ring, top_k: int, idx, scores, ws, str
     _check("hf_block_select",
            lib().hf_block_select(ctypes.byref(g.dims()), _ptr(q), ctypes.byref(ring.desc), int(top_k), _ptr(idx),
                                  _ptr(scores), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def hf_block_select_hier(g: Geometry, q, ring: Ring, top_frames: int, top_k: int, idx, ws, frames=None,
+                         scores=None, frame_scores=None, stream=None) -> None:
+    _check("hf_block_select_hier",
+           lib().hf_block_select_hier(ctypes.byref(g.dims()), _ptr(q), ctypes.byref(ring.desc), int(top_frames),
+                                      int(top_k), _ptr(idx), _ptr(frames), _ptr(scores), _ptr(frame_scores),
+                                      _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def hf_sparse_window_attn(g: Geometry, q, ring: Ring, idx, top_k: int, S, z, out, ws, eps=1e-6, stream=None) -> None:

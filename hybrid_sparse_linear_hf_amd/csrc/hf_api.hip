@@ -75,8 +75,9 @@ Geometry geometry(const hf_dims *d, const hf_kv_ring *r) {
 
 // Workspace layout (offsets 256-byte aligned):
 //   [absorb partials]  [qbar fp64]  [kbar fp64]  [scores fp64]  [S^T bf16]  [z copy fp32]
+//   [frame-pooled keys fp64, up to kMaxHierFrames frames]
 struct WsLayout {
-    size_t absorb, qbar, kbar, sc, st, zc, total;
+    size_t absorb, qbar, kbar, sc, st, zc, fbar, total;
 };
 
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -92,7 +93,9 @@ WsLayout ws_layout(const hf_dims *d) {
     w.sc = w.kbar + al((size_t)BH * nkb * d->D * sizeof(double));
     w.st = w.sc + al((size_t)BH * nqb * nkb * sizeof(double));
     w.zc = w.st + al((size_t)BH * d->D * d->D * sizeof(uint16_t));
-    w.total = w.zc + al((size_t)BH * d->D * sizeof(float));
+    w.fbar = w.zc + al((size_t)BH * d->D * sizeof(float));
+    const int frames = d->W < kMaxHierFrames ? d->W : kMaxHierFrames;
+    w.total = w.fbar + al((size_t)BH * frames * d->D * sizeof(double));
     return w;
 }
 
@@ -129,7 +132,8 @@ hipError_t enqueue_append(const hf_dims *d, const hf_kv_ring *r, const void *kc,
 }
 
 hipError_t enqueue_select(const hf_dims *d, const void *q, const hf_kv_ring *r, int top_k, int32_t *idx,
-                          double *scores, void *ws, hipStream_t s) {
+                          double *scores, void *ws, hipStream_t s, int top_frames = 0, int32_t *fidx = nullptr,
+                          double *fscores = nullptr) {
     const Geometry g = geometry(d, r);
     const WsLayout L = ws_layout(d);
     hf_select_args a{};
@@ -152,6 +156,11 @@ hipError_t enqueue_select(const hf_dims *d, const void *q, const hf_kv_ring *r, 
     a.sc = reinterpret_cast<double *>(wsp(ws, L.sc));
     a.idx = idx;
     a.scores = scores;
+    a.nfr = r->n_committed + d->C;
+    a.top_frames = top_frames;
+    a.fbar = reinterpret_cast<double *>(wsp(ws, L.fbar));
+    a.fidx = fidx;
+    a.fscores = fscores;
     return hf_launch_block_select(a, s);
 }
 
@@ -295,6 +304,34 @@ hf_status hf_block_select(const hf_dims *d, const void *q, const hf_kv_ring *rin
     st = check_ws(d, ws, ws_bytes);
     if (st != HF_OK) return st;
     st = hip_status(enqueue_select(d, q, ring, top_k, idx, scores, ws, stream), "block select launch");
+    return st == HF_OK ? ok() : st;
+}
+
+hf_status hf_block_select_hier(const hf_dims *d, const void *q, const hf_kv_ring *ring, int32_t top_frames,
+                               int32_t top_k, int32_t *idx, int32_t *frames, double *scores, double *frame_scores,
+                               void *ws, size_t ws_bytes, hipStream_t stream) {
+    hf_status st = check_dims(d);
+    if (st == HF_OK) st = check_ring(d, ring);
+    if (st != HF_OK) return st;
+    if (!q || !idx) return fail(HF_ERR_NULL, "q/idx is NULL");
+    const Geometry g = geometry(d, ring);
+    const int nfr = ring->n_committed + d->C;
+    if (nfr > kMaxHierFrames)
+        return fail(HF_ERR_UNSUPPORTED, "window of %d frames exceeds %d for the hierarchical selection", nfr,
+                    kMaxHierFrames);
+    if (top_frames < 1 || top_frames > nfr)
+        return fail(HF_ERR_SHAPE, "top_frames=%d outside [1, frames in the window=%d]", top_frames, nfr);
+    // any top_frames distinct frames touch at least this many key blocks
+    const int64_t per_frame = cdiv(d->T, d->bk);
+    const int64_t least = (int64_t)top_frames * per_frame - (top_frames - 1);
+    const int64_t kmax = least < g.nkb ? least : g.nkb;
+    if (top_k < 1 || top_k > kmax)
+        return fail(HF_ERR_SHAPE, "top_k=%d outside [1, %lld] (key blocks guaranteed inside %d frames)", top_k,
+                    (long long)kmax, top_frames);
+    st = check_ws(d, ws, ws_bytes);
+    if (st != HF_OK) return st;
+    st = hip_status(enqueue_select(d, q, ring, top_k, idx, scores, ws, stream, top_frames, frames, frame_scores),
+                    "hierarchical block select launch");
     return st == HF_OK ? ok() : st;
 }
 

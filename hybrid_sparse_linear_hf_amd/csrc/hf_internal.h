@@ -89,7 +89,13 @@ struct hf_select_args {
     double *sc;                // workspace: scores [BH][nqb][nkb]
     int32_t *idx;
     double *scores;            // may be null
+    // hierarchical selection (top_frames > 0): frames of the window, pooled per frame
+    int nfr, top_frames;
+    double *fbar;              // workspace: frame-pooled keys [BH][nfr][D]
+    int32_t *fidx;             // may be null: kept frames [BH][nqb][top_frames], ascending
+    double *fscores;           // may be null: frame scores [BH][nqb][nfr]
 };
+constexpr int kMaxHierFrames = 64;   // window frames the hierarchical selection handles
 hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s);
 
 struct hf_attn_args {

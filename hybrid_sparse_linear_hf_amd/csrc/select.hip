@@ -5,9 +5,15 @@
 // mean-pooled query block and the mean-pooled key block ([LF-de] §2.2 token
 // compression by mean pooling), scaled by 1/sqrt(D).  Ties go to the lower key block.
 //
+// Hierarchical variant ([LF-de] §2.2 "Hierarchische Spärliche Attention", coarse to fine):
+// keys are also pooled per window frame; each query block first keeps its top_frames
+// frames by pooled query block . frame-pooled keys / sqrt(D), then its top-k key blocks
+// among the blocks that touch a kept frame.
+//
 // Three launches:
-//   pool_kernel   HBM-bound: one workgroup per query or key block sums its rows in fp64
-//                 (sums of bf16 values are exact in fp64) and stores the block mean.
+//   pool_kernel   HBM-bound: one workgroup per query block, key block or (hierarchical)
+//                 window frame sums its rows in fp64 (sums of bf16 values are exact in
+//                 fp64) and stores the mean.
 //   score_kernel  16 x 16 tiles of fp64 scores, each evaluated as sum_d (qbar_d * kbar_d) in
 //                 index order with separately rounded products and sums (the pooled
 //                 tiles are staged in LDS, every load issued up front).
@@ -34,12 +40,13 @@ __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
     constexpr int kRowsPerPass = 256 / kVec;
     __shared__ double red[kRowsPerPass][D];
 
-    const int per_plane = a.nqb + a.nkb;
+    const int nfr = a.top_frames > 0 ? a.nfr : 0;
+    const int per_plane = a.nqb + a.nkb + nfr;
     const int bh = blockIdx.x / per_plane;
     const int blk = blockIdx.x % per_plane;
-    const bool is_q = blk < a.nqb;
-    const int b = is_q ? blk : blk - a.nqb;
-    const int bs = is_q ? a.bq : a.bk;
+    const bool is_q = blk < a.nqb, is_f = blk >= a.nqb + a.nkb;
+    const int b = is_q ? blk : is_f ? blk - a.nqb - a.nkb : blk - a.nqb;
+    const int bs = is_q ? a.bq : is_f ? a.T : a.bk;
     const int N = is_q ? a.Nq : a.Nk;
     const int r0 = b * bs, r1 = min(r0 + bs, N);
 
@@ -64,7 +71,9 @@ __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
     if (threadIdx.x < D) {
         double s = 0.0;
         for (int k = 0; k < kRowsPerPass; ++k) s += red[k][threadIdx.x];
-        double *dst = is_q ? a.qbar + ((size_t)bh * a.nqb + b) * D : a.kbar + ((size_t)bh * a.nkb + b) * D;
+        double *dst = is_q   ? a.qbar + ((size_t)bh * a.nqb + b) * D
+                      : is_f ? a.fbar + ((size_t)bh * a.nfr + b) * D
+                             : a.kbar + ((size_t)bh * a.nkb + b) * D;
         dst[threadIdx.x] = s / (double)(r1 - r0);
     }
 }
@@ -124,26 +133,13 @@ __global__ __launch_bounds__(256) void score_kernel(hf_select_args a, double sca
     if (a.scores) a.scores[((size_t)bh * a.nqb + i) * a.nkb + j] = acc;
 }
 
-// One wave per (plane, query block): radix select of the k-th largest (score, -index)
-// key, then an ascending emit of the kept block indices.  Lane l holds keys of blocks
-// l, l + 64, ... in registers (KPL of them).
+// Radix select over one wave: the k-th largest of the keys held in registers (KPL per
+// lane; key 0 marks an absent candidate and is below every real key).  Returns that key
+// and how many of the keys equal to it are kept (the lowest-indexed ones).
 template <int KPL>
-__global__ __launch_bounds__(256) void topk_kernel(hf_select_args a) {
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const int row = blockIdx.x * 4 + wave;                    // (bh, i) flattened
-    if (row >= a.BH * a.nqb) return;
-    const double *src = a.sc + (size_t)row * a.nkb;
-    uint64_t key[KPL];
-#pragma unroll
-    for (int e = 0; e < KPL; ++e) {
-        const int j = lane + 64 * e;
-        key[e] = j < a.nkb ? order_key(src[j]) : 0;          // 0 is below every real key
-    }
-    const int k = a.top_k;
-
-    // largest v with #{key >= v} >= k, i.e. the k-th largest key (padding keys are 0 and
-    // never counted once v > 0; v = 0 is only reached if fewer than k real keys exist,
-    // which the caller's 1 <= k <= n_kb rules out)
+__device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPL], int k, int &need_eq) {
+    // largest v with #{key >= v} >= k (v = 0 is only reached if fewer than k real keys
+    // exist, which the callers' bounds on k rule out)
     uint64_t prefix = 0;
     for (int bit = 63; bit >= 0; --bit) {
         const uint64_t cand = prefix | (1ull << bit);
@@ -155,31 +151,104 @@ __global__ __launch_bounds__(256) void topk_kernel(hf_select_args a) {
     int gt = 0;
 #pragma unroll
     for (int e = 0; e < KPL; ++e) gt += __popcll(__ballot(key[e] > prefix));
-    const int need_eq = k - gt;  // >= 1 by construction
-    int32_t *out = a.idx + (size_t)row * k;
+    need_eq = k - gt;  // >= 1 by construction
+    return prefix;
+}
+
+// Ascending emit of the kept candidates (index lane + 64 e) to out[0 .. k); returns the
+// kept set as a bit mask when KPL == 1.
+template <int KPL>
+__device__ __forceinline__ uint64_t emit_kept(const uint64_t (&key)[KPL], int n, uint64_t prefix, int need_eq,
+                                              int32_t *out, int lane) {
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int written = 0, eq_seen = 0;
+    uint64_t kept = 0;
 #pragma unroll
     for (int e = 0; e < KPL; ++e) {
         const int j = lane + 64 * e;
-        const bool valid = j < a.nkb;
+        const bool valid = j < n;
         const bool is_gt = valid && key[e] > prefix;
         const bool is_eq = valid && key[e] == prefix;
         const uint64_t eq_b = __ballot(is_eq);
         const int eq_rank = eq_seen + __popcll(eq_b & lt_mask);
         const bool sel = is_gt || (is_eq && eq_rank < need_eq);
         const uint64_t sel_b = __ballot(sel);
-        if (sel) out[written + __popcll(sel_b & lt_mask)] = j;
+        if (sel && out) out[written + __popcll(sel_b & lt_mask)] = j;
         written += __popcll(sel_b);
         eq_seen += __popcll(eq_b);
+        if (e == 0) kept = sel_b;
     }
+    return kept;
+}
+
+// One wave per (plane, query block): radix select of the k-th largest (score, -index)
+// key, then an ascending emit of the kept block indices.  Lane l holds keys of blocks
+// l, l + 64, ... in registers (KPL of them).  HIER: the candidates are first restricted
+// to the key blocks touching the query block's top_frames best window frames (frame
+// scores formed here, lane f scoring frame f, with the block scores' summation order).
+template <int KPL, bool HIER, int D>
+__global__ __launch_bounds__(256) void topk_kernel(hf_select_args a, double scale) {
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int row = blockIdx.x * 4 + wave;                    // (bh, i) flattened
+    if (row >= a.BH * a.nqb) return;
+    uint64_t frames = ~0ull;                                  // kept frames (bit f)
+    if constexpr (HIER) {
+        const int bh = row / a.nqb;
+        double sf = 0.0;
+        if (lane < a.nfr) {
+            const double *qb = a.qbar + (size_t)row * D;
+            const double *fb = a.fbar + ((size_t)bh * a.nfr + lane) * D;
+            double acc = 0.0;
+            {
+#pragma clang fp contract(off)
+#pragma unroll 8
+                for (int d = 0; d < D; ++d) acc = acc + qb[d] * fb[d];
+                sf = acc * scale;
+            }
+            if (a.fscores) a.fscores[(size_t)row * a.nfr + lane] = sf;
+        }
+        const uint64_t fkey[1] = {lane < a.nfr ? order_key(sf) : 0};
+        int need_eq;
+        const uint64_t prefix = kth_key<1>(fkey, a.top_frames, need_eq);
+        frames = emit_kept<1>(fkey, a.nfr, prefix, need_eq,
+                              a.fidx ? a.fidx + (size_t)row * a.top_frames : nullptr, lane);
+    }
+    const double *src = a.sc + (size_t)row * a.nkb;
+    uint64_t key[KPL];
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) {
+        const int j = lane + 64 * e;
+        bool ok = j < a.nkb;
+        if constexpr (HIER) {
+            if (ok) {
+                // frames touched by key block j: f0 .. f1 (at most 17 of them: bk <= 128, T >= 8)
+                const int f0 = j * a.bk / a.T, f1 = (min((j + 1) * a.bk, a.Nk) - 1) / a.T;
+                ok = ((frames >> f0) & ((2ull << (f1 - f0)) - 1)) != 0;
+            }
+        }
+        key[e] = ok ? order_key(src[j]) : 0;
+    }
+    int need_eq;
+    const uint64_t prefix = kth_key<KPL>(key, a.top_k, need_eq);
+    emit_kept<KPL>(key, a.nkb, prefix, need_eq, a.idx + (size_t)row * a.top_k, lane);
 }
 
 }  // namespace
 }  // namespace hf
 
+template <bool HIER, int D>
+static void launch_topk(int kpl, dim3 grid, const hf_select_args &a, double scale, hipStream_t s) {
+    if (kpl <= 1) hipLaunchKernelGGL((hf::topk_kernel<1, HIER, D>), grid, dim3(256), 0, s, a, scale);
+    else if (kpl <= 2) hipLaunchKernelGGL((hf::topk_kernel<2, HIER, D>), grid, dim3(256), 0, s, a, scale);
+    else if (kpl <= 3) hipLaunchKernelGGL((hf::topk_kernel<3, HIER, D>), grid, dim3(256), 0, s, a, scale);
+    else if (kpl <= 4) hipLaunchKernelGGL((hf::topk_kernel<4, HIER, D>), grid, dim3(256), 0, s, a, scale);
+    else if (kpl <= 8) hipLaunchKernelGGL((hf::topk_kernel<8, HIER, D>), grid, dim3(256), 0, s, a, scale);
+    else if (kpl <= 16) hipLaunchKernelGGL((hf::topk_kernel<16, HIER, D>), grid, dim3(256), 0, s, a, scale);
+    else hipLaunchKernelGGL((hf::topk_kernel<24, HIER, D>), grid, dim3(256), 0, s, a, scale);
+}
+
 hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s) {
-    const dim3 grid_pool((unsigned)(a.BH * (a.nqb + a.nkb)));
+    const dim3 grid_pool((unsigned)(a.BH * (a.nqb + a.nkb + (a.top_frames > 0 ? a.nfr : 0))));
     const int ti_n = (a.nqb + hf::kTile - 1) / hf::kTile, tj_n = (a.nkb + hf::kTile - 1) / hf::kTile;
     const dim3 grid_score((unsigned)(a.BH * ti_n * tj_n));
     const dim3 grid_topk((unsigned)((a.BH * a.nqb + 3) / 4));
@@ -192,12 +261,11 @@ hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s) {
         hipLaunchKernelGGL(hf::score_kernel<128>, grid_score, dim3(256), 0, s, a, scale);
     }
     const int kpl = (a.nkb + 63) / 64;
-    if (kpl <= 1) hipLaunchKernelGGL(hf::topk_kernel<1>, grid_topk, dim3(256), 0, s, a);
-    else if (kpl <= 2) hipLaunchKernelGGL(hf::topk_kernel<2>, grid_topk, dim3(256), 0, s, a);
-    else if (kpl <= 3) hipLaunchKernelGGL(hf::topk_kernel<3>, grid_topk, dim3(256), 0, s, a);
-    else if (kpl <= 4) hipLaunchKernelGGL(hf::topk_kernel<4>, grid_topk, dim3(256), 0, s, a);
-    else if (kpl <= 8) hipLaunchKernelGGL(hf::topk_kernel<8>, grid_topk, dim3(256), 0, s, a);
-    else if (kpl <= 16) hipLaunchKernelGGL(hf::topk_kernel<16>, grid_topk, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(hf::topk_kernel<24>, grid_topk, dim3(256), 0, s, a);
+    if (a.top_frames > 0) {
+        if (a.D == 64) launch_topk<true, 64>(kpl, grid_topk, a, scale, s);
+        else launch_topk<true, 128>(kpl, grid_topk, a, scale, s);
+    } else {
+        launch_topk<false, 128>(kpl, grid_topk, a, scale, s);   // D is not used without HIER
+    }
     return hipGetLastError();
 }

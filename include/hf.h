@@ -148,6 +148,29 @@ hf_status hf_block_select(const hf_dims *d, const void *q_dev, const hf_kv_ring 
                           int32_t *idx_dev, double *scores_dev, void *workspace_dev,
                           size_t workspace_bytes, hipStream_t stream);
 
+/* Hierarchical (coarse-to-fine) block selection ([LF-de] §2.2 "Hierarchische Spärliche
+ * Attention": queries and keys compressed by mean pooling at block and frame level; per
+ * query block, frame selection with the frame-level keys, then block selection inside the
+ * selected frames).  For each (b, h, query block i):
+ *   frame score  sf_if = qbar_i . fbar_f / sqrt(D), fbar_f the mean of window frame f's
+ *                T keys; keep the top_frames best frames, ties to the lower frame;
+ *   block score  s_ij as hf_block_select; keep the top_k best key blocks among those that
+ *                touch (share a key with) a kept frame, ties to the lower block;
+ * pooled and scored in fp64, indices written in ASCENDING order.
+ *   idx_dev           int32 [B][H][n_qb][top_k] out (feeds hf_sparse_window_attn)
+ *   frames_dev        NULL or int32 [B][H][n_qb][top_frames] out: kept frames, ascending
+ *                     (logical window frames, 0 = oldest)
+ *   scores_dev        NULL or fp64 [B][H][n_qb][n_kb] out: every block score
+ *   frame_scores_dev  NULL or fp64 [B][H][n_qb][F] out, F = n_committed + C frames
+ * Requires F <= 64, 1 <= top_frames <= F and 1 <= top_k <= min(n_kb,
+ * top_frames * ceil(T / bk) - (top_frames - 1)) (the key blocks any top_frames frames are
+ * sure to touch).  Errors: HF_ERR_UNSUPPORTED (F > 64), HF_ERR_SHAPE (bounds), plus those of
+ * hf_block_select. */
+hf_status hf_block_select_hier(const hf_dims *d, const void *q_dev, const hf_kv_ring *ring, int32_t top_frames,
+                               int32_t top_k, int32_t *idx_dev, int32_t *frames_dev, double *scores_dev,
+                               double *frame_scores_dev, void *workspace_dev, size_t workspace_bytes,
+                               hipStream_t stream);
+
 /* Block-sparse window attention plus linear readout ([HF-de] §2.A, [HF-pt] §2.A.1,
  * 2.A.2 and "Resultado"; [HF-abs]).
  * out[b,h,t,:] = sum_{u in kept blocks of t's block} softmax_u(q_t.k_u / sqrt(D)) v_u

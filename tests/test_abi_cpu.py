@@ -146,3 +146,22 @@ def test_workspace_covers_absorb_partials(B, H, D):
         P = min(nch, pmax)
         need = blocks * P * 64 * D * 4 + blocks * P * 64 * 4
         assert ws >= need, (n_tok, ws, need)
+
+
+def call_hier(g, ring, top_frames, top_k, ws_bytes=None):
+    L = _lib.lib()
+    ws_bytes = hf.workspace_size(g) if ws_bytes is None else ws_bytes
+    return L.hf_block_select_hier(ctypes.byref(g.dims()), FAKE, ctypes.byref(ring), top_frames, top_k, FAKE, None,
+                                  None, None, FAKE, ws_bytes, None)
+
+
+def test_hier_select_bounds():
+    g = geom(W=21)                        # 18 committed + 3 current = 21 frames, n_kb = 512
+    r = ring_desc(n_committed=18)
+    assert call_hier(g, r, 0, 10) == 2 and "top_frames" in last_error()
+    assert call_hier(g, r, 22, 10) == 2
+    # 6 frames of 1560 keys touch at least 6 * 25 - 5 = 145 blocks of 64
+    assert call_hier(g, r, 6, 146) == 2 and "145" in last_error()
+    assert call_hier(g, r, 6, 0) == 2
+    big = geom(W=70, T=64, bk=64)         # 67 + 3 frames > 64
+    assert call_hier(big, ring_desc(n_committed=67), 4, 4) == 3

@@ -134,6 +134,12 @@ def main():
                     help="after timing, run a plain 256 MiB elementwise copy (for counter calibration)")
     ap.add_argument("--keep", type=float, default=None, help="override the kept fraction of key blocks")
     ap.add_argument("--window", type=int, default=None, help="override the window length in frames")
+    ap.add_argument("--mode", choices=("step", "hier", "cag"), default="step",
+                    help="step: the hybrid step (default); hier: hierarchical selection + attention on a 21-frame "
+                         "window; cag: a stream from an empty window under the chunk-aware keep schedule")
+    ap.add_argument("--top-frames", type=int, default=6, help="hier: frames kept per query block")
+    ap.add_argument("--top-k", type=int, default=128, help="hier: key blocks kept per query block")
+    ap.add_argument("--stream", type=int, default=16, help="cag: chunks in the stream")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -149,6 +155,10 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.mode == "hier":
+        return bench_hier(args)
+    if args.mode == "cag":
+        return bench_cag(args)
     cfg = synth.LAYER_832x480
     if args.keep is not None or args.window is not None:
         import dataclasses
@@ -275,6 +285,141 @@ def main():
         cb = cpu_baseline(cfg, min(args.cpu_heads, cfg.H), args.cpu_seconds)
         res["cpu_baseline_ms_per_step"] = round(cb.pop("ms_per_step"), 1)
         res["cpu_baseline"] = cb
+    print(json.dumps(res), flush=True)
+
+
+def _field_ring(cfg, hf, synth, torch, dev):
+    """Ring holding W - C committed frames and the current chunk, a state from the absorbed
+    frames, and the current chunk's queries (the layout of the step benchmark)."""
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    g = hf.Geometry(cfg.B, cfg.H, cfg.D, cfg.T, cfg.C, cfg.W, cfg.bq, cfg.bk)
+    kw = dict(B=cfg.B, H=cfg.H, D=cfg.D, gh=cfg.gh, gw=cfg.gw)
+    ev = cfg.n_evicted
+    ring, ws = hf.Ring(g), hf.new_workspace(g)
+    S = torch.zeros((cfg.B, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dev)
+    z = torch.zeros((cfg.B, cfg.H, cfg.D), dtype=torch.float32, device=dev)
+    hf.hf_linear_absorb(g, to_dev(synth.field_frames(synth.K_ID, 0, ev, **kw)),
+                        to_dev(synth.field_frames(synth.V_ID, 0, ev, **kw)), ev * cfg.T, S, z, ws)
+    for f in range(0, cfg.W, cfg.C):
+        ring.set_state(0, f)
+        hf.hf_ring_append(g, ring, to_dev(synth.field_frames(synth.K_ID, ev + f, cfg.C, **kw)),
+                          to_dev(synth.field_frames(synth.V_ID, ev + f, cfg.C, **kw)))
+    ring.set_state(0, cfg.W - cfg.C)
+    q = to_dev(synth.field_frames(synth.Q_ID, ev + cfg.W - cfg.C, cfg.C, **kw))
+    torch.cuda.synchronize()
+    return g, ring, ws, S, z, q
+
+
+def bench_hier(args):
+    """Hierarchical coarse-to-fine selection ([LF-de] §2.2) feeding the sparse attention, on
+    the 832x480 shapes with a 21-frame window (32760 keys, 512 key blocks): per timed step,
+    hf_block_select_hier (top_frames frames, then top_k blocks inside them) and
+    hf_sparse_window_attn with the readout; the flat selection of the same top_k is timed
+    beside it."""
+    import torch
+    import hybrid_sparse_linear_hf_amd as hf
+    from hybrid_sparse_linear_hf_amd import synth
+
+    cfg = synth.LAYER_832x480_W21
+    dev = torch.device("cuda:0")
+    g, ring, ws, S, z, q = _field_ring(cfg, hf, synth, torch, dev)
+    nfr, nkb = cfg.W, g.n_kb(cfg.W - cfg.C)
+    idx = torch.empty((cfg.B, cfg.H, g.n_qb, args.top_k), dtype=torch.int32, device=dev)
+    idx_flat = torch.empty_like(idx)
+    out = torch.empty((cfg.B, cfg.H, cfg.Nq, cfg.D), dtype=torch.float32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    sel, att, flat = [], [], []
+    for it in range(args.warmup + args.steps):
+        ev[0].record()
+        hf.hf_block_select_hier(g, q, ring, args.top_frames, args.top_k, idx, ws)
+        ev[1].record()
+        hf.hf_sparse_window_attn(g, q, ring, idx, args.top_k, S, z, out, ws)
+        ev[2].record()
+        hf.hf_block_select(g, q, ring, args.top_k, idx_flat, None, ws)
+        ev[3].record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            sel.append(ev[0].elapsed_time(ev[1]))
+            att.append(ev[1].elapsed_time(ev[2]))
+            flat.append(ev[2].elapsed_time(ev[3]))
+    fl = kept_flops(idx.cpu().numpy(), cfg.Nq, nfr * cfg.T, cfg.bq, cfg.bk, cfg.D)
+    t = (np.median(sel) + np.median(att)) * 1e-3
+    res = {"metric": "hierarchical select + sparse attention, 21-frame window (832x480 shape, 1 GPU)",
+           "value": round(fl / t / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(t * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded rank-8 spatial field + noise per head, bf16)",
+           "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "D": cfg.D, "tokens_per_frame": cfg.T,
+                      "chunk_frames": cfg.C, "window_frames": cfg.W, "block": [cfg.bq, cfg.bk], "n_kb": nkb,
+                      "top_frames": args.top_frames, "top_k": args.top_k},
+           "hier_select_us": round(float(np.median(sel)) * 1e3, 2),
+           "flat_select_us": round(float(np.median(flat)) * 1e3, 2),
+           "sparse_attn_readout_us": round(float(np.median(att)) * 1e3, 2),
+           "kept_flops": round(fl),
+           "attn_frac_of_bf16_peak": round(fl / (np.median(att) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    print(json.dumps(res), flush=True)
+
+
+def bench_cag(args):
+    """A stream of `--stream` chunks from an empty window at the 832x480 layer shapes (W=6),
+    every step an hf_hybrid_step with commit, once with the chunk-aware growth keep counts
+    ([LF-de] §2.1: hf_cag_schedule, first chunk dense, stream-wide sparsity 75 %) and once
+    with a uniform 25 % keep.  Reports the wall time of each stream and its kept work."""
+    import torch
+    import hybrid_sparse_linear_hf_amd as hf
+    from hybrid_sparse_linear_hf_amd import synth
+
+    cfg = synth.LAYER_832x480
+    dev = torch.device("cuda:0")
+    g = hf.Geometry(cfg.B, cfg.H, cfg.D, cfg.T, cfg.C, cfg.W, cfg.bq, cfg.bk)
+    kw = dict(B=cfg.B, H=cfg.H, D=cfg.D, gh=cfg.gh, gw=cfg.gw)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    chunks = [tuple(to_dev(synth.field_frames(t, cfg.C * s, cfg.C, **kw)) for t in (synth.Q_ID, synth.K_ID, synth.V_ID))
+              for s in range(args.stream)]
+    n_kb = [g.n_kb(min(cfg.C * s, cfg.W - cfg.C)) for s in range(args.stream)]
+    k_cag, s_cag, beta = hf.hf_cag_schedule(n_kb, 0.9, 0.75, 0.95)
+    k_uni = [max(1, -(-n // 4)) for n in n_kb]
+    out = torch.empty((cfg.B, cfg.H, cfg.Nq, cfg.D), dtype=torch.float32, device=dev)
+
+    def run(ks):
+        ring, ws = hf.Ring(g), hf.new_workspace(g)
+        S = torch.zeros((cfg.B, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dev)
+        z = torch.zeros((cfg.B, cfg.H, cfg.D), dtype=torch.float32, device=dev)
+        idxs = [torch.empty((cfg.B, cfg.H, g.n_qb, k), dtype=torch.int32, device=dev) for k in ks]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s, (q, k, v) in enumerate(chunks):
+            hf.hf_hybrid_step(g, q, k, v, ring, ks[s], hf.HF_STEP_COMMIT, S, z, idxs[s], out, ws)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        fl = sum(kept_flops(i.cpu().numpy(), cfg.Nq, min(cfg.C * (s + 1), cfg.W) * cfg.T, cfg.bq, cfg.bk, cfg.D)
+                 for s, i in enumerate(idxs))
+        return wall, fl
+
+    for _ in range(max(1, args.warmup // 5)):
+        run(k_uni)
+    walls = {"cag": [], "uniform": []}
+    fls = {}
+    for _ in range(5):
+        for name, ks in (("cag", k_cag), ("uniform", k_uni)):
+            w, fl = run(ks)
+            walls[name].append(w)
+            fls[name] = fl
+    wc, wu = float(np.median(walls["cag"])), float(np.median(walls["uniform"]))
+    res = {"metric": "chunk-aware growth stream: kept TFLOP/s over a 16-chunk stream (832x480 shape, 1 GPU)",
+           "value": round(fls["cag"] / wc / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": 5,
+           "warmup": max(1, args.warmup // 5), "ms_per_step": round(wc * 1e3 / args.stream, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded rank-8 spatial field + noise per head, bf16)",
+           "config": {"workload": cfg.name + "_stream", "chunks": args.stream, "s_base": 0.9, "s_target": 0.75,
+                      "s_max": 0.95, "n_kb": n_kb},
+           "cag": {"top_k": k_cag, "sparsity": [round(x, 4) for x in s_cag], "beta": round(beta, 6),
+                   "stream_ms": round(wc * 1e3, 3), "kept_flops": round(fls["cag"])},
+           "uniform_25pct": {"top_k": k_uni, "stream_ms": round(wu * 1e3, 3), "kept_flops": round(fls["uniform"])}}
     print(json.dumps(res), flush=True)
 
 

@@ -75,9 +75,10 @@ Geometry geometry(const hf_dims *d, const hf_kv_ring *r) {
 
 // Workspace layout (offsets 256-byte aligned):
 //   [absorb partials]  [qbar fp64]  [kbar fp64]  [scores fp64]  [S^T bf16]  [z copy fp32]
-//   [frame-pooled keys fp64, up to kMaxHierFrames frames]
+//   [frame-pooled keys fp64, up to kMaxHierFrames frames]  [frame scores fp64]
+//   [per key block frame parts fp64]
 struct WsLayout {
-    size_t absorb, qbar, kbar, sc, st, zc, fbar, total;
+    size_t absorb, qbar, kbar, sc, st, zc, fbar, fsc, part, total;
 };
 
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -95,7 +96,9 @@ WsLayout ws_layout(const hf_dims *d) {
     w.zc = w.st + al((size_t)BH * d->D * d->D * sizeof(uint16_t));
     w.fbar = w.zc + al((size_t)BH * d->D * sizeof(float));
     const int frames = d->W < kMaxHierFrames ? d->W : kMaxHierFrames;
-    w.total = w.fbar + al((size_t)BH * frames * d->D * sizeof(double));
+    w.fsc = w.fbar + al((size_t)BH * frames * d->D * sizeof(double));
+    w.part = w.fsc + al((size_t)BH * nqb * frames * sizeof(double));
+    w.total = w.part + al((size_t)BH * nkb * 2 * d->D * sizeof(double));
     return w;
 }
 
@@ -159,6 +162,8 @@ hipError_t enqueue_select(const hf_dims *d, const void *q, const hf_kv_ring *r, 
     a.nfr = r->n_committed + d->C;
     a.top_frames = top_frames;
     a.fbar = reinterpret_cast<double *>(wsp(ws, L.fbar));
+    a.fsc = reinterpret_cast<double *>(wsp(ws, L.fsc));
+    a.part = reinterpret_cast<double *>(wsp(ws, L.part));
     a.fidx = fidx;
     a.fscores = fscores;
     return hf_launch_block_select(a, s);
@@ -319,6 +324,7 @@ hf_status hf_block_select_hier(const hf_dims *d, const void *q, const hf_kv_ring
     if (nfr > kMaxHierFrames)
         return fail(HF_ERR_UNSUPPORTED, "window of %d frames exceeds %d for the hierarchical selection", nfr,
                     kMaxHierFrames);
+    if (d->bk > d->T) return fail(HF_ERR_UNSUPPORTED, "hierarchical selection needs bk <= T (bk=%d T=%d)", d->bk, d->T);
     if (top_frames < 1 || top_frames > nfr)
         return fail(HF_ERR_SHAPE, "top_frames=%d outside [1, frames in the window=%d]", top_frames, nfr);
     // any top_frames distinct frames touch at least this many key blocks

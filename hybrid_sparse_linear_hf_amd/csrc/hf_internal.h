@@ -92,6 +92,9 @@ struct hf_select_args {
     // hierarchical selection (top_frames > 0): frames of the window, pooled per frame
     int nfr, top_frames;
     double *fbar;              // workspace: frame-pooled keys [BH][nfr][D]
+    double *fsc;               // workspace: frame scores [BH][nqb][nfr]
+    double *part;              // workspace: per key block, sums of its rows in its first frame
+                               // and in the next one [BH][nkb][2][D] (needs bk <= T)
     int32_t *fidx;             // may be null: kept frames [BH][nqb][top_frames], ascending
     double *fscores;           // may be null: frame scores [BH][nqb][nfr]
 };

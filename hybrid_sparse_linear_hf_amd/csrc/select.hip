@@ -8,17 +8,21 @@
 // Hierarchical variant ([LF-de] §2.2 "Hierarchische Spärliche Attention", coarse to fine):
 // keys are also pooled per window frame; each query block first keeps its top_frames
 // frames by pooled query block . frame-pooled keys / sqrt(D), then its top-k key blocks
-// among the blocks that touch a kept frame.
+// among the blocks that touch a kept frame.  The frame pooling reads no key twice: the
+// pool kernel keeps each key block's rows of its two frames apart, frame_pool_kernel adds
+// those parts per frame.
 //
 // Three launches:
-//   pool_kernel   HBM-bound: one workgroup per query block, key block or (hierarchical)
-//                 window frame sums its rows in fp64 (sums of bf16 values are exact in
-//                 fp64) and stores the mean.
+//   pool_kernel   HBM-bound: one workgroup per query or key block sums its rows in fp64
+//                 (sums of bf16 values are exact in fp64) and stores the block mean.
 //   score_kernel  16 x 16 tiles of fp64 scores, each evaluated as sum_d (qbar_d * kbar_d) in
 //                 index order with separately rounded products and sums (the pooled
 //                 tiles are staged in LDS, every load issued up front).
 //   topk_kernel   one wave per query block: radix select of the k-th largest
 //                 (score, -index) key and an ascending emit of the kept indices.
+// The hierarchical variant adds frame_pool_kernel, runs the score kernel a second time
+// over (query block, frame) pairs, and lets the top-k wave select the frames before the
+// blocks.
 #include "hf_internal.h"
 
 namespace hf {
@@ -34,26 +38,29 @@ __device__ __forceinline__ const uint16_t *key_row(const hf_select_args &a, int 
     return a.ring_k + (((size_t)bh * a.W + slot) * a.T + t) * a.D;
 }
 
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
     constexpr int kVec = D / 8;              // 16-byte vectors per row
     constexpr int kRowsPerPass = 256 / kVec;
     __shared__ double red[kRowsPerPass][D];
 
-    const int nfr = a.top_frames > 0 ? a.nfr : 0;
-    const int per_plane = a.nqb + a.nkb + nfr;
+    const int per_plane = a.nqb + a.nkb;
     const int bh = blockIdx.x / per_plane;
     const int blk = blockIdx.x % per_plane;
-    const bool is_q = blk < a.nqb, is_f = blk >= a.nqb + a.nkb;
-    const int b = is_q ? blk : is_f ? blk - a.nqb - a.nkb : blk - a.nqb;
-    const int bs = is_q ? a.bq : is_f ? a.T : a.bk;
+    const bool is_q = blk < a.nqb;
+    const int b = is_q ? blk : blk - a.nqb;
+    const int bs = is_q ? a.bq : a.bk;
     const int N = is_q ? a.Nq : a.Nk;
+    // hierarchical: rows from `fend` on lie in the key block's second frame; their sum is
+    // kept apart (both parts are exact sums, so the block sum is unchanged)
+    const bool split = SPLIT && !is_q;
+    const int fend = split ? min((b * bs / a.T + 1) * a.T, N) : N;
     const int r0 = b * bs, r1 = min(r0 + bs, N);
 
     const int v = threadIdx.x % kVec, ro = threadIdx.x / kVec;
-    double acc[8];
+    double acc[8], acc2[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    for (int e = 0; e < 8; ++e) acc[e] = acc2[e] = 0.0;
 #pragma unroll 4
     for (int r = r0 + ro; r < r1; r += kRowsPerPass) {
         const uint16_t *row = is_q ? a.q + ((size_t)bh * a.Nq + r) * D : key_row(a, bh, r);
@@ -61,9 +68,37 @@ __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            acc[2 * e] += bf16_to_f64(ws[e] & 0xFFFFu);
-            acc[2 * e + 1] += bf16_to_f64(ws[e] >> 16);
+            const double lo = bf16_to_f64(ws[e] & 0xFFFFu), hi = bf16_to_f64(ws[e] >> 16);
+            if constexpr (SPLIT) {
+                const bool first = r < fend;           // adding 0.0 leaves a sum unchanged
+                acc[2 * e] += first ? lo : 0.0;
+                acc[2 * e + 1] += first ? hi : 0.0;
+                acc2[2 * e] += first ? 0.0 : lo;
+                acc2[2 * e + 1] += first ? 0.0 : hi;
+            } else {
+                acc[2 * e] += lo;
+                acc[2 * e + 1] += hi;
+            }
         }
+    }
+    if (SPLIT && split) {
+        // the two frame parts of this key block, for the frame pooling (one LDS buffer,
+        // reduced twice)
+        double *pp = a.part + (((size_t)bh * a.nkb + b) * 2) * D;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[ro][v * 8 + e] = h == 0 ? acc[e] : acc2[e];
+            __syncthreads();
+            if (threadIdx.x < D) {
+                double s = 0.0;
+                for (int k = 0; k < kRowsPerPass; ++k) s += red[k][threadIdx.x];
+                pp[h * D + threadIdx.x] = s;
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += acc2[e];
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[ro][v * 8 + e] = acc[e];
@@ -71,11 +106,35 @@ __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
     if (threadIdx.x < D) {
         double s = 0.0;
         for (int k = 0; k < kRowsPerPass; ++k) s += red[k][threadIdx.x];
-        double *dst = is_q   ? a.qbar + ((size_t)bh * a.nqb + b) * D
-                      : is_f ? a.fbar + ((size_t)bh * a.nfr + b) * D
-                             : a.kbar + ((size_t)bh * a.nkb + b) * D;
+        double *dst = is_q ? a.qbar + ((size_t)bh * a.nqb + b) * D : a.kbar + ((size_t)bh * a.nkb + b) * D;
         dst[threadIdx.x] = s / (double)(r1 - r0);
     }
+}
+
+// Frame-pooled keys (hierarchical selection): frame f's key sum is assembled, in key block
+// order, from the parts of the key blocks that touch it -- a block's first-frame part when
+// the block starts in f, its second-frame part when it starts in f - 1 (bk <= T, so a
+// block touches at most two frames).  The parts are exact sums, so the frame sum is the
+// exact sum of its T rows; then the mean.
+template <int D>
+__global__ __launch_bounds__(D) void frame_pool_kernel(hf_select_args a) {
+    const int bh = blockIdx.x / a.nfr, f = blockIdx.x % a.nfr;
+    const int j0 = f * a.T / a.bk, j1 = ((f + 1) * a.T - 1) / a.bk;
+    constexpr int kBatch = 16;                                 // loads in flight before the adds
+    double s = 0.0;
+    for (int jb = j0; jb <= j1; jb += kBatch) {
+        double v[kBatch];
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e) {
+            const int j = jb + e;
+            const int second = (j * a.bk / a.T) != f;          // block j starts in frame f - 1
+            v[e] = j <= j1 ? a.part[(((size_t)bh * a.nkb + j) * 2 + second) * D + threadIdx.x] : 0.0;
+        }
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e)
+            if (jb + e <= j1) s += v[e];
+    }
+    a.fbar[((size_t)bh * a.nfr + f) * D + threadIdx.x] = s / (double)a.T;
 }
 
 __device__ __forceinline__ uint64_t order_key(double s) {
@@ -184,30 +243,16 @@ __device__ __forceinline__ uint64_t emit_kept(const uint64_t (&key)[KPL], int n,
 // One wave per (plane, query block): radix select of the k-th largest (score, -index)
 // key, then an ascending emit of the kept block indices.  Lane l holds keys of blocks
 // l, l + 64, ... in registers (KPL of them).  HIER: the candidates are first restricted
-// to the key blocks touching the query block's top_frames best window frames (frame
-// scores formed here, lane f scoring frame f, with the block scores' summation order).
-template <int KPL, bool HIER, int D>
-__global__ __launch_bounds__(256) void topk_kernel(hf_select_args a, double scale) {
+// to the key blocks touching the query block's top_frames best window frames (lane f
+// holds frame f's score).
+template <int KPL, bool HIER>
+__global__ __launch_bounds__(256) void topk_kernel(hf_select_args a) {
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int row = blockIdx.x * 4 + wave;                    // (bh, i) flattened
     if (row >= a.BH * a.nqb) return;
     uint64_t frames = ~0ull;                                  // kept frames (bit f)
     if constexpr (HIER) {
-        const int bh = row / a.nqb;
-        double sf = 0.0;
-        if (lane < a.nfr) {
-            const double *qb = a.qbar + (size_t)row * D;
-            const double *fb = a.fbar + ((size_t)bh * a.nfr + lane) * D;
-            double acc = 0.0;
-            {
-#pragma clang fp contract(off)
-#pragma unroll 8
-                for (int d = 0; d < D; ++d) acc = acc + qb[d] * fb[d];
-                sf = acc * scale;
-            }
-            if (a.fscores) a.fscores[(size_t)row * a.nfr + lane] = sf;
-        }
-        const uint64_t fkey[1] = {lane < a.nfr ? order_key(sf) : 0};
+        const uint64_t fkey[1] = {lane < a.nfr ? order_key(a.fsc[(size_t)row * a.nfr + lane]) : 0};
         int need_eq;
         const uint64_t prefix = kth_key<1>(fkey, a.top_frames, need_eq);
         frames = emit_kept<1>(fkey, a.nfr, prefix, need_eq,
@@ -236,36 +281,59 @@ __global__ __launch_bounds__(256) void topk_kernel(hf_select_args a, double scal
 }  // namespace
 }  // namespace hf
 
-template <bool HIER, int D>
-static void launch_topk(int kpl, dim3 grid, const hf_select_args &a, double scale, hipStream_t s) {
-    if (kpl <= 1) hipLaunchKernelGGL((hf::topk_kernel<1, HIER, D>), grid, dim3(256), 0, s, a, scale);
-    else if (kpl <= 2) hipLaunchKernelGGL((hf::topk_kernel<2, HIER, D>), grid, dim3(256), 0, s, a, scale);
-    else if (kpl <= 3) hipLaunchKernelGGL((hf::topk_kernel<3, HIER, D>), grid, dim3(256), 0, s, a, scale);
-    else if (kpl <= 4) hipLaunchKernelGGL((hf::topk_kernel<4, HIER, D>), grid, dim3(256), 0, s, a, scale);
-    else if (kpl <= 8) hipLaunchKernelGGL((hf::topk_kernel<8, HIER, D>), grid, dim3(256), 0, s, a, scale);
-    else if (kpl <= 16) hipLaunchKernelGGL((hf::topk_kernel<16, HIER, D>), grid, dim3(256), 0, s, a, scale);
-    else hipLaunchKernelGGL((hf::topk_kernel<24, HIER, D>), grid, dim3(256), 0, s, a, scale);
+template <bool HIER>
+static void launch_topk(int kpl, dim3 grid, const hf_select_args &a, hipStream_t s) {
+    if (kpl <= 1) hipLaunchKernelGGL((hf::topk_kernel<1, HIER>), grid, dim3(256), 0, s, a);
+    else if (kpl <= 2) hipLaunchKernelGGL((hf::topk_kernel<2, HIER>), grid, dim3(256), 0, s, a);
+    else if (kpl <= 3) hipLaunchKernelGGL((hf::topk_kernel<3, HIER>), grid, dim3(256), 0, s, a);
+    else if (kpl <= 4) hipLaunchKernelGGL((hf::topk_kernel<4, HIER>), grid, dim3(256), 0, s, a);
+    else if (kpl <= 8) hipLaunchKernelGGL((hf::topk_kernel<8, HIER>), grid, dim3(256), 0, s, a);
+    else if (kpl <= 16) hipLaunchKernelGGL((hf::topk_kernel<16, HIER>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((hf::topk_kernel<24, HIER>), grid, dim3(256), 0, s, a);
 }
 
 hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s) {
-    const dim3 grid_pool((unsigned)(a.BH * (a.nqb + a.nkb + (a.top_frames > 0 ? a.nfr : 0))));
+    const dim3 grid_pool((unsigned)(a.BH * (a.nqb + a.nkb)));
     const int ti_n = (a.nqb + hf::kTile - 1) / hf::kTile, tj_n = (a.nkb + hf::kTile - 1) / hf::kTile;
     const dim3 grid_score((unsigned)(a.BH * ti_n * tj_n));
     const dim3 grid_topk((unsigned)((a.BH * a.nqb + 3) / 4));
     const double scale = 1.0 / sqrt((double)a.D);
+    const bool hier = a.top_frames > 0;
     if (a.D == 64) {
-        hipLaunchKernelGGL(hf::pool_kernel<64>, grid_pool, dim3(256), 0, s, a);
+        if (hier)
+            hipLaunchKernelGGL((hf::pool_kernel<64, true>), grid_pool, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((hf::pool_kernel<64, false>), grid_pool, dim3(256), 0, s, a);
         hipLaunchKernelGGL(hf::score_kernel<64>, grid_score, dim3(256), 0, s, a, scale);
     } else {
-        hipLaunchKernelGGL(hf::pool_kernel<128>, grid_pool, dim3(256), 0, s, a);
+        if (hier)
+            hipLaunchKernelGGL((hf::pool_kernel<128, true>), grid_pool, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((hf::pool_kernel<128, false>), grid_pool, dim3(256), 0, s, a);
         hipLaunchKernelGGL(hf::score_kernel<128>, grid_score, dim3(256), 0, s, a, scale);
     }
-    const int kpl = (a.nkb + 63) / 64;
     if (a.top_frames > 0) {
-        if (a.D == 64) launch_topk<true, 64>(kpl, grid_topk, a, scale, s);
-        else launch_topk<true, 128>(kpl, grid_topk, a, scale, s);
-    } else {
-        launch_topk<false, 128>(kpl, grid_topk, a, scale, s);   // D is not used without HIER
+        const dim3 grid_fp((unsigned)(a.BH * a.nfr));
+        if (a.D == 64)
+            hipLaunchKernelGGL(hf::frame_pool_kernel<64>, grid_fp, dim3(64), 0, s, a);
+        else
+            hipLaunchKernelGGL(hf::frame_pool_kernel<128>, grid_fp, dim3(128), 0, s, a);
+        // frame scores: the score kernel over (query block, frame) pairs
+        hf_select_args f = a;
+        f.kbar = a.fbar;
+        f.nkb = a.nfr;
+        f.sc = a.fsc;
+        f.scores = a.fscores;
+        const dim3 grid_fs((unsigned)(a.BH * ti_n * ((a.nfr + hf::kTile - 1) / hf::kTile)));
+        if (a.D == 64)
+            hipLaunchKernelGGL(hf::score_kernel<64>, grid_fs, dim3(256), 0, s, f, scale);
+        else
+            hipLaunchKernelGGL(hf::score_kernel<128>, grid_fs, dim3(256), 0, s, f, scale);
     }
+    const int kpl = (a.nkb + 63) / 64;
+    if (a.top_frames > 0)
+        launch_topk<true>(kpl, grid_topk, a, s);
+    else
+        launch_topk<false>(kpl, grid_topk, a, s);
     return hipGetLastError();
 }

@@ -162,10 +162,10 @@ hf_status hf_block_select(const hf_dims *d, const void *q_dev, const hf_kv_ring 
  *                     (logical window frames, 0 = oldest)
  *   scores_dev        NULL or fp64 [B][H][n_qb][n_kb] out: every block score
  *   frame_scores_dev  NULL or fp64 [B][H][n_qb][F] out, F = n_committed + C frames
- * Requires F <= 64, 1 <= top_frames <= F and 1 <= top_k <= min(n_kb,
+ * Requires bk <= T, F <= 64, 1 <= top_frames <= F and 1 <= top_k <= min(n_kb,
  * top_frames * ceil(T / bk) - (top_frames - 1)) (the key blocks any top_frames frames are
- * sure to touch).  Errors: HF_ERR_UNSUPPORTED (F > 64), HF_ERR_SHAPE (bounds), plus those of
- * hf_block_select. */
+ * sure to touch).  Errors: HF_ERR_UNSUPPORTED (bk > T, F > 64), HF_ERR_SHAPE (bounds), plus
+ * those of hf_block_select. */
 hf_status hf_block_select_hier(const hf_dims *d, const void *q_dev, const hf_kv_ring *ring, int32_t top_frames,
                                int32_t top_k, int32_t *idx_dev, int32_t *frames_dev, double *scores_dev,
                                double *frame_scores_dev, void *workspace_dev, size_t workspace_bytes,

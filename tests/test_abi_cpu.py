@@ -165,3 +165,4 @@ def test_hier_select_bounds():
     assert call_hier(g, r, 6, 0) == 2
     big = geom(W=70, T=64, bk=64)         # 67 + 3 frames > 64
     assert call_hier(big, ring_desc(n_committed=67), 4, 4) == 3
+    assert call_hier(geom(T=40, bk=64), ring_desc(), 1, 1) == 3 and "bk <= T" in last_error()

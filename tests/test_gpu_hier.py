@@ -73,7 +73,7 @@ HIER_EDGE = [
     # B, H, D, T, C, W, bq, bk, n_committed, top_frames, top_k
     (1, 2, 64, 64, 1, 6, 16, 16, 5, 2, 5),       # blocks inside frames
     (2, 1, 128, 40, 2, 7, 32, 16, 5, 3, 6),      # blocks straddling frames (40 = 2.5 blocks)
-    (1, 1, 128, 40, 1, 5, 64, 64, 4, 1, 1),      # blocks longer than a frame
+    (1, 1, 128, 64, 1, 5, 64, 64, 4, 1, 1),      # blocks as long as a frame, top-1
     (1, 3, 64, 72, 2, 4, 64, 32, 1, 3, 4),       # window not yet full
 ]
 

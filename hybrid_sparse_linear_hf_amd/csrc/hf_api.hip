@@ -136,7 +136,7 @@ hipError_t enqueue_append(const hf_dims *d, const hf_kv_ring *r, const void *kc,
 
 hipError_t enqueue_select(const hf_dims *d, const void *q, const hf_kv_ring *r, int top_k, int32_t *idx,
                           double *scores, void *ws, hipStream_t s, int top_frames = 0, int32_t *fidx = nullptr,
-                          double *fscores = nullptr) {
+                          double *fscores = nullptr, const hf_state_args *prep = nullptr) {
     const Geometry g = geometry(d, r);
     const WsLayout L = ws_layout(d);
     hf_select_args a{};
@@ -166,13 +166,16 @@ hipError_t enqueue_select(const hf_dims *d, const void *q, const hf_kv_ring *r, 
     a.part = reinterpret_cast<double *>(wsp(ws, L.part));
     a.fidx = fidx;
     a.fscores = fscores;
+    if (prep) {
+        a.prep = *prep;
+        a.prep_tiles = a.BH * (d->D / 32) * (d->D / 32);
+    }
     return hf_launch_block_select(a, s);
 }
 
 // The state pass of a step: readout operands (S^T bf16, z copy) from the state as it is,
 // and, when `absorb_tokens` > 0, the absorb partials already in the workspace added in.
-hipError_t enqueue_state(const hf_dims *d, float *S, float *z, bool readout, int64_t absorb_tokens, void *ws,
-                         hipStream_t s) {
+hf_state_args state_args(const hf_dims *d, float *S, float *z, bool readout, int64_t absorb_tokens, void *ws) {
     const WsLayout L = ws_layout(d);
     hf_state_args a{};
     a.BH = d->B * d->H;
@@ -183,7 +186,12 @@ hipError_t enqueue_state(const hf_dims *d, float *S, float *z, bool readout, int
     a.P = absorb_tokens > 0 ? hf_absorb_splits(a.BH, d->D, absorb_tokens) : 0;
     a.st = readout ? reinterpret_cast<uint16_t *>(wsp(ws, L.st)) : nullptr;
     a.zc = readout ? reinterpret_cast<float *>(wsp(ws, L.zc)) : nullptr;
-    return hf_launch_state(a, s);
+    return a;
+}
+
+hipError_t enqueue_state(const hf_dims *d, float *S, float *z, bool readout, int64_t absorb_tokens, void *ws,
+                         hipStream_t s) {
+    return hf_launch_state(state_args(d, S, z, readout, absorb_tokens, ws), s);
 }
 
 // Attention (+ readout from the prepared S^T / z copy when `readout`).
@@ -395,8 +403,8 @@ hf_status hf_hybrid_step(const hf_dims *d, const void *q, const void *k_cur, con
     st = check_ws(d, ws, ws_bytes);
     if (st != HF_OK) return st;
 
-    // Order: append; select; readout operands from the state as it is; attention with the
-    // fused readout; then the absorb of the frames this step evicts (still in the ring
+    // Order: append; select, with the readout operands taken from the state as it is by
+    // extra workgroups of its first launch; attention with the fused readout; then the absorb of the frames this step evicts (still in the ring
     // until the next append, and just streamed through the caches by the attention) and
     // the state update.
     hf_kv_ring next = *ring;
@@ -412,9 +420,11 @@ hf_status hf_hybrid_step(const hf_dims *d, const void *q, const void *k_cur, con
     hipError_t e = record(events, 0, stream);
     if (e == hipSuccess && k_cur) e = enqueue_append(d, ring, k_cur, v_cur, stream);
     if (e == hipSuccess) e = record(events, 1, stream);
-    if (e == hipSuccess) e = enqueue_select(d, q, ring, top_k, idx, nullptr, ws, stream);
+    // the readout operands are prepared by extra workgroups of the selection's pool launch
+    const hf_state_args prep = S ? state_args(d, S, z, true, 0, ws) : hf_state_args{};
+    if (e == hipSuccess)
+        e = enqueue_select(d, q, ring, top_k, idx, nullptr, ws, stream, 0, nullptr, nullptr, S ? &prep : nullptr);
     if (e == hipSuccess) e = record(events, 2, stream);
-    if (e == hipSuccess && S) e = enqueue_state(d, S, z, true, 0, ws, stream);
     if (e == hipSuccess) e = record(events, 3, stream);
     if (e == hipSuccess) e = enqueue_attn(d, q, ring, idx, top_k, S != nullptr, eps, out, ws, stream);
     if (e == hipSuccess) e = record(events, 4, stream);

@@ -82,6 +82,16 @@ __device__ __forceinline__ int ring_slot(const RingView &r, int f) {
 // ------------------------------------------------------------------ host-side launch API
 // (implemented in the .hip files, called from hf_api.cpp)
 
+struct hf_state_args {
+    int BH, D;
+    float *S, *z;              // state, read (and updated when part != null)
+    const float *part;         // absorb partials to add (null: none), P splits
+    int P;
+    uint16_t *st;              // out: S^T bf16 of the state as read (null: skip)
+    float *zc;                 // out: copy of z as read (null: skip)
+};
+hipError_t hf_launch_state(const hf_state_args &a, hipStream_t s);
+
 struct hf_select_args {
     int BH, D, T, W, head, Nq, Nk, bq, bk, nqb, nkb, top_k;
     const uint16_t *q, *ring_k;
@@ -95,6 +105,9 @@ struct hf_select_args {
     double *fsc;               // workspace: frame scores [BH][nqb][nfr]
     double *part;              // workspace: per key block, sums of its rows in its first frame
                                // and in the next one [BH][nkb][2][D] (needs bk <= T)
+    // readout preparation run as extra workgroups of the pool launch (prep_tiles > 0)
+    hf_state_args prep;
+    int prep_tiles;
     int32_t *fidx;             // may be null: kept frames [BH][nqb][top_frames], ascending
     double *fscores;           // may be null: frame scores [BH][nqb][nfr]
 };
@@ -127,15 +140,6 @@ size_t hf_absorb_partial_floats(int BH, int D, int P);
 size_t hf_absorb_workspace_bytes(int BH, int D);
 hipError_t hf_launch_absorb_partial(const hf_absorb_args &a, hipStream_t s);
 
-struct hf_state_args {
-    int BH, D;
-    float *S, *z;              // state, read (and updated when part != null)
-    const float *part;         // absorb partials to add (null: none), P splits
-    int P;
-    uint16_t *st;              // out: S^T bf16 of the state as read (null: skip)
-    float *zc;                 // out: copy of z as read (null: skip)
-};
-hipError_t hf_launch_state(const hf_state_args &a, hipStream_t s);
 
 // Chunk-aware growth schedule (schedule.hip); arguments validated by the caller.
 hf_status hf_cag_schedule_impl(int32_t n, const int32_t *nkb, double s_base, double s_target, double s_max,

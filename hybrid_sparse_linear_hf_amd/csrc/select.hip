@@ -23,7 +23,7 @@
 // The hierarchical variant adds frame_pool_kernel, runs the score kernel a second time
 // over (query block, frame) pairs, and lets the top-k wave select the frames before the
 // blocks.
-#include "hf_internal.h"
+#include "state_tile.h"
 
 namespace hf {
 namespace {
@@ -45,6 +45,11 @@ __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
     __shared__ double red[kRowsPerPass][D];
 
     const int per_plane = a.nqb + a.nkb;
+    if ((int)blockIdx.x >= a.BH * per_plane) {
+        // readout operands of a hybrid step (independent of the selection)
+        state_tile<D>(a.prep, (int)blockIdx.x - a.BH * per_plane, reinterpret_cast<float(*)[33]>(&red[0][0]));
+        return;
+    }
     const int bh = blockIdx.x / per_plane;
     const int blk = blockIdx.x % per_plane;
     const bool is_q = blk < a.nqb;
@@ -293,7 +298,7 @@ static void launch_topk(int kpl, dim3 grid, const hf_select_args &a, hipStream_t
 }
 
 hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s) {
-    const dim3 grid_pool((unsigned)(a.BH * (a.nqb + a.nkb)));
+    const dim3 grid_pool((unsigned)(a.BH * (a.nqb + a.nkb) + a.prep_tiles));
     const int ti_n = (a.nqb + hf::kTile - 1) / hf::kTile, tj_n = (a.nkb + hf::kTile - 1) / hf::kTile;
     const dim3 grid_score((unsigned)(a.BH * ti_n * tj_n));
     const dim3 grid_topk((unsigned)((a.BH * a.nqb + 3) / 4));

@@ -108,10 +108,10 @@ typedef struct {
 #define HF_STEP_COMMIT 1u
 
 /* Optional timing hooks for hf_hybrid_step: any non-NULL event is recorded on the
- * step's stream at that point: ev[0] begin, ev[1] after the ring append, ev[2] after
- * block selection, ev[3] after the readout operands are prepared, ev[4] after the
- * attention kernel, ev[5] after the absorb of the evicted frames and the state update
- * (the end of the step).  Events must have been created by the caller with
+ * step's stream at that point: ev[0] begin, ev[1] after the ring append, ev[2] and ev[3]
+ * after block selection (whose first launch also prepares the readout operands, so the
+ * two mark the same point), ev[4] after the attention kernel, ev[5] after the absorb of
+ * the evicted frames and the state update (the end of the step).  Events must have been created by the caller with
  * hipEventCreate. */
 typedef struct {
     hipEvent_t ev[6];
@@ -225,7 +225,8 @@ hf_status hf_cag_schedule(int32_t n_chunks, const int32_t *n_kb, double s_base, 
  *   1. if k_cur_dev and v_cur_dev are given: hf_ring_append (else the caller has
  *      already written the current chunk into its slots);
  *   2. block selection as hf_block_select -> idx_dev ([B][H][n_qb][top_k], an output);
- *   3. the readout operands are taken from (S, z) as they are;
+ *   3. the readout operands are taken from (S, z) as they are (in the same launch as the
+ *      selection's pooling);
  *   4. block-sparse attention with the fused readout, as hf_sparse_window_attn -> out_dev;
  *   5. with HF_STEP_COMMIT, when committing the chunk leaves more than W - C committed
  *      frames, the e oldest window frames are the evicted ones: they are absorbed into

@@ -198,25 +198,6 @@ struct RingLds {
 // the final reductions reuse the stages: 32 KB of accumulator halves, then 32 x 65 floats
 static_assert(sizeof(RawChunk<64>) * kStages >= 32768 + 32 * 65 * 4, "reduction scratch");
 
-// Workgroup barrier that orders LDS accesses only.  __syncthreads() also orders global
-// memory, which makes the compiler wait for every load in flight -- including the
-// direct-to-LDS fetches of later chunks that this barrier must not wait for.  The empty
-// asm statements keep the compiler from moving memory accesses across; the wait drains
-// this wave's LDS reads and writes before the barrier.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited on
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// s_waitcnt with vmcnt(n), expcnt and lgkmcnt at their maxima (no wait on those).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
 // Ring-source geometry: NW = D / 16 waves.  Wave w multiplies rows 32 (w & 1) .. +32 by
 // columns 64 ((w >> 1) % (D / 64)) .. +64 (two 32 x 32 tiles) over one half of each
 // chunk's tokens (the contraction half w / (NW / 2)); the two halves are added at the

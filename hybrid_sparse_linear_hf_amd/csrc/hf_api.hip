@@ -29,7 +29,6 @@ hf_status ok() {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-constexpr int kMaxKeyBlocks = 1536;
 constexpr int64_t kMaxElems = (int64_t)1 << 31;
 
 hf_status check_dims(const hf_dims *d) {

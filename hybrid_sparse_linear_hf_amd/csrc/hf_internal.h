@@ -50,6 +50,26 @@ __device__ __forceinline__ int fast_div(int n, uint32_t magic, int d) {
     return q;
 }
 
+// ------------------------------------------------------------------ LDS pipelines
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also orders global
+// memory, which makes the compiler wait for every load in flight -- including the
+// direct-to-LDS fetches of later stages that this barrier must not wait for.  The empty
+// asm statements keep the compiler from moving memory accesses across; the wait drains
+// this wave's LDS reads and writes before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited on
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt with vmcnt(n), expcnt and lgkmcnt at their maxima (no wait on those).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // ------------------------------------------------------------------ matrix cores
 // D = A * B + C on a 32x32x16 bf16 tile.  Lane l supplies A row (l % 32) and B column
 // (l % 32), 8 contraction elements each (the same 8 for A and B); the accumulator of
@@ -112,6 +132,7 @@ struct hf_select_args {
     double *fscores;           // may be null: frame scores [BH][nqb][nfr]
 };
 constexpr int kMaxHierFrames = 64;   // window frames the hierarchical selection handles
+constexpr int kMaxKeyBlocks = 1536;  // key blocks of a window (sizes the attention's LDS lists)
 hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s);
 
 struct hf_attn_args {

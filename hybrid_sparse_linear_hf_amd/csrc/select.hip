@@ -15,9 +15,10 @@
 // Three launches:
 //   pool_kernel   HBM-bound: one workgroup per query or key block sums its rows in fp64
 //                 (sums of bf16 values are exact in fp64) and stores the block mean.
-//   score_kernel  16 x 16 tiles of fp64 scores, each evaluated as sum_d (qbar_d * kbar_d) in
-//                 index order with separately rounded products and sums (the pooled
-//                 tiles are staged in LDS, every load issued up front).
+//   score_kernel  16 x 16 tiles of fp64 scores, one wave each, 2 x 2 per lane, each
+//                 evaluated as sum_d (qbar_d * kbar_d) in index order with separately
+//                 rounded products and sums (the pooled tiles are staged in LDS, every
+//                 load issued up front).
 //   topk_kernel   one wave per query block: radix select of the k-th largest
 //                 (score, -index) key and an ascending emit of the kept indices.
 // The hierarchical variant adds frame_pool_kernel, runs the score kernel a second time
@@ -149,52 +150,80 @@ __device__ __forceinline__ uint64_t order_key(double s) {
 
 constexpr int kTile = 16;   // score tile: 16 query blocks x 16 key blocks per workgroup
 
-// Scores of a 16 x 16 tile of (query block, key block) pairs: both pooled tiles are staged
-// in LDS (every staging load issued before the first LDS write), then each thread forms one
-// dot product as a sequential sum in index order.
+// Scores of a 16 x 16 tile of (query block, key block) pairs, one wave per tile: both
+// pooled tiles are staged in LDS (every staging load issued before the first LDS write),
+// then each lane forms a 2 x 2 block of dot products, each a sequential sum in index
+// order, reading two features per 16-byte LDS load.
 template <int D>
-__global__ __launch_bounds__(256) void score_kernel(hf_select_args a, double scale) {
-    __shared__ double qs[kTile][D + 1];
-    __shared__ double ks[kTile][D + 1];
+__global__ __launch_bounds__(64) void score_kernel(hf_select_args a, double scale) {
+    constexpr int P = D + 2;                 // row pitch in doubles (16-byte aligned rows)
+    __shared__ __align__(16) double qs[kTile][P];
+    __shared__ __align__(16) double ks[kTile][P];
+    typedef __attribute__((ext_vector_type(2))) double f64x2;
     const int ti_n = (a.nqb + kTile - 1) / kTile, tj_n = (a.nkb + kTile - 1) / kTile;
     const int bh = blockIdx.x / (ti_n * tj_n);
     const int i0 = ((blockIdx.x / tj_n) % ti_n) * kTile, j0 = (blockIdx.x % tj_n) * kTile;
     const int tid = threadIdx.x;
     {
         // rows past the end re-read the last row and are zeroed
-        typedef __attribute__((ext_vector_type(2))) double f64x2;
-        constexpr int kPer = kTile * D / 2 / 256;       // 16-byte loads per thread per matrix
-        f64x2 qv[kPer], kv[kPer];
+        constexpr int kPer = kTile * D / 2 / 64;        // 16-byte loads per lane per matrix
+        constexpr int kBatch = 8;
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-            const int idx = tid + 256 * e, r = idx / (D / 2), d = 2 * (idx % (D / 2));
-            qv[e] = *reinterpret_cast<const f64x2 *>(a.qbar + ((size_t)bh * a.nqb + min(i0 + r, a.nqb - 1)) * D + d);
-            kv[e] = *reinterpret_cast<const f64x2 *>(a.kbar + ((size_t)bh * a.nkb + min(j0 + r, a.nkb - 1)) * D + d);
-        }
+        for (int e0 = 0; e0 < kPer; e0 += kBatch) {
+            f64x2 qv[kBatch], kv[kBatch];
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-            const int idx = tid + 256 * e, r = idx / (D / 2), d = 2 * (idx % (D / 2));
-            const bool qok = i0 + r < a.nqb, kok = j0 + r < a.nkb;
-            qs[r][d] = qok ? qv[e].x : 0.0;
-            qs[r][d + 1] = qok ? qv[e].y : 0.0;
-            ks[r][d] = kok ? kv[e].x : 0.0;
-            ks[r][d + 1] = kok ? kv[e].y : 0.0;
+            for (int e = 0; e < kBatch; ++e) {
+                const int idx = tid + 64 * (e0 + e), r = idx / (D / 2), d = 2 * (idx % (D / 2));
+                qv[e] = *reinterpret_cast<const f64x2 *>(a.qbar + ((size_t)bh * a.nqb + min(i0 + r, a.nqb - 1)) * D + d);
+                kv[e] = *reinterpret_cast<const f64x2 *>(a.kbar + ((size_t)bh * a.nkb + min(j0 + r, a.nkb - 1)) * D + d);
+            }
+#pragma unroll
+            for (int e = 0; e < kBatch; ++e) {
+                const int idx = tid + 64 * (e0 + e), r = idx / (D / 2), d = 2 * (idx % (D / 2));
+                const f64x2 z = {0.0, 0.0};
+                *reinterpret_cast<f64x2 *>(&qs[r][d]) = i0 + r < a.nqb ? qv[e] : z;
+                *reinterpret_cast<f64x2 *>(&ks[r][d]) = j0 + r < a.nkb ? kv[e] : z;
+            }
         }
     }
     __syncthreads();
-    const int ti = tid / kTile, tj = tid % kTile;
-    const int i = i0 + ti, j = j0 + tj;
-    if (i >= a.nqb || j >= a.nkb) return;
-    double acc = 0.0;
+    const int ti = 2 * (tid / 8), tj = 2 * (tid % 8);
+    double acc[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
     {
         // products and sums rounded separately (no fused multiply-add), in index order
 #pragma clang fp contract(off)
-#pragma unroll 8
-        for (int d = 0; d < D; ++d) acc = acc + qs[ti][d] * ks[tj][d];
-        acc = acc * scale;
+#pragma unroll 4
+        for (int d = 0; d < D; d += 2) {
+            const f64x2 q0 = *reinterpret_cast<const f64x2 *>(&qs[ti][d]);
+            const f64x2 q1 = *reinterpret_cast<const f64x2 *>(&qs[ti + 1][d]);
+            const f64x2 k0 = *reinterpret_cast<const f64x2 *>(&ks[tj][d]);
+            const f64x2 k1 = *reinterpret_cast<const f64x2 *>(&ks[tj + 1][d]);
+            acc[0][0] = acc[0][0] + q0.x * k0.x;
+            acc[0][1] = acc[0][1] + q0.x * k1.x;
+            acc[1][0] = acc[1][0] + q1.x * k0.x;
+            acc[1][1] = acc[1][1] + q1.x * k1.x;
+            acc[0][0] = acc[0][0] + q0.y * k0.y;
+            acc[0][1] = acc[0][1] + q0.y * k1.y;
+            acc[1][0] = acc[1][0] + q1.y * k0.y;
+            acc[1][1] = acc[1][1] + q1.y * k1.y;
+        }
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y) acc[x][y] = acc[x][y] * scale;
     }
-    a.sc[((size_t)bh * a.nqb + i) * a.nkb + j] = acc;
-    if (a.scores) a.scores[((size_t)bh * a.nqb + i) * a.nkb + j] = acc;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        const int i = i0 + ti + x;
+        if (i >= a.nqb) continue;
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+            const int j = j0 + tj + y;
+            if (j >= a.nkb) continue;
+            a.sc[((size_t)bh * a.nqb + i) * a.nkb + j] = acc[x][y];
+            if (a.scores) a.scores[((size_t)bh * a.nqb + i) * a.nkb + j] = acc[x][y];
+        }
+    }
 }
 
 // Radix select over one wave: the k-th largest of the keys held in registers (KPL per
@@ -203,7 +232,9 @@ __global__ __launch_bounds__(256) void score_kernel(hf_select_args a, double sca
 template <int KPL>
 __device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPL], int k, int &need_eq) {
     // largest v with #{key >= v} >= k (v = 0 is only reached if fewer than k real keys
-    // exist, which the callers' bounds on k rule out)
+    // exist, which the callers' bounds on k rule out), found bit by bit from the top.  The
+    // search stops early once exactly k keys lie at or above the prefix: those k are the
+    // kept set, whatever their remaining bits.
     uint64_t prefix = 0;
     for (int bit = 63; bit >= 0; --bit) {
         const uint64_t cand = prefix | (1ull << bit);
@@ -211,11 +242,13 @@ __device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPL], int k, i
 #pragma unroll
         for (int e = 0; e < KPL; ++e) cnt += __popcll(__ballot(key[e] >= cand));
         if (cnt >= k) prefix = cand;
+        if (cnt == k) break;
     }
     int gt = 0;
 #pragma unroll
     for (int e = 0; e < KPL; ++e) gt += __popcll(__ballot(key[e] > prefix));
-    need_eq = k - gt;  // >= 1 by construction
+    need_eq = k - gt;  // keys equal to the returned value that are kept (0 after an early stop
+                       // where none equals it)
     return prefix;
 }
 
@@ -309,13 +342,13 @@ hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s) {
             hipLaunchKernelGGL((hf::pool_kernel<64, true>), grid_pool, dim3(256), 0, s, a);
         else
             hipLaunchKernelGGL((hf::pool_kernel<64, false>), grid_pool, dim3(256), 0, s, a);
-        hipLaunchKernelGGL(hf::score_kernel<64>, grid_score, dim3(256), 0, s, a, scale);
+        hipLaunchKernelGGL(hf::score_kernel<64>, grid_score, dim3(64), 0, s, a, scale);
     } else {
         if (hier)
             hipLaunchKernelGGL((hf::pool_kernel<128, true>), grid_pool, dim3(256), 0, s, a);
         else
             hipLaunchKernelGGL((hf::pool_kernel<128, false>), grid_pool, dim3(256), 0, s, a);
-        hipLaunchKernelGGL(hf::score_kernel<128>, grid_score, dim3(256), 0, s, a, scale);
+        hipLaunchKernelGGL(hf::score_kernel<128>, grid_score, dim3(64), 0, s, a, scale);
     }
     if (a.top_frames > 0) {
         const dim3 grid_fp((unsigned)(a.BH * a.nfr));
@@ -331,9 +364,9 @@ hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s) {
         f.scores = a.fscores;
         const dim3 grid_fs((unsigned)(a.BH * ti_n * ((a.nfr + hf::kTile - 1) / hf::kTile)));
         if (a.D == 64)
-            hipLaunchKernelGGL(hf::score_kernel<64>, grid_fs, dim3(256), 0, s, f, scale);
+            hipLaunchKernelGGL(hf::score_kernel<64>, grid_fs, dim3(64), 0, s, f, scale);
         else
-            hipLaunchKernelGGL(hf::score_kernel<128>, grid_fs, dim3(256), 0, s, f, scale);
+            hipLaunchKernelGGL(hf::score_kernel<128>, grid_fs, dim3(64), 0, s, f, scale);
     }
     const int kpl = (a.nkb + 63) / 64;
     if (a.top_frames > 0)

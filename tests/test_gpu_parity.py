@@ -177,6 +177,8 @@ EDGE = [
     (1, 1, 128, 104, 1, 5, 16, 128, 1, 1),    # bq=16, bk=128 (4 subtiles, last partial), top-1
     (1, 3, 64, 72, 1, 4, 64, 32, 0, 3),       # window not yet full (chunk only), keep-all
     (1, 1, 128, 64, 2, 2, 64, 64, 0, 1),      # W == C
+    (1, 2, 128, 136, 1, 4, 64, 64, 3, 2),     # odd number of query blocks (last pair has one), 32-key last block
+    (1, 1, 64, 48, 4, 6, 64, 64, 2, 4),       # D=64, odd number of query blocks, frames of 48 tokens
 ]
 
 

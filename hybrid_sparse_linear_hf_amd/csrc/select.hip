@@ -316,18 +316,104 @@ __global__ __launch_bounds__(256) void topk_kernel(hf_select_args a) {
     emit_kept<KPL>(key, a.nkb, prefix, need_eq, a.idx + (size_t)row * a.top_k, lane);
 }
 
+// Flat selection, scores and top-k in one launch: a workgroup takes kRows query blocks of
+// one plane (one wave each).  The plane's pooled key blocks pass through LDS in chunks of
+// 64 (the next chunk is loaded into registers while the current one is scored); lane l of
+// wave w scores query block w against key block (chunk start + l) as a sequential sum in
+// index order with separately rounded products and sums, exactly as the tiled kernel
+// does.  The row of scores stays in LDS for the wave's radix select.
+constexpr int kRows = 4;
+template <int D, int KPL>
+__global__ __launch_bounds__(64 * kRows) void score_topk_kernel(hf_select_args a, double scale) {
+    constexpr int P = D + 2;                  // row pitch in doubles (16-byte aligned rows)
+    constexpr int CH = 64;                    // key blocks per chunk
+    constexpr int kPer = CH * D / 2 / (64 * kRows);   // 16-byte loads per thread per chunk
+    typedef __attribute__((ext_vector_type(2))) double f64x2;
+    __shared__ __align__(16) double qs[kRows][P];
+    __shared__ __align__(16) double ks[CH][P];
+    __shared__ double srow[kRows][KPL * 64];
+    const int groups = (a.nqb + kRows - 1) / kRows;
+    const int bh = blockIdx.x / groups, i0 = (blockIdx.x % groups) * kRows;
+    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
+    const int i = i0 + w;                     // this wave's query block (past the end: idle)
+    for (int t = tid; t < kRows * D / 2; t += 64 * kRows) {
+        const int r = t / (D / 2), d = 2 * (t % (D / 2));
+        *reinterpret_cast<f64x2 *>(&qs[r][d]) =
+            *reinterpret_cast<const f64x2 *>(a.qbar + ((size_t)bh * a.nqb + min(i0 + r, a.nqb - 1)) * D + d);
+    }
+    const double *kb = a.kbar + (size_t)bh * a.nkb * D;
+    f64x2 nxt[kPer];
+    auto load_chunk = [&](int c0) {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const int t = tid + 64 * kRows * e, r = t / (D / 2), d = 2 * (t % (D / 2));
+            nxt[e] = *reinterpret_cast<const f64x2 *>(kb + (size_t)min(c0 + r, a.nkb - 1) * D + d);
+        }
+    };
+    load_chunk(0);
+    for (int c0 = 0; c0 < a.nkb; c0 += CH) {
+        __syncthreads();                      // everyone is done with the previous chunk
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const int t = tid + 64 * kRows * e, r = t / (D / 2), d = 2 * (t % (D / 2));
+            *reinterpret_cast<f64x2 *>(&ks[r][d]) = nxt[e];
+        }
+        __syncthreads();
+        if (c0 + CH < a.nkb) load_chunk(c0 + CH);
+        const int j = c0 + lane;
+        double acc = 0.0;
+        {
+#pragma clang fp contract(off)
+#pragma unroll 8
+            for (int d = 0; d < D; d += 2) {
+                const f64x2 q = *reinterpret_cast<const f64x2 *>(&qs[w][d]);
+                const f64x2 k = *reinterpret_cast<const f64x2 *>(&ks[lane][d]);
+                acc = acc + q.x * k.x;
+                acc = acc + q.y * k.y;
+            }
+            acc = acc * scale;
+        }
+        if (j < a.nkb) {
+            srow[w][j] = acc;
+            if (a.scores && i < a.nqb) a.scores[((size_t)bh * a.nqb + i) * a.nkb + j] = acc;
+        }
+    }
+    if (i >= a.nqb) return;                   // uniform per wave; no barrier follows
+    uint64_t key[KPL];
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) {
+        const int j = lane + 64 * e;
+        key[e] = j < a.nkb ? order_key(srow[w][j]) : 0;
+    }
+    int need_eq;
+    const uint64_t prefix = kth_key<KPL>(key, a.top_k, need_eq);
+    emit_kept<KPL>(key, a.nkb, prefix, need_eq, a.idx + ((size_t)bh * a.nqb + i) * a.top_k, lane);
+}
+
 }  // namespace
 }  // namespace hf
 
-template <bool HIER>
 static void launch_topk(int kpl, dim3 grid, const hf_select_args &a, hipStream_t s) {
-    if (kpl <= 1) hipLaunchKernelGGL((hf::topk_kernel<1, HIER>), grid, dim3(256), 0, s, a);
-    else if (kpl <= 2) hipLaunchKernelGGL((hf::topk_kernel<2, HIER>), grid, dim3(256), 0, s, a);
-    else if (kpl <= 3) hipLaunchKernelGGL((hf::topk_kernel<3, HIER>), grid, dim3(256), 0, s, a);
-    else if (kpl <= 4) hipLaunchKernelGGL((hf::topk_kernel<4, HIER>), grid, dim3(256), 0, s, a);
-    else if (kpl <= 8) hipLaunchKernelGGL((hf::topk_kernel<8, HIER>), grid, dim3(256), 0, s, a);
-    else if (kpl <= 16) hipLaunchKernelGGL((hf::topk_kernel<16, HIER>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((hf::topk_kernel<24, HIER>), grid, dim3(256), 0, s, a);
+    if (kpl <= 1) hipLaunchKernelGGL((hf::topk_kernel<1, true>), grid, dim3(256), 0, s, a);
+    else if (kpl <= 2) hipLaunchKernelGGL((hf::topk_kernel<2, true>), grid, dim3(256), 0, s, a);
+    else if (kpl <= 3) hipLaunchKernelGGL((hf::topk_kernel<3, true>), grid, dim3(256), 0, s, a);
+    else if (kpl <= 4) hipLaunchKernelGGL((hf::topk_kernel<4, true>), grid, dim3(256), 0, s, a);
+    else if (kpl <= 8) hipLaunchKernelGGL((hf::topk_kernel<8, true>), grid, dim3(256), 0, s, a);
+    else if (kpl <= 16) hipLaunchKernelGGL((hf::topk_kernel<16, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((hf::topk_kernel<24, true>), grid, dim3(256), 0, s, a);
+}
+
+template <int D>
+static void launch_score_topk(int kpl, const hf_select_args &a, double scale, hipStream_t s) {
+    const dim3 grid((unsigned)(a.BH * ((a.nqb + hf::kRows - 1) / hf::kRows)));
+    const dim3 block(64 * hf::kRows);
+    if (kpl <= 1) hipLaunchKernelGGL((hf::score_topk_kernel<D, 1>), grid, block, 0, s, a, scale);
+    else if (kpl <= 2) hipLaunchKernelGGL((hf::score_topk_kernel<D, 2>), grid, block, 0, s, a, scale);
+    else if (kpl <= 3) hipLaunchKernelGGL((hf::score_topk_kernel<D, 3>), grid, block, 0, s, a, scale);
+    else if (kpl <= 4) hipLaunchKernelGGL((hf::score_topk_kernel<D, 4>), grid, block, 0, s, a, scale);
+    else if (kpl <= 8) hipLaunchKernelGGL((hf::score_topk_kernel<D, 8>), grid, block, 0, s, a, scale);
+    else if (kpl <= 16) hipLaunchKernelGGL((hf::score_topk_kernel<D, 16>), grid, block, 0, s, a, scale);
+    else hipLaunchKernelGGL((hf::score_topk_kernel<D, 24>), grid, block, 0, s, a, scale);
 }
 
 hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s) {
@@ -336,42 +422,43 @@ hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s) {
     const dim3 grid_score((unsigned)(a.BH * ti_n * tj_n));
     const dim3 grid_topk((unsigned)((a.BH * a.nqb + 3) / 4));
     const double scale = 1.0 / sqrt((double)a.D);
-    const bool hier = a.top_frames > 0;
-    if (a.D == 64) {
-        if (hier)
-            hipLaunchKernelGGL((hf::pool_kernel<64, true>), grid_pool, dim3(256), 0, s, a);
-        else
+    const int kpl = (a.nkb + 63) / 64;
+    if (a.top_frames == 0) {
+        // flat: pool, then scores and top-k in one launch
+        if (a.D == 64) {
             hipLaunchKernelGGL((hf::pool_kernel<64, false>), grid_pool, dim3(256), 0, s, a);
+            launch_score_topk<64>(kpl, a, scale, s);
+        } else {
+            hipLaunchKernelGGL((hf::pool_kernel<128, false>), grid_pool, dim3(256), 0, s, a);
+            launch_score_topk<128>(kpl, a, scale, s);
+        }
+        return hipGetLastError();
+    }
+    // hierarchical: pool (keeping each key block's frame parts), frame means, block and
+    // frame scores, then the two-level top-k
+    if (a.D == 64) {
+        hipLaunchKernelGGL((hf::pool_kernel<64, true>), grid_pool, dim3(256), 0, s, a);
         hipLaunchKernelGGL(hf::score_kernel<64>, grid_score, dim3(64), 0, s, a, scale);
     } else {
-        if (hier)
-            hipLaunchKernelGGL((hf::pool_kernel<128, true>), grid_pool, dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((hf::pool_kernel<128, false>), grid_pool, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((hf::pool_kernel<128, true>), grid_pool, dim3(256), 0, s, a);
         hipLaunchKernelGGL(hf::score_kernel<128>, grid_score, dim3(64), 0, s, a, scale);
     }
-    if (a.top_frames > 0) {
-        const dim3 grid_fp((unsigned)(a.BH * a.nfr));
-        if (a.D == 64)
-            hipLaunchKernelGGL(hf::frame_pool_kernel<64>, grid_fp, dim3(64), 0, s, a);
-        else
-            hipLaunchKernelGGL(hf::frame_pool_kernel<128>, grid_fp, dim3(128), 0, s, a);
-        // frame scores: the score kernel over (query block, frame) pairs
-        hf_select_args f = a;
-        f.kbar = a.fbar;
-        f.nkb = a.nfr;
-        f.sc = a.fsc;
-        f.scores = a.fscores;
-        const dim3 grid_fs((unsigned)(a.BH * ti_n * ((a.nfr + hf::kTile - 1) / hf::kTile)));
-        if (a.D == 64)
-            hipLaunchKernelGGL(hf::score_kernel<64>, grid_fs, dim3(64), 0, s, f, scale);
-        else
-            hipLaunchKernelGGL(hf::score_kernel<128>, grid_fs, dim3(64), 0, s, f, scale);
-    }
-    const int kpl = (a.nkb + 63) / 64;
-    if (a.top_frames > 0)
-        launch_topk<true>(kpl, grid_topk, a, s);
+    const dim3 grid_fp((unsigned)(a.BH * a.nfr));
+    if (a.D == 64)
+        hipLaunchKernelGGL(hf::frame_pool_kernel<64>, grid_fp, dim3(64), 0, s, a);
     else
-        launch_topk<false>(kpl, grid_topk, a, s);
+        hipLaunchKernelGGL(hf::frame_pool_kernel<128>, grid_fp, dim3(128), 0, s, a);
+    // frame scores: the score kernel over (query block, frame) pairs
+    hf_select_args f = a;
+    f.kbar = a.fbar;
+    f.nkb = a.nfr;
+    f.sc = a.fsc;
+    f.scores = a.fscores;
+    const dim3 grid_fs((unsigned)(a.BH * ti_n * ((a.nfr + hf::kTile - 1) / hf::kTile)));
+    if (a.D == 64)
+        hipLaunchKernelGGL(hf::score_kernel<64>, grid_fs, dim3(64), 0, s, f, scale);
+    else
+        hipLaunchKernelGGL(hf::score_kernel<128>, grid_fs, dim3(64), 0, s, f, scale);
+    launch_topk(kpl, grid_topk, a, s);
     return hipGetLastError();
 }

@@ -403,8 +403,8 @@ hf_status hf_hybrid_step(const hf_dims *d, const void *q, const void *k_cur, con
     if (st != HF_OK) return st;
 
     // Order: append; select, with the readout operands taken from the state as it is by
-    // extra workgroups of its first launch; attention with the fused readout; then the absorb of the frames this step evicts (still in the ring
-    // until the next append, and just streamed through the caches by the attention) and
+    // extra workgroups of its first launch; attention with the fused readout; then the
+    // absorb of the frames this step evicts (still in the ring until the next append) and
     // the state update.
     hf_kv_ring next = *ring;
     int evict = 0;

@@ -56,6 +56,9 @@ def lib():
         L.hfo_linear_readout.argtypes = [_i64, _i64, _i64, _i64, _D, _D, _D, ctypes.c_double, _I64, _i64, _D]
         L.hfo_absorb.argtypes = [_i64, _i64, _i64, _D, _D, _D, _D]
         L.hfo_hybrid_step.argtypes = ([_i64] * 7 + [ctypes.c_double, _D, _D, _D, _D, _D, _I64, _i64, _I32, _D, _D])
+        L.hfo_sparse_attn_bwd.argtypes = [_i64] * 7 + [_D, _D, _D, _I32, _D, _D, _D, _D]
+        L.hfo_linear_readout_bwd.argtypes = [_i64, _i64, _i64, _D, _D, _D, ctypes.c_double, _D, _D, _D, _D]
+        L.hfo_absorb_bwd.argtypes = [_i64, _i64, _i64, _D, _D, _D, _D, _D, _D]
         L.hfo_num_threads.restype = ctypes.c_int
         L.hfo_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -251,3 +254,44 @@ def hier_select(Q, K, bq, bk, T, k_frames, k):
                 cand.sort()
                 idx[b, h, i] = sorted(j for _, j in cand[:k])
     return idx, frames, s, sf
+
+
+# ---------------------------------------------------------------- backward (idx held fixed)
+
+def sparse_attn_bwd(Q, K, V, idx, bq, bk, dO):
+    """Gradients of sum(sparse_attn(Q, K, V, idx) * dO) -> (dQ, dK, dV); the chain rule of
+    the softmax over each query's kept keys (hf_oracle.h states the terms)."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    B, H, Nq, D = Q.shape
+    Nk = K.shape[2]
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    lib().hfo_sparse_attn_bwd(B * H, Nq, Nk, D, bq, bk, idx.shape[-1], _p(Q), _p(K), _p(V), _p(idx, _I32), _p(dO),
+                              _p(dQ), _p(dK), _p(dV))
+    return dQ, dK, dV
+
+
+def linear_readout_bwd(Q, S, z, dO, eps=1e-6):
+    """Gradients of sum(linear_readout(Q, S, z) * dO) -> (dQ, dS, dz)."""
+    Q, S, z, dO = _f64(Q), _f64(S), _f64(z), _f64(dO)
+    B, H, Nq, D = Q.shape
+    dQ, dS, dz = np.zeros_like(Q), np.zeros_like(S), np.zeros_like(z)
+    lib().hfo_linear_readout_bwd(B * H, Nq, D, _p(Q), _p(S), _p(z), eps, _p(dO), _p(dQ), _p(dS), _p(dz))
+    return dQ, dS, dz
+
+
+def absorb_bwd(K, V, dS, dz):
+    """Gradients w.r.t. the absorbed tokens of sum(S_after * dS) + sum(z_after * dz) -> (dK, dV)."""
+    K, V, dS, dz = _f64(K), _f64(V), _f64(dS), _f64(dz)
+    B, H, n, D = K.shape
+    dK, dV = np.zeros_like(K), np.zeros_like(V)
+    lib().hfo_absorb_bwd(B * H, n, D, _p(K), _p(V), _p(dS), _p(dz), _p(dK), _p(dV))
+    return dK, dV
+
+
+def hybrid_step_bwd(Q, K, V, S, z, idx, bq, bk, dO, eps=1e-6):
+    """Backward of the step output sparse_attn + linear_readout with the selection idx held
+    fixed -> (dQ, dK, dV, dS, dz): dQ is the sum of both branches' terms."""
+    dQ1, dK, dV = sparse_attn_bwd(Q, K, V, idx, bq, bk, dO)
+    dQ2, dS, dz = linear_readout_bwd(Q, S, z, dO, eps)
+    return dQ1 + dQ2, dK, dV, dS, dz

@@ -256,3 +256,144 @@ void hfo_hybrid_step(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int64_t bq, 
     free(kbar);
     free(qbar);
 }
+
+/* ---------------------------------------------------------------- backward */
+
+static double phi_prime(double x) { return x > 0.0 ? 1.0 : exp(x); }
+
+/* One plane, every query in order (dK, dV accumulate over queries, so the plane is the
+ * unit of parallel work and the summation order is fixed). */
+static void sparse_plane_bwd(int64_t Nq, int64_t Nk, int64_t D, int64_t bq, int64_t bk, int64_t k,
+                             const double *Q, const double *K, const double *V, const int32_t *sel_all,
+                             const double *dO, double *dQ, double *dK, double *dV, double *P,
+                             double *dP, int64_t *key) {
+    const double scale = 1.0 / sqrt((double)D);
+    const int64_t nqb = ceil_div(Nq, bq);
+    for (int64_t t = 0; t < Nq; ++t) {
+        const int32_t *sel = sel_all + (t / bq) * k;
+        const double *q = Q + t * D, *g = dO + t * D;
+        /* the kept keys of t's block, their logits and softmax weights */
+        int64_t n = 0;
+        double m = -INFINITY;
+        for (int64_t r = 0; r < k; ++r) {
+            const int64_t u0 = (int64_t)sel[r] * bk, u1 = min64(u0 + bk, Nk);
+            for (int64_t u = u0; u < u1; ++u) {
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d) dot += q[d] * K[u * D + d];
+                key[n] = u;
+                P[n] = dot * scale;
+                if (P[n] > m) m = P[n];
+                ++n;
+            }
+        }
+        double denom = 0.0;
+        for (int64_t e = 0; e < n; ++e) {
+            P[e] = exp(P[e] - m);
+            denom += P[e];
+        }
+        for (int64_t e = 0; e < n; ++e) P[e] /= denom;
+        /* dP and Delta */
+        double delta = 0.0;
+        for (int64_t e = 0; e < n; ++e) {
+            const double *v = V + key[e] * D;
+            double s = 0.0;
+            for (int64_t c = 0; c < D; ++c) s += g[c] * v[c];
+            dP[e] = s;
+            delta += P[e] * s;
+        }
+        for (int64_t e = 0; e < n; ++e) {
+            const int64_t u = key[e];
+            const double G = P[e] * (dP[e] - delta);
+            for (int64_t d = 0; d < D; ++d) {
+                dQ[t * D + d] += G * K[u * D + d] * scale;
+                dK[u * D + d] += G * q[d] * scale;
+                dV[u * D + d] += P[e] * g[d];
+            }
+        }
+    }
+    (void)nqb;
+}
+
+void hfo_sparse_attn_bwd(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int64_t bq, int64_t bk,
+                         int64_t k, const double *Q, const double *K, const double *V,
+                         const int32_t *idx, const double *dO, double *dQ, double *dK, double *dV) {
+    const int64_t nqb = ceil_div(Nq, bq);
+#pragma omp parallel
+    {
+        double *P = (double *)malloc((size_t)(k * bk) * sizeof(double));
+        double *dP = (double *)malloc((size_t)(k * bk) * sizeof(double));
+        int64_t *key = (int64_t *)malloc((size_t)(k * bk) * sizeof(int64_t));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t p = 0; p < BH; ++p)
+            sparse_plane_bwd(Nq, Nk, D, bq, bk, k, Q + p * Nq * D, K + p * Nk * D, V + p * Nk * D,
+                             idx + p * nqb * k, dO + p * Nq * D, dQ + p * Nq * D, dK + p * Nk * D,
+                             dV + p * Nk * D, P, dP, key);
+        free(key);
+        free(dP);
+        free(P);
+    }
+}
+
+void hfo_linear_readout_bwd(int64_t BH, int64_t Nq, int64_t D, const double *Q, const double *S,
+                            const double *z, double eps, const double *dO, double *dQ, double *dS,
+                            double *dz) {
+#pragma omp parallel
+    {
+        double *a = (double *)malloc((size_t)D * sizeof(double));
+        double *num = (double *)malloc((size_t)D * sizeof(double));
+        double *dn = (double *)malloc((size_t)D * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t p = 0; p < BH; ++p) {
+            const double *Sp = S + p * D * D, *zp = z + p * D;
+            double *dSp = dS + p * D * D, *dzp = dz + p * D;
+            for (int64_t t = 0; t < Nq; ++t) {
+                const double *q = Q + (p * Nq + t) * D, *g = dO + (p * Nq + t) * D;
+                for (int64_t d = 0; d < D; ++d) a[d] = hfo_phi(q[d]);
+                double den = eps;
+                for (int64_t d = 0; d < D; ++d) den += a[d] * zp[d];
+                double gn = 0.0;
+                for (int64_t c = 0; c < D; ++c) {
+                    double s = 0.0;
+                    for (int64_t d = 0; d < D; ++d) s += a[d] * Sp[d * D + c];
+                    num[c] = s;
+                    gn += g[c] * s;
+                }
+                const double dden = -gn / (den * den);
+                for (int64_t c = 0; c < D; ++c) dn[c] = g[c] / den;
+                for (int64_t d = 0; d < D; ++d) {
+                    double da = zp[d] * dden;
+                    for (int64_t c = 0; c < D; ++c) {
+                        da += Sp[d * D + c] * dn[c];
+                        dSp[d * D + c] += a[d] * dn[c];
+                    }
+                    dzp[d] += a[d] * dden;
+                    dQ[(p * Nq + t) * D + d] += da * phi_prime(q[d]);
+                }
+            }
+        }
+        free(dn);
+        free(num);
+        free(a);
+    }
+}
+
+void hfo_absorb_bwd(int64_t BH, int64_t n, int64_t D, const double *K, const double *V,
+                    const double *dS, const double *dz, double *dK, double *dV) {
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < BH; ++p) {
+        const double *dSp = dS + p * D * D, *dzp = dz + p * D;
+        for (int64_t u = 0; u < n; ++u) {
+            const double *ku = K + (p * n + u) * D, *vu = V + (p * n + u) * D;
+            for (int64_t c = 0; c < D; ++c) {
+                double s = 0.0;
+                for (int64_t a = 0; a < D; ++a) s += hfo_phi(ku[a]) * dSp[a * D + c];
+                dV[(p * n + u) * D + c] += s;
+            }
+            for (int64_t a = 0; a < D; ++a) {
+                double s = dzp[a];
+                for (int64_t c = 0; c < D; ++c) s += dSp[a * D + c] * vu[c];
+                dK[(p * n + u) * D + a] += s * phi_prime(ku[a]);
+            }
+        }
+    }
+}

@@ -98,6 +98,32 @@ void hfo_hybrid_step(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int64_t bq, 
                      const double *S, const double *z, const int64_t *blocks, int64_t n_blocks,
                      int32_t *idx_out, double *scores_out, double *out);
 
+/* ---- backward of the step (the selection idx is held fixed: it is piecewise constant)
+ * Each function below is the chain rule of the forward function above it, written out
+ * term by term; gradients are ADDED into the output arrays (the caller zeroes them). */
+
+/* Sparse attention: with P the softmax weights of query t over its kept keys u,
+ * o_t = sum_u P_tu v_u, dP_tu = dO_t . v_u, Delta_t = sum_u P_tu dP_tu,
+ * G_tu = P_tu (dP_tu - Delta_t):  dQ_t += G_tu k_u / sqrt(D),  dK_u += G_tu q_t / sqrt(D),
+ * dV_u += P_tu dO_t.  Every query block is computed. */
+void hfo_sparse_attn_bwd(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int64_t bq, int64_t bk,
+                         int64_t k, const double *Q, const double *K, const double *V,
+                         const int32_t *idx, const double *dO, double *dQ, double *dK, double *dV);
+
+/* Linear readout r_t = n_t / den_t, n_t[c] = sum_a a_t[a] S[a][c], den_t = a_t . z + eps,
+ * a_t = phi(q_t):  dn = dO_t / den_t, dden = -(dO_t . n_t) / den_t^2,
+ * dS[a][c] += a_t[a] dn[c], dz[a] += a_t[a] dden, da[a] = sum_c S[a][c] dn[c] + z[a] dden,
+ * dQ_t[a] += da[a] phi'(q_t[a]) with phi'(x) = 1 for x > 0, e^x otherwise. */
+void hfo_linear_readout_bwd(int64_t BH, int64_t Nq, int64_t D, const double *Q, const double *S,
+                            const double *z, double eps, const double *dO, double *dQ, double *dS,
+                            double *dz);
+
+/* Absorb S += sum_u phi(k_u)^T v_u, z += sum_u phi(k_u), given the gradients dS, dz of
+ * the state after it:  dV_u[c] += sum_a phi(k_u[a]) dS[a][c],
+ * dK_u[a] += (sum_c dS[a][c] v_u[c] + dz[a]) phi'(k_u[a]).  K, V [BH][n][D]. */
+void hfo_absorb_bwd(int64_t BH, int64_t n, int64_t D, const double *K, const double *V,
+                    const double *dS, const double *dz, double *dK, double *dV);
+
 /* Number of OpenMP threads the oracle runs on (1 when built without OpenMP). */
 int hfo_num_threads(void);
 void hfo_set_num_threads(int n);

@@ -135,9 +135,10 @@ def main():
                     help="after timing, run a plain 256 MiB elementwise copy (for counter calibration)")
     ap.add_argument("--keep", type=float, default=None, help="override the kept fraction of key blocks")
     ap.add_argument("--window", type=int, default=None, help="override the window length in frames")
-    ap.add_argument("--mode", choices=("step", "hier", "cag"), default="step",
+    ap.add_argument("--mode", choices=("step", "hier", "cag", "bwd"), default="step",
                     help="step: the hybrid step (default); hier: hierarchical selection + attention on a 21-frame "
-                         "window; cag: a stream from an empty window under the chunk-aware keep schedule")
+                         "window; cag: a stream from an empty window under the chunk-aware keep schedule; "
+                         "bwd: training forward (with lse) and backward of the attention + readout")
     ap.add_argument("--top-frames", type=int, default=6, help="hier: frames kept per query block")
     ap.add_argument("--top-k", type=int, default=128, help="hier: key blocks kept per query block")
     ap.add_argument("--stream", type=int, default=16, help="cag: chunks in the stream")
@@ -160,6 +161,8 @@ def main():
         return bench_hier(args)
     if args.mode == "cag":
         return bench_cag(args)
+    if args.mode == "bwd":
+        return bench_bwd(args)
     cfg = synth.LAYER_832x480
     if args.keep is not None or args.window is not None:
         import dataclasses
@@ -364,6 +367,58 @@ def bench_hier(args):
            "sparse_attn_readout_us": round(float(np.median(att)) * 1e3, 2),
            "kept_flops": round(fl),
            "attn_frac_of_bf16_peak": round(fl / (np.median(att) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    print(json.dumps(res), flush=True)
+
+
+def bench_bwd(args):
+    """Backward of the attention + readout at the 832x480 layer (selection held fixed):
+    hf_sparse_window_attn_lse then hf_hybrid_attn_backward per timed step.  Algorithmic
+    backward flops = 10 D per kept (query, key) pair (the products S = Q K^T, dP = dO V^T,
+    dV = P^T dO, dQ = G K, dK = G^T Q), i.e. 2.5x the forward's kept flops."""
+    import torch
+    import hybrid_sparse_linear_hf_amd as hf
+    from hybrid_sparse_linear_hf_amd import synth
+
+    cfg = synth.LAYER_832x480
+    dev = torch.device("cuda:0")
+    g, ring, ws, S, z, q = _field_ring(cfg, hf, synth, torch, dev)
+    top_k = cfg.top_k()
+    Nk = cfg.W * cfg.T
+    bws = hf.new_backward_workspace(g, top_k)
+    idx = torch.empty((cfg.B, cfg.H, g.n_qb, top_k), dtype=torch.int32, device=dev)
+    out = torch.empty((cfg.B, cfg.H, cfg.Nq, cfg.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((cfg.B, cfg.H, cfg.Nq), dtype=torch.float32, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(0)
+    dout = torch.randn((cfg.B, cfg.H, cfg.Nq, cfg.D), dtype=torch.float32, device=dev, generator=gen)
+    dq = torch.empty_like(dout)
+    dk = torch.empty((cfg.B, cfg.H, Nk, cfg.D), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    dS, dz = torch.empty_like(S), torch.empty_like(z)
+    hf.hf_block_select(g, q, ring, top_k, idx, None, ws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    fwd, bwd = [], []
+    for it in range(args.warmup + args.steps):
+        ev[0].record()
+        hf.hf_sparse_window_attn_lse(g, q, ring, idx, top_k, S, z, out, lse, ws)
+        ev[1].record()
+        hf.hf_hybrid_attn_backward(g, q, ring, idx, top_k, S, z, out, lse, dout, dq, dk, dv, dS, dz, bws)
+        ev[2].record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            fwd.append(ev[0].elapsed_time(ev[1]))
+            bwd.append(ev[1].elapsed_time(ev[2]))
+    fl = kept_flops(idx.cpu().numpy(), cfg.Nq, Nk, cfg.bq, cfg.bk, cfg.D)
+    tb = float(np.median(bwd)) * 1e-3
+    res = {"metric": "hybrid attention backward (selection fixed), 832x480 layer, 1 GPU",
+           "value": round(2.5 * fl / tb / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(tb * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded rank-8 spatial field + noise per head, bf16)",
+           "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "D": cfg.D, "tokens_per_frame": cfg.T,
+                      "chunk_frames": cfg.C, "window_frames": cfg.W, "block": [cfg.bq, cfg.bk], "top_k": top_k},
+           "forward_lse_us": round(float(np.median(fwd)) * 1e3, 2),
+           "backward_us": round(tb * 1e6, 2),
+           "backward_algorithmic_flops": round(2.5 * fl),
+           "backward_frac_of_bf16_peak": round(2.5 * fl / tb / 1e12 / PEAK_BF16_TFLOPS, 4)}
     print(json.dumps(res), flush=True)
 
 

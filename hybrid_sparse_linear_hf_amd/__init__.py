@@ -7,4 +7,5 @@ The compute lives in libhf.so (HIP kernels behind the C ABI of include/hf.h);
 from ._lib import (HF_STEP_COMMIT, Geometry, HFError, Ring, abi_version, hf_block_select,  # noqa: F401
                    hf_block_select_hier, hf_cag_schedule,
                    hf_hybrid_step, hf_linear_absorb, hf_ring_append, hf_sparse_window_attn, new_workspace,
-                   workspace_size)
+                   workspace_size, backward_workspace_size, new_backward_workspace, hf_sparse_window_attn_lse,
+                   hf_hybrid_attn_backward, hf_linear_absorb_backward)

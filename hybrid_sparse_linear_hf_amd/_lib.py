@@ -70,8 +70,15 @@ def lib():
         f64 = ctypes.c_double
         L.hf_cag_schedule.argtypes = [i32, ctypes.POINTER(i32), f64, f64, f64, ctypes.POINTER(i32),
                                       ctypes.POINTER(f64), ctypes.POINTER(f64)]
+        L.hf_sparse_window_attn_lse.argtypes = [pd, _P, pr, _P, i32, _P, _P, f32, _P, _P, _P, sz, _P]
+        L.hf_backward_workspace_size.argtypes = [pd, i32, ctypes.POINTER(sz)]
+        L.hf_hybrid_attn_backward.argtypes = [pd, _P, pr, _P, i32, _P, _P, f32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                              _P, sz, _P]
+        L.hf_linear_absorb_backward.argtypes = [pd, _P, _P, i64, _P, _P, _P, _P, _P, sz, _P]
         for fn in ("hf_workspace_size", "hf_ring_append", "hf_block_select", "hf_sparse_window_attn",
-                   "hf_linear_absorb", "hf_hybrid_step", "hf_cag_schedule", "hf_block_select_hier"):
+                   "hf_linear_absorb", "hf_hybrid_step", "hf_cag_schedule", "hf_block_select_hier",
+                   "hf_sparse_window_attn_lse", "hf_backward_workspace_size", "hf_hybrid_attn_backward",
+                   "hf_linear_absorb_backward"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -215,3 +222,40 @@ def hf_cag_schedule(n_kb, s_base: float, s_target: float, s_max: float):
     _check("hf_cag_schedule", lib().hf_cag_schedule(n, nkb, float(s_base), float(s_target), float(s_max), k, s,
                                                     ctypes.byref(beta)))
     return list(k), list(s), beta.value
+
+
+# ------------------------------------------------------------------ backward (training)
+
+def backward_workspace_size(g: Geometry, top_k: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("hf_backward_workspace_size", lib().hf_backward_workspace_size(ctypes.byref(g.dims()), int(top_k),
+                                                                          ctypes.byref(n)))
+    return n.value
+
+
+def new_backward_workspace(g: Geometry, top_k: int, device="cuda") -> torch.Tensor:
+    return torch.empty(backward_workspace_size(g, top_k), dtype=torch.uint8, device=device)
+
+
+def hf_sparse_window_attn_lse(g: Geometry, q, ring: Ring, idx, top_k: int, S, z, out, lse, ws, eps=1e-6,
+                              stream=None) -> None:
+    _check("hf_sparse_window_attn_lse",
+           lib().hf_sparse_window_attn_lse(ctypes.byref(g.dims()), _ptr(q), ctypes.byref(ring.desc), _ptr(idx),
+                                           int(top_k), _ptr(S), _ptr(z), float(eps), _ptr(out), _ptr(lse), _ptr(ws),
+                                           ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def hf_hybrid_attn_backward(g: Geometry, q, ring: Ring, idx, top_k: int, S, z, out, lse, dout, dq, dk, dv, dS, dz,
+                            bws, eps=1e-6, stream=None) -> None:
+    _check("hf_hybrid_attn_backward",
+           lib().hf_hybrid_attn_backward(ctypes.byref(g.dims()), _ptr(q), ctypes.byref(ring.desc), _ptr(idx),
+                                         int(top_k), _ptr(S), _ptr(z), float(eps), _ptr(out), _ptr(lse), _ptr(dout),
+                                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dS), _ptr(dz), _ptr(bws),
+                                         bws.numel() if bws is not None else 0, _stream(stream)))
+
+
+def hf_linear_absorb_backward(g: Geometry, k_ev, v_ev, n_tok: int, dS, dz, dk, dv, ws, stream=None) -> None:
+    _check("hf_linear_absorb_backward",
+           lib().hf_linear_absorb_backward(ctypes.byref(g.dims()), _ptr(k_ev), _ptr(v_ev), int(n_tok), _ptr(dS),
+                                           _ptr(dz), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() if ws is not None else 0,
+                                           _stream(stream)))

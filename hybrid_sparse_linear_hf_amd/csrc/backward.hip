@@ -1,0 +1,711 @@
+// Backward of the hybrid step output with the block selection held fixed (the selection is
+// piecewise constant in the inputs).  For query t with kept keys u, P_tu = softmax of
+// q_t.k_u / sqrt(D), r_t = phi(q_t)^T S / (phi(q_t).z + eps), out_t = sum_u P_tu v_u + r_t
+// ([HF-de] §2.A, [HF-pt] §2.A.1, 2.A.2 and "Resultado"; [HF-abs]).  Given dO = dL/dout:
+//   sparse part  dP_tu = dO_t.v_u, Delta_t = dO_t.(out_t - r_t), G_tu = P_tu (dP_tu - Delta_t),
+//                dq_t += sum_u G_tu k_u / sqrt(D), dk_u = sum_t G_tu q_t / sqrt(D),
+//                dv_u = sum_t P_tu dO_t;
+//   readout      n_t = S^T phi(q_t), den_t = phi(q_t).z + eps, dn = dO_t / den_t,
+//                dden = -(dO_t.n_t) / den_t^2, dS += phi(q_t) dn^T, dz += phi(q_t) dden,
+//                dq_t += (S dn + z dden) * phi'(q_t);
+//   absorb       (S += phi(K)^T V, z += sum phi(K)):  dV = phi(K) dS, dK = (V dS^T + dz) * phi'(K).
+//
+// gfx950 design (first version, correctness first).  A prep launch copies the window into
+// logical order in bf16 -- K rows, V rows and K^T -- and each query block's Q^T and dO^T,
+// so that every matrix-core operand is one contiguous 16-byte run read straight from
+// global memory (L2) into its fragment: no LDS staging in the attention passes.
+//   * readout pass: one workgroup per (plane, split of the queries); the products S^T phi(q)
+//     and S dn on the matrix cores, per-query terms in fp32; dS and dz as split partials
+//     (phi(q) and dn staged transposed in LDS), added in split order by a second launch.
+//   * dq pass: one workgroup per query block, one wave per 32-query tile, walking the kept
+//     key blocks in 32-key subtiles: S^T = K Q^T, dP^T = V dO^T, G^T = P^T (dP^T - Delta)
+//     and dq^T += K^T G^T.
+//   * dk/dv pass: one workgroup per key block, one wave per 32-key tile, walking the query
+//     blocks that kept it (a per-plane transpose of the selection, in ascending order):
+//     S = Q K^T, dP = dO V^T, G = P (dP - Delta), dv^T += dO^T P, dk^T += Q^T G.
+//   Products in bf16 with fp32 accumulation; P and G rounded to bf16 as matrix-core
+//   operands.  Every sum has a fixed order: results are deterministic.
+#include "hf_internal.h"
+
+namespace hf {
+namespace {
+
+constexpr int kQB = 64;   // query-block copies (Q^T, dO^T) are padded to 64 queries
+
+__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
+
+__device__ __forceinline__ u32x4 f32x8_to_bf16(const float *p) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+    return u32x4{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w)};
+}
+
+__device__ __forceinline__ float pair_sum_b(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float phi_prime(float x) {
+    const float e = __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+    return x > 0.f ? 1.f : e;
+}
+
+// ---------------------------------------------------------------- prep
+
+// One workgroup per (plane, 64-key tile of the logical window): K rows, V rows and K^T,
+// rows past the window zeroed.  Keys j0 .. j0 + 63 in aligned groups of 8 stay in one frame
+// (T % 8 == 0).
+template <int D>
+__global__ __launch_bounds__(256) void prep_keys_kernel(hf_bwd_args a) {
+    __shared__ __align__(16) uint16_t tk[64][D + 8];
+    __shared__ __align__(16) uint16_t tv[D][64 + 8];
+    const int tiles = a.NkP / 64;
+    const int bh = blockIdx.x / tiles, j0 = (blockIdx.x % tiles) * 64;
+    auto slot_of = [&](int f) {
+        const int s = a.head + f;
+        return s >= a.W ? s - a.W : s;
+    };
+    for (int e = threadIdx.x; e < 64 * D / 8; e += 256) {
+        const int r = e / (D / 8), c8 = (e % (D / 8)) * 8, j = j0 + r;
+        u32x4 v = {0, 0, 0, 0};
+        if (j < a.Nk) {
+            const int f = j / a.T, t = j - f * a.T;
+            v = *reinterpret_cast<const u32x4 *>(a.ring_k + (((size_t)bh * a.W + slot_of(f)) * a.T + t) * D + c8);
+        }
+        *reinterpret_cast<u32x4 *>(a.kr + ((size_t)bh * a.NkP + j) * D + c8) = v;
+        *reinterpret_cast<u32x4 *>(&tk[r][c8]) = v;
+    }
+    for (int e = threadIdx.x; e < D * 8; e += 256) {
+        const int d = e / 8, k8 = (e % 8) * 8, j = j0 + k8;
+        u32x4 v = {0, 0, 0, 0};
+        if (j < a.Nk) {
+            const int f = j / a.T, t = j - f * a.T;
+            v = *reinterpret_cast<const u32x4 *>(a.ring_vt + (((size_t)bh * a.W + slot_of(f)) * D + d) * a.T + t);
+        }
+        *reinterpret_cast<u32x4 *>(&tv[d][k8]) = v;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < D * 8; e += 256) {
+        const int d = e / 8, k8 = (e % 8) * 8;
+        const u32x4 o = {pack2(tk[k8][d], tk[k8 + 1][d]), pack2(tk[k8 + 2][d], tk[k8 + 3][d]),
+                         pack2(tk[k8 + 4][d], tk[k8 + 5][d]), pack2(tk[k8 + 6][d], tk[k8 + 7][d])};
+        *reinterpret_cast<u32x4 *>(a.kt + ((size_t)bh * D + d) * a.NkP + j0 + k8) = o;
+    }
+    for (int e = threadIdx.x; e < 64 * D / 8; e += 256) {
+        const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
+        const u32x4 o = {pack2(tv[c8][r], tv[c8 + 1][r]), pack2(tv[c8 + 2][r], tv[c8 + 3][r]),
+                         pack2(tv[c8 + 4][r], tv[c8 + 5][r]), pack2(tv[c8 + 6][r], tv[c8 + 7][r])};
+        *reinterpret_cast<u32x4 *>(a.vr + ((size_t)bh * a.NkP + j0 + r) * D + c8) = o;
+    }
+}
+
+// A fp32 [BH][D][D] matrix into bf16 rows and bf16 transposed rows, one workgroup per
+// 32 x 32 tile.
+template <int D>
+__device__ void mat_copies(const float *M, uint16_t *mb, uint16_t *mtb, int tile, float (*t)[33]) {
+    constexpr int nt = D / 32;
+    const int bh = tile / (nt * nt), ti = (tile / nt) % nt, tj = tile % nt;
+    const float *src = M + (size_t)bh * D * D;
+    for (int e = threadIdx.x; e < 32 * 32; e += 256) {
+        const int r = e / 32, c = e % 32;
+        const float v = src[(size_t)(32 * ti + r) * D + 32 * tj + c];
+        t[r][c] = v;
+        mb[(size_t)bh * D * D + (size_t)(32 * ti + r) * D + 32 * tj + c] = (uint16_t)f32_to_bf16_bits(v);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 32 * 32; e += 256) {
+        const int r = e / 32, c = e % 32;   // transposed element (c, r) of the tile
+        mtb[(size_t)bh * D * D + (size_t)(32 * tj + r) * D + 32 * ti + c] = (uint16_t)f32_to_bf16_bits(t[c][r]);
+    }
+}
+
+// One workgroup per (plane, query block): dO rows in bf16, the block's Q^T and dO^T (64
+// columns, zero past the block); extra workgroups copy S into bf16 rows and transposed rows.
+template <int D>
+__global__ __launch_bounds__(256) void prep_queries_kernel(hf_bwd_args a) {
+    __shared__ __align__(16) uint16_t tq[kQB][D + 8];
+    __shared__ __align__(16) uint16_t tg[kQB][D + 8];
+    const int nblk = a.BH * a.nqb;
+    if ((int)blockIdx.x >= nblk) {
+        mat_copies<D>(a.S, a.sb, a.stb, (int)blockIdx.x - nblk, reinterpret_cast<float(*)[33]>(&tq[0][0]));
+        return;
+    }
+    const int bh = blockIdx.x / a.nqb, qb = blockIdx.x % a.nqb;
+    const int q0 = qb * a.bq, nq = min(a.bq, a.Nq - q0);
+    for (int e = threadIdx.x; e < kQB * D / 8; e += 256) {
+        const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
+        u32x4 qv = {0, 0, 0, 0}, gv = {0, 0, 0, 0};
+        if (r < nq) {
+            const size_t row = (size_t)bh * a.Nq + q0 + r;
+            qv = *reinterpret_cast<const u32x4 *>(a.q + row * D + c8);
+            gv = f32x8_to_bf16(a.dout + row * D + c8);
+            *reinterpret_cast<u32x4 *>(a.gr + row * D + c8) = gv;
+        }
+        *reinterpret_cast<u32x4 *>(&tq[r][c8]) = qv;
+        *reinterpret_cast<u32x4 *>(&tg[r][c8]) = gv;
+    }
+    __syncthreads();
+    const size_t blk = ((size_t)bh * a.nqb + qb) * D;
+    for (int e = threadIdx.x; e < D * (kQB / 8); e += 256) {
+        const int d = e / (kQB / 8), q8 = (e % (kQB / 8)) * 8;
+        const u32x4 oq = {pack2(tq[q8][d], tq[q8 + 1][d]), pack2(tq[q8 + 2][d], tq[q8 + 3][d]),
+                          pack2(tq[q8 + 4][d], tq[q8 + 5][d]), pack2(tq[q8 + 6][d], tq[q8 + 7][d])};
+        const u32x4 og = {pack2(tg[q8][d], tg[q8 + 1][d]), pack2(tg[q8 + 2][d], tg[q8 + 3][d]),
+                          pack2(tg[q8 + 4][d], tg[q8 + 5][d]), pack2(tg[q8 + 6][d], tg[q8 + 7][d])};
+        *reinterpret_cast<u32x4 *>(a.qt + (blk + d) * kQB + q8) = oq;
+        *reinterpret_cast<u32x4 *>(a.gt + (blk + d) * kQB + q8) = og;
+    }
+}
+
+// Per plane, the query blocks that kept each key block, ascending: count, offsets, fill.
+// Kept lists are ascending, so membership is a binary search.
+__device__ __forceinline__ bool kept_by(const int32_t *sel, int k, int j) {
+    int lo = 0, hi = k - 1;
+    while (lo <= hi) {
+        const int mid = (lo + hi) >> 1;
+        const int v = sel[mid];
+        if (v == j) return true;
+        if (v < j) lo = mid + 1;
+        else hi = mid - 1;
+    }
+    return false;
+}
+
+__global__ __launch_bounds__(256) void csr_kernel(hf_bwd_args a) {
+    __shared__ int cnt[kMaxKeyBlocks];
+    const int bh = blockIdx.x;
+    const int32_t *sel = a.idx + (size_t)bh * a.nqb * a.top_k;
+    for (int j = threadIdx.x; j < a.nkb; j += 256) {
+        int c = 0;
+        for (int i = 0; i < a.nqb; ++i) c += kept_by(sel + (size_t)i * a.top_k, a.top_k, j);
+        cnt[j] = c;
+    }
+    __syncthreads();
+    int32_t *off = a.qoff + (size_t)bh * (a.nkb + 1);
+    if (threadIdx.x == 0) {
+        int s = 0;
+        for (int j = 0; j < a.nkb; ++j) {
+            off[j] = s;
+            const int c = cnt[j];
+            cnt[j] = s;
+            s += c;
+        }
+        off[a.nkb] = s;
+    }
+    __syncthreads();
+    int32_t *list = a.qlist + (size_t)bh * a.nqb * a.top_k;
+    for (int j = threadIdx.x; j < a.nkb; j += 256) {
+        int o = cnt[j];
+        for (int i = 0; i < a.nqb; ++i)
+            if (kept_by(sel + (size_t)i * a.top_k, a.top_k, j)) list[o++] = i;
+    }
+}
+
+// ---------------------------------------------------------------- readout pass
+
+// One workgroup (two waves) per (plane, split); split s takes 64-query chunks
+// s, s + splits, ...  Each wave owns 32 queries of the chunk.
+template <int D>
+__global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
+    __shared__ __align__(16) uint16_t phT[D][kQB + 8];
+    __shared__ __align__(16) uint16_t dnT[D][kQB + 8];
+    __shared__ float dden_s[kQB];
+    const int bh = blockIdx.x / a.splits, sp = blockIdx.x % a.splits;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
+    const int nchunks = (a.Nq + kQB - 1) / kQB;
+    const float *zp = a.z + (size_t)bh * D;
+    const uint16_t *sbp = a.sb + (size_t)bh * D * D, *stp = a.stb + (size_t)bh * D * D;
+    // partial dS: wave w owns output tiles (a-tile XT w + x, c-tile y), x < XT = D/64,
+    // y < D/32
+    constexpr int NT = D / 32, XT = NT / 2;
+    f32x16 accS[XT][NT];
+#pragma unroll
+    for (int x = 0; x < XT; ++x)
+#pragma unroll
+        for (int y = 0; y < NT; ++y) accS[x][y] = f32x16{};
+    float dz_acc = 0.f;
+    for (int ch = sp; ch < nchunks; ch += a.splits) {
+        const int t = ch * kQB + 32 * w + n;
+        const bool valid = t < a.Nq;
+        const size_t row = (size_t)bh * a.Nq + (valid ? t : 0);
+        // phi(q) in the B layout (features 16 ks + 8 g .. + 8) and the denominator
+        u32x4 pq[D / 16];
+        float den = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const u32x4 qv = *reinterpret_cast<const u32x4 *>(a.q + row * D + 16 * ks + 8 * g);
+            const uint32_t wv[4] = {qv.x, qv.y, qv.z, qv.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float f0 = phi_f32(bf16_lo_to_f32(wv[e])), f1 = phi_f32(bf16_hi_to_f32(wv[e]));
+                den = __builtin_fmaf(f0, zp[16 * ks + 8 * g + 2 * e], den);
+                den = __builtin_fmaf(f1, zp[16 * ks + 8 * g + 2 * e + 1], den);
+                o[e] = pack_bf16x2(f0, f1);
+            }
+            pq[ks] = u32x4{o[0], o[1], o[2], o[3]};
+        }
+        den = pair_sum_b(den) + a.eps;
+        const float inv_den = 1.f / den;
+        // n^T = S^T phi(q): lane holds n[c], c = 32 ft + 16 g + i
+        float gn = 0.f, go = 0.f;
+#pragma unroll
+        for (int ft = 0; ft < NT; ++ft) {
+            f32x16 acc = {};
+            const uint16_t *srow = stp + (size_t)(32 * ft + perm32(n)) * D + 8 * g;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+                acc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(srow + 16 * ks)), as_bf16x8(pq[ks]), acc);
+            const float *gp = a.dout + row * D + 32 * ft + 16 * g;
+            const float *op = a.out + row * D + 32 * ft + 16 * g;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const f32x4 gv = *reinterpret_cast<const f32x4 *>(gp + 4 * v);
+                const f32x4 ov = *reinterpret_cast<const f32x4 *>(op + 4 * v);
+                gn += gv.x * acc[4 * v] + gv.y * acc[4 * v + 1] + gv.z * acc[4 * v + 2] + gv.w * acc[4 * v + 3];
+                go += gv.x * ov.x + gv.y * ov.y + gv.z * ov.z + gv.w * ov.w;
+            }
+        }
+        gn = pair_sum_b(gn);
+        go = pair_sum_b(go);
+        const float dden = -gn * inv_den * inv_den;
+        if (valid && g == 0) a.delta[(size_t)bh * a.NqP + t] = go - gn * inv_den;
+        // dn = dO / den in the B layout
+        u32x4 dnf[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const float *gp = a.dout + row * D + 16 * ks + 8 * g;
+            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gp);
+            const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gp + 4);
+            dnf[ks] = u32x4{pack_bf16x2(g0.x * inv_den, g0.y * inv_den), pack_bf16x2(g0.z * inv_den, g0.w * inv_den),
+                            pack_bf16x2(g1.x * inv_den, g1.y * inv_den), pack_bf16x2(g1.z * inv_den, g1.w * inv_den)};
+        }
+        // dphi^T = S dn^T + z dden; dq = dphi * phi'(q) (the first write of dq)
+#pragma unroll
+        for (int ft = 0; ft < NT; ++ft) {
+            f32x16 acc = {};
+            const uint16_t *srow = sbp + (size_t)(32 * ft + perm32(n)) * D + 8 * g;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+                acc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(srow + 16 * ks)), as_bf16x8(dnf[ks]), acc);
+            if (valid) {
+                const int a0 = 32 * ft + 16 * g;
+                const u32x4 q0 = *reinterpret_cast<const u32x4 *>(a.q + row * D + a0);
+                const u32x4 q1 = *reinterpret_cast<const u32x4 *>(a.q + row * D + a0 + 8);
+                const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+                float *dqp = a.dq + row * D + a0;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float r[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 4 * v + e;
+                        const float qx = (i & 1) ? bf16_hi_to_f32(qw[i >> 1]) : bf16_lo_to_f32(qw[i >> 1]);
+                        r[e] = (acc[i] + zp[a0 + i] * dden) * phi_prime(qx);
+                    }
+                    *reinterpret_cast<f32x4 *>(dqp + 4 * v) = f32x4{r[0], r[1], r[2], r[3]};
+                }
+            }
+        }
+        // stage phi(q) and dn transposed (zero for rows past the queries) for the partials
+        const int col = 32 * w + n;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const uint32_t pw[4] = {pq[ks].x, pq[ks].y, pq[ks].z, pq[ks].w};
+            const uint32_t dw[4] = {dnf[ks].x, dnf[ks].y, dnf[ks].z, dnf[ks].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int f = 16 * ks + 8 * g + e;
+                phT[f][col] = valid ? (uint16_t)((e & 1) ? (pw[e >> 1] >> 16) : (pw[e >> 1] & 0xFFFF)) : 0;
+                dnT[f][col] = valid ? (uint16_t)((e & 1) ? (dw[e >> 1] >> 16) : (dw[e >> 1] & 0xFFFF)) : 0;
+            }
+        }
+        if (g == 0) dden_s[col] = valid ? dden : 0.f;
+        __syncthreads();
+        // dS partial += phi^T dn over the chunk's 64 queries (4 contraction steps of 16)
+#pragma unroll
+        for (int x = 0; x < XT; ++x) {
+            const int ar = 32 * (XT * w + x) + n;
+#pragma unroll
+            for (int kq = 0; kq < kQB / 16; ++kq) {
+                const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(&phT[ar][16 * kq + 8 * g]));
+#pragma unroll
+                for (int y = 0; y < NT; ++y) {
+                    const bf16x8 bv = as_bf16x8(*reinterpret_cast<const u32x4 *>(&dnT[32 * y + n][16 * kq + 8 * g]));
+                    accS[x][y] = mfma32(av, bv, accS[x][y]);
+                }
+            }
+        }
+        if (threadIdx.x < D) {
+            float s = 0.f;
+            for (int q = 0; q < kQB; ++q) {
+                const uint16_t pb = phT[threadIdx.x][q];
+                s = __builtin_fmaf(__uint_as_float((uint32_t)pb << 16), dden_s[q], s);
+            }
+            dz_acc += s;
+        }
+        __syncthreads();
+    }
+    // partials: tile (x, y) element i of lane l is (a, c) = (32(XT w+x) + 8(i/4) + 4g + i%4, 32y + n)
+    float *dsp = a.dsp + ((size_t)bh * a.splits + sp) * D * D;
+#pragma unroll
+    for (int x = 0; x < XT; ++x)
+#pragma unroll
+        for (int y = 0; y < NT; ++y)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int ar = 32 * (XT * w + x) + 8 * (i / 4) + 4 * g + (i % 4);
+                dsp[(size_t)ar * D + 32 * y + n] = accS[x][y][i];
+            }
+    if (threadIdx.x < D) a.dzp[((size_t)bh * a.splits + sp) * D + threadIdx.x] = dz_acc;
+}
+
+// dS, dz = sum of the split partials in split order (one workgroup per plane and 32x32
+// tile; the first tile of a plane also adds dz).
+template <int D>
+__global__ __launch_bounds__(256) void reduce_readout_kernel(hf_bwd_args a) {
+    constexpr int nt = D / 32;
+    const int bh = blockIdx.x / (nt * nt), tile = blockIdx.x % (nt * nt);
+    const int r0 = 32 * (tile / nt), c0 = 32 * (tile % nt);
+    for (int e = threadIdx.x; e < 32 * 32; e += 256) {
+        const int r = r0 + e / 32, c = c0 + e % 32;
+        float s = 0.f;
+        for (int p = 0; p < a.splits; ++p) s += a.dsp[((size_t)bh * a.splits + p) * D * D + (size_t)r * D + c];
+        a.dS[(size_t)bh * D * D + (size_t)r * D + c] = s;
+    }
+    if (tile == 0 && threadIdx.x < D) {
+        float s = 0.f;
+        for (int p = 0; p < a.splits; ++p) s += a.dzp[((size_t)bh * a.splits + p) * D + threadIdx.x];
+        a.dz[(size_t)bh * D + threadIdx.x] = s;
+    }
+}
+
+// ---------------------------------------------------------------- dq pass
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void dq_kernel(hf_bwd_args a, float c_log2, float inv_sqrt_d, int lsh) {
+    const int bh = blockIdx.x / a.nqb, qb = blockIdx.x % a.nqb;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
+    const int q0 = qb * a.bq, qend = min(q0 + a.bq, a.Nq);
+    const int t = q0 + 32 * w + n;
+    const bool valid = t < qend;
+    const size_t row = (size_t)bh * a.Nq + (valid ? t : q0);
+    u32x4 qf[D / 16], gf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        qf[ks] = *reinterpret_cast<const u32x4 *>(a.q + row * D + 16 * ks + 8 * g);
+        gf[ks] = *reinterpret_cast<const u32x4 *>(a.gr + row * D + 16 * ks + 8 * g);
+    }
+    const float L = a.lse[row], Dl = a.delta[(size_t)bh * a.NqP + (valid ? t : q0)];
+    const uint16_t *krp = a.kr + (size_t)bh * a.NkP * D, *vrp = a.vr + (size_t)bh * a.NkP * D;
+    const uint16_t *ktp = a.kt + (size_t)bh * D * a.NkP;
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int ft = 0; ft < D / 32; ++ft) acc[ft] = f32x16{};
+    const int32_t *sel = a.idx + ((size_t)bh * a.nqb + qb) * a.top_k;
+    const int nsub = 1 << lsh;
+    for (int r = 0; r < a.top_k; ++r) {
+        const int b = min(max(sel[r], 0), a.nkb - 1);
+        const int bend = min(b * a.bk + a.bk, a.Nk);
+        for (int su = 0; su < nsub; ++su) {
+            const int k0 = b * a.bk + 32 * su;
+            const int nv = min(32, bend - k0);
+            if (nv <= 0) break;
+            f32x16 s = {}, dp = {};
+            const uint16_t *kp = krp + (size_t)(k0 + perm32(n)) * D + 8 * g;
+            const uint16_t *vp = vrp + (size_t)(k0 + perm32(n)) * D + 8 * g;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 16 * ks)), as_bf16x8(qf[ks]), s);
+                dp = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(vp + 16 * ks)), as_bf16x8(gf[ks]), dp);
+            }
+            // lane holds keys 16 g + i of the subtile for query n
+            float gt[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p = (16 * g + i < nv) ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c_log2, -L)) : 0.f;
+                gt[i] = p * (dp[i] - Dl);
+            }
+            u32x4 gfr[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                gfr[ks] = u32x4{pack_bf16x2(gt[8 * ks], gt[8 * ks + 1]), pack_bf16x2(gt[8 * ks + 2], gt[8 * ks + 3]),
+                                pack_bf16x2(gt[8 * ks + 4], gt[8 * ks + 5]), pack_bf16x2(gt[8 * ks + 6], gt[8 * ks + 7])};
+#pragma unroll
+            for (int ft = 0; ft < D / 32; ++ft) {
+                const uint16_t *tp = ktp + (size_t)(32 * ft + perm32(n)) * a.NkP + k0 + 16 * g;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    acc[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(tp + 8 * ks)), as_bf16x8(gfr[ks]), acc[ft]);
+            }
+        }
+    }
+    if (valid) {
+        float *dqp = a.dq + row * D + 16 * g;
+#pragma unroll
+        for (int ft = 0; ft < D / 32; ++ft)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                f32x4 *p4 = reinterpret_cast<f32x4 *>(dqp + 32 * ft + 4 * v);
+                const f32x4 o = *p4;
+                *p4 = f32x4{o.x + acc[ft][4 * v] * inv_sqrt_d, o.y + acc[ft][4 * v + 1] * inv_sqrt_d,
+                            o.z + acc[ft][4 * v + 2] * inv_sqrt_d, o.w + acc[ft][4 * v + 3] * inv_sqrt_d};
+            }
+    }
+}
+
+// ---------------------------------------------------------------- dk / dv pass
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void dkdv_kernel(hf_bwd_args a, float c_log2, float inv_sqrt_d) {
+    const int bh = blockIdx.x / a.nkb, j = blockIdx.x % a.nkb;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
+    const int kj0 = j * a.bk + 32 * w;
+    const int nvk = min(32, min(j * a.bk + a.bk, a.Nk) - kj0);   // keys of this wave (<= 0: none)
+    const int key = kj0 + n;                                     // < NkP whenever nvk > 0
+    const bool kvalid = n < nvk;
+    f32x16 accV[D / 32], accK[D / 32];
+#pragma unroll
+    for (int ft = 0; ft < D / 32; ++ft) accV[ft] = accK[ft] = f32x16{};
+    if (nvk > 0) {
+        u32x4 kf[D / 16], vf[D / 16];
+        const size_t krow = ((size_t)bh * a.NkP + key) * D + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            kf[ks] = *reinterpret_cast<const u32x4 *>(a.kr + krow + 16 * ks);
+            vf[ks] = *reinterpret_cast<const u32x4 *>(a.vr + krow + 16 * ks);
+        }
+        const int32_t *off = a.qoff + (size_t)bh * (a.nkb + 1);
+        const int32_t *list = a.qlist + (size_t)bh * a.nqb * a.top_k;
+        const int p0 = off[j], p1 = off[j + 1];
+        for (int p = p0; p < p1; ++p) {
+            const int i = list[p];
+            const int q0 = i * a.bq, nqv = min(a.bq, a.Nq - q0);
+            const size_t blk = ((size_t)bh * a.nqb + i) * D;
+            for (int qt = 0; 32 * qt < nqv; ++qt) {
+                // S and dP for queries q0 + 32 qt + (rows in perm32 order), this wave's keys
+                const int qr = 32 * qt + perm32(n);
+                const size_t qrow = (size_t)bh * a.Nq + q0 + min(qr, nqv - 1);
+                f32x16 s = {}, dp = {};
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(a.q + qrow * D + 16 * ks + 8 * g)), as_bf16x8(kf[ks]), s);
+                    dp = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(a.gr + qrow * D + 16 * ks + 8 * g)), as_bf16x8(vf[ks]), dp);
+                }
+                // lane (key n) holds queries 32 qt + 16 g + i
+                const int qb0 = 32 * qt + 16 * g;
+                float pv[16], gv[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int qq = qb0 + i;
+                    const bool ok = kvalid && qq < nqv;
+                    const size_t qi = (size_t)q0 + min(qq, nqv - 1);
+                    const float L = a.lse[(size_t)bh * a.Nq + qi];
+                    const float Dl = a.delta[(size_t)bh * a.NqP + qi];
+                    const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c_log2, -L)) : 0.f;
+                    pv[i] = pr;
+                    gv[i] = pr * (dp[i] - Dl);
+                }
+                u32x4 pf[2], gfr[2];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    pf[ks] = u32x4{pack_bf16x2(pv[8 * ks], pv[8 * ks + 1]), pack_bf16x2(pv[8 * ks + 2], pv[8 * ks + 3]),
+                                   pack_bf16x2(pv[8 * ks + 4], pv[8 * ks + 5]), pack_bf16x2(pv[8 * ks + 6], pv[8 * ks + 7])};
+                    gfr[ks] = u32x4{pack_bf16x2(gv[8 * ks], gv[8 * ks + 1]), pack_bf16x2(gv[8 * ks + 2], gv[8 * ks + 3]),
+                                    pack_bf16x2(gv[8 * ks + 4], gv[8 * ks + 5]), pack_bf16x2(gv[8 * ks + 6], gv[8 * ks + 7])};
+                }
+                // dv^T += dO^T P, dk^T += Q^T G (rows d in perm32 order, queries 16 g + 8 ks ..)
+#pragma unroll
+                for (int ft = 0; ft < D / 32; ++ft) {
+                    const size_t trow = (blk + 32 * ft + perm32(n)) * kQB + 32 * qt + 16 * g;
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        accV[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(a.gt + trow + 8 * ks)), as_bf16x8(pf[ks]), accV[ft]);
+                        accK[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(a.qt + trow + 8 * ks)), as_bf16x8(gfr[ks]), accK[ft]);
+                    }
+                }
+            }
+        }
+    }
+    if (kvalid) {
+        // lane (key n) holds features 32 ft + 16 g + i
+        float *dvp = a.dv + ((size_t)bh * a.Nk + key) * D + 16 * g;
+        float *dkp = a.dk + ((size_t)bh * a.Nk + key) * D + 16 * g;
+#pragma unroll
+        for (int ft = 0; ft < D / 32; ++ft)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                *reinterpret_cast<f32x4 *>(dvp + 32 * ft + 4 * v) =
+                    f32x4{accV[ft][4 * v], accV[ft][4 * v + 1], accV[ft][4 * v + 2], accV[ft][4 * v + 3]};
+                *reinterpret_cast<f32x4 *>(dkp + 32 * ft + 4 * v) =
+                    f32x4{accK[ft][4 * v] * inv_sqrt_d, accK[ft][4 * v + 1] * inv_sqrt_d,
+                          accK[ft][4 * v + 2] * inv_sqrt_d, accK[ft][4 * v + 3] * inv_sqrt_d};
+            }
+    }
+}
+
+// ---------------------------------------------------------------- absorb backward
+
+template <int D>
+__global__ __launch_bounds__(256) void absorb_bwd_prep_kernel(hf_absorb_bwd_args a) {
+    __shared__ float t[32][33];
+    mat_copies<D>(a.dS, a.sb, a.stb, blockIdx.x, t);
+}
+
+// One wave per (plane, 32 tokens): dv^T = dS^T phi(K)^T and dphi^T = dS V^T on the matrix
+// cores (rows in perm32 order, so each lane holds 16 consecutive features of its token).
+template <int D>
+__global__ __launch_bounds__(64) void absorb_bwd_kernel(hf_absorb_bwd_args a) {
+    const int64_t tiles = (a.n_tok + 31) / 32;
+    const int bh = (int)(blockIdx.x / tiles);
+    const int64_t u0 = (blockIdx.x % tiles) * 32;
+    const int lane = threadIdx.x, n = lane & 31, g = lane >> 5;
+    const int64_t u = u0 + n;
+    const bool valid = u < a.n_tok;
+    const size_t row = ((size_t)bh * a.n_tok + (valid ? u : u0)) * D;
+    u32x4 phf[D / 16], vf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const u32x4 kv = *reinterpret_cast<const u32x4 *>(a.k + row + 16 * ks + 8 * g);
+        const uint32_t wv[4] = {kv.x, kv.y, kv.z, kv.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(phi_f32(bf16_lo_to_f32(wv[e])), phi_f32(bf16_hi_to_f32(wv[e])));
+        phf[ks] = u32x4{o[0], o[1], o[2], o[3]};
+        vf[ks] = *reinterpret_cast<const u32x4 *>(a.v + row + 16 * ks + 8 * g);
+    }
+    const uint16_t *sbp = a.sb + (size_t)bh * D * D, *stp = a.stb + (size_t)bh * D * D;
+    const float *dzp = a.dz + (size_t)bh * D;
+#pragma unroll
+    for (int ft = 0; ft < D / 32; ++ft) {
+        f32x16 dvt = {}, dpt = {};
+        const uint16_t *r1 = stp + (size_t)(32 * ft + perm32(n)) * D + 8 * g;
+        const uint16_t *r2 = sbp + (size_t)(32 * ft + perm32(n)) * D + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            dvt = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(r1 + 16 * ks)), as_bf16x8(phf[ks]), dvt);
+            dpt = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(r2 + 16 * ks)), as_bf16x8(vf[ks]), dpt);
+        }
+        if (valid) {
+            const int a0 = 32 * ft + 16 * g;
+            const u32x4 k0 = *reinterpret_cast<const u32x4 *>(a.k + row + a0);
+            const u32x4 k1 = *reinterpret_cast<const u32x4 *>(a.k + row + a0 + 8);
+            const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float r[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * v + e;
+                    const float kx = (i & 1) ? bf16_hi_to_f32(kw[i >> 1]) : bf16_lo_to_f32(kw[i >> 1]);
+                    r[e] = (dpt[i] + dzp[a0 + i]) * phi_prime(kx);
+                }
+                *reinterpret_cast<f32x4 *>(a.dk + row + a0 + 4 * v) = f32x4{r[0], r[1], r[2], r[3]};
+                *reinterpret_cast<f32x4 *>(a.dv + row + a0 + 4 * v) = f32x4{dvt[4 * v], dvt[4 * v + 1], dvt[4 * v + 2], dvt[4 * v + 3]};
+            }
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_attn_backward(const hf_bwd_args &a, hipStream_t s) {
+    const int nt = D / 32;
+    const float c_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    const float inv_sqrt_d = (float)(1.0 / sqrt((double)D));
+    const int lsh = a.bk >= 128 ? 2 : (a.bk >= 64 ? 1 : 0);
+    hipLaunchKernelGGL(prep_keys_kernel<D>, dim3((unsigned)(a.BH * (a.NkP / 64))), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(prep_queries_kernel<D>, dim3((unsigned)(a.BH * a.nqb + a.BH * nt * nt)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(csr_kernel, dim3((unsigned)a.BH), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(readout_bwd_kernel<D>, dim3((unsigned)(a.BH * a.splits)), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(reduce_readout_kernel<D>, dim3((unsigned)(a.BH * nt * nt)), dim3(256), 0, s, a);
+    if (a.bq > 32)
+        hipLaunchKernelGGL((dq_kernel<D, 2>), dim3((unsigned)(a.BH * a.nqb)), dim3(128), 0, s, a, c_log2, inv_sqrt_d, lsh);
+    else
+        hipLaunchKernelGGL((dq_kernel<D, 1>), dim3((unsigned)(a.BH * a.nqb)), dim3(64), 0, s, a, c_log2, inv_sqrt_d, lsh);
+    if (a.bk > 64)
+        hipLaunchKernelGGL((dkdv_kernel<D, 4>), dim3((unsigned)(a.BH * a.nkb)), dim3(256), 0, s, a, c_log2, inv_sqrt_d);
+    else if (a.bk > 32)
+        hipLaunchKernelGGL((dkdv_kernel<D, 2>), dim3((unsigned)(a.BH * a.nkb)), dim3(128), 0, s, a, c_log2, inv_sqrt_d);
+    else
+        hipLaunchKernelGGL((dkdv_kernel<D, 1>), dim3((unsigned)(a.BH * a.nkb)), dim3(64), 0, s, a, c_log2, inv_sqrt_d);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_absorb_backward(const hf_absorb_bwd_args &a, hipStream_t s) {
+    const int nt = D / 32;
+    hipLaunchKernelGGL(absorb_bwd_prep_kernel<D>, dim3((unsigned)(a.BH * nt * nt)), dim3(256), 0, s, a);
+    const int64_t tiles = (a.n_tok + 31) / 32;
+    hipLaunchKernelGGL(absorb_bwd_kernel<D>, dim3((unsigned)(a.BH * tiles)), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace hf
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int bwd_splits(int BH, int Nq) {
+    const int chunks = (Nq + hf::kQB - 1) / hf::kQB;
+    int s = 256 / BH;
+    s = s < 1 ? 1 : s;
+    return s < chunks ? s : chunks;
+}
+
+// Workspace: K rows, V rows, K^T, Q^T blocks, dO^T blocks, dO rows, S / S^T bf16, Delta,
+// the selection transpose, readout partials (each region 256-byte aligned).
+static size_t bwd_layout(hf_bwd_args *a, int BH, int D, int Nq, int Nk, int bq, int bk, int top_k, char *base) {
+    const int nqb = (Nq + bq - 1) / bq, nkb = (Nk + bk - 1) / bk;
+    const int NkP = (Nk + 63) / 64 * 64, NqP = nqb * bq;
+    const int splits = bwd_splits(BH, Nq);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += align256(bytes);
+        return base ? base + at : nullptr;
+    };
+    char *kr = take((size_t)BH * NkP * D * 2), *vr = take((size_t)BH * NkP * D * 2), *kt = take((size_t)BH * D * NkP * 2);
+    char *qt = take((size_t)BH * nqb * D * hf::kQB * 2), *gt = take((size_t)BH * nqb * D * hf::kQB * 2);
+    char *gr = take((size_t)BH * Nq * D * 2);
+    char *sb = take((size_t)BH * D * D * 2), *stb = take((size_t)BH * D * D * 2);
+    char *delta = take((size_t)BH * NqP * 4);
+    char *qoff = take((size_t)BH * (nkb + 1) * 4), *qlist = take((size_t)BH * nqb * top_k * 4);
+    char *dsp = take((size_t)BH * splits * D * D * 4), *dzp = take((size_t)BH * splits * D * 4);
+    if (a) {
+        a->NkP = NkP;
+        a->NqP = NqP;
+        a->splits = splits;
+        a->kr = reinterpret_cast<uint16_t *>(kr);
+        a->vr = reinterpret_cast<uint16_t *>(vr);
+        a->kt = reinterpret_cast<uint16_t *>(kt);
+        a->qt = reinterpret_cast<uint16_t *>(qt);
+        a->gt = reinterpret_cast<uint16_t *>(gt);
+        a->gr = reinterpret_cast<uint16_t *>(gr);
+        a->sb = reinterpret_cast<uint16_t *>(sb);
+        a->stb = reinterpret_cast<uint16_t *>(stb);
+        a->delta = reinterpret_cast<float *>(delta);
+        a->qoff = reinterpret_cast<int32_t *>(qoff);
+        a->qlist = reinterpret_cast<int32_t *>(qlist);
+        a->dsp = reinterpret_cast<float *>(dsp);
+        a->dzp = reinterpret_cast<float *>(dzp);
+    }
+    return o;
+}
+
+size_t hf_bwd_workspace_bytes(int BH, int D, int Nq, int Nk, int bq, int bk, int top_k) {
+    return bwd_layout(nullptr, BH, D, Nq, Nk, bq, bk, top_k, nullptr);
+}
+
+void hf_bwd_layout(hf_bwd_args &a, void *ws) {
+    bwd_layout(&a, a.BH, a.D, a.Nq, a.Nk, a.bq, a.bk, a.top_k, static_cast<char *>(ws));
+}
+
+hipError_t hf_launch_attn_backward(const hf_bwd_args &a, hipStream_t s) {
+    if (a.nkb > kMaxKeyBlocks) return hipErrorInvalidValue;
+    return a.D == 64 ? hf::launch_attn_backward<64>(a, s) : hf::launch_attn_backward<128>(a, s);
+}
+
+hipError_t hf_launch_absorb_backward(const hf_absorb_bwd_args &a, hipStream_t s) {
+    if (a.n_tok <= 0) return hipSuccess;
+    return a.D == 64 ? hf::launch_absorb_backward<64>(a, s) : hf::launch_absorb_backward<128>(a, s);
+}

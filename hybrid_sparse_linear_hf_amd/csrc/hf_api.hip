@@ -195,7 +195,7 @@ hipError_t enqueue_state(const hf_dims *d, float *S, float *z, bool readout, int
 
 // Attention (+ readout from the prepared S^T / z copy when `readout`).
 hipError_t enqueue_attn(const hf_dims *d, const void *q, const hf_kv_ring *r, const int32_t *idx, int top_k,
-                        bool readout, float eps, float *out, void *ws, hipStream_t s) {
+                        bool readout, float eps, float *out, void *ws, hipStream_t s, float *lse = nullptr) {
     const Geometry g = geometry(d, r);
     const WsLayout L = ws_layout(d);
     hf_attn_args a{};
@@ -219,6 +219,7 @@ hipError_t enqueue_attn(const hf_dims *d, const void *q, const hf_kv_ring *r, co
     a.zc = readout ? reinterpret_cast<const float *>(wsp(ws, L.zc)) : nullptr;
     a.eps = eps;
     a.out = out;
+    a.lse = lse;
     return hf_launch_sparse_attn(a, s);
 }
 
@@ -348,9 +349,9 @@ hf_status hf_block_select_hier(const hf_dims *d, const void *q, const hf_kv_ring
     return st == HF_OK ? ok() : st;
 }
 
-hf_status hf_sparse_window_attn(const hf_dims *d, const void *q, const hf_kv_ring *ring, const int32_t *idx,
-                                int32_t top_k, const float *S, const float *z, float eps, float *out, void *ws,
-                                size_t ws_bytes, hipStream_t stream) {
+static hf_status sparse_window_attn(const hf_dims *d, const void *q, const hf_kv_ring *ring, const int32_t *idx,
+                                    int32_t top_k, const float *S, const float *z, float eps, float *out, float *lse,
+                                    void *ws, size_t ws_bytes, hipStream_t stream) {
     hf_status st = check_dims(d);
     if (st == HF_OK) st = check_ring(d, ring);
     if (st != HF_OK) return st;
@@ -362,8 +363,110 @@ hf_status hf_sparse_window_attn(const hf_dims *d, const void *q, const hf_kv_rin
     st = check_ws(d, ws, ws_bytes);
     if (st != HF_OK) return st;
     hipError_t e = S ? enqueue_state(d, const_cast<float *>(S), const_cast<float *>(z), true, 0, ws, stream) : hipSuccess;
-    if (e == hipSuccess) e = enqueue_attn(d, q, ring, idx, top_k, S != nullptr, eps, out, ws, stream);
+    if (e == hipSuccess) e = enqueue_attn(d, q, ring, idx, top_k, S != nullptr, eps, out, ws, stream, lse);
     st = hip_status(e, "sparse attention launch");
+    return st == HF_OK ? ok() : st;
+}
+
+hf_status hf_sparse_window_attn(const hf_dims *d, const void *q, const hf_kv_ring *ring, const int32_t *idx,
+                                int32_t top_k, const float *S, const float *z, float eps, float *out, void *ws,
+                                size_t ws_bytes, hipStream_t stream) {
+    return sparse_window_attn(d, q, ring, idx, top_k, S, z, eps, out, nullptr, ws, ws_bytes, stream);
+}
+
+hf_status hf_sparse_window_attn_lse(const hf_dims *d, const void *q, const hf_kv_ring *ring, const int32_t *idx,
+                                    int32_t top_k, const float *S, const float *z, float eps, float *out, float *lse,
+                                    void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!lse) return fail(HF_ERR_NULL, "lse is NULL");
+    return sparse_window_attn(d, q, ring, idx, top_k, S, z, eps, out, lse, ws, ws_bytes, stream);
+}
+
+hf_status hf_backward_workspace_size(const hf_dims *d, int32_t top_k, size_t *bytes) {
+    hf_status st = check_dims(d);
+    if (st != HF_OK) return st;
+    if (!bytes) return fail(HF_ERR_NULL, "bytes is NULL");
+    const int64_t nkb = cdiv((int64_t)d->W * d->T, d->bk);
+    if (top_k < 1 || top_k > nkb) return fail(HF_ERR_SHAPE, "top_k=%d outside [1, %lld]", top_k, (long long)nkb);
+    *bytes = hf_bwd_workspace_bytes(d->B * d->H, d->D, d->C * d->T, d->W * d->T, d->bq, d->bk, top_k);
+    return ok();
+}
+
+hf_status hf_hybrid_attn_backward(const hf_dims *d, const void *q, const hf_kv_ring *ring, const int32_t *idx,
+                                  int32_t top_k, const float *S, const float *z, float eps, const float *out,
+                                  const float *lse, const float *dout, float *dq, float *dk, float *dv, float *dS,
+                                  float *dz, void *ws, size_t ws_bytes, hipStream_t stream) {
+    hf_status st = check_dims(d);
+    if (st == HF_OK) st = check_ring(d, ring);
+    if (st != HF_OK) return st;
+    if (!q || !idx || !S || !z || !out || !lse || !dout) return fail(HF_ERR_NULL, "an input pointer is NULL");
+    if (!dq || !dk || !dv || !dS || !dz) return fail(HF_ERR_NULL, "an output pointer is NULL");
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(HF_ERR_SHAPE, "eps must be finite and >= 0");
+    const Geometry g = geometry(d, ring);
+    if (top_k < 1 || top_k > g.nkb) return fail(HF_ERR_SHAPE, "top_k=%d outside [1, n_kb=%d]", top_k, g.nkb);
+    const size_t need = hf_bwd_workspace_bytes(g.BH, d->D, g.Nq, g.Nk, d->bq, d->bk, top_k);
+    if (!ws) return fail(HF_ERR_WORKSPACE, "backward workspace is NULL (need %zu bytes)", need);
+    if (ws_bytes < need) return fail(HF_ERR_WORKSPACE, "backward workspace of %zu bytes, need %zu", ws_bytes, need);
+    hf_bwd_args a{};
+    a.BH = g.BH;
+    a.D = d->D;
+    a.T = d->T;
+    a.W = d->W;
+    a.head = ring->head;
+    a.Nq = g.Nq;
+    a.Nk = g.Nk;
+    a.bq = d->bq;
+    a.bk = d->bk;
+    a.nqb = g.nqb;
+    a.nkb = g.nkb;
+    a.top_k = top_k;
+    a.q = static_cast<const uint16_t *>(q);
+    a.ring_k = static_cast<const uint16_t *>(ring->k_dev);
+    a.ring_vt = static_cast<const uint16_t *>(ring->vt_dev);
+    a.idx = idx;
+    a.S = S;
+    a.z = z;
+    a.out = out;
+    a.lse = lse;
+    a.dout = dout;
+    a.eps = eps;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dS = dS;
+    a.dz = dz;
+    hf_bwd_layout(a, ws);
+    st = hip_status(hf_launch_attn_backward(a, stream), "backward launch");
+    return st == HF_OK ? ok() : st;
+}
+
+hf_status hf_linear_absorb_backward(const hf_dims *d, const void *k_ev, const void *v_ev, int64_t n_tok,
+                                    const float *dS, const float *dz, float *dk, float *dv, void *ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+    hf_status st = check_dims(d);
+    if (st != HF_OK) return st;
+    if (n_tok < 0) return fail(HF_ERR_SHAPE, "n_tok=%lld < 0", (long long)n_tok);
+    if (!dS || !dz) return fail(HF_ERR_NULL, "dS/dz is NULL");
+    if (n_tok > 0 && (!k_ev || !v_ev || !dk || !dv)) return fail(HF_ERR_NULL, "k_ev/v_ev/dk/dv is NULL");
+    if ((int64_t)d->B * d->H * n_tok * d->D >= kMaxElems)
+        return fail(HF_ERR_UNSUPPORTED, "evicted tensors exceed 2^31 elements");
+    st = check_ws(d, ws, ws_bytes);
+    if (st != HF_OK) return st;
+    if (ws_bytes < (size_t)4 * d->B * d->H * d->D * d->D)
+        return fail(HF_ERR_WORKSPACE, "workspace of %zu bytes is below 4 B H D^2", ws_bytes);
+    if (n_tok == 0) return ok();
+    hf_absorb_bwd_args a{};
+    a.BH = d->B * d->H;
+    a.D = d->D;
+    a.n_tok = n_tok;
+    a.k = static_cast<const uint16_t *>(k_ev);
+    a.v = static_cast<const uint16_t *>(v_ev);
+    a.dS = dS;
+    a.dz = dz;
+    a.sb = static_cast<uint16_t *>(ws);
+    a.stb = a.sb + (size_t)a.BH * d->D * d->D;
+    a.dk = dk;
+    a.dv = dv;
+    st = hip_status(hf_launch_absorb_backward(a, stream), "absorb backward launch");
     return st == HF_OK ? ok() : st;
 }
 

@@ -143,8 +143,40 @@ struct hf_attn_args {
     const float *zc;           // z [BH][D] as read by this step
     float eps;
     float *out;
+    float *lse;                // null, or [BH][Nq]: log2 of each query's softmax sum (base-2 logits)
 };
 hipError_t hf_launch_sparse_attn(const hf_attn_args &a, hipStream_t s);
+
+// Backward of the step output (backward.hip); arguments validated by the caller.
+struct hf_bwd_args {
+    int BH, D, T, W, head, Nq, Nk, bq, bk, nqb, nkb, top_k, NkP, NqP, splits;
+    const uint16_t *q, *ring_k, *ring_vt;
+    const int32_t *idx;
+    const float *S, *z, *out, *lse, *dout;
+    float eps;
+    float *dq, *dk, *dv, *dS, *dz;
+    // workspace
+    uint16_t *kr, *vr, *kt;    // window K rows, V rows [BH][NkP][D], K^T [BH][D][NkP] (logical order, zero pad)
+    uint16_t *qt, *gt;         // per query block Q^T and dO^T [BH][nqb][D][64] (zero pad)
+    uint16_t *gr;              // dO rows in bf16 [BH][NqP][D]
+    uint16_t *sb, *stb;        // S and S^T in bf16 [BH][D][D]
+    float *delta;              // [BH][NqP]: dO . (sparse part of out)
+    int32_t *qoff, *qlist;     // per key block, the query blocks that kept it: [BH][nkb+1], [BH][nqb*top_k]
+    float *dsp, *dzp;          // readout partials [BH][splits][D][D], [BH][splits][D]
+};
+size_t hf_bwd_workspace_bytes(int BH, int D, int Nq, int Nk, int bq, int bk, int top_k);
+void hf_bwd_layout(hf_bwd_args &a, void *ws);
+hipError_t hf_launch_attn_backward(const hf_bwd_args &a, hipStream_t s);
+
+struct hf_absorb_bwd_args {
+    int BH, D;
+    int64_t n_tok;
+    const uint16_t *k, *v;     // evicted tokens [BH][n_tok][D]
+    const float *dS, *dz;
+    uint16_t *sb, *stb;        // workspace: dS and dS^T in bf16 [BH][D][D]
+    float *dk, *dv;            // [BH][n_tok][D]
+};
+hipError_t hf_launch_absorb_backward(const hf_absorb_bwd_args &a, hipStream_t s);
 
 struct hf_absorb_args {
     int BH, D;

@@ -403,7 +403,8 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
     }
 
     // ---- epilogue: normalise, add the linear readout, store fp32
-    const float inv_l = 1.f / pair_sum(sm.l);
+    const float lsum = pair_sum(sm.l);
+    const float inv_l = 1.f / lsum;
 #pragma unroll
     for (int ft = 0; ft < D / 32; ++ft)
 #pragma unroll
@@ -446,6 +447,7 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
         }
     }
     const int row = q0 + 32 * w + n;
+    if (a.lse && g == 0 && row < qend) a.lse[(size_t)bh * a.Nq + row] = sm.m + __log2f(lsum);
     if (row < qend) {
         float *op = a.out + ((size_t)bh * a.Nq + row) * D + 16 * g;
 #pragma unroll

@@ -241,6 +241,60 @@ hf_status hf_hybrid_step(const hf_dims *d, const void *q_dev, const void *k_cur_
                          float eps, int32_t *idx_dev, float *out_dev, void *workspace_dev,
                          size_t workspace_bytes, const hf_step_events *events, hipStream_t stream);
 
+/* ---- Backward of the step (training).  The block selection is held fixed: it is
+ * piecewise constant in the inputs, so no gradient flows through it.  Gradients of a loss
+ * L given dL/dout; for query t with kept keys u and softmax weights P_tu ([HF-de] §2.A,
+ * [HF-pt] §2.A.1, 2.A.2, "Resultado"; [HF-abs]):
+ *   dq_t = sum_u G_tu k_u / sqrt(D) + (S dn_t + z dden_t) * phi'(q_t),
+ *   dk_u = sum_t G_tu q_t / sqrt(D),  dv_u = sum_t P_tu dout_t,
+ *   dS = sum_t phi(q_t) dn_t^T,  dz = sum_t phi(q_t) dden_t,
+ * with G_tu = P_tu (dout_t . v_u - dout_t . (out_t - r_t)), r_t the readout,
+ * dn_t = dout_t / den_t, dden_t = -dout_t . (S^T phi(q_t)) / den_t^2,
+ * den_t = phi(q_t) . z + eps, phi'(x) = 1 for x > 0 and e^x otherwise.
+ * Products run on bf16 matrix cores with fp32 accumulation (P and G rounded to bf16 as
+ * operands); every sum has a fixed order, so results are deterministic. */
+
+/* Forward for training: hf_sparse_window_attn, plus lse_dev fp32 [B][H][C*T] out: for each
+ * query, log2 of its softmax denominator over the kept keys, in base-2 logits
+ * (lse_t = log2 sum_u 2^(q_t.k_u log2(e) / sqrt(D))), which hf_hybrid_attn_backward uses. */
+hf_status hf_sparse_window_attn_lse(const hf_dims *d, const void *q_dev, const hf_kv_ring *ring,
+                                    const int32_t *idx_dev, int32_t top_k, const float *S_dev,
+                                    const float *z_dev, float eps, float *out_dev, float *lse_dev,
+                                    void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace hf_hybrid_attn_backward needs for these dims and top_k (any
+ * window of up to W frames); host call.  Contents need no initialisation. */
+hf_status hf_backward_workspace_size(const hf_dims *d, int32_t top_k, size_t *bytes);
+
+/* Backward of out = sparse window attention + linear readout (the forward of
+ * hf_sparse_window_attn_lse with the same q, ring, idx, S, z, eps):
+ *   inputs   q_dev bf16 [B][H][C*T][D]; ring, idx_dev, top_k, S_dev, z_dev, eps as in the
+ *            forward (S and z required); out_dev and lse_dev fp32 from that forward;
+ *            dout_dev fp32 [B][H][C*T][D] = dL/dout
+ *   outputs  (written, not accumulated) dq_dev fp32 [B][H][C*T][D]; dk_dev, dv_dev fp32
+ *            [B][H][Nk][D] for the window's keys in LOGICAL order (key j = f T + t of
+ *            logical frame f; keys no query block kept get 0); dS_dev fp32 [B][H][D][D];
+ *            dz_dev fp32 [B][H][D]
+ *   workspace_dev of at least hf_backward_workspace_size bytes (HF_ERR_WORKSPACE otherwise).
+ * Errors as hf_sparse_window_attn; the kept lists must be those of the forward. */
+hf_status hf_hybrid_attn_backward(const hf_dims *d, const void *q_dev, const hf_kv_ring *ring,
+                                  const int32_t *idx_dev, int32_t top_k, const float *S_dev,
+                                  const float *z_dev, float eps, const float *out_dev,
+                                  const float *lse_dev, const float *dout_dev, float *dq_dev,
+                                  float *dk_dev, float *dv_dev, float *dS_dev, float *dz_dev,
+                                  void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward of hf_linear_absorb ([HF-abs]: S += sum_u phi(k_u)^T v_u, z += sum_u phi(k_u)):
+ * given dS_dev fp32 [B][H][D][D] and dz_dev fp32 [B][H][D], the gradients of the state
+ * after the absorb, writes dk_dev, dv_dev fp32 [B][H][n_tok][D]:
+ *   dv_u = phi(k_u) dS,   dk_u = (dS v_u + dz) * phi'(k_u)
+ * (bf16 matrix-core products, fp32 accumulation).  The gradient with respect to the state
+ * before the absorb is dS, dz themselves.  workspace_dev as for hf_linear_absorb. */
+hf_status hf_linear_absorb_backward(const hf_dims *d, const void *k_ev_dev, const void *v_ev_dev,
+                                    int64_t n_tok, const float *dS_dev, const float *dz_dev,
+                                    float *dk_dev, float *dv_dev, void *workspace_dev,
+                                    size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

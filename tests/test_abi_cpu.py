@@ -23,7 +23,9 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ("hf_block_select", "hf_sparse_window_attn", "hf_linear_absorb", "hf_hybrid_step", "hf_ring_append",
-              "hf_workspace_size", "hf_last_error", "hf_status_str", "hf_abi_version", "hf_cag_schedule"):
+              "hf_workspace_size", "hf_last_error", "hf_status_str", "hf_abi_version", "hf_cag_schedule",
+              "hf_sparse_window_attn_lse", "hf_backward_workspace_size", "hf_hybrid_attn_backward",
+              "hf_linear_absorb_backward"):
         assert s in syms
 
 
@@ -166,3 +168,48 @@ def test_hier_select_bounds():
     big = geom(W=70, T=64, bk=64)         # 67 + 3 frames > 64
     assert call_hier(big, ring_desc(n_committed=67), 4, 4) == 3
     assert call_hier(geom(T=40, bk=64), ring_desc(), 1, 1) == 3 and "bk <= T" in last_error()
+
+
+def call_backward(g, ring, top_k=37, ws_bytes=None, **ptrs):
+    L = _lib.lib()
+    ws_bytes = hf.backward_workspace_size(g, 37) if ws_bytes is None else ws_bytes
+    p = {k: FAKE for k in ("q", "idx", "S", "z", "out", "lse", "dout", "dq", "dk", "dv", "dS", "dz", "ws")}
+    p.update(ptrs)
+    return L.hf_hybrid_attn_backward(ctypes.byref(g.dims()), p["q"], ctypes.byref(ring), p["idx"], top_k, p["S"],
+                                     p["z"], ctypes.c_float(1e-6), p["out"], p["lse"], p["dout"], p["dq"], p["dk"],
+                                     p["dv"], p["dS"], p["dz"], p["ws"], ws_bytes, None)
+
+
+def test_backward_validation():
+    g, r = geom(), ring_desc()
+    for name in ("q", "idx", "S", "z", "out", "lse", "dout", "dq", "dk", "dv", "dS", "dz"):
+        assert call_backward(g, r, **{name: None}) == 1, name        # HF_ERR_NULL
+    assert call_backward(g, r, top_k=0) == 2                        # HF_ERR_SHAPE
+    assert call_backward(g, r, top_k=148) == 2
+    assert call_backward(g, r, ws_bytes=1024) == 5                  # HF_ERR_WORKSPACE
+    assert "need" in last_error()
+    assert call_backward(g, r, ws=None) == 5
+    assert call_backward(g, ring_desc(head=6)) == 4                 # HF_ERR_RING_STATE
+
+
+def test_backward_workspace_size_scales():
+    a = hf.backward_workspace_size(geom(H=1), 37)
+    b = hf.backward_workspace_size(geom(H=12), 37)
+    assert a < b <= 12 * a   # the readout splits per plane shrink as planes grow
+    with pytest.raises(hf.HFError):
+        hf.backward_workspace_size(geom(), 0)
+
+
+def test_absorb_backward_and_lse_validation():
+    L = _lib.lib()
+    g = geom()
+    ws = hf.workspace_size(g)
+    d = ctypes.byref(g.dims())
+    assert L.hf_linear_absorb_backward(d, FAKE, FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == 2
+    assert L.hf_linear_absorb_backward(d, FAKE, FAKE, 10, None, FAKE, FAKE, FAKE, FAKE, ws, None) == 1
+    assert L.hf_linear_absorb_backward(d, FAKE, FAKE, 10, FAKE, FAKE, None, FAKE, FAKE, ws, None) == 1
+    assert L.hf_linear_absorb_backward(d, FAKE, FAKE, 10, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == 5
+    assert L.hf_linear_absorb_backward(d, None, None, 0, FAKE, FAKE, None, None, FAKE, ws, None) == 0  # no-op
+    r = ring_desc()
+    assert L.hf_sparse_window_attn_lse(d, FAKE, ctypes.byref(r), FAKE, 37, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, None,
+                                       FAKE, ws, None) == 1

@@ -157,47 +157,50 @@ __global__ __launch_bounds__(256) void prep_queries_kernel(hf_bwd_args a) {
     }
 }
 
-// Per plane, the query blocks that kept each key block, ascending: count, offsets, fill.
-// Kept lists are ascending, so membership is a binary search.
-__device__ __forceinline__ bool kept_by(const int32_t *sel, int k, int j) {
-    int lo = 0, hi = k - 1;
-    while (lo <= hi) {
-        const int mid = (lo + hi) >> 1;
-        const int v = sel[mid];
-        if (v == j) return true;
-        if (v < j) lo = mid + 1;
-        else hi = mid - 1;
-    }
-    return false;
-}
-
+// Per plane, the query blocks that kept each key block, ascending: count (LDS atomics over
+// the kept entries), exclusive scan (one wave), then a fill that walks the query blocks in
+// order (a kept list holds distinct blocks, so its entries never collide; entries outside
+// [0, n_kb), a caller error, are skipped).
 __global__ __launch_bounds__(256) void csr_kernel(hf_bwd_args a) {
     __shared__ int cnt[kMaxKeyBlocks];
-    const int bh = blockIdx.x;
+    __shared__ int pos[kMaxKeyBlocks];
+    const int bh = blockIdx.x, tid = threadIdx.x;
     const int32_t *sel = a.idx + (size_t)bh * a.nqb * a.top_k;
-    for (int j = threadIdx.x; j < a.nkb; j += 256) {
-        int c = 0;
-        for (int i = 0; i < a.nqb; ++i) c += kept_by(sel + (size_t)i * a.top_k, a.top_k, j);
-        cnt[j] = c;
+    const int total = a.nqb * a.top_k;
+    for (int j = tid; j < a.nkb; j += 256) cnt[j] = 0;
+    __syncthreads();
+    for (int e = tid; e < total; e += 256) {
+        const int j = sel[e];
+        if (j >= 0 && j < a.nkb) atomicAdd(&cnt[j], 1);
     }
     __syncthreads();
     int32_t *off = a.qoff + (size_t)bh * (a.nkb + 1);
-    if (threadIdx.x == 0) {
-        int s = 0;
-        for (int j = 0; j < a.nkb; ++j) {
-            off[j] = s;
-            const int c = cnt[j];
-            cnt[j] = s;
-            s += c;
+    if (tid < 64) {
+        int base = 0;
+        for (int j0 = 0; j0 < a.nkb; j0 += 64) {
+            const int j = j0 + tid;
+            const int c = j < a.nkb ? cnt[j] : 0;
+            int x = c;
+            for (int d = 1; d < 64; d <<= 1) {
+                const int y = __shfl_up(x, d);
+                if (tid >= d) x += y;
+            }
+            if (j < a.nkb) {
+                off[j] = base + x - c;
+                pos[j] = base + x - c;
+            }
+            base += __shfl(x, 63);
         }
-        off[a.nkb] = s;
+        if (tid == 0) off[a.nkb] = base;
     }
     __syncthreads();
     int32_t *list = a.qlist + (size_t)bh * a.nqb * a.top_k;
-    for (int j = threadIdx.x; j < a.nkb; j += 256) {
-        int o = cnt[j];
-        for (int i = 0; i < a.nqb; ++i)
-            if (kept_by(sel + (size_t)i * a.top_k, a.top_k, j)) list[o++] = i;
+    for (int i = 0; i < a.nqb; ++i) {
+        for (int r = tid; r < a.top_k; r += 256) {
+            const int j = sel[(size_t)i * a.top_k + r];
+            if (j >= 0 && j < a.nkb) list[pos[j]++] = i;
+        }
+        __syncthreads();
     }
 }
 
@@ -382,8 +385,23 @@ __global__ __launch_bounds__(256) void reduce_readout_kernel(hf_bwd_args a) {
 
 // ---------------------------------------------------------------- dq pass
 
+// One workgroup per query block, one wave per 32-query tile.  Each 32-key subtile's K rows,
+// V rows and K^T pass through LDS once for all the waves (rows padded by 16 bytes); the
+// next subtile's operands are loaded into registers while the current one is computed.
+template <int D>
+struct SubtileLds {
+    uint16_t k[32][D + 8], v[32][D + 8];
+    uint16_t kt[D][32 + 8];
+};
+
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void dq_kernel(hf_bwd_args a, float c_log2, float inv_sqrt_d, int lsh) {
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW, 2))) void dq_kernel(hf_bwd_args a, float c_log2, float inv_sqrt_d, int lsh) {
+    constexpr int NTH = 64 * NW;
+    constexpr int CR = 32 * D / 8;           // 16-byte chunks of the K (or V) rows of a subtile
+    constexpr int CT = D * 4;                // 16-byte chunks of its K^T
+    constexpr int PR = CR / NTH, PT = CT / NTH;
+    static_assert(CR % NTH == 0 && CT % NTH == 0, "staging split");
+    __shared__ __align__(16) SubtileLds<D> L;
     const int bh = blockIdx.x / a.nqb, qb = blockIdx.x % a.nqb;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
     const int q0 = qb * a.bq, qend = min(q0 + a.bq, a.Nq);
@@ -396,48 +414,85 @@ __global__ __launch_bounds__(64 * NW) void dq_kernel(hf_bwd_args a, float c_log2
         qf[ks] = *reinterpret_cast<const u32x4 *>(a.q + row * D + 16 * ks + 8 * g);
         gf[ks] = *reinterpret_cast<const u32x4 *>(a.gr + row * D + 16 * ks + 8 * g);
     }
-    const float L = a.lse[row], Dl = a.delta[(size_t)bh * a.NqP + (valid ? t : q0)];
+    const float Lq = a.lse[row], Dl = a.delta[(size_t)bh * a.NqP + (valid ? t : q0)];
     const uint16_t *krp = a.kr + (size_t)bh * a.NkP * D, *vrp = a.vr + (size_t)bh * a.NkP * D;
     const uint16_t *ktp = a.kt + (size_t)bh * D * a.NkP;
     f32x16 acc[D / 32];
 #pragma unroll
     for (int ft = 0; ft < D / 32; ++ft) acc[ft] = f32x16{};
     const int32_t *sel = a.idx + ((size_t)bh * a.nqb + qb) * a.top_k;
-    const int nsub = 1 << lsh;
-    for (int r = 0; r < a.top_k; ++r) {
+    // the subtiles: kept block r, 32-key part su while it holds keys
+    int r = 0, su = 0;
+    auto k0_of = [&](int rr, int ss) { return min(max(sel[rr], 0), a.nkb - 1) * a.bk + 32 * ss; };
+    auto advance = [&](int &rr, int &ss) {
+        const int b = min(max(sel[rr], 0), a.nkb - 1);
+        if (ss + 1 < (1 << lsh) && b * a.bk + 32 * (ss + 1) < min(b * a.bk + a.bk, a.Nk)) {
+            ++ss;
+        } else {
+            ++rr;
+            ss = 0;
+        }
+    };
+    u32x4 pk[PR], pv[PR], pt[PT];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int e0 = 0; e0 < PR; ++e0) {
+            const int e = threadIdx.x + NTH * e0, rr = e / (D / 8), c8 = (e % (D / 8)) * 8;
+            pk[e0] = *reinterpret_cast<const u32x4 *>(krp + (size_t)(k0 + rr) * D + c8);
+            pv[e0] = *reinterpret_cast<const u32x4 *>(vrp + (size_t)(k0 + rr) * D + c8);
+        }
+#pragma unroll
+        for (int e0 = 0; e0 < PT; ++e0) {
+            const int e = threadIdx.x + NTH * e0, d = e / 4, c8 = (e % 4) * 8;
+            pt[e0] = *reinterpret_cast<const u32x4 *>(ktp + (size_t)d * a.NkP + k0 + c8);
+        }
+    };
+    load(k0_of(0, 0));
+    while (r < a.top_k) {
+        const int k0 = k0_of(r, su);
         const int b = min(max(sel[r], 0), a.nkb - 1);
-        const int bend = min(b * a.bk + a.bk, a.Nk);
-        for (int su = 0; su < nsub; ++su) {
-            const int k0 = b * a.bk + 32 * su;
-            const int nv = min(32, bend - k0);
-            if (nv <= 0) break;
-            f32x16 s = {}, dp = {};
-            const uint16_t *kp = krp + (size_t)(k0 + perm32(n)) * D + 8 * g;
-            const uint16_t *vp = vrp + (size_t)(k0 + perm32(n)) * D + 8 * g;
+        const int nv = min(32, min(b * a.bk + a.bk, a.Nk) - k0);
+        __syncthreads();   // everyone is done with the previous subtile
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(kp + 16 * ks)), as_bf16x8(qf[ks]), s);
-                dp = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(vp + 16 * ks)), as_bf16x8(gf[ks]), dp);
-            }
-            // lane holds keys 16 g + i of the subtile for query n
-            float gt[16];
+        for (int e0 = 0; e0 < PR; ++e0) {
+            const int e = threadIdx.x + NTH * e0, rr = e / (D / 8), c8 = (e % (D / 8)) * 8;
+            *reinterpret_cast<u32x4 *>(&L.k[rr][c8]) = pk[e0];
+            *reinterpret_cast<u32x4 *>(&L.v[rr][c8]) = pv[e0];
+        }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = (16 * g + i < nv) ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c_log2, -L)) : 0.f;
-                gt[i] = p * (dp[i] - Dl);
-            }
-            u32x4 gfr[2];
+        for (int e0 = 0; e0 < PT; ++e0) {
+            const int e = threadIdx.x + NTH * e0, d = e / 4, c8 = (e % 4) * 8;
+            *reinterpret_cast<u32x4 *>(&L.kt[d][c8]) = pt[e0];
+        }
+        __syncthreads();
+        advance(r, su);
+        if (r < a.top_k) load(k0_of(r, su));
+        f32x16 s = {}, dp = {};
+        const int kr = perm32(n);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.k[kr][16 * ks + 8 * g])), as_bf16x8(qf[ks]), s);
+            dp = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.v[kr][16 * ks + 8 * g])), as_bf16x8(gf[ks]), dp);
+        }
+        // lane holds keys 16 g + i of the subtile for query n
+        float gt[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p = (16 * g + i < nv) ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c_log2, -Lq)) : 0.f;
+            gt[i] = p * (dp[i] - Dl);
+        }
+        u32x4 gfr[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            gfr[ks] = u32x4{pack_bf16x2(gt[8 * ks], gt[8 * ks + 1]), pack_bf16x2(gt[8 * ks + 2], gt[8 * ks + 3]),
+                            pack_bf16x2(gt[8 * ks + 4], gt[8 * ks + 5]), pack_bf16x2(gt[8 * ks + 6], gt[8 * ks + 7])};
+#pragma unroll
+        for (int ft = 0; ft < D / 32; ++ft) {
+            const int dr = 32 * ft + perm32(n);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                gfr[ks] = u32x4{pack_bf16x2(gt[8 * ks], gt[8 * ks + 1]), pack_bf16x2(gt[8 * ks + 2], gt[8 * ks + 3]),
-                                pack_bf16x2(gt[8 * ks + 4], gt[8 * ks + 5]), pack_bf16x2(gt[8 * ks + 6], gt[8 * ks + 7])};
-#pragma unroll
-            for (int ft = 0; ft < D / 32; ++ft) {
-                const uint16_t *tp = ktp + (size_t)(32 * ft + perm32(n)) * a.NkP + k0 + 16 * g;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    acc[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(tp + 8 * ks)), as_bf16x8(gfr[ks]), acc[ft]);
-            }
+                acc[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.kt[dr][16 * g + 8 * ks])), as_bf16x8(gfr[ks]),
+                                 acc[ft]);
         }
     }
     if (valid) {
@@ -456,76 +511,182 @@ __global__ __launch_bounds__(64 * NW) void dq_kernel(hf_bwd_args a, float c_log2
 
 // ---------------------------------------------------------------- dk / dv pass
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void dkdv_kernel(hf_bwd_args a, float c_log2, float inv_sqrt_d) {
+// LDS of the dk/dv pass: one query block's Q rows, dO rows (bf16), Q^T and dO^T, with rows
+// padded by 16 bytes so that fragment reads of 16 rows hit distinct banks; the same bytes
+// later hold the query-tile halves of the accumulators for the final reduction.
+template <int D>
+struct QBlockLds {
+    uint16_t q[kQB][D + 8], g[kQB][D + 8];
+    uint16_t qt[D][kQB + 8], gt[D][kQB + 8];
+    float lse[kQB], delta[kQB];
+};
+
+// One workgroup per key block: wave (kt, qt) owns the block's 32-key tile kt and the
+// 32-query tile qt of every query block that kept it (NKT key tiles x NQT query tiles).
+// Per query block the workgroup stages the query-side operands in LDS once for all its
+// waves; the two query-tile halves of each key tile are added at the end.
+template <int D, int NKT, int NQT>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NKT * NQT, 64 * NKT * NQT))) void dkdv_kernel(hf_bwd_args a, float c_log2, float inv_sqrt_d) {
+    constexpr int NTH = 64 * NKT * NQT;
+    __shared__ __align__(16) QBlockLds<D> L;
+    static_assert(sizeof(QBlockLds<D>) >= (size_t)2 * D * 32 * 4, "reduction space");
     const int bh = blockIdx.x / a.nkb, j = blockIdx.x % a.nkb;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
-    const int kj0 = j * a.bk + 32 * w;
+    const int kt = w % NKT, qt = w / NKT;
+    const int kj0 = j * a.bk + 32 * kt;
     const int nvk = min(32, min(j * a.bk + a.bk, a.Nk) - kj0);   // keys of this wave (<= 0: none)
     const int key = kj0 + n;                                     // < NkP whenever nvk > 0
     const bool kvalid = n < nvk;
     f32x16 accV[D / 32], accK[D / 32];
 #pragma unroll
     for (int ft = 0; ft < D / 32; ++ft) accV[ft] = accK[ft] = f32x16{};
-    if (nvk > 0) {
-        u32x4 kf[D / 16], vf[D / 16];
-        const size_t krow = ((size_t)bh * a.NkP + key) * D + 8 * g;
+    u32x4 kf[D / 16], vf[D / 16];
+    {
+        const size_t krow = ((size_t)bh * a.NkP + (nvk > 0 ? key : j * a.bk)) * D + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             kf[ks] = *reinterpret_cast<const u32x4 *>(a.kr + krow + 16 * ks);
             vf[ks] = *reinterpret_cast<const u32x4 *>(a.vr + krow + 16 * ks);
         }
-        const int32_t *off = a.qoff + (size_t)bh * (a.nkb + 1);
-        const int32_t *list = a.qlist + (size_t)bh * a.nqb * a.top_k;
-        const int p0 = off[j], p1 = off[j + 1];
-        for (int p = p0; p < p1; ++p) {
-            const int i = list[p];
-            const int q0 = i * a.bq, nqv = min(a.bq, a.Nq - q0);
+    }
+    const int32_t *off = a.qoff + (size_t)bh * (a.nkb + 1);
+    const int32_t *list = a.qlist + (size_t)bh * a.nqb * a.top_k;
+    const int p0 = off[j], p1 = off[j + 1];
+    // the next query block's operands are loaded into registers while the current one is
+    // computed, then written to LDS
+    constexpr int CH = kQB * D / 8;          // 16-byte chunks per operand
+    constexpr bool kAhead = NTH == 256;      // other workgroup sizes would need too many registers
+    constexpr int PER = kAhead ? CH / NTH : 1;   // per thread and operand
+    static_assert(!kAhead || CH % NTH == 0, "staging split");
+    u32x4 pre[4][PER];
+    float pre_l = 0.f, pre_d = 0.f;
+    auto load_block = [&](int p) {
+        const int i = min(max(list[p], 0), a.nqb - 1);
+        const int q0 = i * a.bq, nqv = min(a.bq, a.Nq - q0);
+        const size_t blk = ((size_t)bh * a.nqb + i) * D;
+#pragma unroll
+        for (int e0 = 0; e0 < PER; ++e0) {
+            const int e = threadIdx.x + NTH * e0;
+            const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
+            const size_t row = (size_t)bh * a.Nq + q0 + min(r, nqv - 1);
+            pre[0][e0] = *reinterpret_cast<const u32x4 *>(a.q + row * D + c8);
+            pre[1][e0] = *reinterpret_cast<const u32x4 *>(a.gr + row * D + c8);
+            const int d = e / (kQB / 8), q8 = (e % (kQB / 8)) * 8;
+            pre[2][e0] = *reinterpret_cast<const u32x4 *>(a.qt + (blk + d) * kQB + q8);
+            pre[3][e0] = *reinterpret_cast<const u32x4 *>(a.gt + (blk + d) * kQB + q8);
+        }
+        if (threadIdx.x < kQB) {
+            const size_t qi = (size_t)q0 + min((int)threadIdx.x, nqv - 1);
+            pre_l = a.lse[(size_t)bh * a.Nq + qi];
+            pre_d = a.delta[(size_t)bh * a.NqP + qi];
+        }
+    };
+    if (kAhead && p0 < p1) load_block(p0);
+    for (int p = p0; p < p1; ++p) {
+        const int i = min(max(list[p], 0), a.nqb - 1);
+        const int nqv = min(a.bq, a.Nq - i * a.bq);
+        __syncthreads();   // everyone is done with the previous block
+        if constexpr (kAhead) {
+#pragma unroll
+            for (int e0 = 0; e0 < PER; ++e0) {
+                const int e = threadIdx.x + NTH * e0;
+                const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
+                *reinterpret_cast<u32x4 *>(&L.q[r][c8]) = pre[0][e0];
+                *reinterpret_cast<u32x4 *>(&L.g[r][c8]) = pre[1][e0];
+                const int d = e / (kQB / 8), q8 = (e % (kQB / 8)) * 8;
+                *reinterpret_cast<u32x4 *>(&L.qt[d][q8]) = pre[2][e0];
+                *reinterpret_cast<u32x4 *>(&L.gt[d][q8]) = pre[3][e0];
+            }
+            if (threadIdx.x < kQB) {
+                L.lse[threadIdx.x] = pre_l;
+                L.delta[threadIdx.x] = pre_d;
+            }
+        } else {
+            const int q0 = i * a.bq;
             const size_t blk = ((size_t)bh * a.nqb + i) * D;
-            for (int qt = 0; 32 * qt < nqv; ++qt) {
-                // S and dP for queries q0 + 32 qt + (rows in perm32 order), this wave's keys
-                const int qr = 32 * qt + perm32(n);
-                const size_t qrow = (size_t)bh * a.Nq + q0 + min(qr, nqv - 1);
-                f32x16 s = {}, dp = {};
-#pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(a.q + qrow * D + 16 * ks + 8 * g)), as_bf16x8(kf[ks]), s);
-                    dp = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(a.gr + qrow * D + 16 * ks + 8 * g)), as_bf16x8(vf[ks]), dp);
-                }
-                // lane (key n) holds queries 32 qt + 16 g + i
-                const int qb0 = 32 * qt + 16 * g;
-                float pv[16], gv[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int qq = qb0 + i;
-                    const bool ok = kvalid && qq < nqv;
-                    const size_t qi = (size_t)q0 + min(qq, nqv - 1);
-                    const float L = a.lse[(size_t)bh * a.Nq + qi];
-                    const float Dl = a.delta[(size_t)bh * a.NqP + qi];
-                    const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c_log2, -L)) : 0.f;
-                    pv[i] = pr;
-                    gv[i] = pr * (dp[i] - Dl);
-                }
-                u32x4 pf[2], gfr[2];
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    pf[ks] = u32x4{pack_bf16x2(pv[8 * ks], pv[8 * ks + 1]), pack_bf16x2(pv[8 * ks + 2], pv[8 * ks + 3]),
-                                   pack_bf16x2(pv[8 * ks + 4], pv[8 * ks + 5]), pack_bf16x2(pv[8 * ks + 6], pv[8 * ks + 7])};
-                    gfr[ks] = u32x4{pack_bf16x2(gv[8 * ks], gv[8 * ks + 1]), pack_bf16x2(gv[8 * ks + 2], gv[8 * ks + 3]),
-                                    pack_bf16x2(gv[8 * ks + 4], gv[8 * ks + 5]), pack_bf16x2(gv[8 * ks + 6], gv[8 * ks + 7])};
-                }
-                // dv^T += dO^T P, dk^T += Q^T G (rows d in perm32 order, queries 16 g + 8 ks ..)
-#pragma unroll
-                for (int ft = 0; ft < D / 32; ++ft) {
-                    const size_t trow = (blk + 32 * ft + perm32(n)) * kQB + 32 * qt + 16 * g;
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        accV[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(a.gt + trow + 8 * ks)), as_bf16x8(pf[ks]), accV[ft]);
-                        accK[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(a.qt + trow + 8 * ks)), as_bf16x8(gfr[ks]), accK[ft]);
-                    }
-                }
+            for (int e = threadIdx.x; e < CH; e += NTH) {
+                const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
+                const size_t row = (size_t)bh * a.Nq + q0 + min(r, nqv - 1);
+                *reinterpret_cast<u32x4 *>(&L.q[r][c8]) = *reinterpret_cast<const u32x4 *>(a.q + row * D + c8);
+                *reinterpret_cast<u32x4 *>(&L.g[r][c8]) = *reinterpret_cast<const u32x4 *>(a.gr + row * D + c8);
+                const int d = e / (kQB / 8), q8 = (e % (kQB / 8)) * 8;
+                *reinterpret_cast<u32x4 *>(&L.qt[d][q8]) = *reinterpret_cast<const u32x4 *>(a.qt + (blk + d) * kQB + q8);
+                *reinterpret_cast<u32x4 *>(&L.gt[d][q8]) = *reinterpret_cast<const u32x4 *>(a.gt + (blk + d) * kQB + q8);
+            }
+            for (int e = threadIdx.x; e < kQB; e += NTH) {
+                const size_t qi = (size_t)q0 + min(e, nqv - 1);
+                L.lse[e] = a.lse[(size_t)bh * a.Nq + qi];
+                L.delta[e] = a.delta[(size_t)bh * a.NqP + qi];
             }
         }
+        __syncthreads();
+        if (kAhead && p + 1 < p1) load_block(p + 1);
+        if (nvk <= 0 || 32 * qt >= nqv) continue;   // uniform per wave; no barrier before the next
+        // S and dP for queries 32 qt + (rows in perm32 order), this wave's keys
+        const int qr = 32 * qt + perm32(n);
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.q[qr][16 * ks + 8 * g])), as_bf16x8(kf[ks]), s);
+            dp = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.g[qr][16 * ks + 8 * g])), as_bf16x8(vf[ks]), dp);
+        }
+        // lane (key n) holds queries 32 qt + 16 g + i
+        const int qb0 = 32 * qt + 16 * g;
+        float pv[16], gv[16];
+#pragma unroll
+        for (int i2 = 0; i2 < 16; ++i2) {
+            const int qq = qb0 + i2;
+            const bool ok = kvalid && qq < nqv;
+            const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i2], c_log2, -L.lse[qq])) : 0.f;
+            pv[i2] = pr;
+            gv[i2] = pr * (dp[i2] - L.delta[qq]);
+        }
+        u32x4 pf[2], gfr[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            pf[ks] = u32x4{pack_bf16x2(pv[8 * ks], pv[8 * ks + 1]), pack_bf16x2(pv[8 * ks + 2], pv[8 * ks + 3]),
+                           pack_bf16x2(pv[8 * ks + 4], pv[8 * ks + 5]), pack_bf16x2(pv[8 * ks + 6], pv[8 * ks + 7])};
+            gfr[ks] = u32x4{pack_bf16x2(gv[8 * ks], gv[8 * ks + 1]), pack_bf16x2(gv[8 * ks + 2], gv[8 * ks + 3]),
+                            pack_bf16x2(gv[8 * ks + 4], gv[8 * ks + 5]), pack_bf16x2(gv[8 * ks + 6], gv[8 * ks + 7])};
+        }
+        // dv^T += dO^T P, dk^T += Q^T G (rows d in perm32 order, queries 16 g + 8 ks ..)
+#pragma unroll
+        for (int ft = 0; ft < D / 32; ++ft) {
+            const int dr = 32 * ft + perm32(n);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                accV[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.gt[dr][qb0 + 8 * ks])), as_bf16x8(pf[ks]), accV[ft]);
+                accK[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.qt[dr][qb0 + 8 * ks])), as_bf16x8(gfr[ks]), accK[ft]);
+            }
+        }
+    }
+    if constexpr (NQT > 1) {
+        // query-tile halves, one key tile at a time: the wave with qt = 1 hands its sums to
+        // the wave with qt = 0
+        float *red = reinterpret_cast<float *>(&L);
+        for (int kk = 0; kk < NKT; ++kk) {
+            __syncthreads();
+            if (qt == 1 && kt == kk) {
+#pragma unroll
+                for (int ft = 0; ft < D / 32; ++ft)
+#pragma unroll
+                    for (int i2 = 0; i2 < 16; ++i2) {
+                        red[(0 * (D / 32) + ft) * 16 * 64 + i2 * 64 + lane] = accV[ft][i2];
+                        red[(1 * (D / 32) + ft) * 16 * 64 + i2 * 64 + lane] = accK[ft][i2];
+                    }
+            }
+            __syncthreads();
+            if (qt == 0 && kt == kk) {
+#pragma unroll
+                for (int ft = 0; ft < D / 32; ++ft)
+#pragma unroll
+                    for (int i2 = 0; i2 < 16; ++i2) {
+                        accV[ft][i2] += red[(0 * (D / 32) + ft) * 16 * 64 + i2 * 64 + lane];
+                        accK[ft][i2] += red[(1 * (D / 32) + ft) * 16 * 64 + i2 * 64 + lane];
+                    }
+            }
+        }
+        if (qt != 0) return;
     }
     if (kvalid) {
         // lane (key n) holds features 32 ft + 16 g + i
@@ -622,12 +783,17 @@ hipError_t launch_attn_backward(const hf_bwd_args &a, hipStream_t s) {
         hipLaunchKernelGGL((dq_kernel<D, 2>), dim3((unsigned)(a.BH * a.nqb)), dim3(128), 0, s, a, c_log2, inv_sqrt_d, lsh);
     else
         hipLaunchKernelGGL((dq_kernel<D, 1>), dim3((unsigned)(a.BH * a.nqb)), dim3(64), 0, s, a, c_log2, inv_sqrt_d, lsh);
-    if (a.bk > 64)
-        hipLaunchKernelGGL((dkdv_kernel<D, 4>), dim3((unsigned)(a.BH * a.nkb)), dim3(256), 0, s, a, c_log2, inv_sqrt_d);
-    else if (a.bk > 32)
-        hipLaunchKernelGGL((dkdv_kernel<D, 2>), dim3((unsigned)(a.BH * a.nkb)), dim3(128), 0, s, a, c_log2, inv_sqrt_d);
-    else
-        hipLaunchKernelGGL((dkdv_kernel<D, 1>), dim3((unsigned)(a.BH * a.nkb)), dim3(64), 0, s, a, c_log2, inv_sqrt_d);
+    const dim3 gk((unsigned)(a.BH * a.nkb));
+    // key tiles (bk / 32, at least 1) x query tiles (bq / 32, at least 1) waves
+    if (a.bq > 32) {
+        if (a.bk > 64) hipLaunchKernelGGL((dkdv_kernel<D, 4, 2>), gk, dim3(512), 0, s, a, c_log2, inv_sqrt_d);
+        else if (a.bk > 32) hipLaunchKernelGGL((dkdv_kernel<D, 2, 2>), gk, dim3(256), 0, s, a, c_log2, inv_sqrt_d);
+        else hipLaunchKernelGGL((dkdv_kernel<D, 1, 2>), gk, dim3(128), 0, s, a, c_log2, inv_sqrt_d);
+    } else {
+        if (a.bk > 64) hipLaunchKernelGGL((dkdv_kernel<D, 4, 1>), gk, dim3(256), 0, s, a, c_log2, inv_sqrt_d);
+        else if (a.bk > 32) hipLaunchKernelGGL((dkdv_kernel<D, 2, 1>), gk, dim3(128), 0, s, a, c_log2, inv_sqrt_d);
+        else hipLaunchKernelGGL((dkdv_kernel<D, 1, 1>), gk, dim3(64), 0, s, a, c_log2, inv_sqrt_d);
+    }
     return hipGetLastError();
 }
 

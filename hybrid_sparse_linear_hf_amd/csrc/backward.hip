@@ -511,27 +511,53 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
 
 // ---------------------------------------------------------------- dk / dv pass
 
-// LDS of the dk/dv pass: one query block's Q rows, dO rows (bf16), Q^T and dO^T, with rows
-// padded by 16 bytes so that fragment reads of 16 rows hit distinct banks; the same bytes
-// later hold the query-tile halves of the accumulators for the final reduction.
+constexpr int kBufDword3 = 0x00020000;        // raw buffer resource word 3 (gfx9 family)
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef __attribute__((address_space(3))) void *LdsPtr;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufDword3);
+}
+
+// 16 bytes per lane from the buffer into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(Rsrc r, unsigned char *lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 16, (int)voff, 0, 0, 0);
+}
+
+// 16-byte chunk swizzles of the staged tiles, so that the fragment reads (rows 32 x + perm32(n)
+// of 16 lanes, one chunk) hit distinct LDS bank groups: rows of D/8 chunks (Q, dO) and rows of
+// 8 chunks (Q^T, dO^T, 64 queries each).
 template <int D>
-struct QBlockLds {
-    uint16_t q[kQB][D + 8], g[kQB][D + 8];
-    uint16_t qt[D][kQB + 8], gt[D][kQB + 8];
-    float lse[kQB], delta[kQB];
+__device__ __forceinline__ int swz_row(int r) {
+    if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | ((r >> 1) & 8);
+    else return ((r >> 1) & 3) | ((r >> 2) & 4);
+}
+__device__ __forceinline__ int swz_tr(int r) { return ((r >> 1) & 3) | ((r >> 2) & 4); }
+
+// One query block's operands, staged unpadded with swizzled chunks by direct-to-LDS loads.
+template <int D>
+struct QBlockStage {
+    uint16_t q[kQB * D], g[kQB * D];          // rows of D, chunk c of row r at slot c ^ swz_row(r)
+    uint16_t qt[D * kQB], gt[D * kQB];        // rows of 64 queries, chunk c at slot c ^ swz_tr(r)
 };
 
 // One workgroup per key block: wave (kt, qt) owns the block's 32-key tile kt and the
 // 32-query tile qt of every query block that kept it (NKT key tiles x NQT query tiles).
-// Per query block the workgroup stages the query-side operands in LDS once for all its
-// waves; the two query-tile halves of each key tile are added at the end.
+// Each query block's operands reach LDS once for all the waves, by direct-to-LDS loads into
+// one of two stages, fetched while the previous block is computed; the two query-tile
+// halves of each key tile are added at the end.
 template <int D, int NKT, int NQT>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NKT * NQT, 64 * NKT * NQT))) void dkdv_kernel(hf_bwd_args a, float c_log2, float inv_sqrt_d) {
-    constexpr int NTH = 64 * NKT * NQT;
-    __shared__ __align__(16) QBlockLds<D> L;
-    static_assert(sizeof(QBlockLds<D>) >= (size_t)2 * D * 32 * 4, "reduction space");
+__global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, float c_log2, float inv_sqrt_d) {
+    constexpr int NW = NKT * NQT, NTH = 64 * NW;
+    constexpr int LPR = D / 8, RPI = 64 / LPR;    // chunks per row, rows per load instruction
+    constexpr int NI = kQB * D * 2 / 1024;         // load instructions per operand (16 for D = 128)
+    static_assert(NI % NW == 0 || NW > NI, "load split");
+    __shared__ __align__(16) QBlockStage<D> S[2];
+    __shared__ float s_lse[2][kQB], s_delta[2][kQB];
+    static_assert(sizeof(S) >= (size_t)2 * D * 32 * 4, "reduction space");
     const int bh = blockIdx.x / a.nkb, j = blockIdx.x % a.nkb;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
     const int kt = w % NKT, qt = w / NKT;
     const int kj0 = j * a.bk + 32 * kt;
     const int nvk = min(32, min(j * a.bk + a.bk, a.Nk) - kj0);   // keys of this wave (<= 0: none)
@@ -549,86 +575,55 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NKT * NQT, 64 * NKT *
             vf[ks] = *reinterpret_cast<const u32x4 *>(a.vr + krow + 16 * ks);
         }
     }
+    const Rsrc rq = make_rsrc(a.q + (size_t)bh * a.Nq * D, (uint32_t)((size_t)a.Nq * D * 2));
+    const Rsrc rg = make_rsrc(a.gr + (size_t)bh * a.Nq * D, (uint32_t)((size_t)a.Nq * D * 2));
+    const Rsrc rqt = make_rsrc(a.qt + (size_t)bh * a.nqb * D * kQB, (uint32_t)((size_t)a.nqb * D * kQB * 2));
+    const Rsrc rgt = make_rsrc(a.gt + (size_t)bh * a.nqb * D * kQB, (uint32_t)((size_t)a.nqb * D * kQB * 2));
     const int32_t *off = a.qoff + (size_t)bh * (a.nkb + 1);
     const int32_t *list = a.qlist + (size_t)bh * a.nqb * a.top_k;
     const int p0 = off[j], p1 = off[j + 1];
-    // the next query block's operands are loaded into registers while the current one is
-    // computed, then written to LDS
-    constexpr int CH = kQB * D / 8;          // 16-byte chunks per operand
-    constexpr bool kAhead = NTH == 256;      // other workgroup sizes would need too many registers
-    constexpr int PER = kAhead ? CH / NTH : 1;   // per thread and operand
-    static_assert(!kAhead || CH % NTH == 0, "staging split");
-    u32x4 pre[4][PER];
-    float pre_l = 0.f, pre_d = 0.f;
-    auto load_block = [&](int p) {
+    // fetch query block p into stage st: every wave issues its share of the instructions
+    auto fetch = [&](int p, int st) {
         const int i = min(max(list[p], 0), a.nqb - 1);
         const int q0 = i * a.bq, nqv = min(a.bq, a.Nq - q0);
-        const size_t blk = ((size_t)bh * a.nqb + i) * D;
-#pragma unroll
-        for (int e0 = 0; e0 < PER; ++e0) {
-            const int e = threadIdx.x + NTH * e0;
-            const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
-            const size_t row = (size_t)bh * a.Nq + q0 + min(r, nqv - 1);
-            pre[0][e0] = *reinterpret_cast<const u32x4 *>(a.q + row * D + c8);
-            pre[1][e0] = *reinterpret_cast<const u32x4 *>(a.gr + row * D + c8);
-            const int d = e / (kQB / 8), q8 = (e % (kQB / 8)) * 8;
-            pre[2][e0] = *reinterpret_cast<const u32x4 *>(a.qt + (blk + d) * kQB + q8);
-            pre[3][e0] = *reinterpret_cast<const u32x4 *>(a.gt + (blk + d) * kQB + q8);
+        for (int jj = w; jj < NI; jj += NW) {
+            // rows of D: lane -> row RPI jj + lane / LPR, slot lane % LPR
+            const int r = RPI * jj + lane / LPR, c = (lane % LPR) ^ swz_row<D>(r);
+            const uint32_t ro = (uint32_t)(((q0 + min(r, nqv - 1)) * D + 8 * c) * 2);
+            dma16(rq, reinterpret_cast<unsigned char *>(S[st].q) + jj * 1024, ro);
+            dma16(rg, reinterpret_cast<unsigned char *>(S[st].g) + jj * 1024, ro);
+            // rows of 64 queries: lane -> row 8 jj + lane / 8, slot lane % 8
+            const int rt = 8 * jj + lane / 8, ct = (lane % 8) ^ swz_tr(rt);
+            const uint32_t to = (uint32_t)((((size_t)i * D + rt) * kQB + 8 * ct) * 2);
+            dma16(rqt, reinterpret_cast<unsigned char *>(S[st].qt) + jj * 1024, to);
+            dma16(rgt, reinterpret_cast<unsigned char *>(S[st].gt) + jj * 1024, to);
         }
-        if (threadIdx.x < kQB) {
-            const size_t qi = (size_t)q0 + min((int)threadIdx.x, nqv - 1);
-            pre_l = a.lse[(size_t)bh * a.Nq + qi];
-            pre_d = a.delta[(size_t)bh * a.NqP + qi];
+        for (int e = threadIdx.x; e < kQB; e += NTH) {
+            const size_t qi = (size_t)q0 + min(e, nqv - 1);
+            s_lse[st][e] = a.lse[(size_t)bh * a.Nq + qi];
+            s_delta[st][e] = a.delta[(size_t)bh * a.NqP + qi];
         }
     };
-    if (kAhead && p0 < p1) load_block(p0);
+    if (p0 < p1) fetch(p0, 0);
     for (int p = p0; p < p1; ++p) {
+        const int st = (p - p0) & 1;
         const int i = min(max(list[p], 0), a.nqb - 1);
         const int nqv = min(a.bq, a.Nq - i * a.bq);
-        __syncthreads();   // everyone is done with the previous block
-        if constexpr (kAhead) {
-#pragma unroll
-            for (int e0 = 0; e0 < PER; ++e0) {
-                const int e = threadIdx.x + NTH * e0;
-                const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
-                *reinterpret_cast<u32x4 *>(&L.q[r][c8]) = pre[0][e0];
-                *reinterpret_cast<u32x4 *>(&L.g[r][c8]) = pre[1][e0];
-                const int d = e / (kQB / 8), q8 = (e % (kQB / 8)) * 8;
-                *reinterpret_cast<u32x4 *>(&L.qt[d][q8]) = pre[2][e0];
-                *reinterpret_cast<u32x4 *>(&L.gt[d][q8]) = pre[3][e0];
-            }
-            if (threadIdx.x < kQB) {
-                L.lse[threadIdx.x] = pre_l;
-                L.delta[threadIdx.x] = pre_d;
-            }
-        } else {
-            const int q0 = i * a.bq;
-            const size_t blk = ((size_t)bh * a.nqb + i) * D;
-            for (int e = threadIdx.x; e < CH; e += NTH) {
-                const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
-                const size_t row = (size_t)bh * a.Nq + q0 + min(r, nqv - 1);
-                *reinterpret_cast<u32x4 *>(&L.q[r][c8]) = *reinterpret_cast<const u32x4 *>(a.q + row * D + c8);
-                *reinterpret_cast<u32x4 *>(&L.g[r][c8]) = *reinterpret_cast<const u32x4 *>(a.gr + row * D + c8);
-                const int d = e / (kQB / 8), q8 = (e % (kQB / 8)) * 8;
-                *reinterpret_cast<u32x4 *>(&L.qt[d][q8]) = *reinterpret_cast<const u32x4 *>(a.qt + (blk + d) * kQB + q8);
-                *reinterpret_cast<u32x4 *>(&L.gt[d][q8]) = *reinterpret_cast<const u32x4 *>(a.gt + (blk + d) * kQB + q8);
-            }
-            for (int e = threadIdx.x; e < kQB; e += NTH) {
-                const size_t qi = (size_t)q0 + min(e, nqv - 1);
-                L.lse[e] = a.lse[(size_t)bh * a.Nq + qi];
-                L.delta[e] = a.delta[(size_t)bh * a.NqP + qi];
-            }
-        }
+        // this wave's loads have landed; then everyone's, and everyone is done with block p-1
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         __syncthreads();
-        if (kAhead && p + 1 < p1) load_block(p + 1);
-        if (nvk <= 0 || 32 * qt >= nqv) continue;   // uniform per wave; no barrier before the next
+        if (p + 1 < p1) fetch(p + 1, st ^ 1);
+        if (nvk <= 0 || 32 * qt >= nqv) continue;   // uniform per wave; the barrier is above
+        const uint16_t *Lq = S[st].q, *Lg = S[st].g, *Lqt = S[st].qt, *Lgt = S[st].gt;
         // S and dP for queries 32 qt + (rows in perm32 order), this wave's keys
         const int qr = 32 * qt + perm32(n);
+        const int qsw = swz_row<D>(qr);
         f32x16 s = {}, dp = {};
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-            s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.q[qr][16 * ks + 8 * g])), as_bf16x8(kf[ks]), s);
-            dp = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.g[qr][16 * ks + 8 * g])), as_bf16x8(vf[ks]), dp);
+            const int cs = ((2 * ks + g) ^ qsw) * 8;
+            s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(Lq + qr * D + cs)), as_bf16x8(kf[ks]), s);
+            dp = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(Lg + qr * D + cs)), as_bf16x8(vf[ks]), dp);
         }
         // lane (key n) holds queries 32 qt + 16 g + i
         const int qb0 = 32 * qt + 16 * g;
@@ -637,9 +632,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NKT * NQT, 64 * NKT *
         for (int i2 = 0; i2 < 16; ++i2) {
             const int qq = qb0 + i2;
             const bool ok = kvalid && qq < nqv;
-            const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i2], c_log2, -L.lse[qq])) : 0.f;
+            const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i2], c_log2, -s_lse[st][qq])) : 0.f;
             pv[i2] = pr;
-            gv[i2] = pr * (dp[i2] - L.delta[qq]);
+            gv[i2] = pr * (dp[i2] - s_delta[st][qq]);
         }
         u32x4 pf[2], gfr[2];
 #pragma unroll
@@ -653,17 +648,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NKT * NQT, 64 * NKT *
 #pragma unroll
         for (int ft = 0; ft < D / 32; ++ft) {
             const int dr = 32 * ft + perm32(n);
+            const int dsw = swz_tr(dr);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                accV[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.gt[dr][qb0 + 8 * ks])), as_bf16x8(pf[ks]), accV[ft]);
-                accK[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.qt[dr][qb0 + 8 * ks])), as_bf16x8(gfr[ks]), accK[ft]);
+                const int ct = ((4 * qt + 2 * g + ks) ^ dsw) * 8;
+                accV[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(Lgt + dr * kQB + ct)), as_bf16x8(pf[ks]), accV[ft]);
+                accK[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(Lqt + dr * kQB + ct)), as_bf16x8(gfr[ks]), accK[ft]);
             }
         }
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // no load in flight before the stages are reused
     if constexpr (NQT > 1) {
         // query-tile halves, one key tile at a time: the wave with qt = 1 hands its sums to
         // the wave with qt = 0
-        float *red = reinterpret_cast<float *>(&L);
+        float *red = reinterpret_cast<float *>(&S[0]);
         for (int kk = 0; kk < NKT; ++kk) {
             __syncthreads();
             if (qt == 1 && kt == kk) {

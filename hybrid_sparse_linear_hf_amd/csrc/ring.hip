@@ -11,9 +11,11 @@ constexpr int kTileTok = 64;
 
 // One workgroup per (plane, chunk frame, 64-token tile).  Threads 0..127 transpose V: each
 // owns an 8-token x 8-feature block, loads its 8 rows (16 bytes each), transposes the 8x8
-// block of 16-bit values in registers (byte permutes) and stores 8 rows of V^T.  Threads
-// 128..255 copy the tile's K rows, 8 16-byte vectors each.  Every load of a thread is issued
-// before its first store.
+// block of 16-bit values in registers (byte permutes) and stores 8 rows of V^T.  Lane t of
+// the transposing threads takes token group t % 8 and feature group t / 8, so each store
+// instruction writes eight whole 128-byte V^T row segments (64 tokens) and each load reads
+// 128-byte halves of V rows.  Threads 128..255 copy the tile's K rows, 8 16-byte vectors
+// each.  Every load of a thread is issued before its first store.
 template <int D>
 __global__ __launch_bounds__(256) void ring_append_kernel(hf_append_args a) {
     const int tiles_per_frame = (a.T + kTileTok - 1) / kTileTok;
@@ -28,16 +30,14 @@ __global__ __launch_bounds__(256) void ring_append_kernel(hf_append_args a) {
     const size_t src_row0 = ((size_t)bh * a.C + fc) * a.T + t0;           // in rows of D
     const int tid = threadIdx.x;
     if (tid < 128) {
-        constexpr int kFg = D / 8;                          // feature groups of 8
-        const int fg = tid % kFg, tg = tid / kFg;
-        for (int tgo = tg; tgo < kTileTok / 8; tgo += 128 / kFg) {
-            if (8 * tgo >= ntok) break;
-            const uint16_t *src = a.v_cur + (src_row0 + 8 * tgo) * D + 8 * fg;
+        const int tg = tid % 8, fg = tid / 8;               // token group, feature group
+        if (fg < D / 8 && 8 * tg < ntok) {
+            const uint16_t *src = a.v_cur + (src_row0 + 8 * tg) * D + 8 * fg;
             u32x4 in[8];
 #pragma unroll
             for (int r = 0; r < 8; ++r) in[r] = *reinterpret_cast<const u32x4 *>(src + (size_t)r * D);
-            // out[i] = feature 8fg + i over tokens 8tgo .. 8tgo + 7
-            uint16_t *dst = a.ring_vt + (((size_t)bh * a.W + slot) * D + 8 * fg) * a.T + t0 + 8 * tgo;
+            // out[i] = feature 8fg + i over tokens 8tg .. 8tg + 7
+            uint16_t *dst = a.ring_vt + (((size_t)bh * a.W + slot) * D + 8 * fg) * a.T + t0 + 8 * tg;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;   // high or low halves

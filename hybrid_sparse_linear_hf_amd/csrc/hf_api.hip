@@ -117,7 +117,7 @@ hf_status hip_status(hipError_t e, const char *what) {
 
 // --- enqueue helpers (arguments already validated)
 
-hipError_t enqueue_append(const hf_dims *d, const hf_kv_ring *r, const void *kc, const void *vc, hipStream_t s) {
+hf_append_args append_args(const hf_dims *d, const hf_kv_ring *r, const void *kc, const void *vc) {
     hf_append_args a{};
     a.BH = d->B * d->H;
     a.D = d->D;
@@ -130,12 +130,17 @@ hipError_t enqueue_append(const hf_dims *d, const hf_kv_ring *r, const void *kc,
     a.v_cur = static_cast<const uint16_t *>(vc);
     a.ring_k = static_cast<uint16_t *>(r->k_dev);
     a.ring_vt = static_cast<uint16_t *>(r->vt_dev);
-    return hf_launch_ring_append(a, s);
+    return a;
+}
+
+hipError_t enqueue_append(const hf_dims *d, const hf_kv_ring *r, const void *kc, const void *vc, hipStream_t s) {
+    return hf_launch_ring_append(append_args(d, r, kc, vc), s);
 }
 
 hipError_t enqueue_select(const hf_dims *d, const void *q, const hf_kv_ring *r, int top_k, int32_t *idx,
                           double *scores, void *ws, hipStream_t s, int top_frames = 0, int32_t *fidx = nullptr,
-                          double *fscores = nullptr, const hf_state_args *prep = nullptr) {
+                          double *fscores = nullptr, const hf_state_args *prep = nullptr,
+                          const hf_append_args *app = nullptr) {
     const Geometry g = geometry(d, r);
     const WsLayout L = ws_layout(d);
     hf_select_args a{};
@@ -168,6 +173,12 @@ hipError_t enqueue_select(const hf_dims *d, const void *q, const hf_kv_ring *r, 
     if (prep) {
         a.prep = *prep;
         a.prep_tiles = a.BH * (d->D / 32) * (d->D / 32);
+    }
+    if (app) {
+        a.app = *app;
+        a.app_tiles = hf_append_tiles(*app);
+        a.k_cur = app->k_cur;
+        a.ncom = r->n_committed;
     }
     return hf_launch_block_select(a, s);
 }
@@ -520,12 +531,14 @@ hf_status hf_hybrid_step(const hf_dims *d, const void *q, const void *k_cur, con
     }
     const int64_t evict_tok = (int64_t)evict * d->T;
     hipError_t e = record(events, 0, stream);
-    if (e == hipSuccess && k_cur) e = enqueue_append(d, ring, k_cur, v_cur, stream);
     if (e == hipSuccess) e = record(events, 1, stream);
-    // the readout operands are prepared by extra workgroups of the selection's pool launch
+    // the readout operands and the ring append are extra workgroups of the selection's pool
+    // launch (which then reads the current chunk's keys from k_cur)
     const hf_state_args prep = S ? state_args(d, S, z, true, 0, ws) : hf_state_args{};
+    const hf_append_args app = k_cur ? append_args(d, ring, k_cur, v_cur) : hf_append_args{};
     if (e == hipSuccess)
-        e = enqueue_select(d, q, ring, top_k, idx, nullptr, ws, stream, 0, nullptr, nullptr, S ? &prep : nullptr);
+        e = enqueue_select(d, q, ring, top_k, idx, nullptr, ws, stream, 0, nullptr, nullptr, S ? &prep : nullptr,
+                           k_cur ? &app : nullptr);
     if (e == hipSuccess) e = record(events, 2, stream);
     if (e == hipSuccess) e = record(events, 3, stream);
     if (e == hipSuccess) e = enqueue_attn(d, q, ring, idx, top_k, S != nullptr, eps, out, ws, stream);

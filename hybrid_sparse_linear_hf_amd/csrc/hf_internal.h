@@ -112,6 +112,12 @@ struct hf_state_args {
 };
 hipError_t hf_launch_state(const hf_state_args &a, hipStream_t s);
 
+struct hf_append_args {
+    int BH, D, T, W, head, first_frame, C;
+    const uint16_t *k_cur, *v_cur;
+    uint16_t *ring_k, *ring_vt;
+};
+
 struct hf_select_args {
     int BH, D, T, W, head, Nq, Nk, bq, bk, nqb, nkb, top_k;
     const uint16_t *q, *ring_k;
@@ -128,6 +134,12 @@ struct hf_select_args {
     // readout preparation run as extra workgroups of the pool launch (prep_tiles > 0)
     hf_state_args prep;
     int prep_tiles;
+    // a hybrid step's ring append as extra workgroups after those (app_tiles > 0); the keys
+    // of the current chunk (logical frames >= ncom) are then read from k_cur, not the ring
+    hf_append_args app;
+    int app_tiles;
+    const uint16_t *k_cur;     // null: every key from the ring
+    int ncom;
     int32_t *fidx;             // may be null: kept frames [BH][nqb][top_frames], ascending
     double *fscores;           // may be null: frame scores [BH][nqb][nfr]
 };
@@ -198,9 +210,5 @@ hipError_t hf_launch_absorb_partial(const hf_absorb_args &a, hipStream_t s);
 hf_status hf_cag_schedule_impl(int32_t n, const int32_t *nkb, double s_base, double s_target, double s_max,
                                int32_t *top_k, double *sparsity, double *beta_out);
 
-struct hf_append_args {
-    int BH, D, T, W, head, first_frame, C;
-    const uint16_t *k_cur, *v_cur;
-    uint16_t *ring_k, *ring_vt;
-};
 hipError_t hf_launch_ring_append(const hf_append_args &a, hipStream_t s);
+int hf_append_tiles(const hf_append_args &a);   // workgroups of an append

@@ -24,6 +24,7 @@
 // The hierarchical variant adds frame_pool_kernel, runs the score kernel a second time
 // over (query block, frame) pairs, and lets the top-k wave select the frames before the
 // blocks.
+#include "append_tile.h"
 #include "state_tile.h"
 
 namespace hf {
@@ -31,9 +32,11 @@ namespace {
 
 __device__ __forceinline__ double bf16_to_f64(uint32_t bits) { return (double)__uint_as_float(bits << 16); }
 
-// Row pointer of window key j (logical order) in the ring.
+// Row pointer of window key j (logical order): in the ring, or, for the current chunk's
+// frames when the step appends them in the same launch, in the chunk input.
 __device__ __forceinline__ const uint16_t *key_row(const hf_select_args &a, int bh, int j) {
     const int f = j / a.T, t = j - f * a.T;
+    if (a.k_cur && f >= a.ncom) return a.k_cur + ((size_t)bh * a.Nq + (size_t)(f - a.ncom) * a.T + t) * a.D;
     int slot = a.head + f;
     if (slot >= a.W) slot -= a.W;
     return a.ring_k + (((size_t)bh * a.W + slot) * a.T + t) * a.D;
@@ -47,8 +50,11 @@ __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
 
     const int per_plane = a.nqb + a.nkb;
     if ((int)blockIdx.x >= a.BH * per_plane) {
-        // readout operands of a hybrid step (independent of the selection)
-        state_tile<D>(a.prep, (int)blockIdx.x - a.BH * per_plane, reinterpret_cast<float(*)[33]>(&red[0][0]));
+        const int x = (int)blockIdx.x - a.BH * per_plane;
+        if (x < a.prep_tiles)   // readout operands of a hybrid step (independent of the selection)
+            state_tile<D>(a.prep, x, reinterpret_cast<float(*)[33]>(&red[0][0]));
+        else                    // the step's ring append
+            append_tile<D>(a.app, x - a.prep_tiles);
         return;
     }
     const int bh = blockIdx.x / per_plane;
@@ -417,7 +423,7 @@ static void launch_score_topk(int kpl, const hf_select_args &a, double scale, hi
 }
 
 hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s) {
-    const dim3 grid_pool((unsigned)(a.BH * (a.nqb + a.nkb) + a.prep_tiles));
+    const dim3 grid_pool((unsigned)(a.BH * (a.nqb + a.nkb) + a.prep_tiles + a.app_tiles));
     const int ti_n = (a.nqb + hf::kTile - 1) / hf::kTile, tj_n = (a.nkb + hf::kTile - 1) / hf::kTile;
     const dim3 grid_score((unsigned)(a.BH * ti_n * tj_n));
     const dim3 grid_topk((unsigned)((a.BH * a.nqb + 3) / 4));

@@ -108,11 +108,12 @@ typedef struct {
 #define HF_STEP_COMMIT 1u
 
 /* Optional timing hooks for hf_hybrid_step: any non-NULL event is recorded on the
- * step's stream at that point: ev[0] begin, ev[1] after the ring append, ev[2] and ev[3]
- * after block selection (whose first launch also prepares the readout operands, so the
- * two mark the same point), ev[4] after the attention kernel, ev[5] after the absorb of
- * the evicted frames and the state update (the end of the step).  Events must have been created by the caller with
- * hipEventCreate. */
+ * step's stream at that point: ev[0] and ev[1] at the beginning (the ring append runs as
+ * extra workgroups of the selection's first launch, so it has no interval of its own),
+ * ev[2] and ev[3] after block selection (whose first launch also prepares the readout
+ * operands, so the two mark the same point), ev[4] after the attention kernel, ev[5]
+ * after the absorb of the evicted frames and the state update (the end of the step).
+ * Events must have been created by the caller with hipEventCreate. */
 typedef struct {
     hipEvent_t ev[6];
 } hf_step_events;

@@ -53,6 +53,7 @@ def lib():
         L.hfo_block_scores.argtypes = [_i64, _i64, _i64, _i64, _D, _D, _D]
         L.hfo_select.argtypes = [_i64, _i64, _i64, _i64, _D, _I32]
         L.hfo_sparse_attn.argtypes = [_i64] * 7 + [_D, _D, _D, _I32, _I64, _i64, _D]
+        L.hfo_sparse_attn_rope.argtypes = [_i64] * 10 + [ctypes.c_double, _D, _D, _D, _I32, _I64, _i64, _D]
         L.hfo_linear_readout.argtypes = [_i64, _i64, _i64, _i64, _D, _D, _D, ctypes.c_double, _I64, _i64, _D]
         L.hfo_absorb.argtypes = [_i64, _i64, _i64, _D, _D, _D, _D]
         L.hfo_hybrid_step.argtypes = ([_i64] * 7 + [ctypes.c_double, _D, _D, _D, _D, _D, _I64, _i64, _I32, _D, _D])
@@ -137,6 +138,23 @@ def sparse_attn(Q, K, V, idx, bq, bk, blocks=None, out=None):
     return out
 
 
+def sparse_attn_rope(Q, K, V, idx, bq, bk, T, temporal_dims, cap, base=10000.0, blocks=None, out=None):
+    """Sparse attention with the relative temporal rotary embedding (query rotated by the
+    clamped frame offset to each key's frame; see hfo_sparse_attn_rope)."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    B, H, Nq, D = Q.shape
+    Nk = K.shape[2]
+    if Nq % T or Nk % T or temporal_dims % 2 or not 0 <= temporal_dims <= D or cap < 0:
+        raise ValueError("need whole frames, an even temporal_dims <= D and cap >= 0")
+    k = idx.shape[-1]
+    out = np.zeros_like(Q) if out is None else out
+    bl, nb = _blocks(blocks)
+    lib().hfo_sparse_attn_rope(B * H, Nq, Nk, D, bq, bk, k, T, temporal_dims, cap, base, _p(Q), _p(K), _p(V),
+                               _p(idx, _I32), _p(bl, _I64), nb, _p(out))
+    return out
+
+
 def linear_readout(Q, S, z, bq=64, eps=1e-6, blocks=None, out=None):
     Q, S, z = _f64(Q), _f64(S), _f64(z)
     B, H, Nq, D = Q.shape
@@ -171,6 +189,17 @@ def hybrid_step(Q, K, V, S, z, bq, bk, k, eps=1e-6, blocks=None, want_scores=Fal
     lib().hfo_hybrid_step(B * H, Nq, Nk, D, bq, bk, k, eps, _p(Q), _p(K), _p(V), _p(S), _p(z), _p(bl, _I64), nb,
                           _p(idx, _I32), _p(sc), _p(out))
     return out, idx, sc
+
+
+def hybrid_step_rope(Q, K, V, S, z, bq, bk, k, T, temporal_dims, cap, base=10000.0, eps=1e-6, blocks=None):
+    """The step with the rotary embedding on the softmax branch: selection and readout
+    from the raw features (as hybrid_step), sparse part by sparse_attn_rope.
+    -> (out, idx)."""
+    Q = _f64(Q)
+    _, idx, _ = hybrid_step(Q, K, V, S, z, bq, bk, k, eps=eps, blocks=[(0, 0)])
+    out = sparse_attn_rope(Q, K, V, idx, bq, bk, T, temporal_dims, cap, base, blocks=blocks)
+    lin = linear_readout(Q, S, z, bq, eps, blocks=blocks)
+    return out + lin, idx
 
 
 def cag_schedule(n_kb, s_base, s_target, s_max):

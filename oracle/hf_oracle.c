@@ -115,21 +115,60 @@ void hfo_select(int64_t BH, int64_t nqb, int64_t nkb, int64_t k, const double *s
 /* ---------------------------------------------------------------- sparse attention */
 
 /* One query block: softmax over the union of its kept key blocks. */
+/* Relative temporal rotary embedding of the softmax branch ([HF-de] §2.C "Relative
+ * RoPE", [HF-pt] §2.B.2): the temporal position index is capped and taken as an offset
+ * between frames.  Reading: a query of window frame fq scored against a key of window
+ * frame fk sees the query rotated by the offset delta = clamp(fq - fk, -cap, cap), so
+ * the score is the standard rotary one whenever |fq - fk| <= cap.  Feature pair
+ * (2i, 2i+1), i < DT/2, turns by the angle delta * base^(-2i/DT); features DT.. D-1
+ * (the spatial part) are left as they are. */
+typedef struct {
+    int64_t T;       /* tokens per frame: window frame of key u is u / T */
+    int64_t DT;      /* rotated (temporal) features; 0 = no rotation */
+    int64_t cap;
+    double base;
+} rope_cfg;
+
+static void rope_rotate_query(const double *q, int64_t D, const rope_cfg *rp, int64_t delta, double *qr) {
+    for (int64_t d = 0; d < D; ++d) qr[d] = q[d];
+    for (int64_t i = 0; i < rp->DT / 2; ++i) {
+        const double angle = (double)delta * pow(rp->base, -2.0 * (double)i / (double)rp->DT);
+        const double c = cos(angle), s = sin(angle);
+        qr[2 * i] = q[2 * i] * c - q[2 * i + 1] * s;
+        qr[2 * i + 1] = q[2 * i] * s + q[2 * i + 1] * c;
+    }
+}
+
+/* One query block.  `rp` NULL: plain scores q . k; else q rotated per key frame as above
+ * (query t of the chunk lies in window frame (Nk - Nq + t) / T).  `qr` holds D doubles. */
 static void sparse_block(int64_t Nq, int64_t Nk, int64_t D, int64_t bq, int64_t bk, int64_t k,
                          const double *Q, const double *K, const double *V, const int32_t *sel,
-                         int64_t i, double *out, double *logit) {
+                         int64_t i, const rope_cfg *rp, double *out, double *logit, double *qr) {
     const double scale = 1.0 / sqrt((double)D);
     const int64_t t0 = i * bq, t1 = min64(t0 + bq, Nq);
     for (int64_t t = t0; t < t1; ++t) {
         const double *q = Q + t * D;
+        int64_t qr_frame = -1;   /* key frame the rotated query in qr was made for */
         /* logits over the kept keys, in kept-block order */
         int64_t n = 0;
         double m = -INFINITY;
         for (int64_t r = 0; r < k; ++r) {
             const int64_t u0 = (int64_t)sel[r] * bk, u1 = min64(u0 + bk, Nk);
             for (int64_t u = u0; u < u1; ++u) {
+                const double *qu = q;
+                if (rp) {
+                    const int64_t fk = u / rp->T;
+                    if (fk != qr_frame) {
+                        int64_t delta = (Nk - Nq + t) / rp->T - fk;
+                        if (delta > rp->cap) delta = rp->cap;
+                        if (delta < -rp->cap) delta = -rp->cap;
+                        rope_rotate_query(q, D, rp, delta, qr);
+                        qr_frame = fk;
+                    }
+                    qu = qr;
+                }
                 double dot = 0.0;
-                for (int64_t d = 0; d < D; ++d) dot += q[d] * K[u * D + d];
+                for (int64_t d = 0; d < D; ++d) dot += qu[d] * K[u * D + d];
                 logit[n] = dot * scale;
                 if (logit[n] > m) m = logit[n];
                 ++n;
@@ -154,23 +193,39 @@ static void sparse_block(int64_t Nq, int64_t Nk, int64_t D, int64_t bq, int64_t 
     }
 }
 
-void hfo_sparse_attn(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int64_t bq, int64_t bk,
-                     int64_t k, const double *Q, const double *K, const double *V,
-                     const int32_t *idx, const int64_t *blocks, int64_t n_blocks, double *out) {
+static void sparse_attn(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int64_t bq, int64_t bk,
+                        int64_t k, const rope_cfg *rp, const double *Q, const double *K, const double *V,
+                        const int32_t *idx, const int64_t *blocks, int64_t n_blocks, double *out) {
     const int64_t nqb = ceil_div(Nq, bq);
     const int64_t total = blocks ? n_blocks : BH * nqb;
 #pragma omp parallel
     {
         double *logit = (double *)malloc((size_t)(k * bk) * sizeof(double));
+        double *qr = (double *)malloc((size_t)D * sizeof(double));
 #pragma omp for schedule(dynamic, 1)
         for (int64_t w = 0; w < total; ++w) {
             const int64_t p = blocks ? blocks[2 * w] : w / nqb;
             const int64_t i = blocks ? blocks[2 * w + 1] : w % nqb;
             sparse_block(Nq, Nk, D, bq, bk, k, Q + p * Nq * D, K + p * Nk * D, V + p * Nk * D,
-                         idx + (p * nqb + i) * k, i, out + p * Nq * D, logit);
+                         idx + (p * nqb + i) * k, i, rp, out + p * Nq * D, logit, qr);
         }
+        free(qr);
         free(logit);
     }
+}
+
+void hfo_sparse_attn(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int64_t bq, int64_t bk,
+                     int64_t k, const double *Q, const double *K, const double *V,
+                     const int32_t *idx, const int64_t *blocks, int64_t n_blocks, double *out) {
+    sparse_attn(BH, Nq, Nk, D, bq, bk, k, NULL, Q, K, V, idx, blocks, n_blocks, out);
+}
+
+void hfo_sparse_attn_rope(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int64_t bq, int64_t bk,
+                          int64_t k, int64_t T, int64_t DT, int64_t cap, double base, const double *Q,
+                          const double *K, const double *V, const int32_t *idx, const int64_t *blocks,
+                          int64_t n_blocks, double *out) {
+    const rope_cfg rp = {T, DT, cap, base};
+    sparse_attn(BH, Nq, Nk, D, bq, bk, k, &rp, Q, K, V, idx, blocks, n_blocks, out);
 }
 
 /* ---------------------------------------------------------------- linear branch */

@@ -74,6 +74,20 @@ void hfo_sparse_attn(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int64_t bq, 
                      int64_t k, const double *Q, const double *K, const double *V,
                      const int32_t *idx, const int64_t *blocks, int64_t n_blocks, double *out);
 
+/* hfo_sparse_attn with the relative temporal rotary embedding ([HF-de] §2.C "Relative
+ * RoPE", [HF-pt] §2.B.2: the temporal RoPE index is capped and expressed as a relative
+ * offset).  Reading: with T tokens per frame, key u lies in window frame fk = u / T and
+ * query t of the chunk in frame fq = (Nk - Nq + t) / T (the chunk is the window's last Nq
+ * rows); the score of (t, u) is (R(delta) q_t) . k_u / sqrt(D) with
+ * delta = clamp(fq - fk, -cap, cap), where R(delta) turns feature pair (2i, 2i+1),
+ * i < DT/2, by the angle delta * base^(-2i/DT) and leaves features DT..D-1 unchanged.
+ * For |fq - fk| <= cap this equals the usual rotary score (R(a_t) q_t) . (R(a_u) k_u)
+ * with absolute positions a.  The rest is as hfo_sparse_attn. */
+void hfo_sparse_attn_rope(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int64_t bq, int64_t bk,
+                          int64_t k, int64_t T, int64_t DT, int64_t cap, double base, const double *Q,
+                          const double *K, const double *V, const int32_t *idx, const int64_t *blocks,
+                          int64_t n_blocks, double *out);
+
 /* Linear temporal readout ([HF-de] §2.A "Lineare Zeit-Aufmerksamkeit", [HF-abs]):
  * out[t][c] = sum_a phi(Q[t][a]) S[a][c] / (sum_a phi(Q[t][a]) z[a] + eps).
  * Same `blocks` convention as hfo_sparse_attn (query blocks of size bq). */

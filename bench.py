@@ -142,6 +142,9 @@ def main():
     ap.add_argument("--top-frames", type=int, default=6, help="hier: frames kept per query block")
     ap.add_argument("--top-k", type=int, default=128, help="hier: key blocks kept per query block")
     ap.add_argument("--stream", type=int, default=16, help="cag: chunks in the stream")
+    ap.add_argument("--rope", type=str, default=None, metavar="DT,CAP",
+                    help="step: time the step with the relative temporal rotary embedding (rotated features DT, "
+                         "offset cap CAP frames, base 10000)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -164,6 +167,12 @@ def main():
     if args.mode == "bwd":
         return bench_bwd(args)
     cfg = synth.LAYER_832x480
+    rope = None
+    if args.rope:
+        dt, cap = (int(x) for x in args.rope.split(","))
+        rope = hf.Rope(dt, cap, 10000.0)
+        import dataclasses
+        cfg = dataclasses.replace(cfg, name=f"{cfg.name}_rope{dt}_cap{cap}")
     if args.keep is not None or args.window is not None:
         import dataclasses
         cfg = dataclasses.replace(cfg, keep=args.keep if args.keep is not None else cfg.keep,
@@ -214,7 +223,11 @@ def main():
         q, k, v = chunks[i % len(chunks)]
         idx = idx_bufs[timed_slot] if timed_slot is not None else idx_warm
         events = evs.get(timed_slot) if timed_slot is not None else None
-        hf.hf_hybrid_step(g, q, k, v, ring, top_k, hf.HF_STEP_COMMIT, S, z, idx, out, ws, events=events)
+        if rope is None:
+            hf.hf_hybrid_step(g, q, k, v, ring, top_k, hf.HF_STEP_COMMIT, S, z, idx, out, ws, events=events)
+        else:
+            hf.hf_hybrid_step_rope(g, q, k, v, ring, top_k, hf.HF_STEP_COMMIT, S, z, idx, out, ws, rope,
+                                   events=events)
 
     for i in range(args.warmup):
         step(i)
@@ -274,7 +287,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "traffic_source": traffic_src,
-                     "kernel": "sparse_attn_kernel<128, 2>",
+                     "kernel": f"sparse_attn_kernel<128, 2, {rope.temporal_dims // 16 if rope else 0}>",
                      "flops_per_launch": round(flops.mean()), "launch_us": round(t_attn * 1e6, 2)},
         "phases_us": {"select_append_prep": round(t_sel * 1e6, 2),
                       "readout_prep": round(t_prep * 1e6, 2), "sparse_attn_readout": round(t_attn * 1e6, 2),

@@ -42,6 +42,12 @@ class StepEvents(ctypes.Structure):
     _fields_ = [("ev", ctypes.c_void_p * 6)]
 
 
+class Rope(ctypes.Structure):
+    """Relative temporal rotary embedding (hf_rope): the first `temporal_dims` features of
+    each head turned by the frame offset clamped to +-cap, frequencies base^(-2i/temporal_dims)."""
+    _fields_ = [("temporal_dims", ctypes.c_int32), ("cap", ctypes.c_int32), ("base", ctypes.c_float)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 
@@ -75,10 +81,14 @@ def lib():
         L.hf_hybrid_attn_backward.argtypes = [pd, _P, pr, _P, i32, _P, _P, f32, _P, _P, _P, _P, _P, _P, _P, _P,
                                               _P, sz, _P]
         L.hf_linear_absorb_backward.argtypes = [pd, _P, _P, i64, _P, _P, _P, _P, _P, sz, _P]
+        prope = ctypes.POINTER(Rope)
+        L.hf_sparse_window_attn_rope.argtypes = [pd, _P, pr, _P, i32, _P, _P, f32, prope, _P, _P, sz, _P]
+        L.hf_hybrid_step_rope.argtypes = [pd, _P, _P, _P, pr, i32, u32, _P, _P, f32, prope, _P, _P, _P, sz,
+                                          ctypes.POINTER(StepEvents), _P]
         for fn in ("hf_workspace_size", "hf_ring_append", "hf_block_select", "hf_sparse_window_attn",
                    "hf_linear_absorb", "hf_hybrid_step", "hf_cag_schedule", "hf_block_select_hier",
                    "hf_sparse_window_attn_lse", "hf_backward_workspace_size", "hf_hybrid_attn_backward",
-                   "hf_linear_absorb_backward"):
+                   "hf_linear_absorb_backward", "hf_sparse_window_attn_rope", "hf_hybrid_step_rope"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -210,6 +220,34 @@ def hf_hybrid_step(g: Geometry, q, k_cur, v_cur, ring: Ring, top_k: int, flags: 
                                 int(top_k), int(flags), _ptr(S), _ptr(z), float(eps), _ptr(idx), _ptr(out), _ptr(ws),
                                 ws.numel() if ws is not None else 0, ctypes.byref(ev) if ev is not None else None,
                                 _stream(stream)))
+
+
+def _events(events):
+    if events is None:
+        return None
+    ev = StepEvents()
+    for i, e in enumerate(events):
+        ev.ev[i] = e
+    return ctypes.byref(ev)
+
+
+def hf_sparse_window_attn_rope(g: Geometry, q, ring: Ring, idx, top_k: int, S, z, out, ws, rope: Rope, eps=1e-6,
+                               stream=None) -> None:
+    _check("hf_sparse_window_attn_rope",
+           lib().hf_sparse_window_attn_rope(ctypes.byref(g.dims()), _ptr(q), ctypes.byref(ring.desc), _ptr(idx),
+                                            int(top_k), _ptr(S), _ptr(z), float(eps),
+                                            ctypes.byref(rope) if rope is not None else None, _ptr(out), _ptr(ws),
+                                            ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def hf_hybrid_step_rope(g: Geometry, q, k_cur, v_cur, ring: Ring, top_k: int, flags: int, S, z, idx, out, ws,
+                        rope: Rope, eps=1e-6, events=None, stream=None) -> None:
+    _check("hf_hybrid_step_rope",
+           lib().hf_hybrid_step_rope(ctypes.byref(g.dims()), _ptr(q), _ptr(k_cur), _ptr(v_cur),
+                                     ctypes.byref(ring.desc), int(top_k), int(flags), _ptr(S), _ptr(z), float(eps),
+                                     ctypes.byref(rope) if rope is not None else None, _ptr(idx), _ptr(out),
+                                     _ptr(ws), ws.numel() if ws is not None else 0, _events(events),
+                                     _stream(stream)))
 
 
 def hf_cag_schedule(n_kb, s_base: float, s_target: float, s_max: float):

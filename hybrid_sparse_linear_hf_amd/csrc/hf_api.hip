@@ -206,7 +206,8 @@ hipError_t enqueue_state(const hf_dims *d, float *S, float *z, bool readout, int
 
 // Attention (+ readout from the prepared S^T / z copy when `readout`).
 hipError_t enqueue_attn(const hf_dims *d, const void *q, const hf_kv_ring *r, const int32_t *idx, int top_k,
-                        bool readout, float eps, float *out, void *ws, hipStream_t s, float *lse = nullptr) {
+                        bool readout, float eps, float *out, void *ws, hipStream_t s, float *lse = nullptr,
+                        const hf_rope *rope = nullptr) {
     const Geometry g = geometry(d, r);
     const WsLayout L = ws_layout(d);
     hf_attn_args a{};
@@ -231,6 +232,12 @@ hipError_t enqueue_attn(const hf_dims *d, const void *q, const hf_kv_ring *r, co
     a.eps = eps;
     a.out = out;
     a.lse = lse;
+    a.ncom = r->n_committed;
+    if (rope) {
+        a.rope_dt = rope->temporal_dims;
+        a.rope_cap = rope->cap;
+        a.rope_c1 = (float)(-2.0 * std::log2((double)rope->base) / rope->temporal_dims);
+    }
     return hf_launch_sparse_attn(a, s);
 }
 
@@ -360,9 +367,18 @@ hf_status hf_block_select_hier(const hf_dims *d, const void *q, const hf_kv_ring
     return st == HF_OK ? ok() : st;
 }
 
+static hf_status check_rope(const hf_dims *d, const hf_rope *r) {
+    if (!r) return fail(HF_ERR_NULL, "rope is NULL");
+    const int dt = r->temporal_dims;
+    if (dt != 16 && dt != 32) return fail(HF_ERR_SHAPE, "rope temporal_dims=%d: need 16 or 32", dt);
+    if (r->cap < 0 || r->cap > 1024) return fail(HF_ERR_SHAPE, "rope cap=%d outside [0, 1024]", r->cap);
+    if (!(r->base > 1.f) || !std::isfinite(r->base)) return fail(HF_ERR_SHAPE, "rope base must be finite and > 1");
+    return HF_OK;
+}
+
 static hf_status sparse_window_attn(const hf_dims *d, const void *q, const hf_kv_ring *ring, const int32_t *idx,
                                     int32_t top_k, const float *S, const float *z, float eps, float *out, float *lse,
-                                    void *ws, size_t ws_bytes, hipStream_t stream) {
+                                    void *ws, size_t ws_bytes, hipStream_t stream, const hf_rope *rope = nullptr) {
     hf_status st = check_dims(d);
     if (st == HF_OK) st = check_ring(d, ring);
     if (st != HF_OK) return st;
@@ -374,7 +390,7 @@ static hf_status sparse_window_attn(const hf_dims *d, const void *q, const hf_kv
     st = check_ws(d, ws, ws_bytes);
     if (st != HF_OK) return st;
     hipError_t e = S ? enqueue_state(d, const_cast<float *>(S), const_cast<float *>(z), true, 0, ws, stream) : hipSuccess;
-    if (e == hipSuccess) e = enqueue_attn(d, q, ring, idx, top_k, S != nullptr, eps, out, ws, stream, lse);
+    if (e == hipSuccess) e = enqueue_attn(d, q, ring, idx, top_k, S != nullptr, eps, out, ws, stream, lse, rope);
     st = hip_status(e, "sparse attention launch");
     return st == HF_OK ? ok() : st;
 }
@@ -390,6 +406,15 @@ hf_status hf_sparse_window_attn_lse(const hf_dims *d, const void *q, const hf_kv
                                     void *ws, size_t ws_bytes, hipStream_t stream) {
     if (!lse) return fail(HF_ERR_NULL, "lse is NULL");
     return sparse_window_attn(d, q, ring, idx, top_k, S, z, eps, out, lse, ws, ws_bytes, stream);
+}
+
+hf_status hf_sparse_window_attn_rope(const hf_dims *d, const void *q, const hf_kv_ring *ring, const int32_t *idx,
+                                     int32_t top_k, const float *S, const float *z, float eps, const hf_rope *rope,
+                                     float *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+    hf_status st = check_dims(d);
+    if (st == HF_OK) st = check_rope(d, rope);
+    if (st != HF_OK) return st;
+    return sparse_window_attn(d, q, ring, idx, top_k, S, z, eps, out, nullptr, ws, ws_bytes, stream, rope);
 }
 
 hf_status hf_backward_workspace_size(const hf_dims *d, int32_t top_k, size_t *bytes) {
@@ -499,9 +524,10 @@ hf_status hf_linear_absorb(const hf_dims *d, const void *k_ev, const void *v_ev,
     return st == HF_OK ? ok() : st;
 }
 
-hf_status hf_hybrid_step(const hf_dims *d, const void *q, const void *k_cur, const void *v_cur, hf_kv_ring *ring,
-                         int32_t top_k, uint32_t flags, float *S, float *z, float eps, int32_t *idx, float *out,
-                         void *ws, size_t ws_bytes, const hf_step_events *events, hipStream_t stream) {
+static hf_status hybrid_step(const hf_dims *d, const void *q, const void *k_cur, const void *v_cur, hf_kv_ring *ring,
+                             int32_t top_k, uint32_t flags, float *S, float *z, float eps, const hf_rope *rope,
+                             int32_t *idx, float *out, void *ws, size_t ws_bytes, const hf_step_events *events,
+                             hipStream_t stream) {
     hf_status st = check_dims(d);
     if (st == HF_OK) st = check_ring(d, ring);
     if (st != HF_OK) return st;
@@ -541,7 +567,7 @@ hf_status hf_hybrid_step(const hf_dims *d, const void *q, const void *k_cur, con
                            k_cur ? &app : nullptr);
     if (e == hipSuccess) e = record(events, 2, stream);
     if (e == hipSuccess) e = record(events, 3, stream);
-    if (e == hipSuccess) e = enqueue_attn(d, q, ring, idx, top_k, S != nullptr, eps, out, ws, stream);
+    if (e == hipSuccess) e = enqueue_attn(d, q, ring, idx, top_k, S != nullptr, eps, out, ws, stream, nullptr, rope);
     if (e == hipSuccess) e = record(events, 4, stream);
     if (e == hipSuccess && evict_tok > 0) e = enqueue_absorb_partial(d, nullptr, nullptr, evict_tok, ring, ws, stream);
     if (e == hipSuccess && evict_tok > 0) e = enqueue_state(d, S, z, false, evict_tok, ws, stream);
@@ -549,6 +575,24 @@ hf_status hf_hybrid_step(const hf_dims *d, const void *q, const void *k_cur, con
     if (e != hipSuccess) return hip_status(e, "hybrid step launch");
     *ring = next;
     return ok();
+}
+
+hf_status hf_hybrid_step(const hf_dims *d, const void *q, const void *k_cur, const void *v_cur, hf_kv_ring *ring,
+                         int32_t top_k, uint32_t flags, float *S, float *z, float eps, int32_t *idx, float *out,
+                         void *ws, size_t ws_bytes, const hf_step_events *events, hipStream_t stream) {
+    return hybrid_step(d, q, k_cur, v_cur, ring, top_k, flags, S, z, eps, nullptr, idx, out, ws, ws_bytes, events,
+                       stream);
+}
+
+hf_status hf_hybrid_step_rope(const hf_dims *d, const void *q, const void *k_cur, const void *v_cur, hf_kv_ring *ring,
+                              int32_t top_k, uint32_t flags, float *S, float *z, float eps, const hf_rope *rope,
+                              int32_t *idx, float *out, void *ws, size_t ws_bytes, const hf_step_events *events,
+                              hipStream_t stream) {
+    hf_status st = check_dims(d);
+    if (st == HF_OK) st = check_rope(d, rope);
+    if (st != HF_OK) return st;
+    return hybrid_step(d, q, k_cur, v_cur, ring, top_k, flags, S, z, eps, rope, idx, out, ws, ws_bytes, events,
+                       stream);
 }
 
 }  // extern "C"

@@ -156,6 +156,10 @@ struct hf_attn_args {
     float eps;
     float *out;
     float *lse;                // null, or [BH][Nq]: log2 of each query's softmax sum (base-2 logits)
+    // relative temporal rotation: rope_dt rotated features (0 = off, 16 or 32),
+    // offsets clamped to +-rope_cap, theta_i = 2^(i * rope_c1); ncom = window frames before the chunk
+    int rope_dt, rope_cap, ncom;
+    float rope_c1;
 };
 hipError_t hf_launch_sparse_attn(const hf_attn_args &a, hipStream_t s);
 

@@ -22,6 +22,14 @@
 //     the first product in the register layout the second consumes.  Key rows are read in
 //     the order perm32(m), so each lane holds 16 consecutive keys of its query column, and
 //     value rows (features) likewise, so each lane holds 16 consecutive output features.
+//   * Relative temporal rotary embedding (instances KT > 0; [HF-de] §2.C "Relative RoPE",
+//     [HF-pt] §2.B.2): a query scored against a key of window frame f uses its first DT
+//     features turned pairwise by the clamped frame offset clamp(fq - f, -cap, cap).
+//     The kept list is ascending, so the key frame changes at most once per frame of the
+//     window: the turned fragments (bf16, like every matrix-core operand) are rebuilt in
+//     registers only then.  A subtile that spans several frames runs the temporal
+//     products once per frame on top of a shared spatial product and picks each key's
+//     row.  The readout uses the raw query.
 //   * Softmax in base 2 with the 1/sqrt(D) scale folded into one FMA.  Full subtiles use a
 //     FIXED reference per query row -- the exact row maximum of the first subtile -- so
 //     nothing is ever rescaled; should a later score exceed it by so much that the row sum
@@ -130,8 +138,9 @@ __device__ __forceinline__ float softmax_online(f32x16 s, int nval, int g, float
 
 constexpr int kWaitVm0 = 0x0F70;   // s_waitcnt vmcnt(0), other counters untouched
 
-// D = head dim; NW = waves per workgroup = 32-query tiles per query block (2 when bq == 64).
-template <int D, int NW>
+// D = head dim; NW = waves per workgroup = 32-query tiles per query block (2 when bq == 64);
+// KT = temporal fragments of the relative rotation (DT / 16; 0: no rotation).
+template <int D, int NW, int KT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2))) void
 sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, int lsh) {
     constexpr int LPR = D / 8;            // 16-byte chunks per K row
@@ -169,6 +178,39 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
         for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const u32x4 *>(qp + 16 * ks);
     }
     __syncthreads();
+
+    // rotation: this lane's query frame (window order) and the KT temporal fragments of Q^T
+    // turned for key frame qt_f
+    constexpr bool ROPE = KT > 0;
+    int fq = 0, qt_f = -1;
+    u32x4 qt[ROPE ? KT : 1];
+    if constexpr (ROPE) {
+        const int row = q0 + 32 * w + n;
+        fq = a.ncom + fast_div(row < qend ? row : q0, magicT, a.T);
+    }
+    // feature pair 8ks + 4g + j of the fragments turns by clamp(fq - f, -cap, cap) *
+    // theta_i, theta_i = base^(-2i/DT) = 2^(i * rope_c1)
+    auto set_qt = [&](int f) __attribute__((always_inline)) {
+        if (f == qt_f) return;
+        qt_f = f;
+        const float off = (float)min(max(fq - f, -a.rope_cap), a.rope_cap);
+        // |angle| = 2^(i * rope_c1 + log2|off|): formed from the offset (0 for off = 0), so
+        // that no per-pair frequency stays live in registers between frame changes
+        const float lg = __log2f(fabsf(off));
+#pragma unroll
+        for (int ks = 0; ks < KT; ++ks) {
+            const uint32_t wv[4] = {qf[ks].x, qf[ks].y, qf[ks].z, qf[ks].w};
+            uint32_t o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float ang = copysignf(__builtin_amdgcn_exp2f(__builtin_fmaf((float)(8 * ks + 4 * g + j), a.rope_c1, lg)), off);
+                const float sn = __sinf(ang), cs = __cosf(ang);
+                const float x0 = bf16_lo_to_f32(wv[j]), x1 = bf16_hi_to_f32(wv[j]);
+                o[j] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+            }
+            qt[ks] = u32x4{o[0], o[1], o[2], o[3]};
+        }
+    };
 
     const size_t plane = (size_t)bh * a.W * a.T * D;
     const uint32_t plane_bytes = (uint32_t)((size_t)a.W * a.T * D * 2);
@@ -315,6 +357,35 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) acc[ft] = mfma32(as_bf16x8(vfr[ft][ks]), as_bf16x8(pf[ks]), acc[ft]);
     };
+    // Rotated scores of the nk keys from window key k0 on (keys past nk are masked later).
+    // The spatial fragments do not depend on the frame.  The temporal products run once
+    // per frame of the subtile (more than one only where a frame boundary falls inside it)
+    // into the same accumulator, each with the K fragments of the other frames' keys
+    // zeroed: this lane supplies the A row of key k0 + perm32(n).
+    auto qk_rope = [&](const unsigned char *kb, int k0, int nk) __attribute__((always_inline)) -> f32x16 {
+        const int fa = fast_div(k0, magicT, T), fb = fast_div(k0 + nk - 1, magicT, T);
+        const int myf = fast_div(k0 + rk_row, magicT, T);
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        set_qt(fa);
+        u32x4 kfr[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) kfr[ks] = *reinterpret_cast<const u32x4 *>(kb + koff[ks]);
+        f32x16 s = {};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            if (ks < KT) s = mfma32(as_bf16x8(myf == fa ? kfr[ks] : zero), as_bf16x8(qt[ks < KT ? ks : 0]), s);
+            else s = mfma32(as_bf16x8(kfr[ks]), as_bf16x8(qf[ks]), s);
+        }
+        for (int f = fa + 1; f <= fb; ++f) {     // K fragments read again: nothing stays live
+            set_qt(f);
+#pragma unroll
+            for (int ks = 0; ks < KT; ++ks) {
+                const u32x4 kk = *reinterpret_cast<const u32x4 *>(kb + koff[ks]);
+                s = mfma32(as_bf16x8(myf == f ? kk : zero), as_bf16x8(qt[ks]), s);
+            }
+        }
+        return s;
+    };
     auto qk_tile = [&](int st) -> f32x16 { return qk_from(kst + st * KBYTES); };
     auto pv_tile = [&](int st, const u32x4 (&pf)[2]) { pv_from(vst + st * VBYTES, pf); };
     auto rescale = [&](float alpha) {
@@ -347,7 +418,9 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
         dma_full_v(g0, 0);
         dma_full_k(g1, 1);
         stage_ready();
-        f32x16 s_a = qk_tile(0), s_b;
+        f32x16 s_a, s_b;
+        if constexpr (ROPE) s_a = qk_rope(kst, key0_of(0), kSub);
+        else s_a = qk_tile(0);
         sm.m = tile_max_log2(s_a, c_log2);
         const float moff = -sm.m;
         __syncthreads();            // K stage 0 is refilled in step 0
@@ -358,7 +431,8 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
             dma_full_k(g2, P);
             dma_full_v(g1, 1 - P);
             g1 = g2;
-            s_nxt = qk_from(kst + (1 - P) * KBYTES);
+            if constexpr (ROPE) s_nxt = qk_rope(kst + (1 - P) * KBYTES, key0_of(min(u + 1, last)), kSub);
+            else s_nxt = qk_from(kst + (1 - P) * KBYTES);
             u32x4 pf[2];
             softmax_fixed(s_cur, c_log2, moff, sm.l, pf);
             pv_from(vst + P * VBYTES, pf);
@@ -393,8 +467,11 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
         for (int u = ustart; u < nsubt; ++u) {
             stage_ready();
             if (u + 1 < nsubt) dma_any(key0_of(u + 1), (u + 1) & 1);
-            const int nv = nval_of(key0_of(u));
-            const f32x16 s = qk_tile(u & 1);
+            const int k0 = key0_of(u);
+            const int nv = nval_of(k0);
+            f32x16 s;
+            if constexpr (ROPE) s = qk_rope(kst + (u & 1) * KBYTES, k0, nv);
+            else s = qk_tile(u & 1);
             u32x4 pf[2];
             const float al = softmax_online(s, nv, g, c_log2, sm, pf);
             rescale(al);
@@ -472,16 +549,23 @@ hipError_t hf_launch_sparse_attn(const hf_attn_args &a, hipStream_t s) {
     const int lsh = a.bk >= 128 ? 2 : (a.bk >= 64 ? 1 : 0);     // 32-key subtiles per key block = 2^lsh
     const int nw = a.bq > 32 ? 2 : 1;
     const size_t dyn = 2 * (size_t)128 * a.D + (size_t)a.top_k * sizeof(int32_t) + nw * sizeof(int);   // 2 K + 2 V stages
-    if (a.D == 64) {
-        if (nw == 2)
-            hipLaunchKernelGGL((hf::sparse_attn_kernel<64, 2>), grid, dim3(128), dyn, s, a, magicT, c_log2, per_xcd, lsh);
-        else
-            hipLaunchKernelGGL((hf::sparse_attn_kernel<64, 1>), grid, dim3(64), dyn, s, a, magicT, c_log2, per_xcd, lsh);
-    } else {
-        if (nw == 2)
-            hipLaunchKernelGGL((hf::sparse_attn_kernel<128, 2>), grid, dim3(128), dyn, s, a, magicT, c_log2, per_xcd, lsh);
-        else
-            hipLaunchKernelGGL((hf::sparse_attn_kernel<128, 1>), grid, dim3(64), dyn, s, a, magicT, c_log2, per_xcd, lsh);
-    }
+    auto go = [&](auto kern, int threads) {
+        hipLaunchKernelGGL(kern, grid, dim3(threads), dyn, s, a, magicT, c_log2, per_xcd, lsh);
+    };
+    // one instance per (D, waves, temporal fragments of the rotation)
+    auto pick = [&](auto dc, auto nwc) {
+        constexpr int Dc = decltype(dc)::value, NWc = decltype(nwc)::value;
+        switch (a.rope_dt / 16) {
+        case 1: go(hf::sparse_attn_kernel<Dc, NWc, 1>, 64 * NWc); break;
+        case 2: go(hf::sparse_attn_kernel<Dc, NWc, 2>, 64 * NWc); break;
+        default: go(hf::sparse_attn_kernel<Dc, NWc, 0>, 64 * NWc); break;
+        }
+    };
+    using I64 = std::integral_constant<int, 64>;
+    using I128 = std::integral_constant<int, 128>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    if (a.D == 64) nw == 2 ? pick(I64{}, I2{}) : pick(I64{}, I1{});
+    else nw == 2 ? pick(I128{}, I2{}) : pick(I128{}, I1{});
     return hipGetLastError();
 }

@@ -242,6 +242,35 @@ hf_status hf_hybrid_step(const hf_dims *d, const void *q_dev, const void *k_cur_
                          float eps, int32_t *idx_dev, float *out_dev, void *workspace_dev,
                          size_t workspace_bytes, const hf_step_events *events, hipStream_t stream);
 
+/* ---- Relative temporal rotary embedding of the softmax branch ([HF-de] §2.C "Relative
+ * RoPE", [HF-pt] §2.B.2: the temporal RoPE index is capped and expressed as an offset
+ * between positions).  With it, the score of query t (window frame fq) and key u (window
+ * frame fk) is (R(delta) q_t) . k_u / sqrt(D) with delta = clamp(fq - fk, -cap, cap), where
+ * R(delta) turns feature pair (2i, 2i+1), i < temporal_dims / 2, by the angle
+ * delta * base^(-2i / temporal_dims) and leaves the other features as they are.  Within the
+ * cap this is the usual rotary score with absolute frame positions.  Block selection and
+ * the linear branch use the raw q and k.  The turned query enters the matrix cores in
+ * bf16.  Forward only: the backward entry points below do not take it. */
+typedef struct {
+    int32_t temporal_dims;   /* 16 or 32: the rotated leading features */
+    int32_t cap;             /* largest |frame offset| the rotation sees, 0 .. 1024 */
+    float base;              /* frequency base, finite and > 1 */
+} hf_rope;
+
+/* hf_sparse_window_attn with the rotary embedding; rope must not be NULL (HF_ERR_NULL);
+ * fields outside the ranges above give HF_ERR_SHAPE. */
+hf_status hf_sparse_window_attn_rope(const hf_dims *d, const void *q_dev, const hf_kv_ring *ring,
+                                     const int32_t *idx_dev, int32_t top_k, const float *S_dev,
+                                     const float *z_dev, float eps, const hf_rope *rope, float *out_dev,
+                                     void *workspace_dev, size_t workspace_bytes, hipStream_t stream);
+
+/* hf_hybrid_step with the rotary embedding in its attention (step 4); rope as above. */
+hf_status hf_hybrid_step_rope(const hf_dims *d, const void *q_dev, const void *k_cur_dev, const void *v_cur_dev,
+                              hf_kv_ring *ring, int32_t top_k, uint32_t flags, float *S_dev, float *z_dev,
+                              float eps, const hf_rope *rope, int32_t *idx_dev, float *out_dev,
+                              void *workspace_dev, size_t workspace_bytes, const hf_step_events *events,
+                              hipStream_t stream);
+
 /* ---- Backward of the step (training).  The block selection is held fixed: it is
  * piecewise constant in the inputs, so no gradient flows through it.  Gradients of a loss
  * L given dL/dout; for query t with kept keys u and softmax weights P_tu ([HF-de] §2.A,

@@ -25,7 +25,7 @@ def test_header_declares_the_entry_points():
     for s in ("hf_block_select", "hf_sparse_window_attn", "hf_linear_absorb", "hf_hybrid_step", "hf_ring_append",
               "hf_workspace_size", "hf_last_error", "hf_status_str", "hf_abi_version", "hf_cag_schedule",
               "hf_sparse_window_attn_lse", "hf_backward_workspace_size", "hf_hybrid_attn_backward",
-              "hf_linear_absorb_backward"):
+              "hf_linear_absorb_backward", "hf_sparse_window_attn_rope", "hf_hybrid_step_rope"):
         assert s in syms
 
 
@@ -213,3 +213,30 @@ def test_absorb_backward_and_lse_validation():
     r = ring_desc()
     assert L.hf_sparse_window_attn_lse(d, FAKE, ctypes.byref(r), FAKE, 37, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, None,
                                        FAKE, ws, None) == 1
+
+
+def test_rope_validation():
+    L = _lib.lib()
+    g = geom()
+    d, r = ctypes.byref(g.dims()), ring_desc()
+    ws = hf.workspace_size(g)
+
+    def attn(rope):
+        return L.hf_sparse_window_attn_rope(d, FAKE, ctypes.byref(r), FAKE, 37, None, None, ctypes.c_float(1e-6),
+                                            ctypes.byref(rope) if rope is not None else None, FAKE, FAKE, ws, None)
+
+    def step(rope):
+        return L.hf_hybrid_step_rope(d, FAKE, None, None, ctypes.byref(r), 37, 0, None, None, ctypes.c_float(1e-6),
+                                     ctypes.byref(rope) if rope is not None else None, FAKE, FAKE, FAKE, ws, None,
+                                     None)
+
+    for call in (attn, step):
+        assert call(None) == 1                                   # HF_ERR_NULL
+        for bad in (hf.Rope(48, 3, 1e4), hf.Rope(0, 3, 1e4), hf.Rope(8, 3, 1e4), hf.Rope(32, -1, 1e4),
+                    hf.Rope(32, 1025, 1e4), hf.Rope(32, 3, 1.0), hf.Rope(32, 3, float("inf")),
+                    hf.Rope(32, 3, float("nan"))):
+            assert call(bad) == 2, (bad.temporal_dims, bad.cap, bad.base)   # HF_ERR_SHAPE
+            assert "rope" in last_error()
+    # a valid rotation still runs the usual checks first-come: a bad top_k is rejected
+    assert L.hf_sparse_window_attn_rope(d, FAKE, ctypes.byref(r), FAKE, 0, None, None, ctypes.c_float(1e-6),
+                                        ctypes.byref(hf.Rope(32, 3, 1e4)), FAKE, FAKE, ws, None) == 2

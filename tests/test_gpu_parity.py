@@ -179,6 +179,8 @@ EDGE = [
     (1, 1, 128, 64, 2, 2, 64, 64, 0, 1),      # W == C
     (1, 2, 128, 136, 1, 4, 64, 64, 3, 2),     # odd number of query blocks (last pair has one), 32-key last block
     (1, 1, 64, 48, 4, 6, 64, 64, 2, 4),       # D=64, odd number of query blocks, frames of 48 tokens
+    (1, 1, 64, 512, 1, 48, 64, 16, 47, 1536), # the largest window: 1536 key blocks, all kept
+    (1, 2, 128, 512, 1, 48, 64, 16, 47, 700), # 1536 key blocks, 700 kept
 ]
 
 

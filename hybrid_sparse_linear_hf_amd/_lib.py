@@ -66,6 +66,7 @@ def lib():
         L.hf_status_str.argtypes = [ctypes.c_int]
         L.hf_last_error.restype = ctypes.c_char_p
         L.hf_workspace_size.argtypes = [pd, i32, ctypes.POINTER(sz)]
+        L.hf_ring_init.argtypes = [pd, _P, _P, pr]
         L.hf_ring_append.argtypes = [pd, pr, _P, _P, _P]
         L.hf_block_select.argtypes = [pd, _P, pr, i32, _P, _P, _P, sz, _P]
         L.hf_sparse_window_attn.argtypes = [pd, _P, pr, _P, i32, _P, _P, f32, _P, _P, sz, _P]
@@ -85,7 +86,7 @@ def lib():
         L.hf_sparse_window_attn_rope.argtypes = [pd, _P, pr, _P, i32, _P, _P, f32, prope, _P, _P, sz, _P]
         L.hf_hybrid_step_rope.argtypes = [pd, _P, _P, _P, pr, i32, u32, _P, _P, f32, prope, _P, _P, _P, sz,
                                           ctypes.POINTER(StepEvents), _P]
-        for fn in ("hf_workspace_size", "hf_ring_append", "hf_block_select", "hf_sparse_window_attn",
+        for fn in ("hf_workspace_size", "hf_ring_init", "hf_ring_append", "hf_block_select", "hf_sparse_window_attn",
                    "hf_linear_absorb", "hf_hybrid_step", "hf_cag_schedule", "hf_block_select_hier",
                    "hf_sparse_window_attn_lse", "hf_backward_workspace_size", "hf_hybrid_attn_backward",
                    "hf_linear_absorb_backward", "hf_sparse_window_attn_rope", "hf_hybrid_step_rope"):
@@ -148,7 +149,9 @@ class Ring:
         self.g = g
         self.k = torch.zeros((g.B, g.H, g.W, g.T, g.D), dtype=torch.bfloat16, device=device)
         self.vt = torch.zeros((g.B, g.H, g.W, g.D, g.T), dtype=torch.bfloat16, device=device)
-        self.desc = KVRing(self.k.data_ptr(), self.vt.data_ptr(), 0, 0)
+        self.desc = KVRing()
+        _check("hf_ring_init", lib().hf_ring_init(ctypes.byref(g.dims()), self.k.data_ptr(), self.vt.data_ptr(),
+                                                  ctypes.byref(self.desc)))
 
     @property
     def head(self) -> int:

@@ -314,6 +314,14 @@ hf_status hf_workspace_size(const hf_dims *d, int32_t top_k, size_t *bytes) {
     return ok();
 }
 
+hf_status hf_ring_init(const hf_dims *d, void *k_store, void *vt_store, hf_kv_ring *out) {
+    const hf_status st = check_dims(d);
+    if (st != HF_OK) return st;
+    if (!k_store || !vt_store || !out) return fail(HF_ERR_NULL, "k_store/vt_store/out is NULL");
+    *out = hf_kv_ring{k_store, vt_store, 0, 0};
+    return ok();
+}
+
 hf_status hf_ring_append(const hf_dims *d, const hf_kv_ring *ring, const void *k_cur, const void *v_cur,
                          hipStream_t stream) {
     hf_status st = check_dims(d);

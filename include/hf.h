@@ -128,6 +128,12 @@ const char *hf_last_error(void);
  * entry point; it holds transient per-call data only and needs no initialisation. */
 hf_status hf_workspace_size(const hf_dims *d, int32_t top_k, size_t *bytes);
 
+/* Describe an empty ring over caller-owned storage (host only, no GPU work): checks the
+ * dims, then sets *out = {k_store_dev, vt_store_dev, head 0, n_committed 0}.  The storage
+ * must hold B*H*W*T*D bf16 values each (layouts above); its contents are not read until
+ * frames are committed.  Errors: those of the dims, HF_ERR_NULL for a NULL pointer. */
+hf_status hf_ring_init(const hf_dims *d, void *k_store_dev, void *vt_store_dev, hf_kv_ring *out);
+
 /* Copy the current chunk into the ring: k_cur_dev, v_cur_dev are bf16 [B][H][C*T][D]
  * (row-major).  Frame c of the chunk goes to logical frame n_committed + c; values are
  * written transposed (see hf_kv_ring).  The descriptor is not changed. */

@@ -23,6 +23,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ("hf_block_select", "hf_sparse_window_attn", "hf_linear_absorb", "hf_hybrid_step", "hf_ring_append",
+              "hf_ring_init",
               "hf_workspace_size", "hf_last_error", "hf_status_str", "hf_abi_version", "hf_cag_schedule",
               "hf_sparse_window_attn_lse", "hf_backward_workspace_size", "hf_hybrid_attn_backward",
               "hf_linear_absorb_backward", "hf_sparse_window_attn_rope", "hf_hybrid_step_rope"):
@@ -240,3 +241,14 @@ def test_rope_validation():
     # a valid rotation still runs the usual checks first-come: a bad top_k is rejected
     assert L.hf_sparse_window_attn_rope(d, FAKE, ctypes.byref(r), FAKE, 0, None, None, ctypes.c_float(1e-6),
                                         ctypes.byref(hf.Rope(32, 3, 1e4)), FAKE, FAKE, ws, None) == 2
+
+
+def test_ring_init():
+    L = _lib.lib()
+    g = geom()
+    r = _lib.KVRing(None, None, 5, 2)
+    assert L.hf_ring_init(ctypes.byref(g.dims()), FAKE, FAKE + 64, ctypes.byref(r)) == 0
+    assert (r.k_dev, r.vt_dev, r.head, r.n_committed) == (FAKE, FAKE + 64, 0, 0)
+    assert L.hf_ring_init(ctypes.byref(g.dims()), None, FAKE, ctypes.byref(r)) == 1
+    assert L.hf_ring_init(ctypes.byref(g.dims()), FAKE, FAKE, None) == 1
+    assert L.hf_ring_init(ctypes.byref(geom(D=96).dims()), FAKE, FAKE, ctypes.byref(r)) == 3

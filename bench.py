@@ -191,13 +191,15 @@ def main():
                     help="after timing, run a plain 256 MiB elementwise copy (for counter calibration)")
     ap.add_argument("--keep", type=float, default=None, help="override the kept fraction of key blocks")
     ap.add_argument("--window", type=int, default=None, help="override the window length in frames")
-    ap.add_argument("--mode", choices=("step", "hier", "cag", "bwd"), default="step",
+    ap.add_argument("--mode", choices=("step", "hier", "cag", "bwd", "stack"), default="step",
                     help="step: the hybrid step (default); hier: hierarchical selection + attention on a 21-frame "
                          "window; cag: a stream from an empty window under the chunk-aware keep schedule; "
-                         "bwd: training forward (with lse) and backward of the attention + readout")
+                         "bwd: training forward (with lse) and backward of the attention + readout; stack: a "
+                         "30-layer x 4-stream chunk captured in a HIP graph")
     ap.add_argument("--top-frames", type=int, default=6, help="hier: frames kept per query block")
     ap.add_argument("--top-k", type=int, default=128, help="hier: key blocks kept per query block")
     ap.add_argument("--stream", type=int, default=16, help="cag: chunks in the stream")
+    ap.add_argument("--layers", type=int, default=30, help="stack: layers in the stack")
     ap.add_argument("--rope", type=str, default=None, metavar="DT,CAP",
                     help="step: time the step with the relative temporal rotary embedding (rotated features DT, "
                          "offset cap CAP frames, base 10000)")
@@ -222,6 +224,8 @@ def main():
         return bench_cag(args)
     if args.mode == "bwd":
         return bench_bwd(args)
+    if args.mode == "stack":
+        return bench_stack(args)
     cfg = synth.LAYER_832x480
     rope = None
     if args.rope:
@@ -515,6 +519,96 @@ def bench_bwd(args):
            "backward_us": round(tb * 1e6, 2),
            "backward_algorithmic_flops": round(2.5 * fl),
            "backward_frac_of_bf16_peak": round(2.5 * fl / tb / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    print(json.dumps(res), flush=True)
+
+
+def bench_stack(args):
+    """The attention of a 30-layer stack for 4 batched streams at the 832x480 layer shapes
+    (each layer its own ring, state and seeded bf16 Q/K/V, N(0,1)*0.5): one chunk = 30
+    hf_hybrid_step calls with commit, captured once in a HIP graph and replayed.  Reports
+    the chunk latency and the implied latent frames per second (4 streams x 3 frames per
+    chunk), beside the same 30 calls launched eagerly."""
+    import torch
+    import hybrid_sparse_linear_hf_amd as hf
+    from hybrid_sparse_linear_hf_amd import synth
+
+    base = synth.LAYER_832x480
+    n_layers, B = args.layers, 4
+    g = hf.Geometry(B, base.H, base.D, base.T, base.C, base.W, base.bq, base.bk)
+    hist = g.W - g.C
+    top_k = base.top_k()
+    dev = torch.device("cuda:0")
+    ws = hf.new_workspace(g)
+    out = torch.empty((B, g.H, g.Nq, g.D), dtype=torch.float32, device=dev)
+    layers = []
+    for layer in range(n_layers):
+        gen = torch.Generator(device=dev).manual_seed(1000 + layer)
+
+        def rnd(n):
+            return (torch.randn((B, g.H, n, g.D), generator=gen, device=dev) * 0.5).to(torch.bfloat16)
+
+        ring = hf.Ring(g)
+        hf.hf_ring_append(g, ring, rnd(g.Nq), rnd(g.Nq))      # the window's committed history (W - C = C frames)
+        ring.set_state(0, hist)
+        S = torch.zeros((B, g.H, g.D, g.D), dtype=torch.float32, device=dev)
+        z = torch.zeros((B, g.H, g.D), dtype=torch.float32, device=dev)
+        hf.hf_linear_absorb(g, rnd(g.Nq), rnd(g.Nq), g.Nq, S, z, ws)
+        idx = torch.empty((B, g.H, g.n_qb, top_k), dtype=torch.int32, device=dev)
+        layers.append((ring, S, z, idx, rnd(g.Nq), rnd(g.Nq), rnd(g.Nq)))
+    torch.cuda.synchronize()
+    descs = [(L[0].head, L[0].n_committed) for L in layers]
+
+    def chunk():
+        for ring, S, z, idx, q, k, v in layers:
+            hf.hf_hybrid_step(g, q, k, v, ring, top_k, hf.HF_STEP_COMMIT, S, z, idx, out, ws)
+
+    def reset():     # every step starts from the same window position (replays repeat it)
+        for (ring, *_), d in zip(layers, descs):
+            ring.set_state(*d)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # eager
+    for _ in range(2):
+        reset()
+        chunk()
+    torch.cuda.synchronize()
+    eager = []
+    for _ in range(args.steps):
+        reset()
+        e0.record()
+        chunk()
+        e1.record()
+        torch.cuda.synchronize()
+        eager.append(e0.elapsed_time(e1))
+    # graph
+    reset()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chunk()
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    fl = sum(kept_flops(L[3].cpu().numpy(), g.Nq, (hist + g.C) * g.T, g.bq, g.bk, g.D) for L in layers)
+    res = {"metric": "30-layer x 4-stream attention stack: chunk latency (832x480 layer shapes, HIP graph, 1 GPU)",
+           "value": round(ms, 3), "unit": "ms per chunk", "n_gpus": 1, "steps": args.steps, "warmup": 2,
+           "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic (seeded N(0,1)*0.5 bf16 per layer and stream)",
+           "config": {"workload": f"stack_{n_layers}x4_832x480", "layers": n_layers, "streams": B, "H": g.H, "D": g.D,
+                      "tokens_per_frame": g.T, "chunk_frames": g.C, "window_frames": g.W, "block": [g.bq, g.bk],
+                      "top_k": top_k},
+           "latent_frames_per_s": round(B * g.C / (ms * 1e-3), 1),
+           "kept_tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+           "eager_ms_per_chunk": round(float(np.median(eager)), 3),
+           "wall_ms_per_chunk": round(wall * 1e3 / args.steps, 3),
+           "note": "attention only (no projections, MLP or VAE); not comparable with end-to-end generation rates"}
     print(json.dumps(res), flush=True)
 
 

@@ -191,11 +191,12 @@ def main():
                     help="after timing, run a plain 256 MiB elementwise copy (for counter calibration)")
     ap.add_argument("--keep", type=float, default=None, help="override the kept fraction of key blocks")
     ap.add_argument("--window", type=int, default=None, help="override the window length in frames")
-    ap.add_argument("--mode", choices=("step", "hier", "cag", "bwd", "stack"), default="step",
+    ap.add_argument("--mode", choices=("step", "hier", "cag", "bwd", "stack", "sweep"), default="step",
                     help="step: the hybrid step (default); hier: hierarchical selection + attention on a 21-frame "
                          "window; cag: a stream from an empty window under the chunk-aware keep schedule; "
                          "bwd: training forward (with lse) and backward of the attention + readout; stack: a "
-                         "30-layer x 4-stream chunk captured in a HIP graph")
+                         "30-layer x 4-stream chunk captured in a HIP graph; sweep: keep ratios on a 21-frame window "
+                         "against dense")
     ap.add_argument("--top-frames", type=int, default=6, help="hier: frames kept per query block")
     ap.add_argument("--top-k", type=int, default=128, help="hier: key blocks kept per query block")
     ap.add_argument("--stream", type=int, default=16, help="cag: chunks in the stream")
@@ -226,6 +227,8 @@ def main():
         return bench_bwd(args)
     if args.mode == "stack":
         return bench_stack(args)
+    if args.mode == "sweep":
+        return bench_sweep(args)
     cfg = synth.LAYER_832x480
     rope = None
     if args.rope:
@@ -419,6 +422,65 @@ def _field_ring(cfg, hf, synth, torch, dev):
     q = to_dev(synth.field_frames(synth.Q_ID, ev + cfg.W - cfg.C, cfg.C, **kw))
     torch.cuda.synchronize()
     return g, ring, ws, S, z, q
+
+
+def bench_sweep(args):
+    """The 832x480 shapes with a 21-frame window (32760 keys, 512 key blocks), keep ratio
+    swept over 100 / 50 / 25 / 12.5 %: per ratio, block selection followed by the sparse
+    attention with the readout, against the dense window attention (every block kept, no
+    selection).  The crossover is the keep ratio where selection + sparse stops beating
+    dense."""
+    import torch
+    import hybrid_sparse_linear_hf_amd as hf
+    from hybrid_sparse_linear_hf_amd import synth
+
+    cfg = synth.LAYER_832x480_W21
+    dev = torch.device("cuda:0")
+    g, ring, ws, S, z, q = _field_ring(cfg, hf, synth, torch, dev)
+    nkb = g.n_kb(cfg.W - cfg.C)
+    out = torch.empty((cfg.B, cfg.H, cfg.Nq, cfg.D), dtype=torch.float32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+    def timed(fn_sel, fn_attn):
+        sel, att = [], []
+        for it in range(args.warmup + args.steps):
+            ev[0].record()
+            fn_sel()
+            ev[1].record()
+            fn_attn()
+            ev[2].record()
+            torch.cuda.synchronize()
+            if it >= args.warmup:
+                sel.append(ev[0].elapsed_time(ev[1]))
+                att.append(ev[1].elapsed_time(ev[2]))
+        return float(np.median(sel)) * 1e3, float(np.median(att)) * 1e3
+
+    dense_idx = torch.arange(nkb, dtype=torch.int32, device=dev).expand(cfg.B, cfg.H, g.n_qb, nkb).contiguous()
+    _, t_dense = timed(lambda: None, lambda: hf.hf_sparse_window_attn(g, q, ring, dense_idx, nkb, S, z, out, ws))
+    f_dense = kept_flops(dense_idx.cpu().numpy(), cfg.Nq, cfg.Nk, cfg.bq, cfg.bk, cfg.D)
+    rows = []
+    for keep in (1.0, 0.5, 0.25, 0.125):
+        k = max(1, -(-int(round(keep * 1000)) * nkb // 1000))
+        idx = torch.empty((cfg.B, cfg.H, g.n_qb, k), dtype=torch.int32, device=dev)
+        t_sel, t_att = timed(lambda: hf.hf_block_select(g, q, ring, k, idx, None, ws),
+                             lambda: hf.hf_sparse_window_attn(g, q, ring, idx, k, S, z, out, ws))
+        fl = kept_flops(idx.cpu().numpy(), cfg.Nq, cfg.Nk, cfg.bq, cfg.bk, cfg.D)
+        rows.append({"keep": keep, "top_k": k, "select_us": round(t_sel, 2), "attention_us": round(t_att, 2),
+                     "total_us": round(t_sel + t_att, 2), "attention_tflops": round(fl / (t_att * 1e-6) / 1e12, 1),
+                     "speedup_vs_dense": round(t_dense / (t_sel + t_att), 3)})
+    beats = [r["keep"] for r in rows if r["speedup_vs_dense"] > 1.0]
+    res = {"metric": "keep-ratio sweep on a 21-frame window: select + sparse attention vs dense (832x480 shape, 1 GPU)",
+           "value": rows[2]["total_us"], "unit": "us at keep 25 %", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(rows[2]["total_us"] * 1e-3, 4), "higher_is_better": False,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded rank-8 spatial field + noise per head, bf16)",
+           "config": {"workload": cfg.name, "H": cfg.H, "D": cfg.D, "tokens_per_frame": cfg.T, "chunk_frames": cfg.C,
+                      "window_frames": cfg.W, "block": [cfg.bq, cfg.bk], "n_kb": nkb},
+           "dense_us": round(t_dense, 2), "dense_tflops": round(f_dense / (t_dense * 1e-6) / 1e12, 1),
+           "sweep": rows,
+           "crossover": ("selection + sparse beats dense at every keep ratio below 100 %" if set(beats) >= {0.5, 0.25, 0.125}
+                         else f"selection + sparse beats dense at keep ratios {beats}")}
+    print(json.dumps(res), flush=True)
 
 
 def bench_hier(args):

@@ -30,7 +30,7 @@
 namespace hf {
 namespace {
 
-constexpr int kQB = 64;   // query-block copies (Q^T, dO^T) are padded to 64 queries
+constexpr int kQB = 64;   // query-block stages hold 64 rows (a short block repeats its last query)
 
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
 
@@ -119,41 +119,22 @@ __device__ void mat_copies(const float *M, uint16_t *mb, uint16_t *mtb, int tile
     }
 }
 
-// One workgroup per (plane, query block): dO rows in bf16, the block's Q^T and dO^T (64
-// columns, zero past the block); extra workgroups copy S into bf16 rows and transposed rows.
+// One workgroup per (plane, query block): dO rows in bf16; extra workgroups copy S into
+// bf16 rows and transposed rows.
 template <int D>
 __global__ __launch_bounds__(256) void prep_queries_kernel(hf_bwd_args a) {
-    __shared__ __align__(16) uint16_t tq[kQB][D + 8];
-    __shared__ __align__(16) uint16_t tg[kQB][D + 8];
+    __shared__ float t[32][33];
     const int nblk = a.BH * a.nqb;
     if ((int)blockIdx.x >= nblk) {
-        mat_copies<D>(a.S, a.sb, a.stb, (int)blockIdx.x - nblk, reinterpret_cast<float(*)[33]>(&tq[0][0]));
+        mat_copies<D>(a.S, a.sb, a.stb, (int)blockIdx.x - nblk, t);
         return;
     }
     const int bh = blockIdx.x / a.nqb, qb = blockIdx.x % a.nqb;
     const int q0 = qb * a.bq, nq = min(a.bq, a.Nq - q0);
-    for (int e = threadIdx.x; e < kQB * D / 8; e += 256) {
+    for (int e = threadIdx.x; e < nq * D / 8; e += 256) {
         const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
-        u32x4 qv = {0, 0, 0, 0}, gv = {0, 0, 0, 0};
-        if (r < nq) {
-            const size_t row = (size_t)bh * a.Nq + q0 + r;
-            qv = *reinterpret_cast<const u32x4 *>(a.q + row * D + c8);
-            gv = f32x8_to_bf16(a.dout + row * D + c8);
-            *reinterpret_cast<u32x4 *>(a.gr + row * D + c8) = gv;
-        }
-        *reinterpret_cast<u32x4 *>(&tq[r][c8]) = qv;
-        *reinterpret_cast<u32x4 *>(&tg[r][c8]) = gv;
-    }
-    __syncthreads();
-    const size_t blk = ((size_t)bh * a.nqb + qb) * D;
-    for (int e = threadIdx.x; e < D * (kQB / 8); e += 256) {
-        const int d = e / (kQB / 8), q8 = (e % (kQB / 8)) * 8;
-        const u32x4 oq = {pack2(tq[q8][d], tq[q8 + 1][d]), pack2(tq[q8 + 2][d], tq[q8 + 3][d]),
-                          pack2(tq[q8 + 4][d], tq[q8 + 5][d]), pack2(tq[q8 + 6][d], tq[q8 + 7][d])};
-        const u32x4 og = {pack2(tg[q8][d], tg[q8 + 1][d]), pack2(tg[q8 + 2][d], tg[q8 + 3][d]),
-                          pack2(tg[q8 + 4][d], tg[q8 + 5][d]), pack2(tg[q8 + 6][d], tg[q8 + 7][d])};
-        *reinterpret_cast<u32x4 *>(a.qt + (blk + d) * kQB + q8) = oq;
-        *reinterpret_cast<u32x4 *>(a.gt + (blk + d) * kQB + q8) = og;
+        const size_t row = (size_t)bh * a.Nq + q0 + r;
+        *reinterpret_cast<u32x4 *>(a.gr + row * D + c8) = f32x8_to_bf16(a.dout + row * D + c8);
     }
 }
 
@@ -524,37 +505,75 @@ __device__ __forceinline__ void dma16(Rsrc r, unsigned char *lds, uint32_t voff)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 16, (int)voff, 0, 0, 0);
 }
 
-// 16-byte chunk swizzles of the staged tiles, so that the fragment reads (rows 32 x + perm32(n)
-// of 16 lanes, one chunk) hit distinct LDS bank groups: rows of D/8 chunks (Q, dO) and rows of
-// 8 chunks (Q^T, dO^T, 64 queries each).
+// 16-byte chunk swizzle of the staged Q and dO rows (D/8 chunks each), so that the fragment
+// reads (rows 32 x + perm32(n) of 16 lanes, one chunk) hit distinct LDS bank groups, and the
+// transposing reads (four consecutive rows per chunk column) land on different chunks.
 template <int D>
 __device__ __forceinline__ int swz_row(int r) {
     if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | ((r >> 1) & 8);
     else return ((r >> 1) & 3) | ((r >> 2) & 4);
 }
-__device__ __forceinline__ int swz_tr(int r) { return ((r >> 1) & 3) | ((r >> 2) & 4); }
 
-// One query block's operands, staged unpadded with swizzled chunks by direct-to-LDS loads.
+// One query block's operands, staged unpadded with swizzled chunks by direct-to-LDS loads:
+// Q and dO rows (rows of D, chunk c of row r at slot c ^ swz_row(r)), and the block's lse
+// and Delta values.
 template <int D>
 struct QBlockStage {
-    uint16_t q[kQB * D], g[kQB * D];          // rows of D, chunk c of row r at slot c ^ swz_row(r)
-    uint16_t qt[D * kQB], gt[D * kQB];        // rows of 64 queries, chunk c at slot c ^ swz_tr(r)
+    uint16_t q[kQB * D], g[kQB * D];
 };
+constexpr int kStagesKV = 4;   // query-block stages: up to three blocks ahead are in flight
+
+// Transposing LDS read (gfx950): within each 16-lane group, lane i receives element i % 4 of
+// the 4-element vectors that lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12 of the group point
+// at (one per returned element).
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p) {
+    const v4s16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s16 *)(const_cast<uint16_t *>(p)));
+    return u32x2{(uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16),
+                 (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16)};
+}
+
+// Matrix-core A fragment of X^T from the staged row-major tile X (64 rows of D, swizzled):
+// lane (n, g) receives features 32 ft + perm32(n) of queries q0 .. q0 + 7 (q0 for its lane
+// half), as two transposing reads of four queries.  In a 16-lane group (n = 16 G + i) lane s
+// points at query q0 + 4 h + s / 4, features 32 ft + 8 G + 16 ((s % 4) & 1) + 4 ((s % 4) >> 1)
+// .. + 3, so that lane i receives feature 32 ft + perm32(16 G + i).
+template <int D>
+__device__ __forceinline__ u32x4 xt_frag(const uint16_t *X, int q0, int ft, int lane) {
+    const int s = lane & 15, t = s & 3, G = (lane >> 4) & 1;
+    const int d = 32 * ft + 8 * G + 16 * (t & 1) + 4 * (t >> 1);
+    u32x2 h[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int r = q0 + 4 * hh + (s >> 2);
+        h[hh] = ds_read_tr16(X + r * D + (((d >> 3) ^ swz_row<D>(r)) << 3) + (d & 7));
+    }
+    return u32x4{h[0].x, h[0].y, h[1].x, h[1].y};
+}
 
 // One workgroup per key block: wave (kt, qt) owns the block's 32-key tile kt and the
 // 32-query tile qt of every query block that kept it (NKT key tiles x NQT query tiles).
-// Each query block's operands reach LDS once for all the waves, by direct-to-LDS loads into
-// one of two stages, fetched while the previous block is computed; the two query-tile
-// halves of each key tile are added at the end.
+// Each query block's Q and dO rows reach LDS once for all the waves by direct-to-LDS loads,
+// kStagesKV - 1 blocks ahead of their use; the products that contract over queries read
+// their Q^T / dO^T operands from the same rows with transposing LDS reads.  The two
+// query-tile halves of each key tile are added at the end.
 template <int D, int NKT, int NQT>
 __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, float c_log2, float inv_sqrt_d) {
     constexpr int NW = NKT * NQT, NTH = 64 * NW;
     constexpr int LPR = D / 8, RPI = 64 / LPR;    // chunks per row, rows per load instruction
     constexpr int NI = kQB * D * 2 / 1024;         // load instructions per operand (16 for D = 128)
-    static_assert(NI % NW == 0 || NW > NI, "load split");
-    __shared__ __align__(16) QBlockStage<D> S[2];
-    __shared__ float s_lse[2][kQB], s_delta[2][kQB];
+    static_assert(NI % NW == 0, "load split");
+    // loads each wave issues per query block: its share of the Q and dO rows, and the lse
+    // (even waves) or Delta (odd waves) row -- both when the workgroup has one wave
+    constexpr int PER = 2 * (NI / NW) + (NW == 1 ? 2 : 1);
+    // stages: one fewer when the loads of two blocks ahead would not fit the wait counter
+    constexpr int NS = 2 * PER < 64 ? kStagesKV : kStagesKV - 1;
+    static_assert(PER * (NS - 2) < 64, "vmcnt range");
+    __shared__ __align__(16) QBlockStage<D> S[NS];
+    __shared__ __align__(16) float s_aux[NS][2][kQB];      // lse, Delta
     static_assert(sizeof(S) >= (size_t)2 * D * 32 * 4, "reduction space");
+    (void)NTH;
     const int bh = blockIdx.x / a.nkb, j = blockIdx.x % a.nkb;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
@@ -577,44 +596,47 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
     }
     const Rsrc rq = make_rsrc(a.q + (size_t)bh * a.Nq * D, (uint32_t)((size_t)a.Nq * D * 2));
     const Rsrc rg = make_rsrc(a.gr + (size_t)bh * a.Nq * D, (uint32_t)((size_t)a.Nq * D * 2));
-    const Rsrc rqt = make_rsrc(a.qt + (size_t)bh * a.nqb * D * kQB, (uint32_t)((size_t)a.nqb * D * kQB * 2));
-    const Rsrc rgt = make_rsrc(a.gt + (size_t)bh * a.nqb * D * kQB, (uint32_t)((size_t)a.nqb * D * kQB * 2));
+    const Rsrc rl = make_rsrc(a.lse + (size_t)bh * a.Nq, (uint32_t)((size_t)a.Nq * 4));
+    const Rsrc rd = make_rsrc(a.delta + (size_t)bh * a.NqP, (uint32_t)((size_t)a.NqP * 4));
     const int32_t *off = a.qoff + (size_t)bh * (a.nkb + 1);
     const int32_t *list = a.qlist + (size_t)bh * a.nqb * a.top_k;
     const int p0 = off[j], p1 = off[j + 1];
-    // fetch query block p into stage st: every wave issues its share of the instructions
+    // fetch query block p into stage st: every wave issues its PER instructions
     auto fetch = [&](int p, int st) {
         const int i = min(max(list[p], 0), a.nqb - 1);
         const int q0 = i * a.bq, nqv = min(a.bq, a.Nq - q0);
-        for (int jj = w; jj < NI; jj += NW) {
+#pragma unroll
+        for (int jj = w * (NI / NW); jj < (w + 1) * (NI / NW); ++jj) {
             // rows of D: lane -> row RPI jj + lane / LPR, slot lane % LPR
             const int r = RPI * jj + lane / LPR, c = (lane % LPR) ^ swz_row<D>(r);
             const uint32_t ro = (uint32_t)(((q0 + min(r, nqv - 1)) * D + 8 * c) * 2);
             dma16(rq, reinterpret_cast<unsigned char *>(S[st].q) + jj * 1024, ro);
             dma16(rg, reinterpret_cast<unsigned char *>(S[st].g) + jj * 1024, ro);
-            // rows of 64 queries: lane -> row 8 jj + lane / 8, slot lane % 8
-            const int rt = 8 * jj + lane / 8, ct = (lane % 8) ^ swz_tr(rt);
-            const uint32_t to = (uint32_t)((((size_t)i * D + rt) * kQB + 8 * ct) * 2);
-            dma16(rqt, reinterpret_cast<unsigned char *>(S[st].qt) + jj * 1024, to);
-            dma16(rgt, reinterpret_cast<unsigned char *>(S[st].gt) + jj * 1024, to);
         }
-        for (int e = threadIdx.x; e < kQB; e += NTH) {
-            const size_t qi = (size_t)q0 + min(e, nqv - 1);
-            s_lse[st][e] = a.lse[(size_t)bh * a.Nq + qi];
-            s_delta[st][e] = a.delta[(size_t)bh * a.NqP + qi];
-        }
+        const uint32_t eo = (uint32_t)((q0 + min(lane, nqv - 1)) * 4);
+        if (NW == 1 || (w & 1) == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (LdsPtr)&s_aux[st][0][0], 4, (int)eo, 0, 0, 0);
+        if (NW == 1 || (w & 1) == 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (LdsPtr)&s_aux[st][1][0], 4, (int)eo, 0, 0, 0);
     };
-    if (p0 < p1) fetch(p0, 0);
+#pragma unroll
+    for (int c = 0; c < NS - 1; ++c)
+        if (p0 + c < p1) fetch(p0 + c, c);
     for (int p = p0; p < p1; ++p) {
-        const int st = (p - p0) & 1;
+        const int st = (p - p0) % NS;
         const int i = min(max(list[p], 0), a.nqb - 1);
         const int nqv = min(a.bq, a.Nq - i * a.bq);
-        // this wave's loads have landed; then everyone's, and everyone is done with block p-1
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        // this wave's loads of block p have landed (later blocks may still fly); then
+        // everyone's, and everyone is done with block p - 1, whose stage is refilled next
+        const int later = min(NS - 2, p1 - 1 - p);
+        if (NS > 3 && later >= 2) wait_vm<(NS > 3 ? 2 * PER : 0)>();
+        else if (later == 1) wait_vm<PER>();
+        else wait_vm<0>();
         __syncthreads();
-        if (p + 1 < p1) fetch(p + 1, st ^ 1);
+        if (p + NS - 1 < p1) fetch(p + NS - 1, (p - p0 + NS - 1) % NS);
         if (nvk <= 0 || 32 * qt >= nqv) continue;   // uniform per wave; the barrier is above
-        const uint16_t *Lq = S[st].q, *Lg = S[st].g, *Lqt = S[st].qt, *Lgt = S[st].gt;
+        const uint16_t *Lq = S[st].q, *Lg = S[st].g;
+        const float *s_lse = s_aux[st][0], *s_delta = s_aux[st][1];
         // S and dP for queries 32 qt + (rows in perm32 order), this wave's keys
         const int qr = 32 * qt + perm32(n);
         const int qsw = swz_row<D>(qr);
@@ -632,9 +654,9 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
         for (int i2 = 0; i2 < 16; ++i2) {
             const int qq = qb0 + i2;
             const bool ok = kvalid && qq < nqv;
-            const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i2], c_log2, -s_lse[st][qq])) : 0.f;
+            const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i2], c_log2, -s_lse[qq])) : 0.f;
             pv[i2] = pr;
-            gv[i2] = pr * (dp[i2] - s_delta[st][qq]);
+            gv[i2] = pr * (dp[i2] - s_delta[qq]);
         }
         u32x4 pf[2], gfr[2];
 #pragma unroll
@@ -644,16 +666,16 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
             gfr[ks] = u32x4{pack_bf16x2(gv[8 * ks], gv[8 * ks + 1]), pack_bf16x2(gv[8 * ks + 2], gv[8 * ks + 3]),
                             pack_bf16x2(gv[8 * ks + 4], gv[8 * ks + 5]), pack_bf16x2(gv[8 * ks + 6], gv[8 * ks + 7])};
         }
-        // dv^T += dO^T P, dk^T += Q^T G (rows d in perm32 order, queries 16 g + 8 ks ..)
+        // dv^T += dO^T P, dk^T += Q^T G (rows d in perm32 order; this lane half's queries
+        // 32 qt + 16 g + 8 ks .. + 8, the order in which P and G are packed).  Rows past the
+        // block's end repeat its last query and meet P = G = 0.
 #pragma unroll
         for (int ft = 0; ft < D / 32; ++ft) {
-            const int dr = 32 * ft + perm32(n);
-            const int dsw = swz_tr(dr);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const int ct = ((4 * qt + 2 * g + ks) ^ dsw) * 8;
-                accV[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(Lgt + dr * kQB + ct)), as_bf16x8(pf[ks]), accV[ft]);
-                accK[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(Lqt + dr * kQB + ct)), as_bf16x8(gfr[ks]), accK[ft]);
+                const int q0 = 32 * qt + 16 * g + 8 * ks;
+                accV[ft] = mfma32(as_bf16x8(xt_frag<D>(Lg, q0, ft, lane)), as_bf16x8(pf[ks]), accV[ft]);
+                accK[ft] = mfma32(as_bf16x8(xt_frag<D>(Lq, q0, ft, lane)), as_bf16x8(gfr[ks]), accK[ft]);
             }
         }
     }
@@ -829,7 +851,6 @@ static size_t bwd_layout(hf_bwd_args *a, int BH, int D, int Nq, int Nk, int bq, 
         return base ? base + at : nullptr;
     };
     char *kr = take((size_t)BH * NkP * D * 2), *vr = take((size_t)BH * NkP * D * 2), *kt = take((size_t)BH * D * NkP * 2);
-    char *qt = take((size_t)BH * nqb * D * hf::kQB * 2), *gt = take((size_t)BH * nqb * D * hf::kQB * 2);
     char *gr = take((size_t)BH * Nq * D * 2);
     char *sb = take((size_t)BH * D * D * 2), *stb = take((size_t)BH * D * D * 2);
     char *delta = take((size_t)BH * NqP * 4);
@@ -842,8 +863,6 @@ static size_t bwd_layout(hf_bwd_args *a, int BH, int D, int Nq, int Nk, int bq, 
         a->kr = reinterpret_cast<uint16_t *>(kr);
         a->vr = reinterpret_cast<uint16_t *>(vr);
         a->kt = reinterpret_cast<uint16_t *>(kt);
-        a->qt = reinterpret_cast<uint16_t *>(qt);
-        a->gt = reinterpret_cast<uint16_t *>(gt);
         a->gr = reinterpret_cast<uint16_t *>(gr);
         a->sb = reinterpret_cast<uint16_t *>(sb);
         a->stb = reinterpret_cast<uint16_t *>(stb);

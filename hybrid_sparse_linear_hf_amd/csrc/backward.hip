@@ -193,12 +193,23 @@ template <int D>
 __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
     __shared__ __align__(16) uint16_t phT[D][kQB + 8];
     __shared__ __align__(16) uint16_t dnT[D][kQB + 8];
-    __shared__ float dden_s[kQB];
+    __shared__ __align__(16) float dden_s[kQB];
+    // S and S^T in bf16, staged once for all the workgroup's chunks (rows padded by 16 bytes,
+    // so the 16 rows a fragment read touches fall in distinct bank groups)
+    __shared__ __align__(16) uint16_t s_sb[D][D + 8], s_stb[D][D + 8];
     const int bh = blockIdx.x / a.splits, sp = blockIdx.x % a.splits;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
     const int nchunks = (a.Nq + kQB - 1) / kQB;
     const float *zp = a.z + (size_t)bh * D;
-    const uint16_t *sbp = a.sb + (size_t)bh * D * D, *stp = a.stb + (size_t)bh * D * D;
+    {
+        const uint16_t *sbg = a.sb + (size_t)bh * D * D, *stg = a.stb + (size_t)bh * D * D;
+        for (int e = threadIdx.x; e < D * D / 8; e += 128) {
+            const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
+            *reinterpret_cast<u32x4 *>(&s_sb[r][c8]) = *reinterpret_cast<const u32x4 *>(sbg + r * D + c8);
+            *reinterpret_cast<u32x4 *>(&s_stb[r][c8]) = *reinterpret_cast<const u32x4 *>(stg + r * D + c8);
+        }
+        __syncthreads();
+    }
     // partial dS: wave w owns output tiles (a-tile XT w + x, c-tile y), x < XT = D/64,
     // y < D/32
     constexpr int NT = D / 32, XT = NT / 2;
@@ -236,7 +247,7 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
 #pragma unroll
         for (int ft = 0; ft < NT; ++ft) {
             f32x16 acc = {};
-            const uint16_t *srow = stp + (size_t)(32 * ft + perm32(n)) * D + 8 * g;
+            const uint16_t *srow = &s_stb[32 * ft + perm32(n)][8 * g];
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks)
                 acc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(srow + 16 * ks)), as_bf16x8(pq[ks]), acc);
@@ -268,7 +279,7 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
 #pragma unroll
         for (int ft = 0; ft < NT; ++ft) {
             f32x16 acc = {};
-            const uint16_t *srow = sbp + (size_t)(32 * ft + perm32(n)) * D + 8 * g;
+            const uint16_t *srow = &s_sb[32 * ft + perm32(n)][8 * g];
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks)
                 acc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(srow + 16 * ks)), as_bf16x8(dnf[ks]), acc);
@@ -321,10 +332,22 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
             }
         }
         if (threadIdx.x < D) {
+            // dz partial of feature threadIdx.x over the chunk's queries, in query order;
+            // eight queries per 16-byte read
             float s = 0.f;
-            for (int q = 0; q < kQB; ++q) {
-                const uint16_t pb = phT[threadIdx.x][q];
-                s = __builtin_fmaf(__uint_as_float((uint32_t)pb << 16), dden_s[q], s);
+#pragma unroll
+            for (int q8 = 0; q8 < kQB; q8 += 8) {
+                const u32x4 pv = *reinterpret_cast<const u32x4 *>(&phT[threadIdx.x][q8]);
+                const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&dden_s[q8]);
+                const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&dden_s[q8 + 4]);
+                s = __builtin_fmaf(bf16_lo_to_f32(pv.x), d0.x, s);
+                s = __builtin_fmaf(bf16_hi_to_f32(pv.x), d0.y, s);
+                s = __builtin_fmaf(bf16_lo_to_f32(pv.y), d0.z, s);
+                s = __builtin_fmaf(bf16_hi_to_f32(pv.y), d0.w, s);
+                s = __builtin_fmaf(bf16_lo_to_f32(pv.z), d1.x, s);
+                s = __builtin_fmaf(bf16_hi_to_f32(pv.z), d1.y, s);
+                s = __builtin_fmaf(bf16_lo_to_f32(pv.w), d1.z, s);
+                s = __builtin_fmaf(bf16_hi_to_f32(pv.w), d1.w, s);
             }
             dz_acc += s;
         }
@@ -344,6 +367,21 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
     if (threadIdx.x < D) a.dzp[((size_t)bh * a.splits + sp) * D + threadIdx.x] = dz_acc;
 }
 
+// Sum of `splits` partials p at src[p * stride] in split order; the loads of eight splits
+// are issued before their adds, which keep the order (so the result is the serial sum).
+__device__ __forceinline__ float ordered_split_sum(const float *src, size_t stride, int splits) {
+    float s = 0.f;
+    for (int p0 = 0; p0 < splits; p0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = p0 + u < splits ? src[(size_t)(p0 + u) * stride] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (p0 + u < splits) s += v[u];
+    }
+    return s;
+}
+
 // dS, dz = sum of the split partials in split order (one workgroup per plane and 32x32
 // tile; the first tile of a plane also adds dz).
 template <int D>
@@ -353,15 +391,12 @@ __global__ __launch_bounds__(256) void reduce_readout_kernel(hf_bwd_args a) {
     const int r0 = 32 * (tile / nt), c0 = 32 * (tile % nt);
     for (int e = threadIdx.x; e < 32 * 32; e += 256) {
         const int r = r0 + e / 32, c = c0 + e % 32;
-        float s = 0.f;
-        for (int p = 0; p < a.splits; ++p) s += a.dsp[((size_t)bh * a.splits + p) * D * D + (size_t)r * D + c];
-        a.dS[(size_t)bh * D * D + (size_t)r * D + c] = s;
+        a.dS[(size_t)bh * D * D + (size_t)r * D + c] =
+            ordered_split_sum(a.dsp + (size_t)bh * a.splits * D * D + (size_t)r * D + c, (size_t)D * D, a.splits);
     }
-    if (tile == 0 && threadIdx.x < D) {
-        float s = 0.f;
-        for (int p = 0; p < a.splits; ++p) s += a.dzp[((size_t)bh * a.splits + p) * D + threadIdx.x];
-        a.dz[(size_t)bh * D + threadIdx.x] = s;
-    }
+    if (tile == 0 && threadIdx.x < D)
+        a.dz[(size_t)bh * D + threadIdx.x] =
+            ordered_split_sum(a.dzp + (size_t)bh * a.splits * D + threadIdx.x, (size_t)D, a.splits);
 }
 
 // ---------------------------------------------------------------- dq pass

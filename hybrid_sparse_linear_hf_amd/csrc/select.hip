@@ -12,17 +12,21 @@
 // pool kernel keeps each key block's rows of its two frames apart, frame_pool_kernel adds
 // those parts per frame.
 //
-// Three launches:
-//   pool_kernel   HBM-bound: one workgroup per query or key block sums its rows in fp64
-//                 (sums of bf16 values are exact in fp64) and stores the block mean.
-//   score_kernel  16 x 16 tiles of fp64 scores, one wave each, 2 x 2 per lane, each
-//                 evaluated as sum_d (qbar_d * kbar_d) in index order with separately
-//                 rounded products and sums (the pooled tiles are staged in LDS, every
-//                 load issued up front).
-//   topk_kernel   one wave per query block: radix select of the k-th largest
-//                 (score, -index) key and an ascending emit of the kept indices.
-// The hierarchical variant adds frame_pool_kernel, runs the score kernel a second time
-// over (query block, frame) pairs, and lets the top-k wave select the frames before the
+// Flat selection, two launches:
+//   pool_kernel        HBM-bound: one workgroup per query or key block sums its rows in
+//                      fp64 (sums of bf16 values are exact in fp64) and stores the block
+//                      mean.  In a hybrid step the same launch carries extra workgroups
+//                      that prepare the readout operands and append the chunk to the ring
+//                      (the chunk's key blocks are then pooled from the chunk input).
+//   score_topk_kernel  one wave per query block: its fp64 scores against every pooled
+//                      key block, each evaluated as sum_d (qbar_d * kbar_d) in index
+//                      order with separately rounded products and sums (pooled keys staged
+//                      through LDS in chunks of 64), kept in LDS; then a radix select of the
+//                      k-th largest (score, -index) key and an ascending emit of the kept
+//                      indices.
+// The hierarchical variant pools per frame as well (frame_pool_kernel), scores with the
+// tiled score_kernel (16 x 16 tiles, one wave each, same summation order) over block pairs
+// and over (query block, frame) pairs, and lets topk_kernel select the frames before the
 // blocks.
 #include "append_tile.h"
 #include "state_tile.h"

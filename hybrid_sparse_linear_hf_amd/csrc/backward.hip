@@ -10,19 +10,21 @@
 //                dq_t += (S dn + z dden) * phi'(q_t);
 //   absorb       (S += phi(K)^T V, z += sum phi(K)):  dV = phi(K) dS, dK = (V dS^T + dz) * phi'(K).
 //
-// gfx950 design (first version, correctness first).  A prep launch copies the window into
-// logical order in bf16 -- K rows, V rows and K^T -- and each query block's Q^T and dO^T,
-// so that every matrix-core operand is one contiguous 16-byte run read straight from
-// global memory (L2) into its fragment: no LDS staging in the attention passes.
-//   * readout pass: one workgroup per (plane, split of the queries); the products S^T phi(q)
-//     and S dn on the matrix cores, per-query terms in fp32; dS and dz as split partials
-//     (phi(q) and dn staged transposed in LDS), added in split order by a second launch.
+// gfx950 design.  A prep launch copies the window into logical order in bf16 -- K rows,
+// V rows and K^T -- and dO into bf16 rows, so that the passes below never touch the ring's
+// frame arithmetic.
+//   * readout pass: one workgroup per (plane, split of the queries), S and S^T staged in LDS
+//     once; the products S^T phi(q) and S dn on the matrix cores, per-query terms in fp32;
+//     dS and dz as split partials (phi(q) and dn staged transposed in LDS), added in split
+//     order by a second launch.
 //   * dq pass: one workgroup per query block, one wave per 32-query tile, walking the kept
-//     key blocks in 32-key subtiles: S^T = K Q^T, dP^T = V dO^T, G^T = P^T (dP^T - Delta)
-//     and dq^T += K^T G^T.
-//   * dk/dv pass: one workgroup per key block, one wave per 32-key tile, walking the query
-//     blocks that kept it (a per-plane transpose of the selection, in ascending order):
-//     S = Q K^T, dP = dO V^T, G = P (dP - Delta), dv^T += dO^T P, dk^T += Q^T G.
+//     key blocks in 32-key subtiles staged in LDS: S^T = K Q^T, dP^T = V dO^T,
+//     G^T = P^T (dP^T - Delta) and dq^T += K^T G^T.
+//   * dk/dv pass: one workgroup per key block, one wave per (32-key tile, 32-query tile),
+//     walking the query blocks that kept it (a per-plane transpose of the selection, in
+//     ascending order), their Q and dO rows fetched into LDS three blocks ahead:
+//     S = Q K^T, dP = dO V^T, G = P (dP - Delta), dv^T += dO^T P, dk^T += Q^T G, the
+//     transposed operands read from the same rows by transposing LDS reads.
 //   Products in bf16 with fp32 accumulation; P and G rounded to bf16 as matrix-core
 //   operands.  Every sum has a fixed order: results are deterministic.
 #include "hf_internal.h"

@@ -10,16 +10,17 @@
 //                dq_t += (S dn + z dden) * phi'(q_t);
 //   absorb       (S += phi(K)^T V, z += sum phi(K)):  dV = phi(K) dS, dK = (V dS^T + dz) * phi'(K).
 //
-// gfx950 design.  A prep launch copies the window into logical order in bf16 -- K rows,
-// V rows and K^T -- and dO into bf16 rows, so that the passes below never touch the ring's
-// frame arithmetic.
+// gfx950 design.  A prep launch copies the window into logical order in bf16 -- K rows and
+// V rows -- and dO into bf16 rows, so that the passes below never touch the ring's frame
+// arithmetic.
 //   * readout pass: one workgroup per (plane, split of the queries), S and S^T staged in LDS
 //     once; the products S^T phi(q) and S dn on the matrix cores, per-query terms in fp32;
 //     dS and dz as split partials (phi(q) and dn staged transposed in LDS), added in split
 //     order by a second launch.
 //   * dq pass: one workgroup per query block, one wave per 32-query tile, walking the kept
 //     key blocks in 32-key subtiles staged in LDS: S^T = K Q^T, dP^T = V dO^T,
-//     G^T = P^T (dP^T - Delta) and dq^T += K^T G^T.
+//     G^T = P^T (dP^T - Delta) and dq^T += K^T G^T (K^T read from the staged K rows by
+//     transposing LDS reads).
 //   * dk/dv pass: one workgroup per key block, one wave per (32-key tile, 32-query tile),
 //     walking the query blocks that kept it (a per-plane transpose of the selection, in
 //     ascending order), their Q and dO rows fetched into LDS three blocks ahead:
@@ -54,12 +55,11 @@ __device__ __forceinline__ float phi_prime(float x) {
 
 // ---------------------------------------------------------------- prep
 
-// One workgroup per (plane, 64-key tile of the logical window): K rows, V rows and K^T,
-// rows past the window zeroed.  Keys j0 .. j0 + 63 in aligned groups of 8 stay in one frame
+// One workgroup per (plane, 64-key tile of the logical window): K rows and V rows (V from
+// the ring's V^T frames, transposed through LDS), rows past the window zeroed.  Keys j0 .. j0 + 63 in aligned groups of 8 stay in one frame
 // (T % 8 == 0).
 template <int D>
 __global__ __launch_bounds__(256) void prep_keys_kernel(hf_bwd_args a) {
-    __shared__ __align__(16) uint16_t tk[64][D + 8];
     __shared__ __align__(16) uint16_t tv[D][64 + 8];
     const int tiles = a.NkP / 64;
     const int bh = blockIdx.x / tiles, j0 = (blockIdx.x % tiles) * 64;
@@ -75,7 +75,6 @@ __global__ __launch_bounds__(256) void prep_keys_kernel(hf_bwd_args a) {
             v = *reinterpret_cast<const u32x4 *>(a.ring_k + (((size_t)bh * a.W + slot_of(f)) * a.T + t) * D + c8);
         }
         *reinterpret_cast<u32x4 *>(a.kr + ((size_t)bh * a.NkP + j) * D + c8) = v;
-        *reinterpret_cast<u32x4 *>(&tk[r][c8]) = v;
     }
     for (int e = threadIdx.x; e < D * 8; e += 256) {
         const int d = e / 8, k8 = (e % 8) * 8, j = j0 + k8;
@@ -87,12 +86,6 @@ __global__ __launch_bounds__(256) void prep_keys_kernel(hf_bwd_args a) {
         *reinterpret_cast<u32x4 *>(&tv[d][k8]) = v;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < D * 8; e += 256) {
-        const int d = e / 8, k8 = (e % 8) * 8;
-        const u32x4 o = {pack2(tk[k8][d], tk[k8 + 1][d]), pack2(tk[k8 + 2][d], tk[k8 + 3][d]),
-                         pack2(tk[k8 + 4][d], tk[k8 + 5][d]), pack2(tk[k8 + 6][d], tk[k8 + 7][d])};
-        *reinterpret_cast<u32x4 *>(a.kt + ((size_t)bh * D + d) * a.NkP + j0 + k8) = o;
-    }
     for (int e = threadIdx.x; e < 64 * D / 8; e += 256) {
         const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
         const u32x4 o = {pack2(tv[c8][r], tv[c8 + 1][r]), pack2(tv[c8 + 2][r], tv[c8 + 3][r]),
@@ -403,22 +396,45 @@ __global__ __launch_bounds__(256) void reduce_readout_kernel(hf_bwd_args a) {
 
 // ---------------------------------------------------------------- dq pass
 
-// One workgroup per query block, one wave per 32-query tile.  Each 32-key subtile's K rows,
-// V rows and K^T pass through LDS once for all the waves (rows padded by 16 bytes); the
-// next subtile's operands are loaded into registers while the current one is computed.
+// Transposing LDS read (gfx950): within each 16-lane group, lane i receives element i % 4 of
+// the 4-element vectors that lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12 of the group point
+// at (one per returned element).
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p) {
+    const v4s16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s16 *)(const_cast<uint16_t *>(p)));
+    return u32x2{(uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16),
+                 (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16)};
+}
+
+// Matrix-core A fragment of X^T from row-major rows padded to PITCH elements: lane (n, g)
+// receives features 32 ft + perm32(n) of rows r0 .. r0 + 7 (r0 for its lane half), as two
+// transposing reads of four rows.  In a 16-lane group (n = 16 G + i) lane s points at row
+// r0 + 4 h + s / 4, features 32 ft + 8 G + 16 ((s % 4) & 1) + 4 ((s % 4) >> 1) .. + 3, so that
+// lane i receives feature 32 ft + perm32(16 G + i).
+template <int PITCH>
+__device__ __forceinline__ u32x4 xt_frag_rows(const uint16_t *X, int r0, int ft, int lane) {
+    const int s = lane & 15, t = s & 3, G = (lane >> 4) & 1;
+    const int d = 32 * ft + 8 * G + 16 * (t & 1) + 4 * (t >> 1);
+    const u32x2 h0 = ds_read_tr16(X + (r0 + (s >> 2)) * PITCH + d);
+    const u32x2 h1 = ds_read_tr16(X + (r0 + 4 + (s >> 2)) * PITCH + d);
+    return u32x4{h0.x, h0.y, h1.x, h1.y};
+}
+
+// One workgroup per query block, one wave per 32-query tile.  Each 32-key subtile's K rows
+// and V rows pass through LDS once for all the waves (rows padded by 16 bytes); the next
+// subtile's operands are loaded into registers while the current one is computed.
 template <int D>
 struct SubtileLds {
     uint16_t k[32][D + 8], v[32][D + 8];
-    uint16_t kt[D][32 + 8];
 };
 
 template <int D, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW, 2))) void dq_kernel(hf_bwd_args a, float c_log2, float inv_sqrt_d, int lsh) {
     constexpr int NTH = 64 * NW;
     constexpr int CR = 32 * D / 8;           // 16-byte chunks of the K (or V) rows of a subtile
-    constexpr int CT = D * 4;                // 16-byte chunks of its K^T
-    constexpr int PR = CR / NTH, PT = CT / NTH;
-    static_assert(CR % NTH == 0 && CT % NTH == 0, "staging split");
+    constexpr int PR = CR / NTH;
+    static_assert(CR % NTH == 0, "staging split");
     __shared__ __align__(16) SubtileLds<D> L;
     const int bh = blockIdx.x / a.nqb, qb = blockIdx.x % a.nqb;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
@@ -434,7 +450,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
     }
     const float Lq = a.lse[row], Dl = a.delta[(size_t)bh * a.NqP + (valid ? t : q0)];
     const uint16_t *krp = a.kr + (size_t)bh * a.NkP * D, *vrp = a.vr + (size_t)bh * a.NkP * D;
-    const uint16_t *ktp = a.kt + (size_t)bh * D * a.NkP;
     f32x16 acc[D / 32];
 #pragma unroll
     for (int ft = 0; ft < D / 32; ++ft) acc[ft] = f32x16{};
@@ -451,18 +466,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
             ss = 0;
         }
     };
-    u32x4 pk[PR], pv[PR], pt[PT];
+    u32x4 pk[PR], pv[PR];
     auto load = [&](int k0) {
 #pragma unroll
         for (int e0 = 0; e0 < PR; ++e0) {
             const int e = threadIdx.x + NTH * e0, rr = e / (D / 8), c8 = (e % (D / 8)) * 8;
             pk[e0] = *reinterpret_cast<const u32x4 *>(krp + (size_t)(k0 + rr) * D + c8);
             pv[e0] = *reinterpret_cast<const u32x4 *>(vrp + (size_t)(k0 + rr) * D + c8);
-        }
-#pragma unroll
-        for (int e0 = 0; e0 < PT; ++e0) {
-            const int e = threadIdx.x + NTH * e0, d = e / 4, c8 = (e % 4) * 8;
-            pt[e0] = *reinterpret_cast<const u32x4 *>(ktp + (size_t)d * a.NkP + k0 + c8);
         }
     };
     load(k0_of(0, 0));
@@ -476,11 +486,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
             const int e = threadIdx.x + NTH * e0, rr = e / (D / 8), c8 = (e % (D / 8)) * 8;
             *reinterpret_cast<u32x4 *>(&L.k[rr][c8]) = pk[e0];
             *reinterpret_cast<u32x4 *>(&L.v[rr][c8]) = pv[e0];
-        }
-#pragma unroll
-        for (int e0 = 0; e0 < PT; ++e0) {
-            const int e = threadIdx.x + NTH * e0, d = e / 4, c8 = (e % 4) * 8;
-            *reinterpret_cast<u32x4 *>(&L.kt[d][c8]) = pt[e0];
         }
         __syncthreads();
         advance(r, su);
@@ -506,10 +511,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
                             pack_bf16x2(gt[8 * ks + 4], gt[8 * ks + 5]), pack_bf16x2(gt[8 * ks + 6], gt[8 * ks + 7])};
 #pragma unroll
         for (int ft = 0; ft < D / 32; ++ft) {
-            const int dr = 32 * ft + perm32(n);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                acc[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.kt[dr][16 * g + 8 * ks])), as_bf16x8(gfr[ks]),
+            for (int ks = 0; ks < 2; ++ks)   // K^T rows 32 ft + perm32(n), keys 16 g + 8 ks .. + 8
+                acc[ft] = mfma32(as_bf16x8(xt_frag_rows<D + 8>(&L.k[0][0], 16 * g + 8 * ks, ft, lane)), as_bf16x8(gfr[ks]),
                                  acc[ft]);
         }
     }
@@ -551,31 +555,8 @@ __device__ __forceinline__ int swz_row(int r) {
     else return ((r >> 1) & 3) | ((r >> 2) & 4);
 }
 
-// One query block's operands, staged unpadded with swizzled chunks by direct-to-LDS loads:
-// Q and dO rows (rows of D, chunk c of row r at slot c ^ swz_row(r)), and the block's lse
-// and Delta values.
-template <int D>
-struct QBlockStage {
-    uint16_t q[kQB * D], g[kQB * D];
-};
-constexpr int kStagesKV = 4;   // query-block stages: up to three blocks ahead are in flight
-
-// Transposing LDS read (gfx950): within each 16-lane group, lane i receives element i % 4 of
-// the 4-element vectors that lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12 of the group point
-// at (one per returned element).
-typedef short v4s16 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p) {
-    const v4s16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4s16 *)(const_cast<uint16_t *>(p)));
-    return u32x2{(uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16),
-                 (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16)};
-}
-
-// Matrix-core A fragment of X^T from the staged row-major tile X (64 rows of D, swizzled):
-// lane (n, g) receives features 32 ft + perm32(n) of queries q0 .. q0 + 7 (q0 for its lane
-// half), as two transposing reads of four queries.  In a 16-lane group (n = 16 G + i) lane s
-// points at query q0 + 4 h + s / 4, features 32 ft + 8 G + 16 ((s % 4) & 1) + 4 ((s % 4) >> 1)
-// .. + 3, so that lane i receives feature 32 ft + perm32(16 G + i).
+// The fragment of xt_frag_rows from the staged, chunk-swizzled 64 x D tile X (rows are
+// queries q0 .. q0 + 7 here).
 template <int D>
 __device__ __forceinline__ u32x4 xt_frag(const uint16_t *X, int q0, int ft, int lane) {
     const int s = lane & 15, t = s & 3, G = (lane >> 4) & 1;
@@ -588,6 +569,17 @@ __device__ __forceinline__ u32x4 xt_frag(const uint16_t *X, int q0, int ft, int 
     }
     return u32x4{h[0].x, h[0].y, h[1].x, h[1].y};
 }
+
+
+
+// One query block's operands, staged unpadded with swizzled chunks by direct-to-LDS loads:
+// Q and dO rows (rows of D, chunk c of row r at slot c ^ swz_row(r)), and the block's lse
+// and Delta values.
+template <int D>
+struct QBlockStage {
+    uint16_t q[kQB * D], g[kQB * D];
+};
+constexpr int kStagesKV = 4;   // query-block stages: up to three blocks ahead are in flight
 
 // One workgroup per key block: wave (kt, qt) owns the block's 32-key tile kt and the
 // 32-query tile qt of every query block that kept it (NKT key tiles x NQT query tiles).
@@ -875,7 +867,7 @@ static int bwd_splits(int BH, int Nq) {
     return s < chunks ? s : chunks;
 }
 
-// Workspace: K rows, V rows, K^T, Q^T blocks, dO^T blocks, dO rows, S / S^T bf16, Delta,
+// Workspace: K rows, V rows, dO rows, S / S^T bf16, Delta,
 // the selection transpose, readout partials (each region 256-byte aligned).
 static size_t bwd_layout(hf_bwd_args *a, int BH, int D, int Nq, int Nk, int bq, int bk, int top_k, char *base) {
     const int nqb = (Nq + bq - 1) / bq, nkb = (Nk + bk - 1) / bk;
@@ -887,7 +879,7 @@ static size_t bwd_layout(hf_bwd_args *a, int BH, int D, int Nq, int Nk, int bq, 
         o += align256(bytes);
         return base ? base + at : nullptr;
     };
-    char *kr = take((size_t)BH * NkP * D * 2), *vr = take((size_t)BH * NkP * D * 2), *kt = take((size_t)BH * D * NkP * 2);
+    char *kr = take((size_t)BH * NkP * D * 2), *vr = take((size_t)BH * NkP * D * 2);
     char *gr = take((size_t)BH * Nq * D * 2);
     char *sb = take((size_t)BH * D * D * 2), *stb = take((size_t)BH * D * D * 2);
     char *delta = take((size_t)BH * NqP * 4);
@@ -899,7 +891,6 @@ static size_t bwd_layout(hf_bwd_args *a, int BH, int D, int Nq, int Nk, int bq, 
         a->splits = splits;
         a->kr = reinterpret_cast<uint16_t *>(kr);
         a->vr = reinterpret_cast<uint16_t *>(vr);
-        a->kt = reinterpret_cast<uint16_t *>(kt);
         a->gr = reinterpret_cast<uint16_t *>(gr);
         a->sb = reinterpret_cast<uint16_t *>(sb);
         a->stb = reinterpret_cast<uint16_t *>(stb);

@@ -172,7 +172,7 @@ struct hf_bwd_args {
     float eps;
     float *dq, *dk, *dv, *dS, *dz;
     // workspace
-    uint16_t *kr, *vr, *kt;    // window K rows, V rows [BH][NkP][D], K^T [BH][D][NkP] (logical order, zero pad)
+    uint16_t *kr, *vr;         // window K rows, V rows [BH][NkP][D] (logical order, zero pad)
     uint16_t *gr;              // dO rows in bf16 [BH][NqP][D]
     uint16_t *sb, *stb;        // S and S^T in bf16 [BH][D][D]
     float *delta;              // [BH][NqP]: dO . (sparse part of out)

@@ -94,6 +94,43 @@ __global__ __launch_bounds__(256) void prep_keys_kernel(hf_bwd_args a) {
     }
 }
 
+// The key blocks of every plane in descending order of the number of query blocks that
+// kept them (counting sort, one workgroup).  The dk/dv pass takes its workgroups in this
+// order -- the longest first -- so that no long one starts last; within a count the order
+// is whatever the atomics give, which changes timing only (every workgroup writes its own
+// key block).
+constexpr int kOrderBuckets = 2048;
+__global__ __launch_bounds__(1024) void order_kernel(hf_bwd_args a) {
+    __shared__ int start[kOrderBuckets];
+    __shared__ int part[1024];
+    const int items = a.BH * a.nkb, t = threadIdx.x;
+    auto bucket = [&](int it) {
+        const int32_t *off = a.qoff + (size_t)(it / a.nkb) * (a.nkb + 1);
+        const int j = it % a.nkb;
+        return kOrderBuckets - 1 - min(off[j + 1] - off[j], kOrderBuckets - 1);
+    };
+    start[2 * t] = start[2 * t + 1] = 0;
+    __syncthreads();
+    for (int it = t; it < items; it += 1024) atomicAdd(&start[bucket(it)], 1);
+    __syncthreads();
+    // exclusive scan over the buckets: thread t holds buckets 2t, 2t+1; Hillis-Steele over
+    // the 1024 pair sums
+    const int c0 = start[2 * t], c1 = start[2 * t + 1];
+    part[t] = c0 + c1;
+    __syncthreads();
+    for (int d = 1; d < 1024; d *= 2) {
+        const int v = t >= d ? part[t - d] : 0;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    const int base = part[t] - (c0 + c1);
+    start[2 * t] = base;
+    start[2 * t + 1] = base + c0;
+    __syncthreads();
+    for (int it = t; it < items; it += 1024) a.korder[atomicAdd(&start[bucket(it)], 1)] = it;
+}
+
 // A fp32 [BH][D][D] matrix into bf16 rows and bf16 transposed rows, one workgroup per
 // 32 x 32 tile.
 template <int D>
@@ -603,7 +640,8 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
     __shared__ __align__(16) float s_aux[NS][2][kQB];      // lse, Delta
     static_assert(sizeof(S) >= (size_t)2 * D * 32 * 4, "reduction space");
     (void)NTH;
-    const int bh = blockIdx.x / a.nkb, j = blockIdx.x % a.nkb;
+    const int item = a.korder[blockIdx.x];   // longest work first
+    const int bh = item / a.nkb, j = item % a.nkb;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
     const int kt = w % NKT, qt = w / NKT;
@@ -826,6 +864,7 @@ hipError_t launch_attn_backward(const hf_bwd_args &a, hipStream_t s) {
     hipLaunchKernelGGL(prep_keys_kernel<D>, dim3((unsigned)(a.BH * (a.NkP / 64))), dim3(256), 0, s, a);
     hipLaunchKernelGGL(prep_queries_kernel<D>, dim3((unsigned)(a.BH * a.nqb + a.BH * nt * nt)), dim3(256), 0, s, a);
     hipLaunchKernelGGL(csr_kernel, dim3((unsigned)a.BH), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, s, a);
     hipLaunchKernelGGL(readout_bwd_kernel<D>, dim3((unsigned)(a.BH * a.splits)), dim3(128), 0, s, a);
     hipLaunchKernelGGL(reduce_readout_kernel<D>, dim3((unsigned)(a.BH * nt * nt)), dim3(256), 0, s, a);
     if (a.bq > 32)
@@ -884,6 +923,7 @@ static size_t bwd_layout(hf_bwd_args *a, int BH, int D, int Nq, int Nk, int bq, 
     char *sb = take((size_t)BH * D * D * 2), *stb = take((size_t)BH * D * D * 2);
     char *delta = take((size_t)BH * NqP * 4);
     char *qoff = take((size_t)BH * (nkb + 1) * 4), *qlist = take((size_t)BH * nqb * top_k * 4);
+    char *korder = take((size_t)BH * nkb * 4);
     char *dsp = take((size_t)BH * splits * D * D * 4), *dzp = take((size_t)BH * splits * D * 4);
     if (a) {
         a->NkP = NkP;
@@ -897,6 +937,7 @@ static size_t bwd_layout(hf_bwd_args *a, int BH, int D, int Nq, int Nk, int bq, 
         a->delta = reinterpret_cast<float *>(delta);
         a->qoff = reinterpret_cast<int32_t *>(qoff);
         a->qlist = reinterpret_cast<int32_t *>(qlist);
+        a->korder = reinterpret_cast<int32_t *>(korder);
         a->dsp = reinterpret_cast<float *>(dsp);
         a->dzp = reinterpret_cast<float *>(dzp);
     }

@@ -177,6 +177,7 @@ struct hf_bwd_args {
     uint16_t *sb, *stb;        // S and S^T in bf16 [BH][D][D]
     float *delta;              // [BH][NqP]: dO . (sparse part of out)
     int32_t *qoff, *qlist;     // per key block, the query blocks that kept it: [BH][nkb+1], [BH][nqb*top_k]
+    int32_t *korder;           // [BH*nkb] key blocks (bh * nkb + j) by descending kept-by count
     float *dsp, *dzp;          // readout partials [BH][splits][D][D], [BH][splits][D]
 };
 size_t hf_bwd_workspace_bytes(int BH, int D, int Nq, int Nk, int bq, int bk, int top_k);

@@ -171,22 +171,27 @@ __global__ __launch_bounds__(256) void prep_queries_kernel(hf_bwd_args a) {
 }
 
 // Per plane, the query blocks that kept each key block, ascending: count (LDS atomics over
-// the kept entries), exclusive scan (one wave), then a fill that walks the query blocks in
-// order (a kept list holds distinct blocks, so its entries never collide; entries outside
-// [0, n_kb), a caller error, are skipped).
+// the kept entries, which are also staged in LDS when they fit), exclusive scan (one wave),
+// then a fill that walks the query blocks in order (a kept list holds distinct blocks, so
+// its entries never collide; entries outside [0, n_kb), a caller error, are skipped).
+constexpr int kCsrStaged = 8192;   // kept entries of a plane staged in LDS for the fill
 __global__ __launch_bounds__(256) void csr_kernel(hf_bwd_args a) {
     __shared__ int cnt[kMaxKeyBlocks];
     __shared__ int pos[kMaxKeyBlocks];
+    __shared__ int32_t sel_s[kCsrStaged];
     const int bh = blockIdx.x, tid = threadIdx.x;
-    const int32_t *sel = a.idx + (size_t)bh * a.nqb * a.top_k;
     const int total = a.nqb * a.top_k;
+    const bool staged = total <= kCsrStaged;          // uniform
+    const int32_t *sel = a.idx + (size_t)bh * total;
     for (int j = tid; j < a.nkb; j += 256) cnt[j] = 0;
     __syncthreads();
     for (int e = tid; e < total; e += 256) {
         const int j = sel[e];
+        if (staged) sel_s[e] = j;
         if (j >= 0 && j < a.nkb) atomicAdd(&cnt[j], 1);
     }
     __syncthreads();
+    const int32_t *fsel = staged ? sel_s : sel;        // the fill reads LDS when it can
     int32_t *off = a.qoff + (size_t)bh * (a.nkb + 1);
     if (tid < 64) {
         int base = 0;
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(256) void csr_kernel(hf_bwd_args a) {
     int32_t *list = a.qlist + (size_t)bh * a.nqb * a.top_k;
     for (int i = 0; i < a.nqb; ++i) {
         for (int r = tid; r < a.top_k; r += 256) {
-            const int j = sel[(size_t)i * a.top_k + r];
+            const int j = fsel[(size_t)i * a.top_k + r];
             if (j >= 0 && j < a.nkb) list[pos[j]++] = i;
         }
         __syncthreads();

@@ -438,6 +438,18 @@ __global__ __launch_bounds__(256) void reduce_readout_kernel(hf_bwd_args a) {
 
 // ---------------------------------------------------------------- dq pass
 
+// 16-byte chunk swizzle of staged rows of D (Q and dO rows in the dk/dv pass, K rows in the
+// dq pass): chunk c of row r sits at slot c ^ swz_row(r).  For D = 128 the row's two low
+// bits go to slot bits 2-3, bit 2 to bit 0 and bit 4 to bit 1, so that (a) the fragment
+// reads of rows 32 x + perm32(n), one chunk per 16 lanes, hit 16 distinct bank groups, and
+// (b) the transposing reads -- four consecutive rows, chunk offsets 0 and 2 within them --
+// land on 16 distinct (chunk, half) slots.
+template <int D>
+__device__ __forceinline__ int swz_row(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
+    else return ((r >> 1) & 3) | ((r >> 2) & 4);
+}
+
 // Transposing LDS read (gfx950): within each 16-lane group, lane i receives element i % 4 of
 // the 4-element vectors that lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12 of the group point
 // at (one per returned element).
@@ -449,26 +461,31 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p) {
                  (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16)};
 }
 
-// Matrix-core A fragment of X^T from row-major rows padded to PITCH elements: lane (n, g)
-// receives features 32 ft + perm32(n) of rows r0 .. r0 + 7 (r0 for its lane half), as two
-// transposing reads of four rows.  In a 16-lane group (n = 16 G + i) lane s points at row
-// r0 + 4 h + s / 4, features 32 ft + 8 G + 16 ((s % 4) & 1) + 4 ((s % 4) >> 1) .. + 3, so that
-// lane i receives feature 32 ft + perm32(16 G + i).
-template <int PITCH>
-__device__ __forceinline__ u32x4 xt_frag_rows(const uint16_t *X, int r0, int ft, int lane) {
+// Matrix-core A fragment of X^T from staged, chunk-swizzled rows of D (swz_row): lane
+// (n, g) receives features 32 ft + perm32(n) of rows q0 .. q0 + 7 (q0 for its lane half),
+// as two transposing reads of four rows.  In a 16-lane group (n = 16 G + i) lane s points
+// at row q0 + 4 h + s / 4, features 32 ft + 8 G + 16 ((s % 4) & 1) + 4 ((s % 4) >> 1) .. + 3,
+// so that lane i receives feature 32 ft + perm32(16 G + i).
+template <int D>
+__device__ __forceinline__ u32x4 xt_frag(const uint16_t *X, int q0, int ft, int lane) {
     const int s = lane & 15, t = s & 3, G = (lane >> 4) & 1;
     const int d = 32 * ft + 8 * G + 16 * (t & 1) + 4 * (t >> 1);
-    const u32x2 h0 = ds_read_tr16(X + (r0 + (s >> 2)) * PITCH + d);
-    const u32x2 h1 = ds_read_tr16(X + (r0 + 4 + (s >> 2)) * PITCH + d);
-    return u32x4{h0.x, h0.y, h1.x, h1.y};
+    u32x2 h[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int r = q0 + 4 * hh + (s >> 2);
+        h[hh] = ds_read_tr16(X + r * D + (((d >> 3) ^ swz_row<D>(r)) << 3) + (d & 7));
+    }
+    return u32x4{h[0].x, h[0].y, h[1].x, h[1].y};
 }
 
 // One workgroup per query block, one wave per 32-query tile.  Each 32-key subtile's K rows
-// and V rows pass through LDS once for all the waves (rows padded by 16 bytes); the next
-// subtile's operands are loaded into registers while the current one is computed.
+// (chunk-swizzled) and V rows (padded by 16 bytes) pass through LDS once for all the waves;
+// the next subtile's operands are loaded into registers while the current one is computed.
 template <int D>
 struct SubtileLds {
-    uint16_t k[32][D + 8], v[32][D + 8];
+    uint16_t k[32 * D];           // K rows, chunk-swizzled (swz_row)
+    uint16_t v[32][D + 8];
 };
 
 template <int D, int NW>
@@ -526,7 +543,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
 #pragma unroll
         for (int e0 = 0; e0 < PR; ++e0) {
             const int e = threadIdx.x + NTH * e0, rr = e / (D / 8), c8 = (e % (D / 8)) * 8;
-            *reinterpret_cast<u32x4 *>(&L.k[rr][c8]) = pk[e0];
+            *reinterpret_cast<u32x4 *>(&L.k[rr * D + (((c8 >> 3) ^ swz_row<D>(rr)) << 3)]) = pk[e0];
             *reinterpret_cast<u32x4 *>(&L.v[rr][c8]) = pv[e0];
         }
         __syncthreads();
@@ -536,7 +553,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
         const int kr = perm32(n);
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-            s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.k[kr][16 * ks + 8 * g])), as_bf16x8(qf[ks]), s);
+            s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.k[kr * D + (((2 * ks + g) ^ swz_row<D>(kr)) << 3)])),
+                       as_bf16x8(qf[ks]), s);
             dp = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.v[kr][16 * ks + 8 * g])), as_bf16x8(gf[ks]), dp);
         }
         // lane holds keys 16 g + i of the subtile for query n
@@ -555,7 +573,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
         for (int ft = 0; ft < D / 32; ++ft) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)   // K^T rows 32 ft + perm32(n), keys 16 g + 8 ks .. + 8
-                acc[ft] = mfma32(as_bf16x8(xt_frag_rows<D + 8>(&L.k[0][0], 16 * g + 8 * ks, ft, lane)), as_bf16x8(gfr[ks]),
+                acc[ft] = mfma32(as_bf16x8(xt_frag<D>(L.k, 16 * g + 8 * ks, ft, lane)), as_bf16x8(gfr[ks]),
                                  acc[ft]);
         }
     }
@@ -587,31 +605,6 @@ __device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
 __device__ __forceinline__ void dma16(Rsrc r, unsigned char *lds, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 16, (int)voff, 0, 0, 0);
 }
-
-// 16-byte chunk swizzle of the staged Q and dO rows (D/8 chunks each), so that the fragment
-// reads (rows 32 x + perm32(n) of 16 lanes, one chunk) hit distinct LDS bank groups, and the
-// transposing reads (four consecutive rows per chunk column) land on different chunks.
-template <int D>
-__device__ __forceinline__ int swz_row(int r) {
-    if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | ((r >> 1) & 8);
-    else return ((r >> 1) & 3) | ((r >> 2) & 4);
-}
-
-// The fragment of xt_frag_rows from the staged, chunk-swizzled 64 x D tile X (rows are
-// queries q0 .. q0 + 7 here).
-template <int D>
-__device__ __forceinline__ u32x4 xt_frag(const uint16_t *X, int q0, int ft, int lane) {
-    const int s = lane & 15, t = s & 3, G = (lane >> 4) & 1;
-    const int d = 32 * ft + 8 * G + 16 * (t & 1) + 4 * (t >> 1);
-    u32x2 h[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int r = q0 + 4 * hh + (s >> 2);
-        h[hh] = ds_read_tr16(X + r * D + (((d >> 3) ^ swz_row<D>(r)) << 3) + (d & 7));
-    }
-    return u32x4{h[0].x, h[0].y, h[1].x, h[1].y};
-}
-
 
 
 // One query block's operands, staged unpadded with swizzled chunks by direct-to-LDS loads:

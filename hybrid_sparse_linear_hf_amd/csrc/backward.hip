@@ -35,6 +35,10 @@ namespace {
 
 constexpr int kQB = 64;   // query-block stages hold 64 rows (a short block repeats its last query)
 
+// int32 data a kernel only reads and an earlier launch wrote, addressed through the
+// constant address space so that uniform reads become scalar loads
+typedef const __attribute__((address_space(4))) int32_t *cint32_p;
+
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
 
 __device__ __forceinline__ u32x4 f32x8_to_bf16(const float *p) {
@@ -94,16 +98,19 @@ __global__ __launch_bounds__(256) void prep_keys_kernel(hf_bwd_args a) {
     }
 }
 
-// The key blocks of every plane in descending order of the number of query blocks that
-// kept them (counting sort, one workgroup).  The dk/dv pass takes its workgroups in this
-// order -- the longest first -- so that no long one starts last; within a count the order
-// is whatever the atomics give, which changes timing only (every workgroup writes its own
-// key block).
+// The dk/dv pass's work order.  Key blocks (bh * nkb + j) are cut into 8 contiguous shares,
+// one per XCD (dispatch places workgroup x on XCD x % 8, and the pass maps it to slot
+// (x % 8) * share + x / 8), so that one XCD's L2 holds the Q and dO rows of about one and a
+// half planes; within each share the key blocks are sorted by descending number of query
+// blocks that kept them (counting sort, one workgroup per share), so that the longest work
+// starts first.  Ties are ordered by the atomics, which changes timing only: every workgroup
+// writes its own key block.
 constexpr int kOrderBuckets = 2048;
 __global__ __launch_bounds__(1024) void order_kernel(hf_bwd_args a) {
     __shared__ int start[kOrderBuckets];
     __shared__ int part[1024];
-    const int items = a.BH * a.nkb, t = threadIdx.x;
+    const int items = a.BH * a.nkb, share = (items + 7) / 8, t = threadIdx.x;
+    const int lo = (int)blockIdx.x * share, hi = min(lo + share, items);
     auto bucket = [&](int it) {
         const int32_t *off = a.qoff + (size_t)(it / a.nkb) * (a.nkb + 1);
         const int j = it % a.nkb;
@@ -111,7 +118,7 @@ __global__ __launch_bounds__(1024) void order_kernel(hf_bwd_args a) {
     };
     start[2 * t] = start[2 * t + 1] = 0;
     __syncthreads();
-    for (int it = t; it < items; it += 1024) atomicAdd(&start[bucket(it)], 1);
+    for (int it = lo + t; it < hi; it += 1024) atomicAdd(&start[bucket(it)], 1);
     __syncthreads();
     // exclusive scan over the buckets: thread t holds buckets 2t, 2t+1; Hillis-Steele over
     // the 1024 pair sums
@@ -128,7 +135,7 @@ __global__ __launch_bounds__(1024) void order_kernel(hf_bwd_args a) {
     start[2 * t] = base;
     start[2 * t + 1] = base + c0;
     __syncthreads();
-    for (int it = t; it < items; it += 1024) a.korder[atomicAdd(&start[bucket(it)], 1)] = it;
+    for (int it = lo + t; it < hi; it += 1024) a.korder[lo + atomicAdd(&start[bucket(it)], 1)] = it;
 }
 
 // A fp32 [BH][D][D] matrix into bf16 rows and bf16 transposed rows, one workgroup per
@@ -466,7 +473,7 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p) {
 // as two transposing reads of four rows.  In a 16-lane group (n = 16 G + i) lane s points
 // at row q0 + 4 h + s / 4, features 32 ft + 8 G + 16 ((s % 4) & 1) + 4 ((s % 4) >> 1) .. + 3,
 // so that lane i receives feature 32 ft + perm32(16 G + i).
-template <int D>
+template <int D, bool OPAQUE = false>
 __device__ __forceinline__ u32x4 xt_frag(const uint16_t *X, int q0, int ft, int lane) {
     const int s = lane & 15, t = s & 3, G = (lane >> 4) & 1;
     const int d = 32 * ft + 8 * G + 16 * (t & 1) + 4 * (t >> 1);
@@ -474,7 +481,13 @@ __device__ __forceinline__ u32x4 xt_frag(const uint16_t *X, int q0, int ft, int 
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         const int r = q0 + 4 * hh + (s >> 2);
-        h[hh] = ds_read_tr16(X + r * D + (((d >> 3) ^ swz_row<D>(r)) << 3) + (d & 7));
+        int e = r * D + (((d >> 3) ^ swz_row<D>(r)) << 3) + (d & 7);
+        // OPAQUE (tiles that direct-to-LDS fetches refill): the offset is hidden from the
+        // optimizer, which would otherwise rebuild the second row's address as "first + 1024
+        // bytes" outside the stage object's bounds; the compiler's wait tracking would then
+        // assume the read may touch any stage and wait for every fetch in flight
+        if constexpr (OPAQUE) asm volatile("" : "+v"(e));
+        h[hh] = ds_read_tr16(X + e);
     }
     return u32x4{h[0].x, h[0].y, h[1].x, h[1].y};
 }
@@ -611,8 +624,9 @@ __device__ __forceinline__ void dma16(Rsrc r, unsigned char *lds, uint32_t voff)
 // Q and dO rows (rows of D, chunk c of row r at slot c ^ swz_row(r)), and the block's lse
 // and Delta values.
 template <int D>
-struct QBlockStage {
+struct QStage {
     uint16_t q[kQB * D], g[kQB * D];
+    float aux[2][kQB];            // lse, Delta
 };
 constexpr int kStagesKV = 4;   // query-block stages: up to three blocks ahead are in flight
 
@@ -624,7 +638,8 @@ constexpr int kStagesKV = 4;   // query-block stages: up to three blocks ahead a
 // query-tile halves of each key tile are added at the end.
 template <int D, int NKT, int NQT>
 __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, float c_log2, float inv_sqrt_d) {
-    constexpr int NW = NKT * NQT, NTH = 64 * NW;
+    constexpr int NW = NKT * NQT;
+    constexpr int NTF = D / 32;                    // 32-feature tiles of dk, dv
     constexpr int LPR = D / 8, RPI = 64 / LPR;    // chunks per row, rows per load instruction
     constexpr int NI = kQB * D * 2 / 1024;         // load instructions per operand (16 for D = 128)
     static_assert(NI % NW == 0, "load split");
@@ -634,11 +649,23 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
     // stages: one fewer when the loads of two blocks ahead would not fit the wait counter
     constexpr int NS = 2 * PER < 64 ? kStagesKV : kStagesKV - 1;
     static_assert(PER * (NS - 2) < 64, "vmcnt range");
-    __shared__ __align__(16) QBlockStage<D> S[NS];
-    __shared__ __align__(16) float s_aux[NS][2][kQB];      // lse, Delta
-    static_assert(sizeof(S) >= (size_t)2 * D * 32 * 4, "reduction space");
-    (void)NTH;
-    const int item = a.korder[blockIdx.x];   // longest work first
+    // one __shared__ object per stage, addressed only with compile-time stage numbers: the
+    // compiler then tells each stage's direct-to-LDS writes from the reads of the others and
+    // does not wait for the fetches in flight before reading the current stage
+    __shared__ __align__(16) QStage<D> S0, S1, S2, S3;
+    static_assert(sizeof(S0) >= (size_t)2 * D * 32 * 4, "reduction space");
+    auto stage = [&](auto ic) -> QStage<D> & {
+        constexpr int k = decltype(ic)::value % NS;
+        if constexpr (k == 0) return S0;
+        else if constexpr (k == 1) return S1;
+        else if constexpr (k == 2) return S2;
+        else return S3;
+    };
+    // this XCD's share of the key blocks, longest work first
+    const int items = a.BH * a.nkb, share = (items + 7) / 8;
+    const int slot = (blockIdx.x & 7) * share + (blockIdx.x >> 3);
+    if (slot >= items) return;   // uniform per workgroup, before any barrier
+    const int item = ((cint32_p)a.korder)[slot];
     const int bh = item / a.nkb, j = item % a.nkb;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
@@ -647,9 +674,9 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
     const int nvk = min(32, min(j * a.bk + a.bk, a.Nk) - kj0);   // keys of this wave (<= 0: none)
     const int key = kj0 + n;                                     // < NkP whenever nvk > 0
     const bool kvalid = n < nvk;
-    f32x16 accV[D / 32], accK[D / 32];
+    f32x16 accV[NTF], accK[NTF];
 #pragma unroll
-    for (int ft = 0; ft < D / 32; ++ft) accV[ft] = accK[ft] = f32x16{};
+    for (int fi = 0; fi < NTF; ++fi) accV[fi] = accK[fi] = f32x16{};
     u32x4 kf[D / 16], vf[D / 16];
     {
         const size_t krow = ((size_t)bh * a.NkP + (nvk > 0 ? key : j * a.bk)) * D + 8 * g;
@@ -663,11 +690,15 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
     const Rsrc rg = make_rsrc(a.gr + (size_t)bh * a.Nq * D, (uint32_t)((size_t)a.Nq * D * 2));
     const Rsrc rl = make_rsrc(a.lse + (size_t)bh * a.Nq, (uint32_t)((size_t)a.Nq * 4));
     const Rsrc rd = make_rsrc(a.delta + (size_t)bh * a.NqP, (uint32_t)((size_t)a.NqP * 4));
-    const int32_t *off = a.qoff + (size_t)bh * (a.nkb + 1);
-    const int32_t *list = a.qlist + (size_t)bh * a.nqb * a.top_k;
+    // the work lists are read through scalar loads (constant address space: written by
+    // earlier launches, read-only here), so that no vector load -- and no wait for one -- sits
+    // among the direct-to-LDS fetches, whose counted waits assume they are the only vector
+    // memory operations in flight
+    const cint32_p off = (cint32_p)(a.qoff + (size_t)bh * (a.nkb + 1));
+    const cint32_p list = (cint32_p)(a.qlist + (size_t)bh * a.nqb * a.top_k);
     const int p0 = off[j], p1 = off[j + 1];
-    // fetch query block p into stage st: every wave issues its PER instructions
-    auto fetch = [&](int p, int st) {
+    // fetch query block p into stage T: every wave issues its PER instructions
+    auto fetch = [&](int p, QStage<D> &T) {
         const int i = min(max(list[p], 0), a.nqb - 1);
         const int q0 = i * a.bq, nqv = min(a.bq, a.Nq - q0);
 #pragma unroll
@@ -675,33 +706,39 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
             // rows of D: lane -> row RPI jj + lane / LPR, slot lane % LPR
             const int r = RPI * jj + lane / LPR, c = (lane % LPR) ^ swz_row<D>(r);
             const uint32_t ro = (uint32_t)(((q0 + min(r, nqv - 1)) * D + 8 * c) * 2);
-            dma16(rq, reinterpret_cast<unsigned char *>(S[st].q) + jj * 1024, ro);
-            dma16(rg, reinterpret_cast<unsigned char *>(S[st].g) + jj * 1024, ro);
+            dma16(rq, reinterpret_cast<unsigned char *>(T.q) + jj * 1024, ro);
+            dma16(rg, reinterpret_cast<unsigned char *>(T.g) + jj * 1024, ro);
         }
         const uint32_t eo = (uint32_t)((q0 + min(lane, nqv - 1)) * 4);
         if (NW == 1 || (w & 1) == 0)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (LdsPtr)&s_aux[st][0][0], 4, (int)eo, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (LdsPtr)&T.aux[0][0], 4, (int)eo, 0, 0, 0);
         if (NW == 1 || (w & 1) == 1)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (LdsPtr)&s_aux[st][1][0], 4, (int)eo, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (LdsPtr)&T.aux[1][0], 4, (int)eo, 0, 0, 0);
     };
-#pragma unroll
-    for (int c = 0; c < NS - 1; ++c)
-        if (p0 + c < p1) fetch(p0 + c, c);
-    for (int p = p0; p < p1; ++p) {
-        const int st = (p - p0) % NS;
+    // (a key block no query block kept skips the loop and writes zero gradients)
+    // Every step fetches, past the end repeating the last block into a stage that is not
+    // read again, so that exactly NS - 2 blocks' loads follow block p's at its wait: one
+    // constant count, which the compiler's own wait tracking follows exactly (a fetch under
+    // a branch makes it fall back to waiting for every load in flight).
+    if (p0 < p1) {
+        fetch(p0, stage(std::integral_constant<int, 0>{}));
+        fetch(min(p0 + 1, p1 - 1), stage(std::integral_constant<int, 1>{}));
+        if constexpr (NS > 3) fetch(min(p0 + 2, p1 - 1), stage(std::integral_constant<int, 2>{}));
+    }
+    // block p (the ST-th of its group of NS) is in stage ST
+    auto step = [&](int p, auto ic) __attribute__((always_inline)) {
+        constexpr int ST = decltype(ic)::value;
+        QStage<D> &cur = stage(ic);
         const int i = min(max(list[p], 0), a.nqb - 1);
         const int nqv = min(a.bq, a.Nq - i * a.bq);
-        // this wave's loads of block p have landed (later blocks may still fly); then
-        // everyone's, and everyone is done with block p - 1, whose stage is refilled next
-        const int later = min(NS - 2, p1 - 1 - p);
-        if (NS > 3 && later >= 2) wait_vm<(NS > 3 ? 2 * PER : 0)>();
-        else if (later == 1) wait_vm<PER>();
-        else wait_vm<0>();
-        __syncthreads();
-        if (p + NS - 1 < p1) fetch(p + NS - 1, (p - p0 + NS - 1) % NS);
-        if (nvk <= 0 || 32 * qt >= nqv) continue;   // uniform per wave; the barrier is above
-        const uint16_t *Lq = S[st].q, *Lg = S[st].g;
-        const float *s_lse = s_aux[st][0], *s_delta = s_aux[st][1];
+        // this wave's loads of block p have landed (the next NS - 2 blocks' may still fly);
+        // then everyone's, and everyone is done with block p - 1, whose stage is refilled next
+        wait_vm<(NS - 2) * PER>();
+        lds_barrier();   // not __syncthreads(): its fence would wait for the fetches in flight
+        fetch(min(p + NS - 1, p1 - 1), stage(std::integral_constant<int, ST + NS - 1>{}));
+        if (nvk <= 0 || 32 * qt >= nqv) return;   // uniform per wave; the barrier is above
+        const uint16_t *Lq = cur.q, *Lg = cur.g;
+        const float *s_lse = cur.aux[0], *s_delta = cur.aux[1];
         // S and dP for queries 32 qt + (rows in perm32 order), this wave's keys
         const int qr = 32 * qt + perm32(n);
         const int qsw = swz_row<D>(qr);
@@ -735,58 +772,69 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
         // 32 qt + 16 g + 8 ks .. + 8, the order in which P and G are packed).  Rows past the
         // block's end repeat its last query and meet P = G = 0.
 #pragma unroll
-        for (int ft = 0; ft < D / 32; ++ft) {
+        for (int fi = 0; fi < NTF; ++fi) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int q0 = 32 * qt + 16 * g + 8 * ks;
-                accV[ft] = mfma32(as_bf16x8(xt_frag<D>(Lg, q0, ft, lane)), as_bf16x8(pf[ks]), accV[ft]);
-                accK[ft] = mfma32(as_bf16x8(xt_frag<D>(Lq, q0, ft, lane)), as_bf16x8(gfr[ks]), accK[ft]);
+                accV[fi] = mfma32(as_bf16x8(xt_frag<D, true>(Lg, q0, fi, lane)), as_bf16x8(pf[ks]), accV[fi]);
+                accK[fi] = mfma32(as_bf16x8(xt_frag<D, true>(Lq, q0, fi, lane)), as_bf16x8(gfr[ks]), accK[fi]);
             }
         }
+    };
+    int p = p0;
+    for (; p + NS <= p1; p += NS) {
+        step(p, std::integral_constant<int, 0>{});
+        step(p + 1, std::integral_constant<int, 1>{});
+        step(p + 2, std::integral_constant<int, 2>{});
+        if constexpr (NS > 3) step(p + 3, std::integral_constant<int, 3>{});
     }
+    if (p < p1) step(p, std::integral_constant<int, 0>{});
+    if (p + 1 < p1) step(p + 1, std::integral_constant<int, 1>{});
+    if (NS > 3 && p + 2 < p1) step(p + 2, std::integral_constant<int, 2>{});
     __builtin_amdgcn_s_waitcnt(0x0F70);   // no load in flight before the stages are reused
     if constexpr (NQT > 1) {
-        // query-tile halves, one key tile at a time: the wave with qt = 1 hands its sums to
-        // the wave with qt = 0
-        float *red = reinterpret_cast<float *>(&S[0]);
+        // query-tile halves, one key tile at a time: the waves with qt = 1 hand their sums
+        // to the waves with qt = 0
+        float *red = reinterpret_cast<float *>(&S0);
         for (int kk = 0; kk < NKT; ++kk) {
             __syncthreads();
             if (qt == 1 && kt == kk) {
 #pragma unroll
-                for (int ft = 0; ft < D / 32; ++ft)
+                for (int fi = 0; fi < NTF; ++fi)
 #pragma unroll
                     for (int i2 = 0; i2 < 16; ++i2) {
-                        red[(0 * (D / 32) + ft) * 16 * 64 + i2 * 64 + lane] = accV[ft][i2];
-                        red[(1 * (D / 32) + ft) * 16 * 64 + i2 * 64 + lane] = accK[ft][i2];
+                        red[(0 * (D / 32) + fi) * 16 * 64 + i2 * 64 + lane] = accV[fi][i2];
+                        red[(1 * (D / 32) + fi) * 16 * 64 + i2 * 64 + lane] = accK[fi][i2];
                     }
             }
             __syncthreads();
             if (qt == 0 && kt == kk) {
 #pragma unroll
-                for (int ft = 0; ft < D / 32; ++ft)
+                for (int fi = 0; fi < NTF; ++fi)
 #pragma unroll
                     for (int i2 = 0; i2 < 16; ++i2) {
-                        accV[ft][i2] += red[(0 * (D / 32) + ft) * 16 * 64 + i2 * 64 + lane];
-                        accK[ft][i2] += red[(1 * (D / 32) + ft) * 16 * 64 + i2 * 64 + lane];
+                        accV[fi][i2] += red[(0 * (D / 32) + fi) * 16 * 64 + i2 * 64 + lane];
+                        accK[fi][i2] += red[(1 * (D / 32) + fi) * 16 * 64 + i2 * 64 + lane];
                     }
             }
         }
         if (qt != 0) return;
     }
     if (kvalid) {
-        // lane (key n) holds features 32 ft + 16 g + i
+        // lane (key n) holds features 32 fi + 16 g + i of its feature tiles fi
         float *dvp = a.dv + ((size_t)bh * a.Nk + key) * D + 16 * g;
         float *dkp = a.dk + ((size_t)bh * a.Nk + key) * D + 16 * g;
 #pragma unroll
-        for (int ft = 0; ft < D / 32; ++ft)
+        for (int fi = 0; fi < NTF; ++fi) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                *reinterpret_cast<f32x4 *>(dvp + 32 * ft + 4 * v) =
-                    f32x4{accV[ft][4 * v], accV[ft][4 * v + 1], accV[ft][4 * v + 2], accV[ft][4 * v + 3]};
-                *reinterpret_cast<f32x4 *>(dkp + 32 * ft + 4 * v) =
-                    f32x4{accK[ft][4 * v] * inv_sqrt_d, accK[ft][4 * v + 1] * inv_sqrt_d,
-                          accK[ft][4 * v + 2] * inv_sqrt_d, accK[ft][4 * v + 3] * inv_sqrt_d};
+                *reinterpret_cast<f32x4 *>(dvp + 32 * fi + 4 * v) =
+                    f32x4{accV[fi][4 * v], accV[fi][4 * v + 1], accV[fi][4 * v + 2], accV[fi][4 * v + 3]};
+                *reinterpret_cast<f32x4 *>(dkp + 32 * fi + 4 * v) =
+                    f32x4{accK[fi][4 * v] * inv_sqrt_d, accK[fi][4 * v + 1] * inv_sqrt_d,
+                          accK[fi][4 * v + 2] * inv_sqrt_d, accK[fi][4 * v + 3] * inv_sqrt_d};
             }
+        }
     }
 }
 
@@ -862,19 +910,22 @@ hipError_t launch_attn_backward(const hf_bwd_args &a, hipStream_t s) {
     hipLaunchKernelGGL(prep_keys_kernel<D>, dim3((unsigned)(a.BH * (a.NkP / 64))), dim3(256), 0, s, a);
     hipLaunchKernelGGL(prep_queries_kernel<D>, dim3((unsigned)(a.BH * a.nqb + a.BH * nt * nt)), dim3(256), 0, s, a);
     hipLaunchKernelGGL(csr_kernel, dim3((unsigned)a.BH), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(order_kernel, dim3(8), dim3(1024), 0, s, a);
     hipLaunchKernelGGL(readout_bwd_kernel<D>, dim3((unsigned)(a.BH * a.splits)), dim3(128), 0, s, a);
     hipLaunchKernelGGL(reduce_readout_kernel<D>, dim3((unsigned)(a.BH * nt * nt)), dim3(256), 0, s, a);
     if (a.bq > 32)
         hipLaunchKernelGGL((dq_kernel<D, 2>), dim3((unsigned)(a.BH * a.nqb)), dim3(128), 0, s, a, c_log2, inv_sqrt_d, lsh);
     else
         hipLaunchKernelGGL((dq_kernel<D, 1>), dim3((unsigned)(a.BH * a.nqb)), dim3(64), 0, s, a, c_log2, inv_sqrt_d, lsh);
-    const dim3 gk((unsigned)(a.BH * a.nkb));
-    // key tiles (bk / 32, at least 1) x query tiles (bq / 32, at least 1) waves
+    const dim3 gk((unsigned)((a.BH * a.nkb + 7) / 8 * 8));
+    // key tiles (bk / 32, at least 1) x query tiles (bq / 32, at least 1) waves; with 64 x 64
+    // blocks at D = 128 each of those is split over two waves by feature half (two waves per
+    // SIMD; their S and dP products repeat)
     if (a.bq > 32) {
         if (a.bk > 64) hipLaunchKernelGGL((dkdv_kernel<D, 4, 2>), gk, dim3(512), 0, s, a, c_log2, inv_sqrt_d);
-        else if (a.bk > 32) hipLaunchKernelGGL((dkdv_kernel<D, 2, 2>), gk, dim3(256), 0, s, a, c_log2, inv_sqrt_d);
-        else hipLaunchKernelGGL((dkdv_kernel<D, 1, 2>), gk, dim3(128), 0, s, a, c_log2, inv_sqrt_d);
+        else if (a.bk > 32) {
+            hipLaunchKernelGGL((dkdv_kernel<D, 2, 2>), gk, dim3(256), 0, s, a, c_log2, inv_sqrt_d);
+        } else hipLaunchKernelGGL((dkdv_kernel<D, 1, 2>), gk, dim3(128), 0, s, a, c_log2, inv_sqrt_d);
     } else {
         if (a.bk > 64) hipLaunchKernelGGL((dkdv_kernel<D, 4, 1>), gk, dim3(256), 0, s, a, c_log2, inv_sqrt_d);
         else if (a.bk > 32) hipLaunchKernelGGL((dkdv_kernel<D, 2, 1>), gk, dim3(128), 0, s, a, c_log2, inv_sqrt_d);

@@ -749,17 +749,30 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
             s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(Lq + qr * D + cs)), as_bf16x8(kf[ks]), s);
             dp = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(Lg + qr * D + cs)), as_bf16x8(vf[ks]), dp);
         }
-        // lane (key n) holds queries 32 qt + 16 g + i
+        // lane (key n) holds queries 32 qt + 16 g + i.  Only query rows past the block's end
+        // are masked (they repeat its last query): a key past the end feeds only its own
+        // columns of dv, dk, which are never stored.
         const int qb0 = 32 * qt + 16 * g;
-        float pv[16], gv[16];
+        float lv[16], dl[16];
 #pragma unroll
-        for (int i2 = 0; i2 < 16; ++i2) {
-            const int qq = qb0 + i2;
-            const bool ok = kvalid && qq < nqv;
-            const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i2], c_log2, -s_lse[qq])) : 0.f;
-            pv[i2] = pr;
-            gv[i2] = pr * (dp[i2] - s_delta[qq]);
+        for (int v = 0; v < 4; ++v) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4 *>(s_lse + qb0 + 4 * v);
+            const f32x4 d4 = *reinterpret_cast<const f32x4 *>(s_delta + qb0 + 4 * v);
+            lv[4 * v] = l4.x, lv[4 * v + 1] = l4.y, lv[4 * v + 2] = l4.z, lv[4 * v + 3] = l4.w;
+            dl[4 * v] = d4.x, dl[4 * v + 1] = d4.y, dl[4 * v + 2] = d4.z, dl[4 * v + 3] = d4.w;
         }
+        float pv[16], gv[16];
+        auto terms = [&](auto masked) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i2 = 0; i2 < 16; ++i2) {
+                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i2], c_log2, -lv[i2]));
+                if constexpr (decltype(masked)::value) pr = qb0 + i2 < nqv ? pr : 0.f;
+                pv[i2] = pr;
+                gv[i2] = pr * (dp[i2] - dl[i2]);
+            }
+        };
+        if (32 * qt + 32 <= nqv) terms(std::false_type{});   // uniform per wave
+        else terms(std::true_type{});
         u32x4 pf[2], gfr[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {

@@ -571,12 +571,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
             dp = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.v[kr][16 * ks + 8 * g])), as_bf16x8(gf[ks]), dp);
         }
         // lane holds keys 16 g + i of the subtile for query n
+        // (keys past the subtile's valid ones are masked; a full subtile has none)
         float gt[16];
+        auto terms = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float p = (16 * g + i < nv) ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c_log2, -Lq)) : 0.f;
-            gt[i] = p * (dp[i] - Dl);
-        }
+            for (int i = 0; i < 16; ++i) {
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c_log2, -Lq));
+                if constexpr (decltype(masked)::value) p = 16 * g + i < nv ? p : 0.f;
+                gt[i] = p * (dp[i] - Dl);
+            }
+        };
+        if (nv >= 32) terms(std::false_type{});   // uniform per wave
+        else terms(std::true_type{});
         u32x4 gfr[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)

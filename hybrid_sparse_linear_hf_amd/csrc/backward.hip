@@ -229,6 +229,55 @@ __global__ __launch_bounds__(256) void csr_kernel(hf_bwd_args a) {
     }
 }
 
+// ---------------------------------------------------------------- staged-row helpers
+
+// 16-byte chunk swizzle of staged rows of D (S in the readout pass, Q and dO rows in the dk/dv
+// pass, K rows in the dq pass): chunk c of row r sits at slot c ^ swz_row(r).  For D = 128 the row's two low
+// bits go to slot bits 2-3, bit 2 to bit 0 and bit 4 to bit 1, so that (a) the fragment
+// reads of rows 32 x + perm32(n), one chunk per 16 lanes, hit 16 distinct bank groups, and
+// (b) the transposing reads -- four consecutive rows, chunk offsets 0 and 2 within them --
+// land on 16 distinct (chunk, half) slots.
+template <int D>
+__device__ __forceinline__ int swz_row(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
+    else return ((r >> 1) & 3) | ((r >> 2) & 4);
+}
+
+// Transposing LDS read (gfx950): within each 16-lane group, lane i receives element i % 4 of
+// the 4-element vectors that lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12 of the group point
+// at (one per returned element).
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p) {
+    const v4s16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s16 *)(const_cast<uint16_t *>(p)));
+    return u32x2{(uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16),
+                 (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16)};
+}
+
+// Matrix-core A fragment of X^T from staged, chunk-swizzled rows of D (swz_row): lane
+// (n, g) receives features 32 ft + perm32(n) of rows q0 .. q0 + 7 (q0 for its lane half),
+// as two transposing reads of four rows.  In a 16-lane group (n = 16 G + i) lane s points
+// at row q0 + 4 h + s / 4, features 32 ft + 8 G + 16 ((s % 4) & 1) + 4 ((s % 4) >> 1) .. + 3,
+// so that lane i receives feature 32 ft + perm32(16 G + i).
+template <int D, bool OPAQUE = false>
+__device__ __forceinline__ u32x4 xt_frag(const uint16_t *X, int q0, int ft, int lane) {
+    const int s = lane & 15, t = s & 3, G = (lane >> 4) & 1;
+    const int d = 32 * ft + 8 * G + 16 * (t & 1) + 4 * (t >> 1);
+    u32x2 h[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int r = q0 + 4 * hh + (s >> 2);
+        int e = r * D + (((d >> 3) ^ swz_row<D>(r)) << 3) + (d & 7);
+        // OPAQUE (tiles that direct-to-LDS fetches refill): the offset is hidden from the
+        // optimizer, which would otherwise rebuild the second row's address as "first + 1024
+        // bytes" outside the stage object's bounds; the compiler's wait tracking would then
+        // assume the read may touch any stage and wait for every fetch in flight
+        if constexpr (OPAQUE) asm volatile("" : "+v"(e));
+        h[hh] = ds_read_tr16(X + e);
+    }
+    return u32x4{h[0].x, h[0].y, h[1].x, h[1].y};
+}
+
 // ---------------------------------------------------------------- readout pass
 
 // One workgroup (two waves) per (plane, split); split s takes 64-query chunks
@@ -238,19 +287,19 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
     __shared__ __align__(16) uint16_t phT[D][kQB + 8];
     __shared__ __align__(16) uint16_t dnT[D][kQB + 8];
     __shared__ __align__(16) float dden_s[kQB];
-    // S and S^T in bf16, staged once for all the workgroup's chunks (rows padded by 16 bytes,
-    // so the 16 rows a fragment read touches fall in distinct bank groups)
-    __shared__ __align__(16) uint16_t s_sb[D][D + 8], s_stb[D][D + 8];
+    // S in bf16, staged once for all the workgroup's chunks as chunk-swizzled rows of D
+    // (swz_row): its row fragments are read directly, those of S^T by transposing reads
+    __shared__ __align__(16) uint16_t s_sw[D * D];
     const int bh = blockIdx.x / a.splits, sp = blockIdx.x % a.splits;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
     const int nchunks = (a.Nq + kQB - 1) / kQB;
     const float *zp = a.z + (size_t)bh * D;
     {
-        const uint16_t *sbg = a.sb + (size_t)bh * D * D, *stg = a.stb + (size_t)bh * D * D;
+        const uint16_t *sbg = a.sb + (size_t)bh * D * D;
         for (int e = threadIdx.x; e < D * D / 8; e += 128) {
-            const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
-            *reinterpret_cast<u32x4 *>(&s_sb[r][c8]) = *reinterpret_cast<const u32x4 *>(sbg + r * D + c8);
-            *reinterpret_cast<u32x4 *>(&s_stb[r][c8]) = *reinterpret_cast<const u32x4 *>(stg + r * D + c8);
+            const int r = e / (D / 8), c = e % (D / 8);
+            *reinterpret_cast<u32x4 *>(&s_sw[r * D + ((c ^ swz_row<D>(r)) << 3)]) =
+                *reinterpret_cast<const u32x4 *>(sbg + r * D + 8 * c);
         }
         __syncthreads();
     }
@@ -291,10 +340,9 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
 #pragma unroll
         for (int ft = 0; ft < NT; ++ft) {
             f32x16 acc = {};
-            const uint16_t *srow = &s_stb[32 * ft + perm32(n)][8 * g];
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
-                acc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(srow + 16 * ks)), as_bf16x8(pq[ks]), acc);
+            for (int ks = 0; ks < D / 16; ++ks)   // S^T rows 32 ft + perm32(n), features 16 ks + 8 g .. + 8
+                acc = mfma32(as_bf16x8(xt_frag<D>(s_sw, 16 * ks + 8 * g, ft, lane)), as_bf16x8(pq[ks]), acc);
             const float *gp = a.dout + row * D + 32 * ft + 16 * g;
             const float *op = a.out + row * D + 32 * ft + 16 * g;
 #pragma unroll
@@ -323,10 +371,12 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
 #pragma unroll
         for (int ft = 0; ft < NT; ++ft) {
             f32x16 acc = {};
-            const uint16_t *srow = &s_sb[32 * ft + perm32(n)][8 * g];
+            const int sr = 32 * ft + perm32(n);
+            const uint16_t *srow = s_sw + sr * D;
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks)
-                acc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(srow + 16 * ks)), as_bf16x8(dnf[ks]), acc);
+                acc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(srow + (((2 * ks + g) ^ swz_row<D>(sr)) << 3))),
+                             as_bf16x8(dnf[ks]), acc);
             if (valid) {
                 const int a0 = 32 * ft + 16 * g;
                 const u32x4 q0 = *reinterpret_cast<const u32x4 *>(a.q + row * D + a0);
@@ -411,32 +461,30 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
     if (threadIdx.x < D) a.dzp[((size_t)bh * a.splits + sp) * D + threadIdx.x] = dz_acc;
 }
 
-// Sum of `splits` partials p at src[p * stride] in split order; the loads of eight splits
+// Sum of `splits` partials p at src[p * stride] in split order; the loads of sixteen splits
 // are issued before their adds, which keep the order (so the result is the serial sum).
 __device__ __forceinline__ float ordered_split_sum(const float *src, size_t stride, int splits) {
     float s = 0.f;
-    for (int p0 = 0; p0 < splits; p0 += 8) {
-        float v[8];
+    for (int p0 = 0; p0 < splits; p0 += 16) {
+        float v[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = p0 + u < splits ? src[(size_t)(p0 + u) * stride] : 0.f;
+        for (int u = 0; u < 16; ++u) v[u] = p0 + u < splits ? src[(size_t)(p0 + u) * stride] : 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 16; ++u)
             if (p0 + u < splits) s += v[u];
     }
     return s;
 }
 
-// dS, dz = sum of the split partials in split order (one workgroup per plane and 32x32
-// tile; the first tile of a plane also adds dz).
+// dS, dz = sum of the split partials in split order: one element of dS per thread
+// (D * D / 256 workgroups per plane); the plane's first workgroup also adds dz.
 template <int D>
 __global__ __launch_bounds__(256) void reduce_readout_kernel(hf_bwd_args a) {
-    constexpr int nt = D / 32;
-    const int bh = blockIdx.x / (nt * nt), tile = blockIdx.x % (nt * nt);
-    const int r0 = 32 * (tile / nt), c0 = 32 * (tile % nt);
-    for (int e = threadIdx.x; e < 32 * 32; e += 256) {
-        const int r = r0 + e / 32, c = c0 + e % 32;
-        a.dS[(size_t)bh * D * D + (size_t)r * D + c] =
-            ordered_split_sum(a.dsp + (size_t)bh * a.splits * D * D + (size_t)r * D + c, (size_t)D * D, a.splits);
+    constexpr int per = D * D / 256;
+    const int bh = blockIdx.x / per, tile = blockIdx.x % per;
+    {
+        const int e = 256 * tile + threadIdx.x;
+        a.dS[(size_t)bh * D * D + e] = ordered_split_sum(a.dsp + (size_t)bh * a.splits * D * D + e, (size_t)D * D, a.splits);
     }
     if (tile == 0 && threadIdx.x < D)
         a.dz[(size_t)bh * D + threadIdx.x] =
@@ -445,52 +493,6 @@ __global__ __launch_bounds__(256) void reduce_readout_kernel(hf_bwd_args a) {
 
 // ---------------------------------------------------------------- dq pass
 
-// 16-byte chunk swizzle of staged rows of D (Q and dO rows in the dk/dv pass, K rows in the
-// dq pass): chunk c of row r sits at slot c ^ swz_row(r).  For D = 128 the row's two low
-// bits go to slot bits 2-3, bit 2 to bit 0 and bit 4 to bit 1, so that (a) the fragment
-// reads of rows 32 x + perm32(n), one chunk per 16 lanes, hit 16 distinct bank groups, and
-// (b) the transposing reads -- four consecutive rows, chunk offsets 0 and 2 within them --
-// land on 16 distinct (chunk, half) slots.
-template <int D>
-__device__ __forceinline__ int swz_row(int r) {
-    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
-    else return ((r >> 1) & 3) | ((r >> 2) & 4);
-}
-
-// Transposing LDS read (gfx950): within each 16-lane group, lane i receives element i % 4 of
-// the 4-element vectors that lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12 of the group point
-// at (one per returned element).
-typedef short v4s16 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p) {
-    const v4s16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4s16 *)(const_cast<uint16_t *>(p)));
-    return u32x2{(uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16),
-                 (uint32_t)(uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16)};
-}
-
-// Matrix-core A fragment of X^T from staged, chunk-swizzled rows of D (swz_row): lane
-// (n, g) receives features 32 ft + perm32(n) of rows q0 .. q0 + 7 (q0 for its lane half),
-// as two transposing reads of four rows.  In a 16-lane group (n = 16 G + i) lane s points
-// at row q0 + 4 h + s / 4, features 32 ft + 8 G + 16 ((s % 4) & 1) + 4 ((s % 4) >> 1) .. + 3,
-// so that lane i receives feature 32 ft + perm32(16 G + i).
-template <int D, bool OPAQUE = false>
-__device__ __forceinline__ u32x4 xt_frag(const uint16_t *X, int q0, int ft, int lane) {
-    const int s = lane & 15, t = s & 3, G = (lane >> 4) & 1;
-    const int d = 32 * ft + 8 * G + 16 * (t & 1) + 4 * (t >> 1);
-    u32x2 h[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int r = q0 + 4 * hh + (s >> 2);
-        int e = r * D + (((d >> 3) ^ swz_row<D>(r)) << 3) + (d & 7);
-        // OPAQUE (tiles that direct-to-LDS fetches refill): the offset is hidden from the
-        // optimizer, which would otherwise rebuild the second row's address as "first + 1024
-        // bytes" outside the stage object's bounds; the compiler's wait tracking would then
-        // assume the read may touch any stage and wait for every fetch in flight
-        if constexpr (OPAQUE) asm volatile("" : "+v"(e));
-        h[hh] = ds_read_tr16(X + e);
-    }
-    return u32x4{h[0].x, h[0].y, h[1].x, h[1].y};
-}
 
 // One workgroup per query block, one wave per 32-query tile.  Each 32-key subtile's K rows
 // (chunk-swizzled) and V rows (padded by 16 bytes) pass through LDS once for all the waves;
@@ -931,7 +933,7 @@ hipError_t launch_attn_backward(const hf_bwd_args &a, hipStream_t s) {
     hipLaunchKernelGGL(csr_kernel, dim3((unsigned)a.BH), dim3(256), 0, s, a);
     hipLaunchKernelGGL(order_kernel, dim3(8), dim3(1024), 0, s, a);
     hipLaunchKernelGGL(readout_bwd_kernel<D>, dim3((unsigned)(a.BH * a.splits)), dim3(128), 0, s, a);
-    hipLaunchKernelGGL(reduce_readout_kernel<D>, dim3((unsigned)(a.BH * nt * nt)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(reduce_readout_kernel<D>, dim3((unsigned)(a.BH * (D * D / 256))), dim3(256), 0, s, a);
     if (a.bq > 32)
         hipLaunchKernelGGL((dq_kernel<D, 2>), dim3((unsigned)(a.BH * a.nqb)), dim3(128), 0, s, a, c_log2, inv_sqrt_d, lsh);
     else
@@ -969,7 +971,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static int bwd_splits(int BH, int Nq) {
     const int chunks = (Nq + hf::kQB - 1) / hf::kQB;
-    int s = 256 / BH;
+    int s = 512 / BH;   // the readout pass fits two workgroups per CU
     s = s < 1 ? 1 : s;
     return s < chunks ? s : chunks;
 }

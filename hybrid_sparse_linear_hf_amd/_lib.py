@@ -100,13 +100,70 @@ def _check(fn: str, status: int) -> None:
         raise HFError(fn, status, lib().hf_last_error().decode())
 
 
-def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+_DTYPE_NAME = {torch.bfloat16: "bfloat16", torch.float32: "float32", torch.float64: "float64",
+               torch.int32: "int32", torch.uint8: "uint8"}
 
 
-def _stream(stream=None):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+class _T:
+    """A checked tensor argument (or None), turned into a raw pointer by _call."""
+    __slots__ = ("name", "t")
+
+    def __init__(self, name: str, t):
+        self.name, self.t = name, t
+
+
+def _arg(fn: str, name: str, t, dtype, numel: int | None, optional: bool = False) -> _T:
+    """Check one tensor argument before its pointer crosses the C ABI, which cannot see
+    dtypes, strides, sizes or devices: `dtype`, a contiguous layout and exactly `numel`
+    elements (None: any size).  The device is checked by _call, after every argument's
+    format, so a call fails on the first malformed argument whatever its device."""
+    if t is None:
+        if optional:
+            return _T(name, None)
+        raise ValueError(f"{fn}: {name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{fn}: {name} must be a torch.Tensor, not {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{fn}: {name} must be {_DTYPE_NAME[dtype]}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{fn}: {name} must be contiguous (shape {tuple(t.shape)}, strides {t.stride()})")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{fn}: {name} must hold {numel} elements, got {t.numel()} (shape {tuple(t.shape)})")
+    return _T(name, t)
+
+
+def _ws(fn: str, ws, name: str = "ws"):
+    """(checked tensor, bytes) of a workspace: a contiguous uint8 tensor (size checked by the library)."""
+    if ws is None:
+        return _T(name, None), 0
+    return _arg(fn, name, ws, torch.uint8, None), ws.numel()
+
+
+def _call(fn: str, cfunc, *args) -> None:
+    """Every checked tensor must live on a GPU; then call the C entry point with raw
+    pointers in their place and raise HFError on a non-zero status."""
+    for a in args:
+        if isinstance(a, _T) and a.t is not None and a.t.device.type != "cuda":
+            raise ValueError(f"{fn}: {a.name} must be on a GPU, got device {a.t.device}")
+    raw = [((None if a.t is None else ctypes.c_void_p(a.t.data_ptr())) if isinstance(a, _T)
+            else a.handle() if isinstance(a, _Stream) else a) for a in args]
+    _check(fn, cfunc(*raw))
+
+
+class _Stream:
+    """The HIP stream argument (torch's current stream by default), resolved by _call."""
+    __slots__ = ("s",)
+
+    def __init__(self, s):
+        self.s = s
+
+    def handle(self):
+        s = torch.cuda.current_stream() if self.s is None else self.s
+        return ctypes.c_void_p(s.cuda_stream)
+
+
+def _stream(stream=None) -> _Stream:
+    return _Stream(stream)
 
 
 def abi_version() -> int:
@@ -177,52 +234,21 @@ def new_workspace(g: Geometry, device="cuda") -> torch.Tensor:
 
 
 # ------------------------------------------------------------------ entry points
+# Each wrapper checks its tensors against the geometry (dtype, contiguity, element count,
+# device) before anything reaches the library, then passes the raw pointers.
 
-def hf_ring_append(g: Geometry, ring: Ring, k_cur, v_cur, stream=None) -> None:
-    _check("hf_ring_append", lib().hf_ring_append(ctypes.byref(g.dims()), ctypes.byref(ring.desc), _ptr(k_cur),
-                                                  _ptr(v_cur), _stream(stream)))
-
-
-def hf_block_select(g: Geometry, q, ring: Ring, top_k: int, idx, scores, ws, stream=None) -> None:
-    _check("hf_block_select",
-           lib().hf_block_select(ctypes.byref(g.dims()), _ptr(q), ctypes.byref(ring.desc), int(top_k), _ptr(idx),
-                                 _ptr(scores), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+_BF16, _F32, _F64, _I32 = torch.bfloat16, torch.float32, torch.float64, torch.int32
 
 
-def hf_block_select_hier(g: Geometry, q, ring: Ring, top_frames: int, top_k: int, idx, ws, frames=None,
-                         scores=None, frame_scores=None, stream=None) -> None:
-    _check("hf_block_select_hier",
-           lib().hf_block_select_hier(ctypes.byref(g.dims()), _ptr(q), ctypes.byref(ring.desc), int(top_frames),
-                                      int(top_k), _ptr(idx), _ptr(frames), _ptr(scores), _ptr(frame_scores),
-                                      _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+def _planes(g: Geometry) -> int:
+    return g.B * g.H
 
 
-def hf_sparse_window_attn(g: Geometry, q, ring: Ring, idx, top_k: int, S, z, out, ws, eps=1e-6, stream=None) -> None:
-    _check("hf_sparse_window_attn",
-           lib().hf_sparse_window_attn(ctypes.byref(g.dims()), _ptr(q), ctypes.byref(ring.desc), _ptr(idx),
-                                       int(top_k), _ptr(S), _ptr(z), float(eps), _ptr(out), _ptr(ws),
-                                       ws.numel() if ws is not None else 0, _stream(stream)))
-
-
-def hf_linear_absorb(g: Geometry, k_ev, v_ev, n_tok: int, S, z, ws, stream=None) -> None:
-    _check("hf_linear_absorb",
-           lib().hf_linear_absorb(ctypes.byref(g.dims()), _ptr(k_ev), _ptr(v_ev), int(n_tok), _ptr(S), _ptr(z),
-                                  _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
-
-
-def hf_hybrid_step(g: Geometry, q, k_cur, v_cur, ring: Ring, top_k: int, flags: int, S, z, idx, out, ws,
-                   eps=1e-6, events=None, stream=None) -> None:
-    """`events`: None or a sequence of 6 raw hipEvent_t handles (ints or None)."""
-    ev = None
-    if events is not None:
-        ev = StepEvents()
-        for i, e in enumerate(events):
-            ev.ev[i] = e
-    _check("hf_hybrid_step",
-           lib().hf_hybrid_step(ctypes.byref(g.dims()), _ptr(q), _ptr(k_cur), _ptr(v_cur), ctypes.byref(ring.desc),
-                                int(top_k), int(flags), _ptr(S), _ptr(z), float(eps), _ptr(idx), _ptr(out), _ptr(ws),
-                                ws.numel() if ws is not None else 0, ctypes.byref(ev) if ev is not None else None,
-                                _stream(stream)))
+def _state_args(fn: str, g: Geometry, S, z, optional: bool):
+    BH, D = _planes(g), g.D
+    if (S is None) != (z is None):
+        raise ValueError(f"{fn}: give both S and z or neither")
+    return (_arg(fn, "S", S, _F32, BH * D * D, optional), _arg(fn, "z", z, _F32, BH * D, optional))
 
 
 def _events(events):
@@ -234,23 +260,104 @@ def _events(events):
     return ctypes.byref(ev)
 
 
+def hf_ring_append(g: Geometry, ring: Ring, k_cur, v_cur, stream=None) -> None:
+    fn, n = "hf_ring_append", _planes(g) * g.Nq * g.D
+    kp, vp = _arg(fn, "k_cur", k_cur, _BF16, n), _arg(fn, "v_cur", v_cur, _BF16, n)
+    _call(fn, lib().hf_ring_append, ctypes.byref(g.dims()), ctypes.byref(ring.desc), kp, vp, _stream(stream))
+
+
+def hf_block_select(g: Geometry, q, ring: Ring, top_k: int, idx, scores, ws, stream=None) -> None:
+    fn, BH, nkb = "hf_block_select", _planes(g), g.n_kb(ring.n_committed)
+    qp = _arg(fn, "q", q, _BF16, BH * g.Nq * g.D)
+    ip = _arg(fn, "idx", idx, _I32, BH * g.n_qb * int(top_k))
+    sp = _arg(fn, "scores", scores, _F64, BH * g.n_qb * nkb, optional=True)
+    wp, wn = _ws(fn, ws)
+    _call(fn, lib().hf_block_select, ctypes.byref(g.dims()), qp, ctypes.byref(ring.desc), int(top_k), ip, sp, wp, wn,
+                                     _stream(stream))
+
+
+def hf_block_select_hier(g: Geometry, q, ring: Ring, top_frames: int, top_k: int, idx, ws, frames=None,
+                         scores=None, frame_scores=None, stream=None) -> None:
+    fn, BH, nkb = "hf_block_select_hier", _planes(g), g.n_kb(ring.n_committed)
+    nfr = ring.n_committed + g.C
+    qp = _arg(fn, "q", q, _BF16, BH * g.Nq * g.D)
+    ip = _arg(fn, "idx", idx, _I32, BH * g.n_qb * int(top_k))
+    fp = _arg(fn, "frames", frames, _I32, BH * g.n_qb * int(top_frames), optional=True)
+    sp = _arg(fn, "scores", scores, _F64, BH * g.n_qb * nkb, optional=True)
+    fsp = _arg(fn, "frame_scores", frame_scores, _F64, BH * g.n_qb * nfr, optional=True)
+    wp, wn = _ws(fn, ws)
+    _call(fn, lib().hf_block_select_hier, ctypes.byref(g.dims()), qp, ctypes.byref(ring.desc), int(top_frames),
+                                          int(top_k), ip, fp, sp, fsp, wp, wn, _stream(stream))
+
+
+def _attn_args(fn: str, g: Geometry, q, idx, top_k: int, S, z, out):
+    BH = _planes(g)
+    qp = _arg(fn, "q", q, _BF16, BH * g.Nq * g.D)
+    ip = _arg(fn, "idx", idx, _I32, BH * g.n_qb * int(top_k))
+    Sp, zp = _state_args(fn, g, S, z, optional=True)
+    op = _arg(fn, "out", out, _F32, BH * g.Nq * g.D)
+    return qp, ip, Sp, zp, op
+
+
+def hf_sparse_window_attn(g: Geometry, q, ring: Ring, idx, top_k: int, S, z, out, ws, eps=1e-6, stream=None) -> None:
+    fn = "hf_sparse_window_attn"
+    qp, ip, Sp, zp, op = _attn_args(fn, g, q, idx, top_k, S, z, out)
+    wp, wn = _ws(fn, ws)
+    _call(fn, lib().hf_sparse_window_attn, ctypes.byref(g.dims()), qp, ctypes.byref(ring.desc), ip, int(top_k), Sp,
+                                           zp, float(eps), op, wp, wn, _stream(stream))
+
+
+def hf_linear_absorb(g: Geometry, k_ev, v_ev, n_tok: int, S, z, ws, stream=None) -> None:
+    fn, n = "hf_linear_absorb", _planes(g) * int(n_tok) * g.D
+    opt = int(n_tok) == 0
+    kp, vp = _arg(fn, "k_ev", k_ev, _BF16, n, opt), _arg(fn, "v_ev", v_ev, _BF16, n, opt)
+    Sp, zp = _state_args(fn, g, S, z, optional=False)
+    wp, wn = _ws(fn, ws)
+    _call(fn, lib().hf_linear_absorb, ctypes.byref(g.dims()), kp, vp, int(n_tok), Sp, zp, wp, wn, _stream(stream))
+
+
+def _step_args(fn: str, g: Geometry, q, k_cur, v_cur, top_k: int, S, z, idx, out):
+    BH = _planes(g)
+    n = BH * g.Nq * g.D
+    qp = _arg(fn, "q", q, _BF16, n)
+    if (k_cur is None) != (v_cur is None):
+        raise ValueError(f"{fn}: give both k_cur and v_cur or neither")
+    kp, vp = _arg(fn, "k_cur", k_cur, _BF16, n, True), _arg(fn, "v_cur", v_cur, _BF16, n, True)
+    Sp, zp = _state_args(fn, g, S, z, optional=True)
+    ip = _arg(fn, "idx", idx, _I32, BH * g.n_qb * int(top_k))
+    op = _arg(fn, "out", out, _F32, n)
+    return qp, kp, vp, Sp, zp, ip, op
+
+
+def hf_hybrid_step(g: Geometry, q, k_cur, v_cur, ring: Ring, top_k: int, flags: int, S, z, idx, out, ws,
+                   eps=1e-6, events=None, stream=None) -> None:
+    """`events`: None or a sequence of 6 raw hipEvent_t handles (ints or None)."""
+    fn = "hf_hybrid_step"
+    qp, kp, vp, Sp, zp, ip, op = _step_args(fn, g, q, k_cur, v_cur, top_k, S, z, idx, out)
+    wp, wn = _ws(fn, ws)
+    _call(fn, lib().hf_hybrid_step, ctypes.byref(g.dims()), qp, kp, vp, ctypes.byref(ring.desc), int(top_k),
+                                    int(flags), Sp, zp, float(eps), ip, op, wp, wn, _events(events), _stream(stream))
+
+
 def hf_sparse_window_attn_rope(g: Geometry, q, ring: Ring, idx, top_k: int, S, z, out, ws, rope: Rope, eps=1e-6,
                                stream=None) -> None:
-    _check("hf_sparse_window_attn_rope",
-           lib().hf_sparse_window_attn_rope(ctypes.byref(g.dims()), _ptr(q), ctypes.byref(ring.desc), _ptr(idx),
-                                            int(top_k), _ptr(S), _ptr(z), float(eps),
-                                            ctypes.byref(rope) if rope is not None else None, _ptr(out), _ptr(ws),
-                                            ws.numel() if ws is not None else 0, _stream(stream)))
+    fn = "hf_sparse_window_attn_rope"
+    qp, ip, Sp, zp, op = _attn_args(fn, g, q, idx, top_k, S, z, out)
+    wp, wn = _ws(fn, ws)
+    _call(fn, lib().hf_sparse_window_attn_rope, ctypes.byref(g.dims()), qp, ctypes.byref(ring.desc), ip, int(top_k),
+                                                Sp, zp, float(eps), ctypes.byref(rope) if rope is not None else None,
+                                                op, wp, wn, _stream(stream))
 
 
 def hf_hybrid_step_rope(g: Geometry, q, k_cur, v_cur, ring: Ring, top_k: int, flags: int, S, z, idx, out, ws,
                         rope: Rope, eps=1e-6, events=None, stream=None) -> None:
-    _check("hf_hybrid_step_rope",
-           lib().hf_hybrid_step_rope(ctypes.byref(g.dims()), _ptr(q), _ptr(k_cur), _ptr(v_cur),
-                                     ctypes.byref(ring.desc), int(top_k), int(flags), _ptr(S), _ptr(z), float(eps),
-                                     ctypes.byref(rope) if rope is not None else None, _ptr(idx), _ptr(out),
-                                     _ptr(ws), ws.numel() if ws is not None else 0, _events(events),
-                                     _stream(stream)))
+    fn = "hf_hybrid_step_rope"
+    qp, kp, vp, Sp, zp, ip, op = _step_args(fn, g, q, k_cur, v_cur, top_k, S, z, idx, out)
+    wp, wn = _ws(fn, ws)
+    _call(fn, lib().hf_hybrid_step_rope, ctypes.byref(g.dims()), qp, kp, vp, ctypes.byref(ring.desc), int(top_k),
+                                         int(flags), Sp, zp, float(eps),
+                                         ctypes.byref(rope) if rope is not None else None, ip, op, wp, wn,
+                                         _events(events), _stream(stream))
 
 
 def hf_cag_schedule(n_kb, s_base: float, s_target: float, s_max: float):
@@ -280,23 +387,39 @@ def new_backward_workspace(g: Geometry, top_k: int, device="cuda") -> torch.Tens
 
 def hf_sparse_window_attn_lse(g: Geometry, q, ring: Ring, idx, top_k: int, S, z, out, lse, ws, eps=1e-6,
                               stream=None) -> None:
-    _check("hf_sparse_window_attn_lse",
-           lib().hf_sparse_window_attn_lse(ctypes.byref(g.dims()), _ptr(q), ctypes.byref(ring.desc), _ptr(idx),
-                                           int(top_k), _ptr(S), _ptr(z), float(eps), _ptr(out), _ptr(lse), _ptr(ws),
-                                           ws.numel() if ws is not None else 0, _stream(stream)))
+    fn = "hf_sparse_window_attn_lse"
+    qp, ip, Sp, zp, op = _attn_args(fn, g, q, idx, top_k, S, z, out)
+    lp = _arg(fn, "lse", lse, _F32, _planes(g) * g.Nq)
+    wp, wn = _ws(fn, ws)
+    _call(fn, lib().hf_sparse_window_attn_lse, ctypes.byref(g.dims()), qp, ctypes.byref(ring.desc), ip, int(top_k),
+                                               Sp, zp, float(eps), op, lp, wp, wn, _stream(stream))
 
 
 def hf_hybrid_attn_backward(g: Geometry, q, ring: Ring, idx, top_k: int, S, z, out, lse, dout, dq, dk, dv, dS, dz,
                             bws, eps=1e-6, stream=None) -> None:
-    _check("hf_hybrid_attn_backward",
-           lib().hf_hybrid_attn_backward(ctypes.byref(g.dims()), _ptr(q), ctypes.byref(ring.desc), _ptr(idx),
-                                         int(top_k), _ptr(S), _ptr(z), float(eps), _ptr(out), _ptr(lse), _ptr(dout),
-                                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dS), _ptr(dz), _ptr(bws),
-                                         bws.numel() if bws is not None else 0, _stream(stream)))
+    fn, BH = "hf_hybrid_attn_backward", _planes(g)
+    nq, nk = BH * g.Nq * g.D, BH * (ring.n_committed + g.C) * g.T * g.D
+    qp, ip, Sp, zp, op = _attn_args(fn, g, q, idx, top_k, S, z, out)
+    if Sp.t is None:
+        raise ValueError(f"{fn}: S and z are required")
+    lp = _arg(fn, "lse", lse, _F32, BH * g.Nq)
+    gp = _arg(fn, "dout", dout, _F32, nq)
+    dqp = _arg(fn, "dq", dq, _F32, nq)
+    dkp, dvp = _arg(fn, "dk", dk, _F32, nk), _arg(fn, "dv", dv, _F32, nk)
+    dSp, dzp = _arg(fn, "dS", dS, _F32, BH * g.D * g.D), _arg(fn, "dz", dz, _F32, BH * g.D)
+    wp, wn = _ws(fn, bws, "bws")
+    _call(fn, lib().hf_hybrid_attn_backward, ctypes.byref(g.dims()), qp, ctypes.byref(ring.desc), ip, int(top_k), Sp,
+                                             zp, float(eps), op, lp, gp, dqp, dkp, dvp, dSp, dzp, wp, wn,
+                                             _stream(stream))
 
 
 def hf_linear_absorb_backward(g: Geometry, k_ev, v_ev, n_tok: int, dS, dz, dk, dv, ws, stream=None) -> None:
-    _check("hf_linear_absorb_backward",
-           lib().hf_linear_absorb_backward(ctypes.byref(g.dims()), _ptr(k_ev), _ptr(v_ev), int(n_tok), _ptr(dS),
-                                           _ptr(dz), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() if ws is not None else 0,
-                                           _stream(stream)))
+    fn, BH = "hf_linear_absorb_backward", _planes(g)
+    n = BH * int(n_tok) * g.D
+    opt = int(n_tok) == 0
+    kp, vp = _arg(fn, "k_ev", k_ev, _BF16, n, opt), _arg(fn, "v_ev", v_ev, _BF16, n, opt)
+    dSp, dzp = _arg(fn, "dS", dS, _F32, BH * g.D * g.D), _arg(fn, "dz", dz, _F32, BH * g.D)
+    dkp, dvp = _arg(fn, "dk", dk, _F32, n, opt), _arg(fn, "dv", dv, _F32, n, opt)
+    wp, wn = _ws(fn, ws)
+    _call(fn, lib().hf_linear_absorb_backward, ctypes.byref(g.dims()), kp, vp, int(n_tok), dSp, dzp, dkp, dvp, wp, wn,
+                                               _stream(stream))

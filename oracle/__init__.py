@@ -203,43 +203,49 @@ def hybrid_step_rope(Q, K, V, S, z, bq, bk, k, T, temporal_dims, cap, base=10000
 
 
 def cag_schedule(n_kb, s_base, s_target, s_max):
-    """Chunk-aware growth schedule ([LF-de] §2.1 "Chunk-bewusstes Wachstum"), written out
-    plainly: chunk 0 is dense; chunk i >= 1 has sparsity s_base - alpha_i * beta with
+    """Chunk-aware growth schedule ([LF-de] §2.1 "Chunk-bewusstes Wachstum"): chunk 0 is
+    dense; chunk i >= 1 has sparsity s_i = clip(s_base - alpha_i * beta, 0, s_max) with
     alpha_i = 1 / sqrt(i + 1) (the page's alpha proportional to one over a square root,
-    read against the chunk's position), clipped to [0, s_max]; its keep count is
-    ceil((1 - s_i) * n_kb[i]) within [1, n_kb[i]]; beta is the smallest value for which
-    the kept key blocks of all chunks reach (1 - s_target) of the dense total.  beta is
-    located by halving an interval that starts at [0, s_base * sqrt(n) + 1] (the upper
-    end makes every chunk dense).  Returns (keep counts, sparsities, beta)."""
+    read against the chunk's position) and keeps k_i = ceil((1 - s_i) * n_kb[i]) key
+    blocks; beta is the least value at which the kept blocks of all chunks reach
+    (1 - s_target) of the dense total.
+
+    Worked out exactly rather than searched: for 1 <= m < n = n_kb[i], chunk i keeps more
+    than m blocks exactly when (1 - s_i) n > m, i.e. s_i < c = 1 - m / n.  Since s_i never
+    exceeds s_max and c > 0, that holds for every beta when s_max < c, and otherwise
+    exactly when s_base - beta / sqrt(i + 1) < c, i.e. beta > t = (s_base - 1 + m / n) *
+    sqrt(i + 1).  So the total kept is a constant plus the number of breakpoints t below
+    beta; the least beta reaching the goal is 0 if the total at 0 already does, else the
+    r-th smallest breakpoint, r the number of blocks still missing (the total jumps just
+    after it, so this is the infimum of the betas that reach the goal).  The keep counts
+    returned are those just above that beta.  Returns (keep counts, sparsities, beta)."""
     import math
     n = len(n_kb)
-
-    def sparsity(i, beta):
-        if i == 0:
-            return 0.0
-        return min(max(s_base - (1.0 / math.sqrt(i + 1)) * beta, 0.0), s_max)
-
-    def keep(s, nkb):
-        return int(min(max(math.ceil((1.0 - s) * nkb), 1), nkb))
-
-    def work(beta):
-        return sum(keep(sparsity(i, beta), n_kb[i]) for i in range(n))
-
-    goal = (1.0 - s_target) * float(sum(n_kb))
-    beta = 0.0
-    if work(0.0) < goal:
-        lo, hi = 0.0, s_base * math.sqrt(n) + 1.0
-        for _ in range(200):
-            mid = 0.5 * (lo + hi)
-            if mid <= lo or mid >= hi:
-                break
-            if work(mid) >= goal:
-                hi = mid
+    base = n_kb[0] + (n - 1)                 # chunk 0 dense, every later chunk keeps >= 1
+    always = 0
+    points = []                              # (t, chunk)
+    for i in range(1, n):
+        for m in range(1, n_kb[i]):
+            if s_max < 1.0 - m / n_kb[i]:
+                always += 1
             else:
-                lo = mid
-        beta = hi
-    ss = [sparsity(i, beta) for i in range(n)]
-    return [keep(ss[i], n_kb[i]) for i in range(n)], ss, beta
+                points.append(((s_base - 1.0 + m / n_kb[i]) * math.sqrt(i + 1), i))
+    points.sort()
+    goal = math.ceil((1.0 - s_target) * float(sum(n_kb)))     # kept totals are integers
+    below0 = sum(1 for t, _ in points if t < 0.0)
+    if base + always + below0 >= goal:
+        beta = 0.0
+        passed = [(t, i) for t, i in points if t < 0.0]
+    else:
+        beta = points[goal - base - always - 1][0]
+        passed = [(t, i) for t, i in points if t <= beta]
+    keep = [n_kb[0]] + [1] * (n - 1)
+    for i in range(1, n):
+        keep[i] += sum(1 for m in range(1, n_kb[i]) if s_max < 1.0 - m / n_kb[i])
+    for _, i in passed:
+        keep[i] += 1
+    ss = [0.0] + [min(max(s_base - beta / math.sqrt(i + 1), 0.0), s_max) for i in range(1, n)]
+    return keep, ss, beta
 
 
 def frames_of_block(j, bk, Nk, T):

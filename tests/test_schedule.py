@@ -1,6 +1,7 @@
-"""Chunk-aware growth schedule ([LF-de] §2.1): the oracle pinned to hand-computed cases
-and invariants, and the library's host implementation (hf_cag_schedule, no GPU work)
-compared with it exactly."""
+"""Chunk-aware growth schedule ([LF-de] §2.1): the oracle (exact enumeration of the
+breakpoints of the kept-block total) pinned to hand-computed cases and invariants, and the
+library's host implementation (hf_cag_schedule, a bisection, no GPU work) compared with it:
+keep counts exactly, beta and the sparsities to 1e-12."""
 
 import math
 
@@ -65,8 +66,9 @@ def test_library_matches_oracle(seed):
     got = hf.hf_cag_schedule(n_kb, *args)
     ref = oracle.cag_schedule(n_kb, *args)
     assert got[0] == ref[0]
-    assert got[1] == ref[1]
-    assert got[2] == ref[2]
+    # the bisection stops within rounding of the breakpoint the oracle finds exactly
+    assert abs(got[2] - ref[2]) <= 1e-12 * max(1.0, ref[2])
+    assert np.allclose(got[1], ref[1], rtol=0, atol=1e-12)
 
 
 def test_library_rejects_bad_arguments():
@@ -77,3 +79,30 @@ def test_library_rejects_bad_arguments():
     for bad in ((1.0, 0.2, 0.9), (0.5, -0.1, 0.9), (0.5, 0.2, float("nan"))):
         with pytest.raises(hf.HFError):
             hf.hf_cag_schedule([10, 10], *bad)
+
+
+def brute_keep(n_kb, s_base, s_max, beta):
+    """The schedule's keep counts at one beta, straight from the definition."""
+    ks = [n_kb[0]]
+    for i in range(1, len(n_kb)):
+        s = min(max(s_base - beta / math.sqrt(i + 1), 0.0), s_max)
+        ks.append(int(min(max(math.ceil((1.0 - s) * n_kb[i]), 1), n_kb[i])))
+    return ks
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_oracle_against_scan_of_beta(seed):
+    """Scanning beta on a fine grid with the definition: the first grid point that reaches the
+    goal lies just above the oracle's beta, and gives the oracle's keep counts."""
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.integers(2, 7))
+    n_kb = [int(x) for x in rng.integers(2, 40, n)]
+    s_base, s_target, s_max = float(rng.uniform(0.3, 0.95)), float(rng.uniform(0.05, 0.4)), float(rng.uniform(0.5, 0.97))
+    k, s, beta = oracle.cag_schedule(n_kb, s_base, s_target, s_max)
+    goal = (1.0 - s_target) * sum(n_kb)
+    step = 1e-4
+    grid = np.arange(0.0, s_base * math.sqrt(n) + 1.0 + step, step)
+    first = next(b for b in grid if sum(brute_keep(n_kb, s_base, s_max, b)) >= goal)
+    assert beta <= first < beta + step + 1e-12
+    if beta > 0 and first - beta > 1e-9:
+        assert brute_keep(n_kb, s_base, s_max, first) == k

@@ -9,4 +9,4 @@ from ._lib import (HF_STEP_COMMIT, Geometry, HFError, Ring, abi_version, hf_bloc
                    hf_hybrid_step, hf_linear_absorb, hf_ring_append, hf_sparse_window_attn, new_workspace,
                    workspace_size, backward_workspace_size, new_backward_workspace, hf_sparse_window_attn_lse,
                    hf_hybrid_attn_backward, hf_linear_absorb_backward, Rope, hf_sparse_window_attn_rope,
-                   hf_hybrid_step_rope)
+                   hf_hybrid_step_rope, hf_hybrid_step_noalloc)

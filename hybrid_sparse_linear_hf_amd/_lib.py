@@ -86,10 +86,13 @@ def lib():
         L.hf_sparse_window_attn_rope.argtypes = [pd, _P, pr, _P, i32, _P, _P, f32, prope, _P, _P, sz, _P]
         L.hf_hybrid_step_rope.argtypes = [pd, _P, _P, _P, pr, i32, u32, _P, _P, f32, prope, _P, _P, _P, sz,
                                           ctypes.POINTER(StepEvents), _P]
+        L.hf_hybrid_step_noalloc.argtypes = [pd, _P, _P, _P, pr, i32, u32, _P, _P, f32, _P, _P,
+                                             ctypes.POINTER(StepEvents), _P]
         for fn in ("hf_workspace_size", "hf_ring_init", "hf_ring_append", "hf_block_select", "hf_sparse_window_attn",
                    "hf_linear_absorb", "hf_hybrid_step", "hf_cag_schedule", "hf_block_select_hier",
                    "hf_sparse_window_attn_lse", "hf_backward_workspace_size", "hf_hybrid_attn_backward",
-                   "hf_linear_absorb_backward", "hf_sparse_window_attn_rope", "hf_hybrid_step_rope"):
+                   "hf_linear_absorb_backward", "hf_sparse_window_attn_rope", "hf_hybrid_step_rope",
+                   "hf_hybrid_step_noalloc"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -337,6 +340,16 @@ def hf_hybrid_step(g: Geometry, q, k_cur, v_cur, ring: Ring, top_k: int, flags: 
     wp, wn = _ws(fn, ws)
     _call(fn, lib().hf_hybrid_step, ctypes.byref(g.dims()), qp, kp, vp, ctypes.byref(ring.desc), int(top_k),
                                     int(flags), Sp, zp, float(eps), ip, op, wp, wn, _events(events), _stream(stream))
+
+
+def hf_hybrid_step_noalloc(g: Geometry, q, k_cur, v_cur, ring: Ring, top_k: int, flags: int, S, z, idx, out,
+                           eps=1e-6, events=None, stream=None) -> None:
+    """hf_hybrid_step without a workspace: the library's fixed per-GPU scratch array holds the
+    step's transient data (calls overlapping in time on one GPU race on it)."""
+    fn = "hf_hybrid_step_noalloc"
+    qp, kp, vp, Sp, zp, ip, op = _step_args(fn, g, q, k_cur, v_cur, top_k, S, z, idx, out)
+    _call(fn, lib().hf_hybrid_step_noalloc, ctypes.byref(g.dims()), qp, kp, vp, ctypes.byref(ring.desc), int(top_k),
+          int(flags), Sp, zp, float(eps), ip, op, _events(events), _stream(stream))
 
 
 def hf_sparse_window_attn_rope(g: Geometry, q, ring: Ring, idx, top_k: int, S, z, out, ws, rope: Rope, eps=1e-6,

@@ -17,7 +17,8 @@ CSRC = PKG / "csrc"
 LIB = PKG / "libhf.so"
 ARCH = os.environ.get("HF_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["hf_api.hip", "ring.hip", "select.hip", "sparse_attn.hip", "absorb.hip", "state.hip", "schedule.hip", "backward.hip"]
+SOURCES = ["hf_api.hip", "ring.hip", "select.hip", "sparse_attn.hip", "absorb.hip", "state.hip", "schedule.hip",
+           "backward.hip", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -532,10 +532,12 @@ hf_status hf_linear_absorb(const hf_dims *d, const void *k_ev, const void *v_ev,
     return st == HF_OK ? ok() : st;
 }
 
-static hf_status hybrid_step(const hf_dims *d, const void *q, const void *k_cur, const void *v_cur, hf_kv_ring *ring,
-                             int32_t top_k, uint32_t flags, float *S, float *z, float eps, const hf_rope *rope,
-                             int32_t *idx, float *out, void *ws, size_t ws_bytes, const hf_step_events *events,
-                             hipStream_t stream) {
+}  // extern "C"
+
+// Validation of a step's arguments, workspace aside (sets the error message).
+hf_status hf_step_validate(const hf_dims *d, const void *q, const void *k_cur, const void *v_cur,
+                           const hf_kv_ring *ring, int32_t top_k, uint32_t flags, const float *S, const float *z,
+                           float eps, const int32_t *idx, const float *out) {
     hf_status st = check_dims(d);
     if (st == HF_OK) st = check_ring(d, ring);
     if (st != HF_OK) return st;
@@ -547,9 +549,23 @@ static hf_status hybrid_step(const hf_dims *d, const void *q, const void *k_cur,
     if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(HF_ERR_SHAPE, "eps must be finite and >= 0");
     const Geometry g = geometry(d, ring);
     if (top_k < 1 || top_k > g.nkb) return fail(HF_ERR_SHAPE, "top_k=%d outside [1, n_kb=%d]", top_k, g.nkb);
-    st = check_ws(d, ws, ws_bytes);
-    if (st != HF_OK) return st;
+    return HF_OK;
+}
 
+// Bytes at the start of the workspace layout that a step uses (everything before the
+// hierarchical selection's buffers); dims already validated.
+size_t hf_step_workspace_bytes(const hf_dims *d) { return ws_layout(d).fbar; }
+
+hf_status hf_fail_unsupported(const char *msg, size_t need, size_t have) {
+    return fail(HF_ERR_UNSUPPORTED, "%s: needs %zu bytes, holds %zu", msg, need, have);
+}
+
+hf_status hf_fail_hip(hipError_t e, const char *what) { return hip_status(e, what); }
+
+// Enqueue a validated step on `ws` (at least hf_step_workspace_bytes bytes).
+hf_status hf_step_enqueue(const hf_dims *d, const void *q, const void *k_cur, const void *v_cur, hf_kv_ring *ring,
+                          int32_t top_k, uint32_t flags, float *S, float *z, float eps, const hf_rope *rope,
+                          int32_t *idx, float *out, void *ws, const hf_step_events *events, hipStream_t stream) {
     // Order: append; select, with the readout operands taken from the state as it is by
     // extra workgroups of its first launch; attention with the fused readout; then the
     // absorb of the frames this step evicts (still in the ring until the next append) and
@@ -584,6 +600,18 @@ static hf_status hybrid_step(const hf_dims *d, const void *q, const void *k_cur,
     *ring = next;
     return ok();
 }
+
+static hf_status hybrid_step(const hf_dims *d, const void *q, const void *k_cur, const void *v_cur, hf_kv_ring *ring,
+                             int32_t top_k, uint32_t flags, float *S, float *z, float eps, const hf_rope *rope,
+                             int32_t *idx, float *out, void *ws, size_t ws_bytes, const hf_step_events *events,
+                             hipStream_t stream) {
+    hf_status st = hf_step_validate(d, q, k_cur, v_cur, ring, top_k, flags, S, z, eps, idx, out);
+    if (st == HF_OK) st = check_ws(d, ws, ws_bytes);
+    if (st != HF_OK) return st;
+    return hf_step_enqueue(d, q, k_cur, v_cur, ring, top_k, flags, S, z, eps, rope, idx, out, ws, events, stream);
+}
+
+extern "C" {
 
 hf_status hf_hybrid_step(const hf_dims *d, const void *q, const void *k_cur, const void *v_cur, hf_kv_ring *ring,
                          int32_t top_k, uint32_t flags, float *S, float *z, float eps, int32_t *idx, float *out,

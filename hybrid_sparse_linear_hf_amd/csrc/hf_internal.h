@@ -216,3 +216,15 @@ hf_status hf_cag_schedule_impl(int32_t n, const int32_t *nkb, double s_base, dou
 
 hipError_t hf_launch_ring_append(const hf_append_args &a, hipStream_t s);
 int hf_append_tiles(const hf_append_args &a);   // workgroups of an append
+
+// A hybrid step split into validation and enqueue (hf_api.hip), so that entry points with
+// another source of workspace memory share both.
+hf_status hf_step_validate(const hf_dims *d, const void *q, const void *k_cur, const void *v_cur,
+                           const hf_kv_ring *ring, int32_t top_k, uint32_t flags, const float *S, const float *z,
+                           float eps, const int32_t *idx, const float *out);
+size_t hf_step_workspace_bytes(const hf_dims *d);   // dims validated
+hf_status hf_step_enqueue(const hf_dims *d, const void *q, const void *k_cur, const void *v_cur, hf_kv_ring *ring,
+                          int32_t top_k, uint32_t flags, float *S, float *z, float eps, const hf_rope *rope,
+                          int32_t *idx, float *out, void *ws, const hf_step_events *events, hipStream_t stream);
+hf_status hf_fail_unsupported(const char *msg, size_t need, size_t have);
+hf_status hf_fail_hip(hipError_t e, const char *what);

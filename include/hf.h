@@ -31,7 +31,9 @@
  *
  *  * Memory: every pointer argument named *_dev is DEVICE memory owned by the caller;
  *    hf_dims / hf_kv_ring structs and `bytes` out-parameters are HOST memory.  The
- *    library never allocates, frees, or keeps a pointer after returning.
+ *    library never allocates, frees, or keeps a pointer after returning (the one entry
+ *    point for callers that cannot allocate, hf_hybrid_step_noalloc, uses a fixed device
+ *    array the library holds per GPU).
  *  * Asynchrony: work is enqueued on `stream` (0 = the null stream) and the call
  *    returns without waiting.  A device fault surfaces at the caller's next
  *    synchronisation.
@@ -247,6 +249,21 @@ hf_status hf_hybrid_step(const hf_dims *d, const void *q_dev, const void *k_cur_
                          hf_kv_ring *ring, int32_t top_k, uint32_t flags, float *S_dev, float *z_dev,
                          float eps, int32_t *idx_dev, float *out_dev, void *workspace_dev,
                          size_t workspace_bytes, const hf_step_events *events, hipStream_t stream);
+
+/* hf_hybrid_step for callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same step, the same kernels
+ * and arguments, but no workspace -- its transient data live in a fixed device array of
+ * 32 MiB that the library holds on each GPU it runs on until the process ends.  The call
+ * allocates and frees nothing.  Calls that overlap in time on one GPU (different streams
+ * or threads) race on that array; calls in one stream order are safe.  The stream's device
+ * (the current device for the null stream) runs the work.  Errors: those of hf_hybrid_step,
+ * HF_ERR_UNSUPPORTED when the step's transient data would exceed 32 MiB (the 832x480 layer
+ * with 12 heads needs about 11 MiB, four such streams batched about 22 MiB), HF_ERR_HIP when
+ * the array's device address cannot be obtained. */
+hf_status hf_hybrid_step_noalloc(const hf_dims *d, const void *q_dev, const void *k_cur_dev, const void *v_cur_dev,
+                                 hf_kv_ring *ring, int32_t top_k, uint32_t flags, float *S_dev, float *z_dev,
+                                 float eps, int32_t *idx_dev, float *out_dev, const hf_step_events *events,
+                                 hipStream_t stream);
 
 /* ---- Relative temporal rotary embedding of the softmax branch ([HF-de] §2.C "Relative
  * RoPE", [HF-pt] §2.B.2: the temporal RoPE index is capped and expressed as an offset

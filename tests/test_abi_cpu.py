@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
               "hf_ring_init",
               "hf_workspace_size", "hf_last_error", "hf_status_str", "hf_abi_version", "hf_cag_schedule",
               "hf_sparse_window_attn_lse", "hf_backward_workspace_size", "hf_hybrid_attn_backward",
-              "hf_linear_absorb_backward", "hf_sparse_window_attn_rope", "hf_hybrid_step_rope"):
+              "hf_linear_absorb_backward", "hf_sparse_window_attn_rope", "hf_hybrid_step_rope",
+              "hf_hybrid_step_noalloc"):
         assert s in syms
 
 
@@ -252,3 +253,20 @@ def test_ring_init():
     assert L.hf_ring_init(ctypes.byref(g.dims()), None, FAKE, ctypes.byref(r)) == 1
     assert L.hf_ring_init(ctypes.byref(g.dims()), FAKE, FAKE, None) == 1
     assert L.hf_ring_init(ctypes.byref(geom(D=96).dims()), FAKE, FAKE, ctypes.byref(r)) == 3
+
+
+def test_noalloc_step_rejects_oversized_and_bad_arguments():
+    """The allocation-free step checks its arguments and the size of its transient data (at
+    most 32 MiB) before it touches the GPU."""
+    L = _lib.lib()
+    ring = ring_desc()
+
+    def call(g, top_k=37, q=FAKE):
+        return L.hf_hybrid_step_noalloc(ctypes.byref(g.dims()), q, None, None, ctypes.byref(ring), top_k, 1, FAKE,
+                                        FAKE, ctypes.c_float(1e-6), FAKE, FAKE, None, None)
+
+    assert call(geom(B=8, H=16)) == 3, last_error()
+    assert "32 MiB" in last_error()
+    assert call(geom(), q=None) == 1
+    assert call(geom(), top_k=0) == 2
+    assert (ring.head, ring.n_committed) == (0, 3)

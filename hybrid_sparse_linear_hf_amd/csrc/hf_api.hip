@@ -207,7 +207,7 @@ hipError_t enqueue_state(const hf_dims *d, float *S, float *z, bool readout, int
 // Attention (+ readout from the prepared S^T / z copy when `readout`).
 hipError_t enqueue_attn(const hf_dims *d, const void *q, const hf_kv_ring *r, const int32_t *idx, int top_k,
                         bool readout, float eps, float *out, void *ws, hipStream_t s, float *lse = nullptr,
-                        const hf_rope *rope = nullptr) {
+                        const hf_rope *rope = nullptr, int64_t absorb_tok = 0) {
     const Geometry g = geometry(d, r);
     const WsLayout L = ws_layout(d);
     hf_attn_args a{};
@@ -238,27 +238,22 @@ hipError_t enqueue_attn(const hf_dims *d, const void *q, const hf_kv_ring *r, co
         a.rope_cap = rope->cap;
         a.rope_c1 = (float)(-2.0 * std::log2((double)rope->base) / rope->temporal_dims);
     }
+    if (absorb_tok > 0) {   // the step's evicted tokens: split partials by extra workgroups of this launch
+        a.ab_E = (int)absorb_tok;
+        a.ab_part = reinterpret_cast<float *>(wsp(ws, L.absorb));
+    }
     return hf_launch_sparse_attn(a, s);
 }
 
-// Absorb partial sums into the workspace: from row-major buffers (k, v) or from the e
-// oldest frames of the ring (ring != null).
-hipError_t enqueue_absorb_partial(const hf_dims *d, const void *k, const void *v, int64_t n_tok,
-                                  const hf_kv_ring *ring, void *ws, hipStream_t s) {
+// Absorb partial sums of row-major evicted tokens (k, v) into the workspace.
+hipError_t enqueue_absorb_partial(const hf_dims *d, const void *k, const void *v, int64_t n_tok, void *ws,
+                                  hipStream_t s) {
     hf_absorb_args a{};
     a.BH = d->B * d->H;
     a.D = d->D;
     a.n_tok = n_tok;
-    if (ring) {
-        a.ring_k = static_cast<const uint16_t *>(ring->k_dev);
-        a.ring_vt = static_cast<const uint16_t *>(ring->vt_dev);
-        a.W = d->W;
-        a.T = d->T;
-        a.head = ring->head;
-    } else {
-        a.k = static_cast<const uint16_t *>(k);
-        a.v = static_cast<const uint16_t *>(v);
-    }
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
     a.part = reinterpret_cast<float *>(wsp(ws, ws_layout(d).absorb));
     if (hf_absorb_partial_floats(a.BH, a.D, hf_absorb_splits(a.BH, a.D, n_tok)) * sizeof(float) >
         hf_absorb_workspace_bytes(a.BH, a.D))
@@ -526,7 +521,7 @@ hf_status hf_linear_absorb(const hf_dims *d, const void *k_ev, const void *v_ev,
     st = check_ws(d, ws, ws_bytes);
     if (st != HF_OK) return st;
     if (n_tok == 0) return ok();
-    hipError_t e = enqueue_absorb_partial(d, k_ev, v_ev, n_tok, nullptr, ws, stream);
+    hipError_t e = enqueue_absorb_partial(d, k_ev, v_ev, n_tok, ws, stream);
     if (e == hipSuccess) e = enqueue_state(d, S, z, false, n_tok, ws, stream);
     st = hip_status(e, "absorb launch");
     return st == HF_OK ? ok() : st;
@@ -567,9 +562,9 @@ hf_status hf_step_enqueue(const hf_dims *d, const void *q, const void *k_cur, co
                           int32_t top_k, uint32_t flags, float *S, float *z, float eps, const hf_rope *rope,
                           int32_t *idx, float *out, void *ws, const hf_step_events *events, hipStream_t stream) {
     // Order: append; select, with the readout operands taken from the state as it is by
-    // extra workgroups of its first launch; attention with the fused readout; then the
-    // absorb of the frames this step evicts (still in the ring until the next append) and
-    // the state update.
+    // extra workgroups of its first launch; attention with the fused readout, whose launch
+    // also forms the absorb partials of the frames this step evicts (still in the ring until
+    // the next append); the state pass that adds them.
     hf_kv_ring next = *ring;
     int evict = 0;
     if (flags & HF_STEP_COMMIT) {
@@ -591,9 +586,13 @@ hf_status hf_step_enqueue(const hf_dims *d, const void *q, const void *k_cur, co
                            k_cur ? &app : nullptr);
     if (e == hipSuccess) e = record(events, 2, stream);
     if (e == hipSuccess) e = record(events, 3, stream);
-    if (e == hipSuccess) e = enqueue_attn(d, q, ring, idx, top_k, S != nullptr, eps, out, ws, stream, nullptr, rope);
+    // attention with the fused readout; extra workgroups of the same launch form the split
+    // partial sums of the evicted frames (the oldest window frames, which the append does not
+    // touch), beside the attention -- the readout reads the copy of the state the pool launch
+    // made -- and the state pass adds them to (S, z) in split order
+    if (e == hipSuccess)
+        e = enqueue_attn(d, q, ring, idx, top_k, S != nullptr, eps, out, ws, stream, nullptr, rope, evict_tok);
     if (e == hipSuccess) e = record(events, 4, stream);
-    if (e == hipSuccess && evict_tok > 0) e = enqueue_absorb_partial(d, nullptr, nullptr, evict_tok, ring, ws, stream);
     if (e == hipSuccess && evict_tok > 0) e = enqueue_state(d, S, z, false, evict_tok, ws, stream);
     if (e == hipSuccess) e = record(events, 5, stream);
     if (e != hipSuccess) return hip_status(e, "hybrid step launch");

@@ -160,6 +160,12 @@ struct hf_attn_args {
     // offsets clamped to +-rope_cap, theta_i = 2^(i * rope_c1); ncom = window frames before the chunk
     int rope_dt, rope_cap, ncom;
     float rope_c1;
+    // absorb of the ab_E oldest window tokens (the frames a committed step evicts), run by
+    // extra workgroups of the same launch (ab_E = 0: none): split partial sums into ab_part
+    // (workspace, hf_absorb_partial_floats floats, the layout the state pass adds up)
+    int ab_E;
+    float *ab_part;
+    int ab_P, ab_items, ab_nab;   // set by the launcher: splits, work items, workgroups (items rounded up to 8)
 };
 hipError_t hf_launch_sparse_attn(const hf_attn_args &a, hipStream_t s);
 
@@ -197,11 +203,7 @@ hipError_t hf_launch_absorb_backward(const hf_absorb_bwd_args &a, hipStream_t s)
 struct hf_absorb_args {
     int BH, D;
     int64_t n_tok;
-    // source: either plain row-major buffers (k, v) or ring frames (ring_k, ring_vt, W, T, head)
-    const uint16_t *k, *v;
-    const uint16_t *ring_k, *ring_vt;
-    int W, T, head;
-    uint32_t magicT;           // div_magic(T), set by the launcher
+    const uint16_t *k, *v;     // row-major evicted tokens [BH][n_tok][D]
     float *part;               // workspace: partial sums (hf_absorb_partial_floats floats)
 };
 int hf_absorb_splits(int BH, int D, int64_t n_tok);

@@ -36,6 +36,7 @@
 //     reaches 2^32, the block is recomputed with an online (rescaling) softmax.  Short
 //     subtiles (the tail of a short last key block; every subtile when bk < 32) use the
 //     online softmax with masking.
+#include <algorithm>
 #include <type_traits>
 
 #include "hf_internal.h"
@@ -138,6 +139,232 @@ __device__ __forceinline__ float softmax_online(f32x16 s, int nval, int g, float
 
 constexpr int kWaitVm0 = 0x0F70;   // s_waitcnt vmcnt(0), other counters untouched
 
+// ------------------------------------------------------------------ absorb role
+// In a committed step, extra workgroups at the front of the attention launch absorb the
+// evicted tokens -- the ab_E oldest keys of the window, still in their ring slots -- into
+// split partial sums of the linear state, which grows by every token that leaves the
+// window ([HF-abs]; [HF-de] §2.A "Lineare Zeit-Aufmerksamkeit"; [HF-pt] §2.A.1):
+//     S[a][c] += sum_u phi(K_u[a]) V_u[c],      z[a] += sum_u phi(K_u[a]).
+// The attention's readout reads a copy of the state made before the launch, so the two
+// roles never touch the same data, and the absorb runs beside the attention instead of
+// after it; the state pass that follows the launch adds the partials in split order.
+//   * Work item = (plane, split of the token range[, 64-row half of S when one wave cannot
+//     hold all rows]).  Each wave owns 64 rows of S (32 for D = 64 with two waves) and all
+//     D columns, and the workgroup walks its split in 16-token steps.
+//   * The steps stream through a ring of kAbStages LDS stages with direct-to-LDS loads,
+//     kAbStages - 1 steps ahead (counted waits, one LDS-only barrier per step): K rows (the
+//     item's features of each token) and V^T rows (16 tokens of every feature).  gfx950's
+//     transposing LDS read (within each 16-lane group, lane i receives element i % 4 of the
+//     4-element vectors lanes i / 4 + 4 e point at) turns the K rows into the phi(K)^T
+//     operand (8 tokens of one feature per lane); phi is evaluated in fp32 and split into
+//     bf16 hi + lo halves, so with V exact in bf16 the two products per fragment keep
+//     fp32-grade accuracy.
+//   * Each wave writes its rows' partial (and z) straight from its accumulators into the
+//     split's slot of the workspace: no atomics, the result is deterministic.
+
+constexpr int kAbStages = 4;                 // LDS stages (steps in flight + 1)
+
+template <int D, int NW>
+struct AbShape {
+    static constexpr int R = (D / NW < 64) ? D / NW : 64;   // rows of S per wave
+    static constexpr int RTW = R / 32;                       // 32-row tiles per wave
+    static constexpr int CT = D / 32;                        // 32-column tiles
+    static constexpr int ROWS = R * NW;                      // rows (features) per item
+    static constexpr int GROUPS = D / ROWS;                  // items per (plane, split)
+    static constexpr int RW = ROWS * 2;                      // bytes per staged K row
+    static constexpr int RC = RW / 16;                       // 16-byte chunks per K row
+    static constexpr int KB = 16 * RW;                       // K stage bytes (16 tokens)
+    static constexpr int SB = KB + D * 32;                   // stage bytes (+ V^T: D x 16 tokens)
+    static constexpr int KI = KB / 1024, VI = D * 32 / 1024; // load instructions per step
+    static constexpr int PW = (KI + VI) / NW;                // ... per wave
+};
+
+// K stage swizzle: 16-byte chunk c of token row r sits at slot c ^ ((RC / 4) (r % 4)), so the
+// four rows a transposing read touches hit distinct bank groups.
+template <int RC>
+__device__ __forceinline__ int ab_kswz(int r) { return (RC / 4) * (r & 3); }
+
+// LDS reads of one absorb step, in one asm block that also waits for them: per 32-row tile
+// two transposing reads of K (token rows 0-3 and 4-7 from the lane's base, 4 RW bytes
+// apart) and CT 16-byte V^T fragments (1 KB apart).  Written out so that the compiler, which
+// cannot tell which direct-to-LDS load an LDS read depends on, adds no wait for every load
+// in flight: the caller's counted wait covers the step's loads.  Every output is complete
+// when the block ends.
+template <int RTW, int CT, int RW>
+__device__ __forceinline__ void ab_lds_reads(const uint32_t (&ka)[RTW], uint32_t va, u32x2 (&r)[RTW][2],
+                                             u32x4 (&vf)[CT]) {
+    if constexpr (RTW == 2 && CT == 4) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8\n\t"
+            "ds_read_b64_tr_b16 %1, %8 offset:%11\n\t"
+            "ds_read_b64_tr_b16 %2, %9\n\t"
+            "ds_read_b64_tr_b16 %3, %9 offset:%11\n\t"
+            "ds_read_b128 %4, %10\n\t"
+            "ds_read_b128 %5, %10 offset:1024\n\t"
+            "ds_read_b128 %6, %10 offset:2048\n\t"
+            "ds_read_b128 %7, %10 offset:3072\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(vf[0]), "=&v"(vf[1]),
+              "=&v"(vf[2]), "=&v"(vf[3])
+            : "v"(ka[0]), "v"(ka[1]), "v"(va), "i"(4 * RW)
+            : "memory");
+    } else if constexpr (RTW == 2 && CT == 2) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %6\n\t"
+            "ds_read_b64_tr_b16 %1, %6 offset:%9\n\t"
+            "ds_read_b64_tr_b16 %2, %7\n\t"
+            "ds_read_b64_tr_b16 %3, %7 offset:%9\n\t"
+            "ds_read_b128 %4, %8\n\t"
+            "ds_read_b128 %5, %8 offset:1024\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(vf[0]), "=&v"(vf[1])
+            : "v"(ka[0]), "v"(ka[1]), "v"(va), "i"(4 * RW)
+            : "memory");
+    } else {
+        static_assert(RTW == 1 && CT == 2, "absorb tile shape");
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %4\n\t"
+            "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
+            "ds_read_b128 %2, %5\n\t"
+            "ds_read_b128 %3, %5 offset:1024\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(vf[0]), "=&v"(vf[1])
+            : "v"(ka[0]), "v"(va), "i"(4 * RW)
+            : "memory");
+    }
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char *p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char *)p;
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void absorb_role(const hf_attn_args &a, int ab, unsigned char *lds, uint32_t magicT) {
+    using A = AbShape<D, NW>;
+    constexpr int RTW = A::RTW, CT = A::CT, RW = A::RW, RC = A::RC, SB = A::SB;
+    const int P = a.ab_P;
+    const int grp = ab % A::GROUPS, p = (ab / A::GROUPS) % P, bh = ab / (A::GROUPS * P);
+    const int E = a.ab_E, nsteps = (E + 15) >> 4;
+    const int s0 = (int)((int64_t)p * nsteps / P), s1 = (int)((int64_t)(p + 1) * nsteps / P);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
+    const int T = a.T, W = a.W, head = a.head;
+    const int F0 = grp * A::ROWS;            // the item's first feature (row of S)
+    const size_t plane = (size_t)bh * W * T * D;
+    const uint32_t plane_bytes = (uint32_t)((size_t)W * T * D * 2);
+    const Rsrc rk = make_rsrc(a.ring_k + plane, plane_bytes);
+    const Rsrc rv = make_rsrc(a.ring_vt + plane, plane_bytes);
+    auto slot_of = [&](int f) -> int {
+        const int s = head + f;
+        return s >= W ? s - W : s;
+    };
+    // Step h (tokens 16 h ..) into stage st; h is clamped to the split's last step (loads of
+    // padding steps are never consumed).  Instruction j of the step is issued by wave j % NW.
+    //   K, j < KI: lane -> token row (64 j + lane) / RC, slot (64 j + lane) % RC holding chunk
+    //     slot ^ ab_kswz(row) of the item's features.
+    //   V^T, j >= KI: lane -> feature row 32 (j - KI) + lane / 2, slot lane % 2 holding token
+    //     chunk (lane % 2) ^ (row / 8 % 2) (8 tokens of one frame: T and E are multiples of 8).
+    // Tokens at or past E re-read the last ones (finite data; their phi is masked to 0).
+    auto fetch = [&](int h, int st) {
+        h = min(h, s1 - 1);
+        unsigned char *kd = lds + st * SB, *vd = kd + A::KB;
+        const int kb = 16 * h;
+#pragma unroll
+        for (int jj = 0; jj < A::PW; ++jj) {
+            const int j = w + NW * jj;
+            if (j < A::KI) {
+                const int e = 64 * j + lane, r = e / RC, c = (e % RC) ^ ab_kswz<RC>(r);
+                const int t = min(kb + r, E - 1);
+                const int ft = fast_div(t, magicT, T);
+                dma16(rk, kd + j * 1024, (uint32_t)(((slot_of(ft) * T + (t - ft * T)) * D + F0 + 8 * c) * 2));
+            } else {
+                const int fr = 32 * (j - A::KI) + (lane >> 1);
+                const int t8 = min(kb + 8 * ((lane & 1) ^ ((fr >> 3) & 1)), E - 8);
+                const int f8 = fast_div(t8, magicT, T);
+                dma16(rv, vd + (j - A::KI) * 1024, (uint32_t)(((slot_of(f8) * D + fr) * T + (t8 - f8 * T)) * 2));
+            }
+        }
+    };
+
+    // Per 32-row tile of the wave: transposing-read address in a K stage -- token row s16 / 4
+    // (+ the 8-token base of the lane half), features 16 Gh + 4 (s16 % 4) .. + 3 of the tile,
+    // so lane i of 16-lane group Gh receives feature 16 Gh + i of four consecutive tokens.
+    // V^T fragment of column tile ct: row 32 ct + n, token chunk g at its swizzled slot.
+    const int s16 = lane & 15, Gh = (lane >> 4) & 1;
+    int kro[RTW];
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) {
+        const int r = 8 * g + (s16 >> 2);
+        const int fo = w * A::R + 32 * t + 16 * Gh + 4 * (s16 & 3);   // feature within the item
+        kro[t] = r * RW + (((fo >> 3) ^ ab_kswz<RC>(r)) << 4) + (fo & 7) * 2;
+    }
+    const int vro = A::KB + n * 32 + ((g ^ ((n >> 3) & 1)) << 4);
+    f32x16 acc[RTW][CT];
+#pragma unroll
+    for (int t = 0; t < RTW; ++t)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[t][ct] = f32x16{};
+    float zs[RTW];
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) zs[t] = 0.f;
+
+#pragma unroll
+    for (int i = 0; i < kAbStages - 1; ++i) fetch(s0 + i, i);
+    for (int h = s0; h < s1; ++h) {
+        const int st = (h - s0) % kAbStages;
+        wait_vm<A::PW * (kAbStages - 2)>();       // this wave's loads of step h have landed
+        lds_barrier();                            // every wave's; step h - 1's stage is free
+        fetch(h + kAbStages - 1, (h - s0 + kAbStages - 1) % kAbStages);
+        const unsigned char *sb = lds + st * SB;
+        uint32_t ka[RTW];
+#pragma unroll
+        for (int t = 0; t < RTW; ++t) ka[t] = lds_addr(sb + kro[t]);
+        u32x2 r[RTW][2];
+        u32x4 vf[CT];
+        ab_lds_reads<RTW, CT, RW>(ka, lds_addr(sb + vro), r, vf);
+        const int nv = E - 16 * h - 8 * g;        // tokens of the lane's 8 that are absorbed
+#pragma unroll
+        for (int t = 0; t < RTW; ++t) {
+            const uint32_t raw[4] = {r[t][0].x, r[t][0].y, r[t][1].x, r[t][1].y};
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float f0 = phi_f32(bf16_lo_to_f32(raw[e])), f1 = phi_f32(bf16_hi_to_f32(raw[e]));
+                f0 = 2 * e < nv ? f0 : 0.f;
+                f1 = 2 * e + 1 < nv ? f1 : 0.f;
+                zs[t] += f0;
+                zs[t] += f1;
+                hi[e] = pack_bf16x2(f0, f1);
+                lo[e] = pack_bf16x2(f0 - bf16_lo_to_f32(hi[e]), f1 - bf16_hi_to_f32(hi[e]));
+            }
+            const bf16x8 ah = as_bf16x8(u32x4{hi[0], hi[1], hi[2], hi[3]});
+            const bf16x8 al = as_bf16x8(u32x4{lo[0], lo[1], lo[2], lo[3]});
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                acc[t][ct] = mfma32(ah, as_bf16x8(vf[ct]), acc[t][ct]);
+                acc[t][ct] = mfma32(al, as_bf16x8(vf[ct]), acc[t][ct]);
+            }
+        }
+    }
+    wait_vm<0>();     // the padding steps' loads land before the workgroup releases its LDS
+
+    // partials in the state pass's layout: 64-row block rb of plane bh, split p at slot
+    // (bh (D / 64) + rb) P + p, 64 x D floats; z partials after all of them
+    const size_t items = (size_t)a.BH * (D / 64) * P;
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) {
+        const int rbase = F0 + w * A::R + 32 * t;      // the tile's first row (feature)
+        const size_t slot = ((size_t)bh * (D / 64) + rbase / 64) * P + p;
+        float *part = a.ab_part + slot * 64 * D + (size_t)(rbase % 64) * D;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) part[(size_t)(8 * (i >> 2) + 4 * g + (i & 3)) * D + 32 * ct + n] = acc[t][ct][i];
+        const float zt = pair_sum(zs[t]);
+        if (g == 0) a.ab_part[items * 64 * D + slot * 64 + rbase % 64 + n] = zt;
+    }
+}
+
 // D = head dim; NW = waves per workgroup = 32-query tiles per query block (2 when bq == 64);
 // KT = temporal fragments of the relative rotation (DT / 16; 0: no rotation).
 template <int D, int NW, int KT>
@@ -152,7 +379,14 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
 
     // dynamic LDS: [K stage 0][K stage 1][V stage 0][V stage 1][kept list][NW flags]
     extern __shared__ __align__(16) unsigned char dyn[];
-    const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    // the absorb role's workgroups come first (a multiple of 8 of them, so that the
+    // attention's workgroup-to-XCD remap below is unchanged)
+    if ((int)blockIdx.x < a.ab_nab) {
+        if ((int)blockIdx.x < a.ab_items) absorb_role<D, NW>(a, blockIdx.x, dyn, magicT);
+        return;
+    }
+    const int bid = (int)blockIdx.x - a.ab_nab;
+    const int item = (bid & 7) * per_xcd + (bid >> 3);
     if (item >= a.BH * a.nqb) return;   // uniform per workgroup
     const int bh = item / a.nqb, qb = item - bh * a.nqb;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -540,15 +774,26 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
 }  // namespace
 }  // namespace hf
 
-hipError_t hf_launch_sparse_attn(const hf_attn_args &a, hipStream_t s) {
+hipError_t hf_launch_sparse_attn(const hf_attn_args &a_in, hipStream_t s) {
+    hf_attn_args a = a_in;
+    const int nw = a.bq > 32 ? 2 : 1;
+    // absorb items: (plane, split[, 64-row half of S for one-wave workgroups at D = 128])
+    a.ab_P = a.ab_E > 0 ? hf_absorb_splits(a.BH, a.D, a.ab_E) : 1;
+    a.ab_items = a.ab_E > 0 ? a.BH * a.ab_P * ((a.D == 128 && nw == 1) ? 2 : 1) : 0;
+    a.ab_nab = (a.ab_items + 7) & ~7;
     const int items = a.BH * a.nqb;
     const int per_xcd = (items + 7) / 8;
-    const dim3 grid((unsigned)(per_xcd * 8));
+    const dim3 grid((unsigned)(a.ab_nab + per_xcd * 8));
     const uint32_t magicT = hf::div_magic((uint32_t)a.T);
     const float c_log2 = (float)(1.4426950408889634 / sqrt((double)a.D));
     const int lsh = a.bk >= 128 ? 2 : (a.bk >= 64 ? 1 : 0);     // 32-key subtiles per key block = 2^lsh
-    const int nw = a.bq > 32 ? 2 : 1;
-    const size_t dyn = 2 * (size_t)128 * a.D + (size_t)a.top_k * sizeof(int32_t) + nw * sizeof(int);   // 2 K + 2 V stages
+    size_t dyn = 2 * (size_t)128 * a.D + (size_t)a.top_k * sizeof(int32_t) + nw * sizeof(int);   // 2 K + 2 V stages
+    // a step's absorb role streams through kAbStages stages (at most the attention's stages:
+    // 8, 6 or 4 KB each)
+    static_assert(hf::kAbStages * hf::AbShape<128, 2>::SB <= 2 * 128 * 128, "absorb LDS, D=128");
+    static_assert(hf::kAbStages * hf::AbShape<128, 1>::SB <= 2 * 128 * 128, "absorb LDS, D=128, one wave");
+    static_assert(hf::kAbStages * hf::AbShape<64, 2>::SB <= 2 * 128 * 64, "absorb LDS, D=64");
+    static_assert(hf::kAbStages * hf::AbShape<64, 1>::SB <= 2 * 128 * 64, "absorb LDS, D=64, one wave");
     auto go = [&](auto kern, int threads) {
         hipLaunchKernelGGL(kern, grid, dim3(threads), dyn, s, a, magicT, c_log2, per_xcd, lsh);
     };

@@ -113,8 +113,9 @@ typedef struct {
  * step's stream at that point: ev[0] and ev[1] at the beginning (the ring append runs as
  * extra workgroups of the selection's first launch, so it has no interval of its own),
  * ev[2] and ev[3] after block selection (whose first launch also prepares the readout
- * operands, so the two mark the same point), ev[4] after the attention kernel, ev[5]
- * after the absorb of the evicted frames and the state update (the end of the step).
+ * operands, so the two mark the same point), ev[4] after the attention launch (whose extra
+ * workgroups also form the absorb partials of the evicted frames), ev[5] after the state
+ * pass that adds them to the state (the end of the step).
  * Events must have been created by the caller with hipEventCreate. */
 typedef struct {
     hipEvent_t ev[6];
@@ -239,8 +240,10 @@ hf_status hf_cag_schedule(int32_t n_chunks, const int32_t *n_kb, double s_base, 
  *   4. block-sparse attention with the fused readout, as hf_sparse_window_attn -> out_dev;
  *   5. with HF_STEP_COMMIT, when committing the chunk leaves more than W - C committed
  *      frames, the e oldest window frames are the evicted ones: they are absorbed into
- *      (S, z) as hf_linear_absorb would (those frames stay in the ring until the next
- *      append, so they are read right after the attention has streamed them);
+ *      (S, z) -- S += sum phi(K_ev)^T V_ev, z += sum phi(K_ev), fp32 with bf16 hi/lo
+ *      products as hf_linear_absorb: extra workgroups of the attention launch form split
+ *      partial sums straight from the frames' ring slots (those frames stay in the ring
+ *      until the next append), and a state pass adds them in split order;
  *   6. with HF_STEP_COMMIT: n_committed += C - e and head = (head + e) % W.
  * The output therefore reads the state before this step's evictions, and on return the
  * state includes them.  `ring` is updated on success only.  S_dev/z_dev may be NULL only

@@ -90,6 +90,8 @@ RING_ABSORB = [
     (1, 16, 128, 1560, 3, 6, 64, 64, 37),   # 4680 tokens per plane, chunks straddle frames
     (2, 16, 64, 96, 32, 64, 64, 64, 4),     # D=64, 3072 tokens per plane
     (1, 32, 64, 40, 80, 160, 64, 64, 3),    # frames shorter than a chunk, 3200 tokens per plane
+    (1, 2, 128, 1024, 8, 16, 64, 64, 8),    # 8192 tokens per plane: the most splits
+    (1, 3, 128, 1560, 3, 6, 32, 64, 37),    # one-wave attention workgroups (bq = 32)
 ]
 
 

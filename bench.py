@@ -276,21 +276,21 @@ def main():
     idx_warm = torch.empty_like(idx_bufs[0])
     out = torch.empty((cfg.B, cfg.H, cfg.Nq, cfg.D), dtype=torch.float32, device=dev)
     hip = HipEvents()
-    # Phase events are recorded in every EVENT_STRIDE-th timed step only: each recorded
-    # event costs several microseconds of GPU timeline, which would otherwise inflate the
-    # step time being measured.
-    event_slots = list(range(0, args.steps, EVENT_STRIDE))
+    # Phase events are recorded on a subset of the timed steps only (every EVENT_STRIDE-th,
+    # and on at least 5 steps): each recorded event costs several microseconds of GPU
+    # timeline, which would otherwise inflate the step time being measured.
+    stride = max(1, min(EVENT_STRIDE, args.steps // 5))
+    event_slots = list(range(0, args.steps, stride))
     evs = {s: [hip.create() for _ in range(6)] for s in event_slots}
 
-    def step(i, timed_slot=None):
+    def step(i, timed_slot=None, flags=hf.HF_STEP_COMMIT):
         q, k, v = chunks[i % len(chunks)]
         idx = idx_bufs[timed_slot] if timed_slot is not None else idx_warm
         events = evs.get(timed_slot) if timed_slot is not None else None
         if rope is None:
-            hf.hf_hybrid_step(g, q, k, v, ring, top_k, hf.HF_STEP_COMMIT, S, z, idx, out, ws, events=events)
+            hf.hf_hybrid_step(g, q, k, v, ring, top_k, flags, S, z, idx, out, ws, events=events)
         else:
-            hf.hf_hybrid_step_rope(g, q, k, v, ring, top_k, hf.HF_STEP_COMMIT, S, z, idx, out, ws, rope,
-                                   events=events)
+            hf.hf_hybrid_step_rope(g, q, k, v, ring, top_k, flags, S, z, idx, out, ws, rope, events=events)
 
     for i in range(args.warmup):
         step(i)
@@ -301,9 +301,35 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert n_total == args.warmup + args.steps
+    # What the absorb adds to a step, on one window: the last step's chunk attended on the
+    # ring as it is now, R times with the commit (state and descriptor restored between the
+    # repetitions; the commit itself writes nothing the next repetition reads) and R times
+    # without it.  Same window, same kept blocks, same cache state for both: the difference
+    # of the attention launches (whose extra workgroups form the absorb partials in a
+    # committed step) plus the state pass that adds them (ev4 -> ev5) is the absorb's cost.
+    R = 12
+    q_ab, k_ab, v_ab = chunks[(n_total - 1) % len(chunks)]
+    S_snap, z_snap, desc = S.clone(), z.clone(), (ring.head, ring.n_committed)
+    ev_ab = [[hip.create() for _ in range(6)] for _ in range(2 * R)]
+    for r in range(2 * R):
+        ring.set_state(*desc)
+        S.copy_(S_snap)
+        z.copy_(z_snap)
+        hf.hf_hybrid_step(g, q_ab, k_ab, v_ab, ring, top_k, hf.HF_STEP_COMMIT if r < R else 0, S, z, idx_warm, out,
+                          ws, events=ev_ab[r])
+    torch.cuda.synchronize()
+    ring.set_state(*desc)
+    S.copy_(S_snap)
+    z.copy_(z_snap)
+    ab_attn = [hip.elapsed_ms(e[3], e[4]) for e in ev_ab[2:R]]
+    ab_state = [hip.elapsed_ms(e[4], e[5]) for e in ev_ab[2:R]]
+    nc_attn = [hip.elapsed_ms(e[3], e[4]) for e in ev_ab[R + 2:]]
+    t_attn_c = float(np.median(ab_attn)) * 1e-3
+    t_attn_nc = float(np.median(nc_attn)) * 1e-3
+    t_state_ab = float(np.median(ab_state)) * 1e-3
 
     # [steps, 5] ms: (empty) | select (its pool launch also appends the chunk to the ring and prepares
-    # the readout operands) | (empty) | attention + readout | absorb + state update
+    # the readout operands) | (empty) | attention + readout (+ the absorb partials) | state pass
     phases = np.array([[hip.elapsed_ms(e[p], e[p + 1]) for p in range(5)] for e in evs.values()])
     step_ms = np.array([hip.elapsed_ms(e[0], e[5]) for e in evs.values()])
     if args.calib_copy:
@@ -337,7 +363,8 @@ def main():
     t_sel = phases[:, 1].mean() * 1e-3
     t_prep = phases[:, 2].mean() * 1e-3
     t_attn = phases[:, 3].mean() * 1e-3
-    t_abs = phases[:, 4].mean() * 1e-3     # absorb partial sums + state update
+    t_state = phases[:, 4].mean() * 1e-3   # the state pass adding the absorb partials
+    t_abs = max(t_attn_c - t_attn_nc, 0.0) + t_state_ab   # what the absorb adds to a step
     attn_tflops = flops.mean() / t_attn / 1e12
     traffic, traffic_src = pmc_traffic(ATTN_PMC_SUMMARY, ATTN_SOURCES)
     BH, T, D = cfg.B * cfg.H, cfg.T, cfg.D
@@ -374,15 +401,23 @@ def main():
                      "frac_of_measured_gemm": round(attn_tflops / peaks["bf16_gemm_tflops"], 4),
                      "hot_cache_launch_us": round(t_attn_hot * 1e6, 2),
                      "hot_cache_note": "the last step's attention repeated on resident operands; includes the "
-                                       "readout-operand launch"},
+                                       "readout-operand launch",
+                     "launch_note": "in a committed step the attention launch also forms the absorb partials"},
         "phases_us": {"select_append_prep": round(t_sel * 1e6, 2),
-                      "readout_prep": round(t_prep * 1e6, 2), "sparse_attn_readout": round(t_attn * 1e6, 2),
-                      "absorb_and_state": round(t_abs * 1e6, 2)},
+                      "readout_prep": round(t_prep * 1e6, 2),
+                      "sparse_attn_readout_and_absorb_partials": round(t_attn * 1e6, 2),
+                      "state_pass": round(t_state * 1e6, 2)},
         "absorb_roofline": {"bound": "hbm", "achieved": round(absorb_bytes / t_abs / 1e9, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(absorb_bytes / t_abs / 1e9 / PEAK_HBM_GBS, 4),
-                            "bytes_per_launch": absorb_bytes,
+                            "bytes_per_launch": absorb_bytes, "added_us_per_step": round(t_abs * 1e6, 2),
+                            "attention_launch_us_with_commit": round(t_attn_c * 1e6, 2),
+                            "attention_launch_us_without_commit": round(t_attn_nc * 1e6, 2),
+                            "state_pass_us": round(t_state_ab * 1e6, 2),
                             "frac_of_measured_copy": round(absorb_bytes / t_abs / 1e9 / peaks["copy_gbs"], 4),
-                            "note": "absorb kernel + the state update that adds its partial sums (ev4 -> ev5)"},
+                            "note": "what absorbing the 3 evicted frames adds to a step: the attention launch with "
+                                    "the commit (its extra workgroups form the absorb partials) minus the same launch "
+                                    "without it, on one window (medians of 10 repetitions each), plus the state pass "
+                                    "that adds the partials (HIP events, including the events' own cost)"},
         "select_roofline": {"bound": "hbm", "achieved": round(select_bytes / t_sel / 1e9, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "bytes_per_launch": select_bytes,
                             "note": "pool (+ ring append + readout operands) and score/top-k launches (ev1 -> ev2)"},
@@ -469,6 +504,7 @@ def bench_sweep(args):
                      "total_us": round(t_sel + t_att, 2), "attention_tflops": round(fl / (t_att * 1e-6) / 1e12, 1),
                      "speedup_vs_dense": round(t_dense / (t_sel + t_att), 3)})
     beats = [r["keep"] for r in rows if r["speedup_vs_dense"] > 1.0]
+    cpu = cpu_baseline_sweep(cfg, [r["top_k"] for r in rows], args.cpu_seconds) if args.cpu_heads > 0 else None
     res = {"metric": "keep-ratio sweep on a 21-frame window: select + sparse attention vs dense (832x480 shape, 1 GPU)",
            "value": rows[2]["total_us"], "unit": "us at keep 25 %", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(rows[2]["total_us"] * 1e-3, 4), "higher_is_better": False,
@@ -479,8 +515,38 @@ def bench_sweep(args):
            "dense_us": round(t_dense, 2), "dense_tflops": round(f_dense / (t_dense * 1e-6) / 1e12, 1),
            "sweep": rows,
            "crossover": ("selection + sparse beats dense at every keep ratio below 100 %" if set(beats) >= {0.5, 0.25, 0.125}
-                         else f"selection + sparse beats dense at keep ratios {beats}")}
+                         else f"selection + sparse beats dense at keep ratios {beats}"),
+           "cpu_baseline": cpu}
     print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_sweep(cfg, top_ks, seconds):
+    """The fp64 oracle (test infrastructure) at each keep ratio of the sweep, on a bounded
+    sample: head 0, selection over every query block and the sparse attention + readout on
+    its first 8 query blocks, repeated until `seconds` / len(top_ks) of wall time."""
+    import oracle
+    from hybrid_sparse_linear_hf_amd import synth
+
+    inp = synth.field_step_inputs(cfg, heads=[0])
+    f64 = synth.f64_from_bf16_bits
+    Q, K, V = f64(inp["q"]), f64(inp["k_win"]), f64(inp["v_win"])
+    S0, z0 = oracle.absorb(f64(inp["k_ev"]), f64(inp["v_ev"]))
+    blocks = [(0, i) for i in range(8)]
+    out = []
+    for k in top_ks:
+        reps, fl = 0, 0.0
+        t0 = time.perf_counter()
+        while True:
+            _, idx, _ = oracle.hybrid_step(Q, K, V, S0, z0, cfg.bq, cfg.bk, k, blocks=blocks)
+            fl += kept_flops(idx[:, :, :8], cfg.Nq, cfg.Nk, cfg.bq, cfg.bk, cfg.D)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= seconds / len(top_ks):
+                break
+        out.append({"top_k": k, "value": round(fl / dt / 1e12, 5), "ms_per_sample": round(dt / reps * 1e3, 1)})
+    return {"unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": "head 0 of 12: selection over all 74 query blocks, sparse attention + readout on query blocks "
+                      "0-7 (fp64), per keep ratio", "per_keep": out}
 
 
 def bench_hier(args):

@@ -267,6 +267,19 @@ int hf_absorb_splits(int BH, int D, int64_t n_tok) {
     return nch < P ? (int)(nch > 0 ? nch : 1) : P;
 }
 
+// Splits of a hybrid step's absorb, which runs beside the attention: about 72 workgroups in
+// all -- enough to stream the evicted frames while the attention runs, few enough to leave
+// it its slots -- and at least one 16-token step each.  Never more than hf_absorb_splits
+// allows for these planes, so the partials fit the same workspace.
+int hf_step_absorb_splits(int BH, int D, int64_t n_tok) {
+    const int64_t steps = (n_tok + 15) / 16;
+    int64_t P = 72 / BH;
+    const int64_t cap = hf_absorb_splits(BH, D, (int64_t)1 << 30);
+    P = P < cap ? P : cap;
+    P = P < steps ? P : steps;
+    return (int)(P < 1 ? 1 : P);
+}
+
 // Workspace floats of the partials for P splits: BH*D/64*P blocks of 64 x D, then as many
 // blocks of 64 z values.
 size_t hf_absorb_partial_floats(int BH, int D, int P) {

@@ -185,7 +185,9 @@ hipError_t enqueue_select(const hf_dims *d, const void *q, const hf_kv_ring *r, 
 
 // The state pass of a step: readout operands (S^T bf16, z copy) from the state as it is,
 // and, when `absorb_tokens` > 0, the absorb partials already in the workspace added in.
-hf_state_args state_args(const hf_dims *d, float *S, float *z, bool readout, int64_t absorb_tokens, void *ws) {
+// `step_absorb`: the partials come from a step's absorb (its own split count).
+hf_state_args state_args(const hf_dims *d, float *S, float *z, bool readout, int64_t absorb_tokens, void *ws,
+                         bool step_absorb = false) {
     const WsLayout L = ws_layout(d);
     hf_state_args a{};
     a.BH = d->B * d->H;
@@ -193,15 +195,16 @@ hf_state_args state_args(const hf_dims *d, float *S, float *z, bool readout, int
     a.S = S;
     a.z = z;
     a.part = absorb_tokens > 0 ? reinterpret_cast<const float *>(wsp(ws, L.absorb)) : nullptr;
-    a.P = absorb_tokens > 0 ? hf_absorb_splits(a.BH, d->D, absorb_tokens) : 0;
+    a.P = absorb_tokens <= 0 ? 0
+          : (step_absorb ? hf_step_absorb_splits(a.BH, d->D, absorb_tokens) : hf_absorb_splits(a.BH, d->D, absorb_tokens));
     a.st = readout ? reinterpret_cast<uint16_t *>(wsp(ws, L.st)) : nullptr;
     a.zc = readout ? reinterpret_cast<float *>(wsp(ws, L.zc)) : nullptr;
     return a;
 }
 
 hipError_t enqueue_state(const hf_dims *d, float *S, float *z, bool readout, int64_t absorb_tokens, void *ws,
-                         hipStream_t s) {
-    return hf_launch_state(state_args(d, S, z, readout, absorb_tokens, ws), s);
+                         hipStream_t s, bool step_absorb = false) {
+    return hf_launch_state(state_args(d, S, z, readout, absorb_tokens, ws, step_absorb), s);
 }
 
 // Attention (+ readout from the prepared S^T / z copy when `readout`).
@@ -561,10 +564,10 @@ hf_status hf_fail_hip(hipError_t e, const char *what) { return hip_status(e, wha
 hf_status hf_step_enqueue(const hf_dims *d, const void *q, const void *k_cur, const void *v_cur, hf_kv_ring *ring,
                           int32_t top_k, uint32_t flags, float *S, float *z, float eps, const hf_rope *rope,
                           int32_t *idx, float *out, void *ws, const hf_step_events *events, hipStream_t stream) {
-    // Order: append; select, with the readout operands taken from the state as it is by
-    // extra workgroups of its first launch; attention with the fused readout, whose launch
-    // also forms the absorb partials of the frames this step evicts (still in the ring until
-    // the next append); the state pass that adds them.
+    // Order: select -- its pool launch also takes the readout operands from the state as it
+    // is, its score + top-k launch also appends the chunk to the ring; attention with the
+    // fused readout, whose launch also forms the absorb partials of the frames this step
+    // evicts (still in the ring until the next append); the state pass that adds them.
     hf_kv_ring next = *ring;
     int evict = 0;
     if (flags & HF_STEP_COMMIT) {
@@ -577,8 +580,8 @@ hf_status hf_step_enqueue(const hf_dims *d, const void *q, const void *k_cur, co
     const int64_t evict_tok = (int64_t)evict * d->T;
     hipError_t e = record(events, 0, stream);
     if (e == hipSuccess) e = record(events, 1, stream);
-    // the readout operands and the ring append are extra workgroups of the selection's pool
-    // launch (which then reads the current chunk's keys from k_cur)
+    // the readout operands are extra workgroups of the selection's pool launch (which reads
+    // the current chunk's keys from k_cur), the ring append those of its score launch
     const hf_state_args prep = S ? state_args(d, S, z, true, 0, ws) : hf_state_args{};
     const hf_append_args app = k_cur ? append_args(d, ring, k_cur, v_cur) : hf_append_args{};
     if (e == hipSuccess)
@@ -593,7 +596,7 @@ hf_status hf_step_enqueue(const hf_dims *d, const void *q, const void *k_cur, co
     if (e == hipSuccess)
         e = enqueue_attn(d, q, ring, idx, top_k, S != nullptr, eps, out, ws, stream, nullptr, rope, evict_tok);
     if (e == hipSuccess) e = record(events, 4, stream);
-    if (e == hipSuccess && evict_tok > 0) e = enqueue_state(d, S, z, false, evict_tok, ws, stream);
+    if (e == hipSuccess && evict_tok > 0) e = enqueue_state(d, S, z, false, evict_tok, ws, stream, true);
     if (e == hipSuccess) e = record(events, 5, stream);
     if (e != hipSuccess) return hip_status(e, "hybrid step launch");
     *ring = next;

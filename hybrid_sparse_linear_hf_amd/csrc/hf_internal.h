@@ -134,8 +134,9 @@ struct hf_select_args {
     // readout preparation run as extra workgroups of the pool launch (prep_tiles > 0)
     hf_state_args prep;
     int prep_tiles;
-    // a hybrid step's ring append as extra workgroups after those (app_tiles > 0); the keys
-    // of the current chunk (logical frames >= ncom) are then read from k_cur, not the ring
+    // a hybrid step's ring append, run as extra workgroups of the score + top-k launch
+    // (app_tiles > 0); the pool then reads the keys of the current chunk (logical frames
+    // >= ncom) from k_cur, not the ring
     hf_append_args app;
     int app_tiles;
     const uint16_t *k_cur;     // null: every key from the ring
@@ -207,6 +208,7 @@ struct hf_absorb_args {
     float *part;               // workspace: partial sums (hf_absorb_partial_floats floats)
 };
 int hf_absorb_splits(int BH, int D, int64_t n_tok);
+int hf_step_absorb_splits(int BH, int D, int64_t n_tok);   // the absorb inside a step's attention launch
 size_t hf_absorb_partial_floats(int BH, int D, int P);
 size_t hf_absorb_workspace_bytes(int BH, int D);
 hipError_t hf_launch_absorb_partial(const hf_absorb_args &a, hipStream_t s);

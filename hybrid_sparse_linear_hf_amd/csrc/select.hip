@@ -16,14 +16,15 @@
 //   pool_kernel        HBM-bound: one workgroup per query or key block sums its rows in
 //                      fp64 (sums of bf16 values are exact in fp64) and stores the block
 //                      mean.  In a hybrid step the same launch carries extra workgroups
-//                      that prepare the readout operands and append the chunk to the ring
-//                      (the chunk's key blocks are then pooled from the chunk input).
+//                      that prepare the readout operands, and the chunk's key blocks are
+//                      pooled from the chunk input.
 //   score_topk_kernel  one wave per query block: its fp64 scores against every pooled
 //                      key block, each evaluated as sum_d (qbar_d * kbar_d) in index
 //                      order with separately rounded products and sums (pooled keys staged
 //                      through LDS in chunks of 64), kept in LDS; then a radix select of the
 //                      k-th largest (score, -index) key and an ascending emit of the kept
-//                      indices.
+//                      indices.  In a hybrid step the same launch carries the ring append of
+//                      the chunk as extra workgroups, whose copying overlaps the scoring.
 // The hierarchical variant pools per frame as well (frame_pool_kernel), scores with the
 // tiled score_kernel (16 x 16 tiles, one wave each, same summation order) over block pairs
 // and over (query block, frame) pairs, and lets topk_kernel select the frames before the
@@ -57,8 +58,6 @@ __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
         const int x = (int)blockIdx.x - a.BH * per_plane;
         if (x < a.prep_tiles)   // readout operands of a hybrid step (independent of the selection)
             state_tile<D>(a.prep, x, reinterpret_cast<float(*)[33]>(&red[0][0]));
-        else                    // the step's ring append
-            append_tile<D>(a.app, x - a.prep_tiles);
         return;
     }
     const int bh = blockIdx.x / per_plane;
@@ -343,6 +342,13 @@ __global__ __launch_bounds__(64 * kRows) void score_topk_kernel(hf_select_args a
     __shared__ __align__(16) double ks[CH][P];
     __shared__ double srow[kRows][KPL * 64];
     const int groups = (a.nqb + kRows - 1) / kRows;
+    if ((int)blockIdx.x >= a.BH * groups) {
+        // a hybrid step's ring append: pure copying, which fills the slots this latency-bound
+        // scoring leaves idle (nothing here reads the ring: the current chunk's keys were
+        // pooled from the chunk input)
+        append_tile<D>(a.app, (int)blockIdx.x - a.BH * groups);
+        return;
+    }
     const int bh = blockIdx.x / groups, i0 = (blockIdx.x % groups) * kRows;
     const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
     const int i = i0 + w;                     // this wave's query block (past the end: idle)
@@ -415,7 +421,7 @@ static void launch_topk(int kpl, dim3 grid, const hf_select_args &a, hipStream_t
 
 template <int D>
 static void launch_score_topk(int kpl, const hf_select_args &a, double scale, hipStream_t s) {
-    const dim3 grid((unsigned)(a.BH * ((a.nqb + hf::kRows - 1) / hf::kRows)));
+    const dim3 grid((unsigned)(a.BH * ((a.nqb + hf::kRows - 1) / hf::kRows) + a.app_tiles));
     const dim3 block(64 * hf::kRows);
     if (kpl <= 1) hipLaunchKernelGGL((hf::score_topk_kernel<D, 1>), grid, block, 0, s, a, scale);
     else if (kpl <= 2) hipLaunchKernelGGL((hf::score_topk_kernel<D, 2>), grid, block, 0, s, a, scale);
@@ -427,7 +433,9 @@ static void launch_score_topk(int kpl, const hf_select_args &a, double scale, hi
 }
 
 hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s) {
-    const dim3 grid_pool((unsigned)(a.BH * (a.nqb + a.nkb) + a.prep_tiles + a.app_tiles));
+    // a step's ring append runs as extra workgroups of the score + top-k launch (flat
+    // selection; the hierarchical path is never given one)
+    const dim3 grid_pool((unsigned)(a.BH * (a.nqb + a.nkb) + a.prep_tiles));
     const int ti_n = (a.nqb + hf::kTile - 1) / hf::kTile, tj_n = (a.nkb + hf::kTile - 1) / hf::kTile;
     const dim3 grid_score((unsigned)(a.BH * ti_n * tj_n));
     const dim3 grid_topk((unsigned)((a.BH * a.nqb + 3) / 4));

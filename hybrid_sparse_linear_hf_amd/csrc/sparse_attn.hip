@@ -778,7 +778,7 @@ hipError_t hf_launch_sparse_attn(const hf_attn_args &a_in, hipStream_t s) {
     hf_attn_args a = a_in;
     const int nw = a.bq > 32 ? 2 : 1;
     // absorb items: (plane, split[, 64-row half of S for one-wave workgroups at D = 128])
-    a.ab_P = a.ab_E > 0 ? hf_absorb_splits(a.BH, a.D, a.ab_E) : 1;
+    a.ab_P = a.ab_E > 0 ? hf_step_absorb_splits(a.BH, a.D, a.ab_E) : 1;
     a.ab_items = a.ab_E > 0 ? a.BH * a.ab_P * ((a.D == 128 && nw == 1) ? 2 : 1) : 0;
     a.ab_nab = (a.ab_items + 7) & ~7;
     const int items = a.BH * a.nqb;

@@ -111,7 +111,7 @@ typedef struct {
 
 /* Optional timing hooks for hf_hybrid_step: any non-NULL event is recorded on the
  * step's stream at that point: ev[0] and ev[1] at the beginning (the ring append runs as
- * extra workgroups of the selection's first launch, so it has no interval of its own),
+ * extra workgroups of the selection's second launch, so it has no interval of its own),
  * ev[2] and ev[3] after block selection (whose first launch also prepares the readout
  * operands, so the two mark the same point), ev[4] after the attention launch (whose extra
  * workgroups also form the absorb partials of the evicted frames), ev[5] after the state

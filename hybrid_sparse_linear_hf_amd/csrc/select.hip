@@ -14,9 +14,11 @@
 //
 // Flat selection, two launches:
 //   pool_kernel        HBM-bound: one workgroup per query or key block sums its rows in
-//                      fp64 (sums of bf16 values are exact in fp64) and stores the block
-//                      mean.  In a hybrid step the same launch carries extra workgroups
-//                      that prepare the readout operands, and the chunk's key blocks are
+//                      fp64 and stores the block mean.  The sums are exact while the
+//                      magnitudes in one feature span at most 2^39 over 64 rows (8 bits of
+//                      a bf16 significand + 6 bits of carries + the span fit in 53).
+//                      In a hybrid step the same launch carries extra workgroups that
+//                      prepare the readout operands, and the chunk's key blocks are
 //                      pooled from the chunk input.
 //   score_topk_kernel  one wave per query block: its fp64 scores against every pooled
 //                      key block, each evaluated as sum_d (qbar_d * kbar_d) in index

@@ -148,7 +148,10 @@ hf_status hf_ring_append(const hf_dims *d, const hf_kv_ring *ring, const void *k
  * For each (b, h, query block i): qbar_i = mean of Q over block i, kbar_j = mean of the
  * window keys over key block j, score s_ij = qbar_i . kbar_j / sqrt(D) (pooled and
  * scored in fp64); keep the top_k largest, ties to the lower j, written in ASCENDING
- * order.
+ * order.  The pooled sums are exact in fp64, so independent of summation order, when the
+ * nonzero magnitudes summed into one pooled feature span at most 2^(45 - ceil(log2 n))
+ * (n rows summed: 2^39 for 64-row blocks, 2^34 for 1560-token frames); beyond that
+ * span a score may differ from an exact evaluation in its last bits.
  *   q_dev          bf16 [B][H][C*T][D] current chunk queries
  *   idx_dev        int32 [B][H][n_qb][top_k] out, n_qb = ceil(C*T/bq)
  *   scores_dev     fp64 [B][H][n_qb][n_kb] out (may be NULL), n_kb = ceil(Nk/bk)

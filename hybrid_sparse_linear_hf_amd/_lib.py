@@ -34,7 +34,7 @@ class Dims(ctypes.Structure):
 
 
 class KVRing(ctypes.Structure):
-    _fields_ = [("k_dev", ctypes.c_void_p), ("vt_dev", ctypes.c_void_p), ("head", ctypes.c_int32),
+    _fields_ = [("k_dev", ctypes.c_void_p), ("vg_dev", ctypes.c_void_p), ("head", ctypes.c_int32),
                 ("n_committed", ctypes.c_int32)]
 
 
@@ -202,16 +202,22 @@ class Geometry:
 
 
 class Ring:
-    """Device storage of the KV ring (keys [B,H,W,T,D], values transposed [B,H,W,D,T]) plus
-    the host descriptor (head, n_committed)."""
+    """Device storage of the KV ring (keys [B,H,W,T,D], values in 8-token groups
+    [B,H,W,T/8,D,8]) plus the host descriptor (head, n_committed)."""
 
     def __init__(self, g: Geometry, device="cuda"):
         self.g = g
         self.k = torch.zeros((g.B, g.H, g.W, g.T, g.D), dtype=torch.bfloat16, device=device)
-        self.vt = torch.zeros((g.B, g.H, g.W, g.D, g.T), dtype=torch.bfloat16, device=device)
+        self.vg = torch.zeros((g.B, g.H, g.W, g.T // 8, g.D, 8), dtype=torch.bfloat16, device=device)
         self.desc = KVRing()
-        _check("hf_ring_init", lib().hf_ring_init(ctypes.byref(g.dims()), self.k.data_ptr(), self.vt.data_ptr(),
+        _check("hf_ring_init", lib().hf_ring_init(ctypes.byref(g.dims()), self.k.data_ptr(), self.vg.data_ptr(),
                                                   ctypes.byref(self.desc)))
+
+    @staticmethod
+    def grouped(v: "torch.Tensor") -> "torch.Tensor":
+        """Values [..., T, D] in the ring's value layout [..., T/8, D, 8]."""
+        *lead, t, d = v.shape
+        return v.reshape(*lead, t // 8, 8, d).transpose(-1, -2)
 
     @property
     def head(self) -> int:

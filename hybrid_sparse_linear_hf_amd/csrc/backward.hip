@@ -60,8 +60,8 @@ __device__ __forceinline__ float phi_prime(float x) {
 // ---------------------------------------------------------------- prep
 
 // One workgroup per (plane, 64-key tile of the logical window): K rows and V rows (V from
-// the ring's V^T frames, transposed through LDS), rows past the window zeroed.  Keys j0 .. j0 + 63 in aligned groups of 8 stay in one frame
-// (T % 8 == 0).
+// the ring's 8-token groups, transposed through LDS), rows past the window zeroed.  Keys
+// j0 .. j0 + 63 in aligned groups of 8 stay in one frame (T % 8 == 0).
 template <int D>
 __global__ __launch_bounds__(256) void prep_keys_kernel(hf_bwd_args a) {
     __shared__ __align__(16) uint16_t tv[D][64 + 8];
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void prep_keys_kernel(hf_bwd_args a) {
         u32x4 v = {0, 0, 0, 0};
         if (j < a.Nk) {
             const int f = j / a.T, t = j - f * a.T;
-            v = *reinterpret_cast<const u32x4 *>(a.ring_vt + (((size_t)bh * a.W + slot_of(f)) * D + d) * a.T + t);
+            v = *reinterpret_cast<const u32x4 *>(a.ring_vg + (((size_t)bh * a.W + slot_of(f)) * a.T + t) * D + 8 * d);
         }
         *reinterpret_cast<u32x4 *>(&tv[d][k8]) = v;
     }

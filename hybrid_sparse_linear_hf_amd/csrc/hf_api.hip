@@ -51,7 +51,7 @@ hf_status check_dims(const hf_dims *d) {
 
 hf_status check_ring(const hf_dims *d, const hf_kv_ring *r) {
     if (!r) return fail(HF_ERR_NULL, "ring is NULL");
-    if (!r->k_dev || !r->vt_dev) return fail(HF_ERR_NULL, "ring storage pointer is NULL");
+    if (!r->k_dev || !r->vg_dev) return fail(HF_ERR_NULL, "ring storage pointer is NULL");
     if (r->head < 0 || r->head >= d->W) return fail(HF_ERR_RING_STATE, "ring head=%d outside [0, W=%d)", r->head, d->W);
     if (r->n_committed < 0 || r->n_committed > d->W - d->C)
         return fail(HF_ERR_RING_STATE, "ring n_committed=%d outside [0, W-C=%d]", r->n_committed, d->W - d->C);
@@ -129,7 +129,7 @@ hf_append_args append_args(const hf_dims *d, const hf_kv_ring *r, const void *kc
     a.k_cur = static_cast<const uint16_t *>(kc);
     a.v_cur = static_cast<const uint16_t *>(vc);
     a.ring_k = static_cast<uint16_t *>(r->k_dev);
-    a.ring_vt = static_cast<uint16_t *>(r->vt_dev);
+    a.ring_vg = static_cast<uint16_t *>(r->vg_dev);
     return a;
 }
 
@@ -228,7 +228,7 @@ hipError_t enqueue_attn(const hf_dims *d, const void *q, const hf_kv_ring *r, co
     a.top_k = top_k;
     a.q = static_cast<const uint16_t *>(q);
     a.ring_k = static_cast<const uint16_t *>(r->k_dev);
-    a.ring_vt = static_cast<const uint16_t *>(r->vt_dev);
+    a.ring_vg = static_cast<const uint16_t *>(r->vg_dev);
     a.idx = idx;
     a.st = readout ? reinterpret_cast<const uint16_t *>(wsp(ws, L.st)) : nullptr;
     a.zc = readout ? reinterpret_cast<const float *>(wsp(ws, L.zc)) : nullptr;
@@ -312,11 +312,11 @@ hf_status hf_workspace_size(const hf_dims *d, int32_t top_k, size_t *bytes) {
     return ok();
 }
 
-hf_status hf_ring_init(const hf_dims *d, void *k_store, void *vt_store, hf_kv_ring *out) {
+hf_status hf_ring_init(const hf_dims *d, void *k_store, void *vg_store, hf_kv_ring *out) {
     const hf_status st = check_dims(d);
     if (st != HF_OK) return st;
-    if (!k_store || !vt_store || !out) return fail(HF_ERR_NULL, "k_store/vt_store/out is NULL");
-    *out = hf_kv_ring{k_store, vt_store, 0, 0};
+    if (!k_store || !vg_store || !out) return fail(HF_ERR_NULL, "k_store/vg_store/out is NULL");
+    *out = hf_kv_ring{k_store, vg_store, 0, 0};
     return ok();
 }
 
@@ -463,7 +463,7 @@ hf_status hf_hybrid_attn_backward(const hf_dims *d, const void *q, const hf_kv_r
     a.top_k = top_k;
     a.q = static_cast<const uint16_t *>(q);
     a.ring_k = static_cast<const uint16_t *>(ring->k_dev);
-    a.ring_vt = static_cast<const uint16_t *>(ring->vt_dev);
+    a.ring_vg = static_cast<const uint16_t *>(ring->vg_dev);
     a.idx = idx;
     a.S = S;
     a.z = z;

@@ -83,19 +83,6 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // 16*g + i, i = 0..15, in accumulator slot i.
 __device__ __forceinline__ int perm32(int m) { return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3); }
 
-// ------------------------------------------------------------------ ring addressing
-
-struct RingView {
-    const uint16_t *k;   // [BH][W][T][D]
-    const uint16_t *vt;  // [BH][W][D][T]
-    int W, T, D, head;
-};
-
-// Slot of logical window frame f.
-__device__ __forceinline__ int ring_slot(const RingView &r, int f) {
-    int s = r.head + f;
-    return s >= r.W ? s - r.W : s;
-}
 
 }  // namespace hf
 
@@ -115,7 +102,7 @@ hipError_t hf_launch_state(const hf_state_args &a, hipStream_t s);
 struct hf_append_args {
     int BH, D, T, W, head, first_frame, C;
     const uint16_t *k_cur, *v_cur;
-    uint16_t *ring_k, *ring_vt;
+    uint16_t *ring_k, *ring_vg;
 };
 
 struct hf_select_args {
@@ -150,7 +137,7 @@ hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s);
 
 struct hf_attn_args {
     int BH, D, T, W, head, Nq, Nk, bq, bk, nqb, nkb, top_k;
-    const uint16_t *q, *ring_k, *ring_vt;
+    const uint16_t *q, *ring_k, *ring_vg;
     const int32_t *idx;
     const uint16_t *st;        // S^T in bf16 [BH][D][D] (null: sparse part only)
     const float *zc;           // z [BH][D] as read by this step
@@ -173,7 +160,7 @@ hipError_t hf_launch_sparse_attn(const hf_attn_args &a, hipStream_t s);
 // Backward of the step output (backward.hip); arguments validated by the caller.
 struct hf_bwd_args {
     int BH, D, T, W, head, Nq, Nk, bq, bk, nqb, nkb, top_k, NkP, NqP, splits;
-    const uint16_t *q, *ring_k, *ring_vt;
+    const uint16_t *q, *ring_k, *ring_vg;
     const int32_t *idx;
     const float *S, *z, *out, *lse, *dout;
     float eps;

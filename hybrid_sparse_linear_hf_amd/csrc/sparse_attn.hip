@@ -12,12 +12,12 @@
 //     a SIMD and the hardware overlaps one wave's softmax with the other's matrix-core
 //     work.  Workgroup ids are remapped so that the query blocks of one plane run on one
 //     XCD and share its L2 for the window's K/V.
-//   * The kept key blocks are walked in 32-key subtiles.  Each subtile's K rows and V^T
-//     columns are fetched with direct-to-LDS buffer loads (16 bytes per lane, whole 256-byte
-//     K rows and 64-byte V^T row segments per instruction, so every load is coalesced) into
-//     a double-buffered LDS stage, one subtile ahead of the compute; the two waves share
-//     the fetch.  Chunk positions are XOR-swizzled per row, so that the 16-byte reads in
-//     matrix-core operand order hit distinct LDS banks.
+//   * The kept key blocks are walked in 32-key subtiles.  Each subtile's K rows and its four
+//     8-key V groups (the ring keeps values as [8-token group][D][8]) are fetched with
+//     direct-to-LDS buffer loads (16 bytes per lane, 1 KB of contiguous whole cache lines per
+//     instruction) into a double-buffered LDS stage, one subtile ahead of the compute; the
+//     two waves share the fetch.  16-byte chunk positions are XOR-swizzled, so that the
+//     reads in matrix-core operand order hit distinct LDS banks.
 //   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16: the probabilities leave
 //     the first product in the register layout the second consumes.  Key rows are read in
 //     the order perm32(m), so each lane holds 16 consecutive keys of its query column, and
@@ -71,15 +71,16 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// LDS chunk swizzles (16-byte chunks).  K rows hold D/8 chunks; V^T rows (one feature,
-// the subtile's 32 keys) hold 4.  Chosen so that the operand reads below touch 16 distinct
-// bank groups per 16 lanes.
+// LDS swizzles (16-byte chunks), chosen so that the operand reads below touch 16 distinct
+// bank groups per 16 lanes.  K rows hold D/8 chunks, permuted per row.  A V group holds D
+// 16-byte feature rows; feature f sits at position vslot(f) (bit 3 ^= bit 4): the 16 lanes
+// of a read take features perm32(0 .. 15) = {0-3, 16-19, 4-7, 20-23} (+ 8 for the next 16).
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
     if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | ((r >> 1) & 8);
     else return ((r >> 1) & 3) | ((r >> 2) & 4);
 }
-__device__ __forceinline__ int swz_v(int f) { return ((f >> 4) & 1) | (((f >> 2) & 1) << 1); }
+__device__ __forceinline__ int vslot(int f) { return f ^ ((f >> 1) & 8); }
 
 struct SmState {
     float m;     // reference maximum of s * c_log2 (base-2 logits)
@@ -153,7 +154,7 @@ constexpr int kWaitVm0 = 0x0F70;   // s_waitcnt vmcnt(0), other counters untouch
 //     D columns, and the workgroup walks its split in 16-token steps.
 //   * The steps stream through a ring of kAbStages LDS stages with direct-to-LDS loads,
 //     kAbStages - 1 steps ahead (counted waits, one LDS-only barrier per step): K rows (the
-//     item's features of each token) and V^T rows (16 tokens of every feature).  gfx950's
+//     item's features of each token) and the two 8-token V groups.  gfx950's
 //     transposing LDS read (within each 16-lane group, lane i receives element i % 4 of the
 //     4-element vectors lanes i / 4 + 4 e point at) turns the K rows into the phi(K)^T
 //     operand (8 tokens of one feature per lane); phi is evaluated in fp32 and split into
@@ -174,7 +175,7 @@ struct AbShape {
     static constexpr int RW = ROWS * 2;                      // bytes per staged K row
     static constexpr int RC = RW / 16;                       // 16-byte chunks per K row
     static constexpr int KB = 16 * RW;                       // K stage bytes (16 tokens)
-    static constexpr int SB = KB + D * 32;                   // stage bytes (+ V^T: D x 16 tokens)
+    static constexpr int SB = KB + D * 32;                   // stage bytes (+ V: two 8-token groups)
     static constexpr int KI = KB / 1024, VI = D * 32 / 1024; // load instructions per step
     static constexpr int PW = (KI + VI) / NW;                // ... per wave
 };
@@ -186,7 +187,7 @@ __device__ __forceinline__ int ab_kswz(int r) { return (RC / 4) * (r & 3); }
 
 // LDS reads of one absorb step, in one asm block that also waits for them: per 32-row tile
 // two transposing reads of K (token rows 0-3 and 4-7 from the lane's base, 4 RW bytes
-// apart) and CT 16-byte V^T fragments (1 KB apart).  Written out so that the compiler, which
+// apart) and CT 16-byte V fragments (512 bytes apart).  Written out so that the compiler, which
 // cannot tell which direct-to-LDS load an LDS read depends on, adds no wait for every load
 // in flight: the caller's counted wait covers the step's loads.  Every output is complete
 // when the block ends.
@@ -200,9 +201,9 @@ __device__ __forceinline__ void ab_lds_reads(const uint32_t (&ka)[RTW], uint32_t
             "ds_read_b64_tr_b16 %2, %9\n\t"
             "ds_read_b64_tr_b16 %3, %9 offset:%11\n\t"
             "ds_read_b128 %4, %10\n\t"
-            "ds_read_b128 %5, %10 offset:1024\n\t"
-            "ds_read_b128 %6, %10 offset:2048\n\t"
-            "ds_read_b128 %7, %10 offset:3072\n\t"
+            "ds_read_b128 %5, %10 offset:512\n\t"
+            "ds_read_b128 %6, %10 offset:1024\n\t"
+            "ds_read_b128 %7, %10 offset:1536\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(vf[0]), "=&v"(vf[1]),
               "=&v"(vf[2]), "=&v"(vf[3])
@@ -215,7 +216,7 @@ __device__ __forceinline__ void ab_lds_reads(const uint32_t (&ka)[RTW], uint32_t
             "ds_read_b64_tr_b16 %2, %7\n\t"
             "ds_read_b64_tr_b16 %3, %7 offset:%9\n\t"
             "ds_read_b128 %4, %8\n\t"
-            "ds_read_b128 %5, %8 offset:1024\n\t"
+            "ds_read_b128 %5, %8 offset:512\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(vf[0]), "=&v"(vf[1])
             : "v"(ka[0]), "v"(ka[1]), "v"(va), "i"(4 * RW)
@@ -226,7 +227,7 @@ __device__ __forceinline__ void ab_lds_reads(const uint32_t (&ka)[RTW], uint32_t
             "ds_read_b64_tr_b16 %0, %4\n\t"
             "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
             "ds_read_b128 %2, %5\n\t"
-            "ds_read_b128 %3, %5 offset:1024\n\t"
+            "ds_read_b128 %3, %5 offset:512\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(vf[0]), "=&v"(vf[1])
             : "v"(ka[0]), "v"(va), "i"(4 * RW)
@@ -253,7 +254,7 @@ __device__ __forceinline__ void absorb_role(const hf_attn_args &a, int ab, unsig
     const size_t plane = (size_t)bh * W * T * D;
     const uint32_t plane_bytes = (uint32_t)((size_t)W * T * D * 2);
     const Rsrc rk = make_rsrc(a.ring_k + plane, plane_bytes);
-    const Rsrc rv = make_rsrc(a.ring_vt + plane, plane_bytes);
+    const Rsrc rv = make_rsrc(a.ring_vg + plane, plane_bytes);
     auto slot_of = [&](int f) -> int {
         const int s = head + f;
         return s >= W ? s - W : s;
@@ -262,8 +263,8 @@ __device__ __forceinline__ void absorb_role(const hf_attn_args &a, int ab, unsig
     // padding steps are never consumed).  Instruction j of the step is issued by wave j % NW.
     //   K, j < KI: lane -> token row (64 j + lane) / RC, slot (64 j + lane) % RC holding chunk
     //     slot ^ ab_kswz(row) of the item's features.
-    //   V^T, j >= KI: lane -> feature row 32 (j - KI) + lane / 2, slot lane % 2 holding token
-    //     chunk (lane % 2) ^ (row / 8 % 2) (8 tokens of one frame: T and E are multiples of 8).
+    //   V, j >= KI: 1 KB of the step's two 8-token groups as they lie in the ring ([group]
+    //     [D][8]; a group is 8 tokens of one frame: T and E are multiples of 8).
     // Tokens at or past E re-read the last ones (finite data; their phi is masked to 0).
     auto fetch = [&](int h, int st) {
         h = min(h, s1 - 1);
@@ -278,10 +279,11 @@ __device__ __forceinline__ void absorb_role(const hf_attn_args &a, int ab, unsig
                 const int ft = fast_div(t, magicT, T);
                 dma16(rk, kd + j * 1024, (uint32_t)(((slot_of(ft) * T + (t - ft * T)) * D + F0 + 8 * c) * 2));
             } else {
-                const int fr = 32 * (j - A::KI) + (lane >> 1);
-                const int t8 = min(kb + 8 * ((lane & 1) ^ ((fr >> 3) & 1)), E - 8);
+                constexpr int VIG = D / 64;       // instructions per group
+                const int jv = j - A::KI;
+                const int t8 = min(kb + 8 * (jv / VIG), E - 8);
                 const int f8 = fast_div(t8, magicT, T);
-                dma16(rv, vd + (j - A::KI) * 1024, (uint32_t)(((slot_of(f8) * D + fr) * T + (t8 - f8 * T)) * 2));
+                dma16(rv, vd + jv * 1024, (uint32_t)((slot_of(f8) * T + (t8 - f8 * T)) * D * 2 + (jv % VIG) * 1024 + lane * 16));
             }
         }
     };
@@ -289,7 +291,7 @@ __device__ __forceinline__ void absorb_role(const hf_attn_args &a, int ab, unsig
     // Per 32-row tile of the wave: transposing-read address in a K stage -- token row s16 / 4
     // (+ the 8-token base of the lane half), features 16 Gh + 4 (s16 % 4) .. + 3 of the tile,
     // so lane i of 16-lane group Gh receives feature 16 Gh + i of four consecutive tokens.
-    // V^T fragment of column tile ct: row 32 ct + n, token chunk g at its swizzled slot.
+    // V fragment of column tile ct: group g, feature row 32 ct + n.
     const int s16 = lane & 15, Gh = (lane >> 4) & 1;
     int kro[RTW];
 #pragma unroll
@@ -298,7 +300,7 @@ __device__ __forceinline__ void absorb_role(const hf_attn_args &a, int ab, unsig
         const int fo = w * A::R + 32 * t + 16 * Gh + 4 * (s16 & 3);   // feature within the item
         kro[t] = r * RW + (((fo >> 3) ^ ab_kswz<RC>(r)) << 4) + (fo & 7) * 2;
     }
-    const int vro = A::KB + n * 32 + ((g ^ ((n >> 3) & 1)) << 4);
+    const int vro = A::KB + g * D * 16 + n * 16;
     f32x16 acc[RTW][CT];
 #pragma unroll
     for (int t = 0; t < RTW; ++t)
@@ -449,7 +451,7 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
     const size_t plane = (size_t)bh * a.W * a.T * D;
     const uint32_t plane_bytes = (uint32_t)((size_t)a.W * a.T * D * 2);
     const Rsrc rk = make_rsrc(a.ring_k + plane, plane_bytes);
-    const Rsrc rv = make_rsrc(a.ring_vt + plane, plane_bytes);
+    const Rsrc rv = make_rsrc(a.ring_vg + plane, plane_bytes);
     const int T = a.T, W = a.W, head = a.head;
 
     // ---- subtile list: 2^lsh subtiles per kept block, minus the empty tail of a short last
@@ -479,15 +481,18 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
     };
 
     // ---- per-lane load plan; this wave issues K instructions w*KW .. and V instructions w*VW ..
-    // Both stages are row-major with chunk positions swizzled per row: K row r (key r of the
-    // subtile) holds D/8 chunks, V^T row f (feature f) the subtile's 4 eight-key chunks.
-    // One instruction fetches RPI whole K rows, or 16 whole V^T row segments.
+    // The K stage is row-major with chunk positions swizzled per row (K row r = key r of the
+    // subtile, D/8 chunks); one instruction fetches RPI whole K rows.  The V stage holds the
+    // subtile's four 8-key groups as they lie in the ring ([group][D][8], 16 D bytes each,
+    // the 16-byte row of feature f at position vslot(f)); one instruction fetches 1 KB of a
+    // group, whole cache lines.  In the ring the rows of key j and the group of keys j .. j+7
+    // (j a multiple of 8) both start at byte (slot T + t) D 2, t = j's token in its frame.
     // Subtiles start at multiples of 32 keys and T is a multiple of 8, so a frame boundary
-    // inside a subtile falls on a multiple of 8 keys and never inside a K instruction's rows:
-    // the K frame choice is a scalar offset.  A V^T instruction spans all 32 keys, so a
-    // subtile that crosses a frame boundary takes a per-lane path.
-    uint32_t kvo[KW], vvo[VW];
-    int krow[KW], vkr[VW];
+    // inside a subtile falls on a multiple of 8 keys, never inside an instruction's rows or
+    // group: every frame choice is a scalar offset.
+    constexpr int VIG = D / 64;           // V instructions per 8-key group
+    uint32_t kvo[KW];
+    int krow[KW];
 #pragma unroll
     for (int jj = 0; jj < KW; ++jj) {
         const int j = w * KW + jj;
@@ -496,17 +501,15 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
         krow[jj] = r;
         kvo[jj] = (uint32_t)((lane / LPR) * D * 2 + c * 16);      // within the instruction's rows
     }
-#pragma unroll
-    for (int jj = 0; jj < VW; ++jj) {
-        const int f = 16 * (w * VW + jj) + (lane >> 2);
-        const int c = (lane & 3) ^ swz_v(f);
-        vkr[jj] = 8 * c;
-        vvo[jj] = (uint32_t)(f * T * 2 + c * 16);
-    }
+    // LDS position 64 h + lane of a group holds feature vslot(64 h + lane) (an involution
+    // that leaves bits 5 and up alone)
+    const uint32_t vlo = (uint32_t)(vslot(lane) * 16);
     // Frame geometry of a full subtile (T >= 32): its keys lie in frame f0 from token t0 on
-    // and, from key `split` (a multiple of 8) on, in frame f0 + 1.  Wave-uniform scalars.
+    // and, from key `split` (a multiple of 8) on, in frame f0 + 1.  Wave-uniform scalars:
+    // kb0 + 2 D i is the byte offset of the subtile's key i (and of its group) if i < split,
+    // kb1 + 2 D i otherwise.
     struct Geo {
-        uint32_t kb0, kb1, vb0, vb1;
+        uint32_t kb0, kb1;
         int split;
     };
     auto geo_of = [&](int k0) -> Geo {
@@ -514,8 +517,7 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
         const int t0 = k0 - f0 * T;
         const int split = T - t0;
         const int s0 = slot_of(f0), s1 = slot_of(f0 + 1);
-        return Geo{(uint32_t)((s0 * T + t0) * D * 2), (uint32_t)((s1 * T - split) * D * 2),
-                   (uint32_t)(s0 * D * T * 2 + t0 * 2), (uint32_t)(s1 * D * T * 2 - split * 2), split};
+        return Geo{(uint32_t)((s0 * T + t0) * D * 2), (uint32_t)((s1 * T - split) * D * 2), split};
     };
     auto dma_full_k = [&](const Geo &ge, int st) {
 #pragma unroll
@@ -526,15 +528,11 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
         }
     };
     auto dma_full_v = [&](const Geo &ge, int st) {
-        if (ge.split >= kSub) {
 #pragma unroll
-            for (int jj = 0; jj < VW; ++jj)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LdsPtr)(vst + st * VBYTES + (w * VW + jj) * 1024), 16, (int)vvo[jj],
-                                                         (int)ge.vb0, 0, 0);
-        } else {
-#pragma unroll
-            for (int jj = 0; jj < VW; ++jj)
-                dma16(rv, vst + st * VBYTES + (w * VW + jj) * 1024, (vkr[jj] < ge.split ? ge.vb0 : ge.vb1) + vvo[jj]);
+        for (int jj = 0; jj < VW; ++jj) {
+            const int j = w * VW + jj;
+            const uint32_t so = (8 * (j / VIG) < ge.split ? ge.kb0 : ge.kb1) + (uint32_t)(j * 1024);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LdsPtr)(vst + st * VBYTES + j * 1024), 16, (int)vlo, (int)so, 0, 0);
         }
     };
     // General plan (short subtiles, any T): rows past the valid keys re-read the last one.
@@ -549,10 +547,11 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
         }
 #pragma unroll
         for (int jj = 0; jj < VW; ++jj) {
-            const int j = k0 + min(vkr[jj], (nv - 1) & ~7);
+            const int jv = w * VW + jj;
+            const int j = k0 + min(8 * (jv / VIG), (nv - 1) & ~7);
             const int f = fast_div(j, magicT, T);
-            const uint32_t off = (uint32_t)(slot_of(f) * D * T * 2 + (j - f * T) * 2) + (vvo[jj] - (uint32_t)(vkr[jj] * 2));
-            dma16(rv, vst + st * VBYTES + (w * VW + jj) * 1024, off);
+            const uint32_t off = (uint32_t)((slot_of(f) * T + (j - f * T)) * D * 2 + (jv % VIG) * 1024) + vlo;
+            dma16(rv, vst + st * VBYTES + jv * 1024, off);
         }
     };
 
@@ -564,9 +563,11 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
     uint32_t koff[D / 16];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) koff[ks] = (uint32_t)(rk_row * D * 2 + (((2 * ks + g) ^ rk_swz) << 4));
+    // V fragment of product ks: the lane's 8 keys are group 2 g + ks (the key order the
+    // probabilities leave the QK product in), feature row 32 ft + rk_row
     uint32_t voff[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) voff[ks] = (uint32_t)(rk_row * 64 + (((2 * g + ks) ^ swz_v(rk_row)) << 4));
+    for (int ks = 0; ks < 2; ++ks) voff[ks] = (uint32_t)((2 * g + ks) * D * 16 + vslot(rk_row) * 16);
     auto qk_from = [&](const unsigned char *kb) -> f32x16 {
         u32x4 kfr[D / 16];
 #pragma unroll
@@ -585,7 +586,7 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
         for (int ft = 0; ft < D / 32; ++ft)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                vfr[ft][ks] = *reinterpret_cast<const u32x4 *>(vb + ft * 2048 + voff[ks]);
+                vfr[ft][ks] = *reinterpret_cast<const u32x4 *>(vb + ft * 512 + voff[ks]);
 #pragma unroll
         for (int ft = 0; ft < D / 32; ++ft)
 #pragma unroll

@@ -87,9 +87,13 @@ typedef struct {
 
 /* KV cache as a ring of W frame slots (the windowed KV cache with eviction of
  * [HF-de] §1 / [HF-pt] §1).
- *   k_dev   bf16 [B][H][W][T][D]  key frames, row-major (D contiguous)
- *   vt_dev  bf16 [B][H][W][D][T]  value frames stored TRANSPOSED per frame (T contiguous),
- *                                 the layout the matrix cores read them in
+ *   k_dev   bf16 [B][H][W][T][D]       key frames, row-major (D contiguous)
+ *   vg_dev  bf16 [B][H][W][T/8][D][8]  value frames in 8-token GROUPS: for each group of 8
+ *                                      consecutive tokens of a frame, D rows of the 8
+ *                                      tokens' values (value feature f of token 8g + j at
+ *                                      [g][f][j]); a 16-byte row is the 8-key slice of one
+ *                                      feature that the matrix cores take as an operand, and
+ *                                      the keys of a group are one contiguous 16*D bytes
  *   head         slot holding the oldest frame of the window, 0 <= head < W
  *   n_committed  frames already committed to the window, 0 <= n_committed <= W - C
  * Logical window frame f (0 = oldest) lives in slot (head + f) % W.  A step's window
@@ -100,7 +104,7 @@ typedef struct {
  * across frame boundaries; a short last block is allowed. */
 typedef struct {
     void *k_dev;
-    void *vt_dev;
+    void *vg_dev;
     int32_t head;
     int32_t n_committed;
 } hf_kv_ring;
@@ -132,14 +136,14 @@ const char *hf_last_error(void);
 hf_status hf_workspace_size(const hf_dims *d, int32_t top_k, size_t *bytes);
 
 /* Describe an empty ring over caller-owned storage (host only, no GPU work): checks the
- * dims, then sets *out = {k_store_dev, vt_store_dev, head 0, n_committed 0}.  The storage
+ * dims, then sets *out = {k_store_dev, vg_store_dev, head 0, n_committed 0}.  The storage
  * must hold B*H*W*T*D bf16 values each (layouts above); its contents are not read until
  * frames are committed.  Errors: those of the dims, HF_ERR_NULL for a NULL pointer. */
-hf_status hf_ring_init(const hf_dims *d, void *k_store_dev, void *vt_store_dev, hf_kv_ring *out);
+hf_status hf_ring_init(const hf_dims *d, void *k_store_dev, void *vg_store_dev, hf_kv_ring *out);
 
 /* Copy the current chunk into the ring: k_cur_dev, v_cur_dev are bf16 [B][H][C*T][D]
  * (row-major).  Frame c of the chunk goes to logical frame n_committed + c; values are
- * written transposed (see hf_kv_ring).  The descriptor is not changed. */
+ * written in 8-token groups (see hf_kv_ring).  The descriptor is not changed. */
 hf_status hf_ring_append(const hf_dims *d, const hf_kv_ring *ring, const void *k_cur_dev,
                          const void *v_cur_dev, hipStream_t stream);
 

@@ -34,7 +34,7 @@ def fill_ring(ring: hf.Ring, k_bits: np.ndarray, v_bits: np.ndarray, n_frames: i
     for f in range(n_frames):
         s = (head + f) % g.W
         ring.k[:, :, s] = k[:, :, f]
-        ring.vt[:, :, s] = v[:, :, f].transpose(-1, -2)
+        ring.vg[:, :, s] = hf.Ring.grouped(v[:, :, f])
     torch.cuda.synchronize()
 
 

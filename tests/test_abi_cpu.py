@@ -249,7 +249,7 @@ def test_ring_init():
     g = geom()
     r = _lib.KVRing(None, None, 5, 2)
     assert L.hf_ring_init(ctypes.byref(g.dims()), FAKE, FAKE + 64, ctypes.byref(r)) == 0
-    assert (r.k_dev, r.vt_dev, r.head, r.n_committed) == (FAKE, FAKE + 64, 0, 0)
+    assert (r.k_dev, r.vg_dev, r.head, r.n_committed) == (FAKE, FAKE + 64, 0, 0)
     assert L.hf_ring_init(ctypes.byref(g.dims()), None, FAKE, ctypes.byref(r)) == 1
     assert L.hf_ring_init(ctypes.byref(g.dims()), FAKE, FAKE, None) == 1
     assert L.hf_ring_init(ctypes.byref(geom(D=96).dims()), FAKE, FAKE, ctypes.byref(r)) == 3

@@ -33,11 +33,11 @@ class Layer:
         self.idx = torch.empty((g.B, g.H, g.n_qb, self.top_k), dtype=torch.int32, device="cuda")
         self.out = torch.empty((g.B, g.H, g.Nq, g.D), dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
-        self.saved = [t.clone() for t in (self.ring.k, self.ring.vt, self.S, self.z)]
+        self.saved = [t.clone() for t in (self.ring.k, self.ring.vg, self.S, self.z)]
         self.desc = (self.ring.head, self.ring.n_committed)
 
     def restore(self):
-        for dst, src in zip((self.ring.k, self.ring.vt, self.S, self.z), self.saved):
+        for dst, src in zip((self.ring.k, self.ring.vg, self.S, self.z), self.saved):
             dst.copy_(src)
         self.out.fill_(float("nan"))
         self.idx.fill_(-1)
@@ -48,7 +48,7 @@ class Layer:
                           self.idx, self.out, ws)
 
     def snapshot(self):
-        return [t.clone() for t in (self.out, self.idx, self.S, self.z, self.ring.k, self.ring.vt)]
+        return [t.clone() for t in (self.out, self.idx, self.S, self.z, self.ring.k, self.ring.vg)]
 
 
 @pytest.mark.parametrize("geom", [hf.Geometry(B=2, H=2, D=128, T=96, C=2, W=5, bq=64, bk=32),

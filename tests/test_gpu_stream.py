@@ -76,7 +76,10 @@ def test_ring_append_layout():
     V = dev_bf16(v).view(g.B, g.H, g.C, g.T, g.D)
     for c, slot in enumerate((0, 1)):
         assert torch.equal(ring.k[:, :, slot], K[:, :, c])
-        assert torch.equal(ring.vt[:, :, slot], V[:, :, c].transpose(-1, -2))
+        # value feature f of token 8 gi + j at [gi][f][j]
+        Vc = V[:, :, c]
+        assert torch.equal(ring.vg[:, :, slot], torch.stack([Vc[:, :, 8 * gi:8 * gi + 8].transpose(-1, -2)
+                                                             for gi in range(g.T // 8)], dim=2))
     assert torch.count_nonzero(ring.k[:, :, 2:]) == 0
 
 

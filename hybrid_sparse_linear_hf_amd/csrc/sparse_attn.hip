@@ -722,8 +722,22 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[ft][i] *= inv_l;
     if (a.st) {
-        // B operand phi(q) / (phi(q) . z + eps) in the Q^T fragment layout, so that the
-        // readout accumulates straight onto the normalised sparse output
+        // S^T (bf16, row r = output feature r) is staged once per workgroup in the LDS the
+        // K/V stages used, its rows laid out and swizzled like K rows, while the readout's
+        // B operand phi(q) / (phi(q) . z + eps) is formed in the Q^T fragment layout (the
+        // readout then accumulates straight onto the normalised sparse output)
+        lds_barrier();              // every wave is done with the stages
+        {
+            const Rsrc rs = make_rsrc(a.st + (size_t)bh * D * D, (uint32_t)(D * D * 2));
+#pragma unroll
+            for (int ft = 0; ft < D / 32; ++ft)
+#pragma unroll
+                for (int jj = 0; jj < KW; ++jj) {
+                    const int j = w * KW + jj;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LdsPtr)(dyn + ft * KBYTES + j * 1024), 16, (int)kvo[jj],
+                                                             (32 * ft + RPI * j) * D * 2, 0, 0);
+                }
+        }
         const float *zp = a.zc + (size_t)bh * D + 8 * g;
         float den = 0.f;
 #pragma unroll
@@ -749,13 +763,16 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
                 o[e] = pack_bf16x2(phi_f32(bf16_lo_to_f32(wv[e])) * inv_den, phi_f32(bf16_hi_to_f32(wv[e])) * inv_den);
             pq[ks] = u32x4{o[0], o[1], o[2], o[3]};
         }
-        const uint16_t *stp = a.st + (size_t)bh * D * D + 8 * g;
+        wait_vm<0>();
+        lds_barrier();
 #pragma unroll
         for (int ft = 0; ft < D / 32; ++ft) {
-            const uint16_t *srow = stp + (size_t)(32 * ft + perm32(n)) * D;
+            // row 32 ft + perm32(n), features 16 ks + 8 g .. + 7 (the K-row read pattern)
+            u32x4 sf[D / 16];
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
-                acc[ft] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(srow + 16 * ks)), as_bf16x8(pq[ks]), acc[ft]);
+            for (int ks = 0; ks < D / 16; ++ks) sf[ks] = *reinterpret_cast<const u32x4 *>(dyn + ft * KBYTES + koff[ks]);
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) acc[ft] = mfma32(as_bf16x8(sf[ks]), as_bf16x8(pq[ks]), acc[ft]);
         }
     }
     const int row = q0 + 32 * w + n;

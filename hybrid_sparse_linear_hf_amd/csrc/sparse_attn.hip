@@ -379,7 +379,8 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
     constexpr int KW = NK / NW, VW = NV / NW;
     constexpr int KBYTES = kSub * D * 2, VBYTES = D * 64;
 
-    // dynamic LDS: [K stage 0][K stage 1][V stage 0][V stage 1][kept list][NW flags]
+    // dynamic LDS: [K stage 0][K stage 1][V stage 0][V stage 1][V stage 2] (40 KB at D = 128,
+    // so that four workgroups share a CU's 160 KB)
     extern __shared__ __align__(16) unsigned char dyn[];
     // the absorb role's workgroups come first (a multiple of 8 of them, so that the
     // attention's workgroup-to-XCD remap below is unchanged)
@@ -394,14 +395,13 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
     const int q0 = qb * a.bq, qend = min(q0 + a.bq, a.Nq);
-    unsigned char *const kst = dyn, *const vst = dyn + 2 * KBYTES;
-    int32_t *s_blist = reinterpret_cast<int32_t *>(dyn + 2 * (KBYTES + VBYTES));
-    int *s_flag = reinterpret_cast<int *>(s_blist + a.top_k);
+    unsigned char *const kst = dyn, *const vst = dyn + 2 * KBYTES;   // 2 K stages, 3 V stages
 
     // kept blocks -> LDS (out-of-range entries, a caller error, are clamped so that no load
     // leaves the window)
-    const int32_t *sel = a.idx + ((size_t)bh * a.nqb + qb) * a.top_k;
-    for (int t = threadIdx.x; t < a.top_k; t += 64 * NW) s_blist[t] = min(max(sel[t], 0), a.nkb - 1);
+    typedef const __attribute__((address_space(4))) int32_t *KeptPtr;
+    const KeptPtr sel = (KeptPtr)(a.idx + ((size_t)bh * a.nqb + qb) * a.top_k);
+    auto kept = [&](int t) -> int { return min(max(sel[t], 0), a.nkb - 1); };
 
     // this wave's Q^T B fragments: query q0 + 32w + n (clamped into the block), features
     // 16ks + 8g .. + 8
@@ -413,7 +413,6 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const u32x4 *>(qp + 16 * ks);
     }
-    __syncthreads();
 
     // rotation: this lane's query frame (window order) and the KT temporal fragments of Q^T
     // turned for key frame qt_f
@@ -460,7 +459,7 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
     int nsubt = a.top_k << lsh;
     int nfull = (a.bk >= kSub && T >= kSub) ? nsubt : 0;
     {
-        const int lastb = s_blist[a.top_k - 1];
+        const int lastb = kept(a.top_k - 1);
         if (lastb == a.nkb - 1 && a.bk >= kSub) {
             const int len = a.Nk - lastb * a.bk;
             nsubt -= nsub_blk - (len + kSub - 1) / kSub;
@@ -468,7 +467,7 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
         }
     }
     auto key0_of = [&](int u) -> int {
-        const int b = __builtin_amdgcn_readfirstlane(s_blist[u >> lsh]);
+        const int b = kept(u >> lsh);
         return b * a.bk + ((u & (nsub_blk - 1)) << 5);
     };
     auto nval_of = [&](int k0) -> int {
@@ -642,47 +641,67 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
     int ustart = 0;            // first subtile of the online loop
     if (nfull > 0) {
         // ---- fast path over the full subtiles, software-pipelined: step u computes
-        // S_{u+1} = K_{u+1} Q^T while the softmax of S_u runs, then O += V_u P_u.  K runs one
-        // subtile ahead of V, so K_{u+2} and V_{u+1} are fetched during step u into the K / V
-        // stages that step u-1 finished with (the barrier closing each step orders this).
+        // S_{u+1} = K_{u+1} Q^T while the softmax of S_u runs, then O += V_u P_u.  K streams
+        // through two stages and V through three, so K_{u+2} and V_{u+2} are fetched during
+        // step u into the stages that step u-1 finished with (the barrier closing each step
+        // orders this): every K fetch has a step to land, every V fetch two.
         // Past the last subtile the fetches repeat it and the extra product is discarded.
         const int last = nfull - 1;
         const Geo g0 = geo_of(key0_of(0));
-        Geo g1 = geo_of(key0_of(min(1, last)));
+        const Geo g1 = geo_of(key0_of(min(1, last)));
         dma_full_k(g0, 0);
         dma_full_v(g0, 0);
         dma_full_k(g1, 1);
-        stage_ready();
+        dma_full_v(g1, 1);
+        wait_vm<0>();
+        lds_barrier();
         f32x16 s_a, s_b;
         if constexpr (ROPE) s_a = qk_rope(kst, key0_of(0), kSub);
         else s_a = qk_tile(0);
         sm.m = tile_max_log2(s_a, c_log2);
         const float moff = -sm.m;
-        __syncthreads();            // K stage 0 is refilled in step 0
-        // one step with stage parity P (compile-time): S_u in s_cur, S_{u+1} -> s_nxt
-        auto step = [&](int u, auto par, const f32x16 &s_cur, f32x16 &s_nxt) {
-            constexpr int P = decltype(par)::value;
+        lds_barrier();              // K stage 0 is refilled in step 0
+        // step u: fetch K_{u+2} into K stage u % 2, then V_{u+2} into V stage (u+2) % 3 (V_{u-1}'s);
+        // QK of u+1 from K stage (u+1) % 2, softmax of u, PV of u from V stage u % 3; close by
+        // waiting for all but the V_{u+2} loads
+        auto step = [&](int u, auto kp, auto vp, auto vf, const f32x16 &s_cur, f32x16 &s_nxt) {
+            constexpr int KP = decltype(kp)::value, VP = decltype(vp)::value, VF = decltype(vf)::value;
             const Geo g2 = geo_of(key0_of(min(u + 2, last)));
-            dma_full_k(g2, P);
-            dma_full_v(g1, 1 - P);
-            g1 = g2;
-            if constexpr (ROPE) s_nxt = qk_rope(kst + (1 - P) * KBYTES, key0_of(min(u + 1, last)), kSub);
-            else s_nxt = qk_from(kst + (1 - P) * KBYTES);
+            dma_full_k(g2, KP);
+            dma_full_v(g2, VF);
+            if constexpr (ROPE) s_nxt = qk_rope(kst + (1 - KP) * KBYTES, key0_of(min(u + 1, last)), kSub);
+            else s_nxt = qk_from(kst + (1 - KP) * KBYTES);
             u32x4 pf[2];
             softmax_fixed(s_cur, c_log2, moff, sm.l, pf);
-            pv_from(vst + P * VBYTES, pf);
-            stage_ready();
+            pv_from(vst + VP * VBYTES, pf);
+            wait_vm<VW>();
+            lds_barrier();
         };
+        using C0 = std::integral_constant<int, 0>;
+        using C1 = std::integral_constant<int, 1>;
+        using C2 = std::integral_constant<int, 2>;
         int u = 0;
-        for (; u + 1 < nfull; u += 2) {
-            step(u, std::integral_constant<int, 0>{}, s_a, s_b);
-            step(u + 1, std::integral_constant<int, 1>{}, s_b, s_a);
+        for (; u + 5 < nfull; u += 6) {
+            step(u, C0{}, C0{}, C2{}, s_a, s_b);
+            step(u + 1, C1{}, C1{}, C0{}, s_b, s_a);
+            step(u + 2, C0{}, C2{}, C1{}, s_a, s_b);
+            step(u + 3, C1{}, C0{}, C2{}, s_b, s_a);
+            step(u + 4, C0{}, C1{}, C0{}, s_a, s_b);
+            step(u + 5, C1{}, C2{}, C1{}, s_b, s_a);
         }
-        if (u < nfull) step(u, std::integral_constant<int, 0>{}, s_a, s_b);
+        const int rem = nfull - u;
+        if (rem > 0) step(u, C0{}, C0{}, C2{}, s_a, s_b);
+        if (rem > 1) step(u + 1, C1{}, C1{}, C0{}, s_b, s_a);
+        if (rem > 2) step(u + 2, C0{}, C2{}, C1{}, s_a, s_b);
+        if (rem > 3) step(u + 3, C1{}, C0{}, C2{}, s_b, s_a);
+        if (rem > 4) step(u + 4, C0{}, C1{}, C0{}, s_a, s_b);
+        wait_vm<0>();
+        lds_barrier();
         // a score far above its reference (row sum >= 2^32): recompute the block online
+        int *const s_flag = reinterpret_cast<int *>(vst + 2 * VBYTES);
         const int bad = __builtin_amdgcn_ballot_w64(!(sm.l < kFixedRefLimit)) != 0;
         if (lane == 0) s_flag[w] = bad;
-        __syncthreads();
+        lds_barrier();
         int any_bad = 0;
 #pragma unroll
         for (int i = 0; i < NW; ++i) any_bad |= s_flag[i];
@@ -805,9 +824,8 @@ hipError_t hf_launch_sparse_attn(const hf_attn_args &a_in, hipStream_t s) {
     const uint32_t magicT = hf::div_magic((uint32_t)a.T);
     const float c_log2 = (float)(1.4426950408889634 / sqrt((double)a.D));
     const int lsh = a.bk >= 128 ? 2 : (a.bk >= 64 ? 1 : 0);     // 32-key subtiles per key block = 2^lsh
-    size_t dyn = 2 * (size_t)128 * a.D + (size_t)a.top_k * sizeof(int32_t) + nw * sizeof(int);   // 2 K + 2 V stages
-    // a step's absorb role streams through kAbStages stages (at most the attention's stages:
-    // 8, 6 or 4 KB each)
+    const size_t dyn = 5 * (size_t)64 * a.D;     // 2 K stages + 3 V stages
+    // a step's absorb role streams through kAbStages stages within the attention's LDS
     static_assert(hf::kAbStages * hf::AbShape<128, 2>::SB <= 2 * 128 * 128, "absorb LDS, D=128");
     static_assert(hf::kAbStages * hf::AbShape<128, 1>::SB <= 2 * 128 * 128, "absorb LDS, D=128, one wave");
     static_assert(hf::kAbStages * hf::AbShape<64, 2>::SB <= 2 * 128 * 64, "absorb LDS, D=64");

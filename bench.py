@@ -35,7 +35,7 @@ ROOT = Path(__file__).resolve().parent
 ATTN_SOURCES = [ROOT / "hybrid_sparse_linear_hf_amd" / "csrc" / n for n in ("sparse_attn.hip", "hf_internal.h")]
 ATTN_PMC_SUMMARY = ROOT / "profiles" / "hybrid_step_832x480_layer_hbm_traffic.md"
 METRIC = "hybrid-attn chunk step ms + TFLOP/s on kept blocks (832x480 shape, 1 GPU)"
-EVENT_STRIDE = 10              # timed steps per step that records the phase events
+PHASE_STEPS = 20               # untimed steps after the timed region that record the phase events
 
 
 class HipEvents:
@@ -276,17 +276,16 @@ def main():
     idx_warm = torch.empty_like(idx_bufs[0])
     out = torch.empty((cfg.B, cfg.H, cfg.Nq, cfg.D), dtype=torch.float32, device=dev)
     hip = HipEvents()
-    # Phase events are recorded on a subset of the timed steps only (every EVENT_STRIDE-th,
-    # and on at least 5 steps): each recorded event costs several microseconds of GPU
-    # timeline, which would otherwise inflate the step time being measured.
-    stride = max(1, min(EVENT_STRIDE, args.steps // 5))
-    event_slots = list(range(0, args.steps, stride))
-    evs = {s: [hip.create() for _ in range(6)] for s in event_slots}
+    # The timed steps record no events: each recorded event costs several microseconds of
+    # GPU timeline.  The phase events come from PHASE_STEPS further steps of the same stream
+    # after the timed region.
+    evs = [[hip.create() for _ in range(6)] for _ in range(PHASE_STEPS)]
+    idx_ph = [torch.empty_like(idx_warm) for _ in range(PHASE_STEPS)]
 
-    def step(i, timed_slot=None, flags=hf.HF_STEP_COMMIT):
+    def step(i, timed_slot=None, flags=hf.HF_STEP_COMMIT, events=None, idx=None):
         q, k, v = chunks[i % len(chunks)]
-        idx = idx_bufs[timed_slot] if timed_slot is not None else idx_warm
-        events = evs.get(timed_slot) if timed_slot is not None else None
+        if idx is None:
+            idx = idx_bufs[timed_slot] if timed_slot is not None else idx_warm
         if rope is None:
             hf.hf_hybrid_step(g, q, k, v, ring, top_k, flags, S, z, idx, out, ws, events=events)
         else:
@@ -327,11 +326,16 @@ def main():
     t_attn_c = float(np.median(ab_attn)) * 1e-3
     t_attn_nc = float(np.median(nc_attn)) * 1e-3
     t_state_ab = float(np.median(ab_state)) * 1e-3
+    # phase events: further steps of the stream
+    for p in range(PHASE_STEPS):
+        step(n_total + p, events=evs[p], idx=idx_ph[p])
+    torch.cuda.synchronize()
+    n_total += PHASE_STEPS
 
     # [steps, 5] ms: (empty) | select (its pool launch also appends the chunk to the ring and prepares
     # the readout operands) | (empty) | attention + readout (+ the absorb partials) | state pass
-    phases = np.array([[hip.elapsed_ms(e[p], e[p + 1]) for p in range(5)] for e in evs.values()])
-    step_ms = np.array([hip.elapsed_ms(e[0], e[5]) for e in evs.values()])
+    phases = np.array([[hip.elapsed_ms(e[p], e[p + 1]) for p in range(5)] for e in evs])
+    step_ms = np.array([hip.elapsed_ms(e[0], e[5]) for e in evs])
     if args.calib_copy:
         # plain copy kernel of known size: reads and writes 256 MiB each
         src = torch.randn(64 << 20, device=dev)
@@ -343,7 +347,7 @@ def main():
     # hot-cache attention: the last step's queries and kept lists again on the ring as it is
     # now (same shapes and access pattern; operands resident in L2 / MALL), with the readout
     q_last = chunks[(n_total - 1) % len(chunks)][0]
-    idx_last = idx_bufs[args.steps - 1]
+    idx_last = idx_ph[-1]
     attn_hot = []
     for rep in range(23):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -358,6 +362,7 @@ def main():
     t_attn_hot = float(np.median([a.elapsed_time(b) for a, b in attn_hot[3:]])) * 1e-3
     peaks = measured_peaks(torch, dev)
     flops = np.array([kept_flops(b.cpu().numpy(), cfg.Nq, cfg.Nk, cfg.bq, cfg.bk, cfg.D) for b in idx_bufs])
+    flops_ph = np.array([kept_flops(b.cpu().numpy(), cfg.Nq, cfg.Nk, cfg.bq, cfg.bk, cfg.D) for b in idx_ph])
     ms_step = wall * 1e3 / args.steps
     value = flops.sum() / wall / 1e12
     t_sel = phases[:, 1].mean() * 1e-3
@@ -365,7 +370,7 @@ def main():
     t_attn = phases[:, 3].mean() * 1e-3
     t_state = phases[:, 4].mean() * 1e-3   # the state pass adding the absorb partials
     t_abs = max(t_attn_c - t_attn_nc, 0.0) + t_state_ab   # what the absorb adds to a step
-    attn_tflops = flops.mean() / t_attn / 1e12
+    attn_tflops = flops_ph.mean() / t_attn / 1e12
     traffic, traffic_src = pmc_traffic(ATTN_PMC_SUMMARY, ATTN_SOURCES)
     BH, T, D = cfg.B * cfg.H, cfg.T, cfg.D
     absorb_bytes = BH * (cfg.C * T * D * 2 * 2 + 2 * (D * D + D) * 4)
@@ -397,7 +402,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "traffic_source": traffic_src,
                      "kernel": f"sparse_attn_kernel<128, 2, {rope.temporal_dims // 16 if rope else 0}>",
-                     "flops_per_launch": round(flops.mean()), "launch_us": round(t_attn * 1e6, 2),
+                     "flops_per_launch": round(flops_ph.mean()), "launch_us": round(t_attn * 1e6, 2),
                      "frac_of_measured_gemm": round(attn_tflops / peaks["bf16_gemm_tflops"], 4),
                      "hot_cache_launch_us": round(t_attn_hot * 1e6, 2),
                      "hot_cache_note": "the last step's attention repeated on resident operands; includes the "

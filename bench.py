@@ -371,7 +371,10 @@ def main():
     t_state = phases[:, 4].mean() * 1e-3   # the state pass adding the absorb partials
     t_abs = max(t_attn_c - t_attn_nc, 0.0) + t_state_ab   # what the absorb adds to a step
     attn_tflops = flops_ph.mean() / t_attn / 1e12
-    traffic, traffic_src = pmc_traffic(ATTN_PMC_SUMMARY, ATTN_SOURCES)
+    if rope is None:
+        traffic, traffic_src = pmc_traffic(ATTN_PMC_SUMMARY, ATTN_SOURCES)
+    else:
+        traffic, traffic_src = None, "the counter summary covers the unrotated kernel instance only"
     BH, T, D = cfg.B * cfg.H, cfg.T, cfg.D
     absorb_bytes = BH * (cfg.C * T * D * 2 * 2 + 2 * (D * D + D) * 4)
     append_bytes = BH * cfg.C * T * D * 2 * 2 * 2

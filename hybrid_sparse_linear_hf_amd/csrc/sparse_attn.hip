@@ -664,16 +664,20 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
         // step u: fetch K_{u+2} into K stage u % 2, then V_{u+2} into V stage (u+2) % 3 (V_{u-1}'s);
         // QK of u+1 from K stage (u+1) % 2, softmax of u, PV of u from V stage u % 3; close by
         // waiting for all but the V_{u+2} loads
-        auto step = [&](int u, auto kp, auto vp, auto vf, const f32x16 &s_cur, f32x16 &s_nxt) {
-            constexpr int KP = decltype(kp)::value, VP = decltype(vp)::value, VF = decltype(vf)::value;
+        // step u with K parity KP = u % 2 (compile-time) and V stages vp = u % 3, vf =
+        // (u + 2) % 3: compile-time too (loop unrolled by six) where the registers allow
+        // it, else wave-uniform runtime values (unrolled by two)
+        auto step = [&](int u, auto kp, auto vpc, auto vfc, const f32x16 &s_cur, f32x16 &s_nxt) {
+            constexpr int KP = decltype(kp)::value;
+            const int vp = vpc, vf = vfc;
             const Geo g2 = geo_of(key0_of(min(u + 2, last)));
             dma_full_k(g2, KP);
-            dma_full_v(g2, VF);
+            dma_full_v(g2, vf);
             if constexpr (ROPE) s_nxt = qk_rope(kst + (1 - KP) * KBYTES, key0_of(min(u + 1, last)), kSub);
             else s_nxt = qk_from(kst + (1 - KP) * KBYTES);
             u32x4 pf[2];
             softmax_fixed(s_cur, c_log2, moff, sm.l, pf);
-            pv_from(vst + VP * VBYTES, pf);
+            pv_from(vst + vp * VBYTES, pf);
             wait_vm<VW>();
             lds_barrier();
         };
@@ -681,20 +685,34 @@ sparse_attn_kernel(hf_attn_args a, uint32_t magicT, float c_log2, int per_xcd, i
         using C1 = std::integral_constant<int, 1>;
         using C2 = std::integral_constant<int, 2>;
         int u = 0;
-        for (; u + 5 < nfull; u += 6) {
-            step(u, C0{}, C0{}, C2{}, s_a, s_b);
-            step(u + 1, C1{}, C1{}, C0{}, s_b, s_a);
-            step(u + 2, C0{}, C2{}, C1{}, s_a, s_b);
-            step(u + 3, C1{}, C0{}, C2{}, s_b, s_a);
-            step(u + 4, C0{}, C1{}, C0{}, s_a, s_b);
-            step(u + 5, C1{}, C2{}, C1{}, s_b, s_a);
+        if constexpr (!ROPE && NW == 2) {
+            for (; u + 5 < nfull; u += 6) {
+                step(u, C0{}, C0{}, C2{}, s_a, s_b);
+                step(u + 1, C1{}, C1{}, C0{}, s_b, s_a);
+                step(u + 2, C0{}, C2{}, C1{}, s_a, s_b);
+                step(u + 3, C1{}, C0{}, C2{}, s_b, s_a);
+                step(u + 4, C0{}, C1{}, C0{}, s_a, s_b);
+                step(u + 5, C1{}, C2{}, C1{}, s_b, s_a);
+            }
+            const int rem = nfull - u;
+            if (rem > 0) step(u, C0{}, C0{}, C2{}, s_a, s_b);
+            if (rem > 1) step(u + 1, C1{}, C1{}, C0{}, s_b, s_a);
+            if (rem > 2) step(u + 2, C0{}, C2{}, C1{}, s_a, s_b);
+            if (rem > 3) step(u + 3, C1{}, C0{}, C2{}, s_b, s_a);
+            if (rem > 4) step(u + 4, C0{}, C1{}, C0{}, s_a, s_b);
+        } else {
+            auto next3 = [](int x) { return x == 2 ? 0 : x + 1; };
+            int vp = 0, vf = 2;
+            for (; u + 1 < nfull; u += 2) {
+                step(u, C0{}, vp, vf, s_a, s_b);
+                vp = next3(vp);
+                vf = next3(vf);
+                step(u + 1, C1{}, vp, vf, s_b, s_a);
+                vp = next3(vp);
+                vf = next3(vf);
+            }
+            if (u < nfull) step(u, C0{}, vp, vf, s_a, s_b);
         }
-        const int rem = nfull - u;
-        if (rem > 0) step(u, C0{}, C0{}, C2{}, s_a, s_b);
-        if (rem > 1) step(u + 1, C1{}, C1{}, C0{}, s_b, s_a);
-        if (rem > 2) step(u + 2, C0{}, C2{}, C1{}, s_a, s_b);
-        if (rem > 3) step(u + 3, C1{}, C0{}, C2{}, s_b, s_a);
-        if (rem > 4) step(u + 4, C0{}, C1{}, C0{}, s_a, s_b);
         wait_vm<0>();
         lds_barrier();
         // a score far above its reference (row sum >= 2^32): recompute the block online

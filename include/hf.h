@@ -147,8 +147,8 @@ hf_status hf_ring_init(const hf_dims *d, void *k_store_dev, void *vg_store_dev, 
 hf_status hf_ring_append(const hf_dims *d, const hf_kv_ring *ring, const void *k_cur_dev,
                          const void *v_cur_dev, hipStream_t stream);
 
-/* Block selection ([HF-de] §2.A "nur die wichtigsten Blöcke (Top-K)", [HF-pt] §2.A.2
- * "blocos mais ativos"; pooling as [LF-de] §2.2 token compression).
+/* Block selection ([HF-de] §2.A, item "Block-Sparse Sliding Window Attention"; [HF-pt]
+ * §2.A.2; pooling as in [LF-de] §2.2, item "Token-Kompression").
  * For each (b, h, query block i): qbar_i = mean of Q over block i, kbar_j = mean of the
  * window keys over key block j, score s_ij = qbar_i . kbar_j / sqrt(D) (pooled and
  * scored in fp64); keep the top_k largest, ties to the lower j, written in ASCENDING

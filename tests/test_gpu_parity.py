@@ -242,3 +242,25 @@ def test_absorb_parity(n_tok):
         np.testing.assert_array_equal(zg, z0)
     assert np.abs(Sg - So).max() <= 1e-4 * max(1.0, np.abs(So).max())
     assert np.abs(zg - zo).max() <= 1e-5 * max(1.0, np.abs(zo).max())
+
+
+@pytest.mark.parametrize("D,bq", [(128, 64), (64, 64), (128, 32)])
+@pytest.mark.parametrize("top_k", [1, 2, 3, 4, 5, 6, 7, 8, 11])
+def test_fast_path_step_counts(D, bq, top_k):
+    """32-key blocks, every one full, so a query block walks exactly top_k fast-path steps:
+    covers the step loop's body (six steps at a time where it is unrolled by six) and
+    every remainder, for the unrolled (two waves, no rotation) and the two-step (one
+    wave) instances."""
+    B, H, T, C, W, bk, ncom = 1, 2, 96, 1, 4, 32, 3
+    print(f"case: fast path D={D} bq={bq} top_k={top_k}", flush=True)
+    g = hf.Geometry(B, H, D, T, C, W, bq, bk)
+    rng = np.random.default_rng(500 + 10 * top_k + D + bq)
+    b = synth.bf16_bits_from_f32
+    mk = lambda n: b(rng.standard_normal((B, H, n, D)).astype(np.float32))
+    nfr = ncom + C
+    inp = StepInputs(mk(C * T), mk(nfr * T), mk(nfr * T), mk(T), mk(T))
+    idx, sc, out, S, z = run_select_attn(g, inp, ncom, top_k, head=2)
+    So, zo = oracle.absorb(inp.Kev, inp.Vev)
+    ref, idx_o, sc_o = oracle.hybrid_step(inp.Q, inp.K, inp.V, So, zo, bq, bk, top_k, want_scores=True)
+    np.testing.assert_array_equal(idx, idx_o)
+    assert_close(out, ref, f"fast path D={D} bq={bq} top_k={top_k}")

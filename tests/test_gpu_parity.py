@@ -97,7 +97,8 @@ def sample_blocks(BH, nqb, stride=9):
 
 
 def test_layer_832x480_parity():
-    """12 heads x 128, 4680 queries, 9360-key window, 64x64 blocks, 37 of 147 kept, state of 18 frames."""
+    """12 heads x 128, 4680 queries, 9360-key window, 64x64 blocks, 37 of 147 kept, state of 18
+    frames: every score, kept list and output row."""
     print("case: 832x480 layer (H=12, D=128, T=1560, C=3, W=6, top-37)", flush=True)
     cfg = synth.LAYER_832x480
     g = geometry(cfg)
@@ -107,16 +108,11 @@ def test_layer_832x480_parity():
     So, zo = oracle.absorb(inp.Kev, inp.Vev)
     assert np.linalg.norm(S - So) / np.linalg.norm(So) < 2e-3
     assert np.linalg.norm(z - zo) / np.linalg.norm(zo) < 2e-3
-    blocks = sample_blocks(cfg.B * cfg.H, cfg.n_qb)
-    ref, idx_o, sc_o = oracle.hybrid_step(inp.Q, inp.K, inp.V, So, zo, cfg.bq, cfg.bk, k, blocks=blocks,
-                                          want_scores=True)
+    ref, idx_o, sc_o = oracle.hybrid_step(inp.Q, inp.K, inp.V, So, zo, cfg.bq, cfg.bk, k, want_scores=True)
     np.testing.assert_array_equal(sc, sc_o)
     np.testing.assert_array_equal(idx, idx_o)
-    rows = rows_of_blocks(blocks, cfg.Nq, cfg.bq, (cfg.B * cfg.H, cfg.Nq))
-    o = out.reshape(-1, cfg.Nq, cfg.D)[rows]
-    r = ref.reshape(-1, cfg.Nq, cfg.D)[rows]
-    mx, mr = assert_close(o, r, "832x480 layer")
-    print(f"832x480: {len(blocks)} blocks checked, max-abs {mx:.2e} mean-rel {mr:.2e}")
+    mx, mr = assert_close(out, ref, "832x480 layer")
+    print(f"832x480: every row, max-abs {mx:.2e} mean-rel {mr:.2e}")
 
 
 
@@ -144,31 +140,29 @@ def test_window21_keep_sweep(keep):
     print(f"W=21 top-{k}: {len(blocks)} blocks checked, max-abs {mx:.2e} mean-rel {mr:.2e}")
 
 
+@pytest.mark.timeout(900)
 def test_four_streams_per_layer_seeds():
-    """Four independent streams batched (B=4) at 832x480 shapes on heads 3 and 11, for layers
-    0 and 29 of a stack (each layer seeds its own Q/K/V and state); sampled query blocks."""
+    """Four independent streams batched (B=4) at 832x480 shapes on all 12 heads, for layers
+    0, 15 and 29 of a stack (each layer seeds its own Q/K/V and state): every block's
+    scores and kept list, every output row, and the absorbed state."""
     base = synth.LAYER_832x480
     cfg = synth.StepConfig("832x480_4streams", B=4, H=base.H, D=base.D, T=base.T, C=base.C, W=base.W,
                            bq=base.bq, bk=base.bk, keep=base.keep, n_evicted=base.n_evicted)
-    heads = [3, 11]
+    heads = list(range(cfg.H))
     k = cfg.top_k()
     g = hf.Geometry(cfg.B, len(heads), cfg.D, cfg.T, cfg.C, cfg.W, cfg.bq, cfg.bk)
-    for layer in (0, 29):
-        print(f"case: 4 streams, layer {layer}, heads {heads}, top-{k}", flush=True)
+    for layer in (0, 15, 29):
+        print(f"case: 4 streams, layer {layer}, all heads, top-{k}", flush=True)
         d = synth.field_step_inputs(cfg, layer=layer, heads=heads)
         inp = StepInputs(d["q"], d["k_win"], d["v_win"], d["k_ev"], d["v_ev"])
         idx, sc, out, S, z = run_select_attn(g, inp, cfg.W - cfg.C, k, head=layer % cfg.W)
         So, zo = oracle.absorb(inp.Kev, inp.Vev)
         assert np.linalg.norm(S - So) / np.linalg.norm(So) < 2e-3
-        blocks = sample_blocks(cfg.B * len(heads), cfg.n_qb, stride=23)
-        ref, idx_o, sc_o = oracle.hybrid_step(inp.Q, inp.K, inp.V, So, zo, cfg.bq, cfg.bk, k, blocks=blocks,
-                                              want_scores=True)
+        ref, idx_o, sc_o = oracle.hybrid_step(inp.Q, inp.K, inp.V, So, zo, cfg.bq, cfg.bk, k, want_scores=True)
         np.testing.assert_array_equal(sc, sc_o)
         np.testing.assert_array_equal(idx, idx_o)
-        rows = rows_of_blocks(blocks, cfg.Nq, cfg.bq, (cfg.B * len(heads), cfg.Nq))
-        mx, mr = assert_close(out.reshape(-1, cfg.Nq, cfg.D)[rows], ref.reshape(-1, cfg.Nq, cfg.D)[rows],
-                              f"layer {layer}")
-        print(f"layer {layer}: {len(blocks)} blocks checked, max-abs {mx:.2e} mean-rel {mr:.2e}")
+        mx, mr = assert_close(out, ref, f"layer {layer}")
+        print(f"layer {layer}: every row, max-abs {mx:.2e} mean-rel {mr:.2e}", flush=True)
 
 EDGE = [
     # B, H, D, T, C, W, bq, bk, n_committed, top_k

@@ -191,15 +191,16 @@ def main():
                     help="after timing, run a plain 256 MiB elementwise copy (for counter calibration)")
     ap.add_argument("--keep", type=float, default=None, help="override the kept fraction of key blocks")
     ap.add_argument("--window", type=int, default=None, help="override the window length in frames")
-    ap.add_argument("--mode", choices=("step", "hier", "cag", "bwd", "stack", "sweep"), default="step",
+    ap.add_argument("--mode", choices=("step", "hier", "cag", "bwd", "stack", "sweep", "horizon"), default="step",
                     help="step: the hybrid step (default); hier: hierarchical selection + attention on a 21-frame "
                          "window; cag: a stream from an empty window under the chunk-aware keep schedule; "
                          "bwd: training forward (with lse) and backward of the attention + readout; stack: a "
                          "30-layer x 4-stream chunk captured in a HIP graph; sweep: keep ratios on a 21-frame window "
-                         "against dense")
+                         "against dense; horizon: 200 consecutive committed steps timed one by one")
     ap.add_argument("--top-frames", type=int, default=6, help="hier: frames kept per query block")
     ap.add_argument("--top-k", type=int, default=128, help="hier: key blocks kept per query block")
     ap.add_argument("--stream", type=int, default=16, help="cag: chunks in the stream")
+    ap.add_argument("--horizon", type=int, default=200, help="horizon: committed steps in the stream")
     ap.add_argument("--layers", type=int, default=30, help="stack: layers in the stack")
     ap.add_argument("--rope", type=str, default=None, metavar="DT,CAP",
                     help="step: time the step with the relative temporal rotary embedding (rotated features DT, "
@@ -229,6 +230,8 @@ def main():
         return bench_stack(args)
     if args.mode == "sweep":
         return bench_sweep(args)
+    if args.mode == "horizon":
+        return bench_horizon(args)
     cfg = synth.LAYER_832x480
     rope = None
     if args.rope:
@@ -769,6 +772,147 @@ def bench_stack(args):
            "wall_ms_per_chunk": round(wall * 1e3 / args.steps, 3),
            "note": "attention only (no projections, MLP or VAE); not comparable with end-to-end generation rates"}
     print(json.dumps(res), flush=True)
+
+def _frames_par(synth, tensor_id, f0, n, cfg, heads):
+    """synth.field_frames of several heads drawn on a thread pool (one head per task)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(min(16, len(heads))) as ex:
+        parts = ex.map(lambda h: synth.field_frames(tensor_id, f0, n, B=cfg.B, D=cfg.D, gh=cfg.gh, gw=cfg.gw,
+                                                    heads=[h]), heads)
+        return np.concatenate(list(parts), axis=1)
+
+
+def bench_horizon(args):
+    """The long-horizon stream at the 832x480 layer shapes: from a state of 18 absorbed frames
+    and 3 committed window frames, `--horizon` consecutive hf_hybrid_step calls with commit,
+    each appending a 3-frame chunk and absorbing the 3 frames it evicts into the fp32 state
+    (S 12x128x128, z 12x128).  The stream runs twice from the same start: once timed by the
+    wall clock alone, once with an event between consecutive steps for the per-step times.
+    The chunks (distinct seeded field frames) rotate through the stream, all resident in
+    device memory before the first step."""
+    import torch
+    import hybrid_sparse_linear_hf_amd as hf
+    from hybrid_sparse_linear_hf_amd import synth
+
+    cfg = synth.LAYER_832x480
+    dev = torch.device("cuda:0")
+    g = hf.Geometry(cfg.B, cfg.H, cfg.D, cfg.T, cfg.C, cfg.W, cfg.bq, cfg.bk)
+    heads = list(range(cfg.H))
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def frames(tid, f0, n):
+        return to_dev(_frames_par(synth, tid, f0, n, cfg, heads))
+
+    ev, hist, n = cfg.n_evicted, cfg.W - cfg.C, args.horizon
+    k_ev, v_ev, k_hist, v_hist = frames(synth.K_ID, 0, ev), frames(synth.V_ID, 0, ev), \
+        frames(synth.K_ID, ev, hist), frames(synth.V_ID, ev, hist)
+    first = ev + hist
+    chunks = [tuple(frames(t, first + cfg.C * c, cfg.C) for t in (synth.Q_ID, synth.K_ID, synth.V_ID))
+              for c in range(args.chunks)]
+    ring, ws = hf.Ring(g), hf.new_workspace(g)
+    S = torch.zeros((cfg.B, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dev)
+    z = torch.zeros_like(S[..., 0])
+    top_k = cfg.top_k()
+    idx = [torch.empty((cfg.B, cfg.H, g.n_qb, top_k), dtype=torch.int32, device=dev) for _ in range(n)]
+    out = torch.empty((cfg.B, cfg.H, cfg.Nq, cfg.D), dtype=torch.float32, device=dev)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+
+    def start():
+        S.zero_()
+        z.zero_()
+        hf.hf_linear_absorb(g, k_ev, v_ev, ev * cfg.T, S, z, ws)
+        ring.set_state(0, 0)
+        hf.hf_ring_append(g, ring, k_hist, v_hist)
+        ring.set_state(0, hist)
+        torch.cuda.synchronize()
+
+    def stream(events):
+        for s in range(n):
+            q, k, v = chunks[s % len(chunks)]
+            if events:
+                marks[s].record()
+            hf.hf_hybrid_step(g, q, k, v, ring, top_k, hf.HF_STEP_COMMIT, S, z, idx[s], out, ws)
+        if events:
+            marks[n].record()
+
+    start()               # warm-up pass (code objects, caches)
+    stream(False)
+    start()
+    t0 = time.perf_counter()
+    stream(False)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    state_norm = float(torch.linalg.vector_norm(S).item())
+    start()
+    stream(True)
+    torch.cuda.synchronize()
+    per = np.array([marks[s].elapsed_time(marks[s + 1]) for s in range(n)])
+    fl = np.array([kept_flops(i.cpu().numpy(), cfg.Nq, cfg.Nk, cfg.bq, cfg.bk, cfg.D) for i in idx])
+    ms = wall * 1e3 / n
+    q10 = max(1, n // 10)
+    slope = float(np.polyfit(np.arange(n), per, 1)[0]) * 1e3 if n > 1 else 0.0
+    res = {"metric": f"long-horizon stream: ms per committed chunk step over {n} steps (832x480 shape, 1 GPU)",
+           "value": round(ms, 4), "unit": "ms per step", "n_gpus": 1, "steps": n, "warmup": n,
+           "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic (seeded rank-8 spatial field + noise per head, bf16)",
+           "config": {"workload": cfg.name + f"_horizon{n}", "B": cfg.B, "H": cfg.H, "D": cfg.D,
+                      "tokens_per_frame": cfg.T, "chunk_frames": cfg.C, "window_frames": cfg.W,
+                      "block": [cfg.bq, cfg.bk], "top_k": top_k, "state_frames_at_start": ev,
+                      "state_frames_at_end": ev + cfg.C * n, "rotating_chunks": args.chunks},
+           "kept_tflops": round(fl.sum() / wall / 1e12, 2),
+           "per_step_ms": {"median": round(float(np.median(per)), 4), "p90": round(float(np.percentile(per, 90)), 4),
+                           "max": round(float(per.max()), 4), "min": round(float(per.min()), 4),
+                           f"first_{q10}_mean": round(float(per[:q10].mean()), 4),
+                           f"last_{q10}_mean": round(float(per[-q10:].mean()), 4),
+                           "slope_us_per_step": round(slope, 4)},
+           "per_step_note": "HIP events between consecutive steps of a second pass from the same start (each "
+                            "event adds a few microseconds); value is the wall clock of the pass without events",
+           "final_state_fro_norm": round(state_norm, 3),
+           "cpu_baseline": None}
+    if args.cpu_heads > 0:
+        res["cpu_baseline"] = cpu_baseline_horizon(cfg, min(args.cpu_heads, cfg.H), args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_horizon(cfg, sample_heads, seconds):
+    """The fp64 oracle (test infrastructure) running the same stream on a bounded sample: the
+    first consecutive steps on `sample_heads` heads (the window of frames, select + sparse
+    attention + readout, then the 3 evicted frames absorbed into the state), until `seconds`
+    of wall time have passed.  Drawing the frames is not timed."""
+    import oracle
+    from hybrid_sparse_linear_hf_amd import synth
+
+    heads = list(range(sample_heads))
+    f64 = synth.f64_from_bf16_bits
+    T, C, ev, hist = cfg.T, cfg.C, cfg.n_evicted, cfg.W - cfg.C
+    S, z = oracle.absorb(f64(_frames_par(synth, synth.K_ID, 0, ev, cfg, heads)),
+                         f64(_frames_par(synth, synth.V_ID, 0, ev, cfg, heads)))
+    win_k = f64(_frames_par(synth, synth.K_ID, ev, hist, cfg, heads))
+    win_v = f64(_frames_par(synth, synth.V_ID, ev, hist, cfg, heads))
+    k = cfg.top_k()
+    steps, busy = [], 0.0
+    f = ev + hist
+    while busy < seconds:
+        q, kc, vc = (f64(_frames_par(synth, t, f, C, cfg, heads)) for t in (synth.Q_ID, synth.K_ID, synth.V_ID))
+        t0 = time.perf_counter()
+        K = np.concatenate([win_k, kc], axis=2)
+        V = np.concatenate([win_v, vc], axis=2)
+        oracle.hybrid_step(q, K, V, S, z, cfg.bq, cfg.bk, k)
+        S, z = oracle.absorb(K[:, :, :C * T], V[:, :, :C * T], S, z)   # the oldest C frames leave the window
+        win_k, win_v = K[:, :, C * T:], V[:, :, C * T:]
+        dt = time.perf_counter() - t0
+        steps.append(dt)
+        busy += dt
+        f += C
+    per = float(np.median(steps)) * 1e3
+    return {"value": round(per, 1), "unit": "ms per step", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the first {len(steps)} consecutive committed steps of the stream on {sample_heads} of "
+                      f"{cfg.H} heads (fp64), {busy:.1f} s of oracle time",
+            "cpu_model": cpu_model(), "per_step_ms": [round(x * 1e3, 1) for x in steps],
+            "ms_per_step_all_heads_est": round(per * cfg.H / sample_heads, 1)}
 
 
 def bench_cag(args):

@@ -83,6 +83,48 @@ def test_ring_append_layout():
     assert torch.count_nonzero(ring.k[:, :, 2:]) == 0
 
 
+@pytest.mark.parametrize("g,head,ncom", [
+    # frames of 200 tokens (a ragged 8-token tail of 64-token tiles), the chunk wrapping round
+    # the ring; D = 64; a 1560-token frame at the layer shapes
+    (hf.Geometry(B=1, H=2, D=128, T=200, C=2, W=5, bq=64, bk=64), 4, 3),
+    (hf.Geometry(B=2, H=1, D=64, T=136, C=1, W=4, bq=32, bk=32), 1, 2),
+    (hf.Geometry(B=1, H=2, D=128, T=1560, C=3, W=6, bq=64, bk=64), 5, 3),
+])
+def test_step_appends_chunk_to_ring(g, head, ncom):
+    """A committed hf_hybrid_step leaves the chunk in its ring slots bit for bit (keys as
+    rows, values in 8-token groups; written by extra workgroups of the selection's score
+    launch, while its pool launch reads the chunk's keys from the input); the other slots
+    keep their contents."""
+    print(f"case: step append, D={g.D} T={g.T} C={g.C} W={g.W} head={head} ncom={ncom}", flush=True)
+    rng = np.random.default_rng(14)
+    ring = hf.Ring(g)
+    before_k = torch.from_numpy(rng.integers(0, 1 << 14, ring.k.shape, dtype=np.int16)).cuda().view(torch.bfloat16)
+    before_v = torch.from_numpy(rng.integers(0, 1 << 14, ring.vg.shape, dtype=np.int16)).cuda().view(torch.bfloat16)
+    ring.k.copy_(before_k)
+    ring.vg.copy_(before_v)
+    ring.set_state(head, ncom)
+    q, k, v = random_chunks(g, 1, seed=15)[0]
+    top_k = max(1, g.n_kb(ncom) // 4)
+    idx = torch.empty((g.B, g.H, g.n_qb, top_k), dtype=torch.int32, device="cuda")
+    out = torch.empty((g.B, g.H, g.Nq, g.D), dtype=torch.float32, device="cuda")
+    S = torch.zeros((g.B, g.H, g.D, g.D), dtype=torch.float32, device="cuda")
+    z = torch.zeros((g.B, g.H, g.D), dtype=torch.float32, device="cuda")
+    hf.hf_hybrid_step(g, dev_bf16(q), dev_bf16(k), dev_bf16(v), ring, top_k, hf.HF_STEP_COMMIT, S, z, idx, out,
+                      hf.new_workspace(g))
+    torch.cuda.synchronize()
+    K = dev_bf16(k).view(g.B, g.H, g.C, g.T, g.D)
+    V = dev_bf16(v).view(g.B, g.H, g.C, g.T, g.D)
+    slots = [(head + ncom + c) % g.W for c in range(g.C)]
+    for c, slot in enumerate(slots):
+        assert torch.equal(ring.k[:, :, slot], K[:, :, c]), f"keys of chunk frame {c}"
+        Vc = V[:, :, c]
+        want = torch.stack([Vc[:, :, 8 * gi:8 * gi + 8].transpose(-1, -2) for gi in range(g.T // 8)], dim=2)
+        assert torch.equal(ring.vg[:, :, slot], want), f"values of chunk frame {c}"
+    for slot in set(range(g.W)) - set(slots):
+        assert torch.equal(ring.k[:, :, slot], before_k[:, :, slot])
+        assert torch.equal(ring.vg[:, :, slot], before_v[:, :, slot])
+
+
 @pytest.mark.timeout(900)
 def test_long_horizon_832x480_all_heads():
     """The long-horizon stream at the 832x480 layer shapes (12 heads x 128, T=1560, C=3, W=6,

@@ -179,23 +179,38 @@ __global__ __launch_bounds__(256) void prep_queries_kernel(hf_bwd_args a) {
 
 // Per plane, the query blocks that kept each key block, ascending: count (LDS atomics over
 // the kept entries, which are also staged in LDS when they fit), exclusive scan (one wave),
-// then a fill that walks the query blocks in order (a kept list holds distinct blocks, so
-// its entries never collide; entries outside [0, n_kb), a caller error, are skipped).
+// then the fill.  When the plane's (key block, query block) bitmap fits in LDS, every entry
+// finds its own slot: query block i goes to the key block's list at the number of query
+// blocks below i that kept it (a population count of the bitmap row), all entries at once.
+// Otherwise a fill walks the query blocks in order.  A kept list holds distinct blocks, so
+// entries never collide; entries outside [0, n_kb), a caller error, are skipped.
 constexpr int kCsrStaged = 8192;   // kept entries of a plane staged in LDS for the fill
+constexpr int kCsrBitWords = 4096; // 64-bit words of the bitmap (n_kb * ceil(n_qb / 64))
 __global__ __launch_bounds__(256) void csr_kernel(hf_bwd_args a) {
     __shared__ int cnt[kMaxKeyBlocks];
     __shared__ int pos[kMaxKeyBlocks];
     __shared__ int32_t sel_s[kCsrStaged];
+    __shared__ unsigned long long bits[kCsrBitWords];
     const int bh = blockIdx.x, tid = threadIdx.x;
     const int total = a.nqb * a.top_k;
     const bool staged = total <= kCsrStaged;          // uniform
+    const int words = (a.nqb + 63) / 64;              // bitmap words per key block
+    const bool by_rank = a.nkb * words <= kCsrBitWords;   // uniform
     const int32_t *sel = a.idx + (size_t)bh * total;
     for (int j = tid; j < a.nkb; j += 256) cnt[j] = 0;
+    if (by_rank)
+        for (int e = tid; e < a.nkb * words; e += 256) bits[e] = 0ull;
     __syncthreads();
     for (int e = tid; e < total; e += 256) {
         const int j = sel[e];
         if (staged) sel_s[e] = j;
-        if (j >= 0 && j < a.nkb) atomicAdd(&cnt[j], 1);
+        if (j >= 0 && j < a.nkb) {
+            atomicAdd(&cnt[j], 1);
+            if (by_rank) {
+                const int i = e / a.top_k;
+                atomicOr(&bits[j * words + (i >> 6)], 1ull << (i & 63));
+            }
+        }
     }
     __syncthreads();
     const int32_t *fsel = staged ? sel_s : sel;        // the fill reads LDS when it can
@@ -220,6 +235,18 @@ __global__ __launch_bounds__(256) void csr_kernel(hf_bwd_args a) {
     }
     __syncthreads();
     int32_t *list = a.qlist + (size_t)bh * a.nqb * a.top_k;
+    if (by_rank) {
+        for (int e = tid; e < total; e += 256) {
+            const int j = fsel[e];
+            if (j < 0 || j >= a.nkb) continue;
+            const int i = e / a.top_k, wi = i >> 6;
+            const unsigned long long *row = &bits[j * words];
+            int rank = __popcll(row[wi] & ((1ull << (i & 63)) - 1ull));
+            for (int q = 0; q < wi; ++q) rank += __popcll(row[q]);
+            list[pos[j] + rank] = i;
+        }
+        return;
+    }
     for (int i = 0; i < a.nqb; ++i) {
         for (int r = tid; r < a.top_k; r += 256) {
             const int j = fsel[(size_t)i * a.top_k + r];
@@ -751,11 +778,36 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
         const int qr = 32 * qt + perm32(n);
         const int qsw = swz_row<D>(qr);
         f32x16 s = {}, dp = {};
+        // the Q and dO fragments of four contraction steps are read in one asm block that
+        // waits for all eight reads at its end (every output is complete when it ends): left
+        // to itself the compiler, short of registers at one wave per SIMD, issues each
+        // step's two reads just before its two products and waits for each pair.  A
+        // stage's dO rows sit kQB * D * 2 bytes after its Q rows.
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            const int cs = ((2 * ks + g) ^ qsw) * 8;
-            s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(Lq + qr * D + cs)), as_bf16x8(kf[ks]), s);
-            dp = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(Lg + qr * D + cs)), as_bf16x8(vf[ks]), dp);
+        for (int k0 = 0; k0 < D / 16; k0 += 4) {
+            uint32_t ad[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                ad[kk] = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t *)(Lq + qr * D + ((2 * (k0 + kk) + g) ^ qsw) * 8);
+            u32x4 fq[4], fg[4];
+            asm volatile(
+                "ds_read_b128 %0, %8\n\t"
+                "ds_read_b128 %4, %8 offset:%12\n\t"
+                "ds_read_b128 %1, %9\n\t"
+                "ds_read_b128 %5, %9 offset:%12\n\t"
+                "ds_read_b128 %2, %10\n\t"
+                "ds_read_b128 %6, %10 offset:%12\n\t"
+                "ds_read_b128 %3, %11\n\t"
+                "ds_read_b128 %7, %11 offset:%12\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(fq[0]), "=&v"(fq[1]), "=&v"(fq[2]), "=&v"(fq[3]), "=&v"(fg[0]), "=&v"(fg[1]), "=&v"(fg[2]), "=&v"(fg[3])
+                : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "i"(kQB * D * 2)
+                : "memory");
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                s = mfma32(as_bf16x8(fq[kk]), as_bf16x8(kf[k0 + kk]), s);
+                dp = mfma32(as_bf16x8(fg[kk]), as_bf16x8(vf[k0 + kk]), dp);
+            }
         }
         // lane (key n) holds queries 32 qt + 16 g + i.  Only query rows past the block's end
         // are masked (they repeat its last query): a key past the end feeds only its own
@@ -792,15 +844,24 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
         // dv^T += dO^T P, dk^T += Q^T G (rows d in perm32 order; this lane half's queries
         // 32 qt + 16 g + 8 ks .. + 8, the order in which P and G are packed).  Rows past the
         // block's end repeat its last query and meet P = G = 0.
+        // all transposed fragments of one operand are read before its products
+        u32x4 xg[NTF][2];
 #pragma unroll
-        for (int fi = 0; fi < NTF; ++fi) {
+        for (int fi = 0; fi < NTF; ++fi)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int q0 = 32 * qt + 16 * g + 8 * ks;
-                accV[fi] = mfma32(as_bf16x8(xt_frag<D, true>(Lg, q0, fi, lane)), as_bf16x8(pf[ks]), accV[fi]);
-                accK[fi] = mfma32(as_bf16x8(xt_frag<D, true>(Lq, q0, fi, lane)), as_bf16x8(gfr[ks]), accK[fi]);
-            }
-        }
+            for (int ks = 0; ks < 2; ++ks) xg[fi][ks] = xt_frag<D, true>(Lg, 32 * qt + 16 * g + 8 * ks, fi, lane);
+#pragma unroll
+        for (int fi = 0; fi < NTF; ++fi)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) accV[fi] = mfma32(as_bf16x8(xg[fi][ks]), as_bf16x8(pf[ks]), accV[fi]);
+#pragma unroll
+        for (int fi = 0; fi < NTF; ++fi)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) xg[fi][ks] = xt_frag<D, true>(Lq, 32 * qt + 16 * g + 8 * ks, fi, lane);
+#pragma unroll
+        for (int fi = 0; fi < NTF; ++fi)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) accK[fi] = mfma32(as_bf16x8(xg[fi][ks]), as_bf16x8(gfr[ks]), accK[fi]);
     };
     int p = p0;
     for (; p + NS <= p1; p += NS) {

@@ -84,6 +84,9 @@ CASES = [
     (1, 1, 128, 104, 1, 5, 16, 128, 1, 1, 3),     # bq=16, bk=128 (last block partial)
     (1, 2, 128, 136, 1, 4, 64, 64, 3, 4, 4),      # odd number of query blocks
     (1, 1, 64, 48, 4, 6, 64, 32, 2, 6, 5),        # D=64, T=48
+    # 200 query blocks x 1400 key blocks: the selection's transpose is too large for its
+    # LDS bitmap and takes the ordered fill
+    (1, 1, 64, 800, 4, 28, 16, 16, 24, 3, 6),
 ]
 
 

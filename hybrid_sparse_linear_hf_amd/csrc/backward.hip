@@ -18,7 +18,8 @@
 //     dS and dz as split partials (phi(q) and dn staged transposed in LDS), added in split
 //     order by a second launch.
 //   * dq pass: one workgroup per query block, one wave per 32-query tile, walking the kept
-//     key blocks in 32-key subtiles staged in LDS: S^T = K Q^T, dP^T = V dO^T,
+//     key blocks in 32-key subtiles staged in LDS (two stages filled by direct-to-LDS
+//     loads, one subtile ahead): S^T = K Q^T, dP^T = V dO^T,
 //     G^T = P^T (dP^T - Delta) and dq^T += K^T G^T (K^T read from the staged K rows by
 //     transposing LDS reads).
 //   * dk/dv pass: one workgroup per key block, one wave per (32-key tile, 32-query tile),
@@ -520,23 +521,57 @@ __global__ __launch_bounds__(256) void reduce_readout_kernel(hf_bwd_args a) {
 
 // ---------------------------------------------------------------- dq pass
 
+constexpr int kBufDword3 = 0x00020000;        // raw buffer resource word 3 (gfx9 family)
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef __attribute__((address_space(3))) void *LdsPtr;
 
-// One workgroup per query block, one wave per 32-query tile.  Each 32-key subtile's K rows
-// (chunk-swizzled) and V rows (padded by 16 bytes) pass through LDS once for all the waves;
-// the next subtile's operands are loaded into registers while the current one is computed.
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufDword3);
+}
+
+// 16 bytes per lane from the buffer into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(Rsrc r, unsigned char *lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 16, (int)voff, 0, 0, 0);
+}
+
+// One workgroup per query block, one wave per 32-query tile, walking the kept key blocks in
+// 32-key subtiles.  Each subtile's K and V rows (both chunk-swizzled, swz_row) reach LDS by
+// direct-to-LDS loads into one of two stages, the next subtile's while the current one is
+// computed.  The loads go through buffer resources bounded by the plane's rows, so rows past
+// the padded window read as zero.
 template <int D>
-struct SubtileLds {
-    uint16_t k[32 * D];           // K rows, chunk-swizzled (swz_row)
-    uint16_t v[32][D + 8];
+struct DqStage {
+    uint16_t k[32 * D];
+    uint16_t v[32 * D];
 };
+
+// Fragments of four contraction steps (k-steps k0 .. k0 + 3) of the rows that lane reads in
+// the S and dP products -- K at the four addresses, V at the same offsets in the V rows --
+// in one asm block that waits for all eight reads at its end (every output is complete when
+// it ends); left to itself the compiler, short of registers, issues each step's reads just
+// before its products and waits for each pair.
+template <int D>
+__device__ __forceinline__ void dq_kv_reads(const uint32_t (&ad)[2], u32x4 (&fk)[2], u32x4 (&fv)[2]) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %2, %4 offset:%6\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %3, %5 offset:%6\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(fk[0]), "=&v"(fk[1]), "=&v"(fv[0]), "=&v"(fv[1])
+        : "v"(ad[0]), "v"(ad[1]), "i"(32 * D * 2)
+        : "memory");
+}
 
 template <int D, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW, 2))) void dq_kernel(hf_bwd_args a, float c_log2, float inv_sqrt_d, int lsh) {
-    constexpr int NTH = 64 * NW;
-    constexpr int CR = 32 * D / 8;           // 16-byte chunks of the K (or V) rows of a subtile
-    constexpr int PR = CR / NTH;
-    static_assert(CR % NTH == 0, "staging split");
-    __shared__ __align__(16) SubtileLds<D> L;
+    constexpr int LPR = D / 8, RPI = 64 / LPR;      // chunks per row, rows per load instruction
+    constexpr int NI = 32 * D * 2 / 1024;           // load instructions per operand and subtile
+    constexpr int PW = NI / NW;                     // ... per wave
+    static_assert(NI % NW == 0, "load split");
+    // one __shared__ object per stage, addressed only with compile-time stage numbers, so
+    // that the compiler tells one stage's direct-to-LDS writes from the other's reads
+    __shared__ __align__(16) DqStage<D> S0, S1;
     const int bh = blockIdx.x / a.nqb, qb = blockIdx.x % a.nqb;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
     const int q0 = qb * a.bq, qend = min(q0 + a.bq, a.Nq);
@@ -550,56 +585,70 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
         gf[ks] = *reinterpret_cast<const u32x4 *>(a.gr + row * D + 16 * ks + 8 * g);
     }
     const float Lq = a.lse[row], Dl = a.delta[(size_t)bh * a.NqP + (valid ? t : q0)];
-    const uint16_t *krp = a.kr + (size_t)bh * a.NkP * D, *vrp = a.vr + (size_t)bh * a.NkP * D;
+    const uint32_t plane_bytes = (uint32_t)((size_t)a.NkP * D * 2);
+    const Rsrc rk = make_rsrc(a.kr + (size_t)bh * a.NkP * D, plane_bytes);
+    const Rsrc rv = make_rsrc(a.vr + (size_t)bh * a.NkP * D, plane_bytes);
     f32x16 acc[D / 32];
 #pragma unroll
     for (int ft = 0; ft < D / 32; ++ft) acc[ft] = f32x16{};
-    const int32_t *sel = a.idx + ((size_t)bh * a.nqb + qb) * a.top_k;
-    // the subtiles: kept block r, 32-key part su while it holds keys
-    int r = 0, su = 0;
-    auto k0_of = [&](int rr, int ss) { return min(max(sel[rr], 0), a.nkb - 1) * a.bk + 32 * ss; };
-    auto advance = [&](int &rr, int &ss) {
-        const int b = min(max(sel[rr], 0), a.nkb - 1);
-        if (ss + 1 < (1 << lsh) && b * a.bk + 32 * (ss + 1) < min(b * a.bk + a.bk, a.Nk)) {
-            ++ss;
-        } else {
-            ++rr;
-            ss = 0;
-        }
-    };
-    u32x4 pk[PR], pv[PR];
-    auto load = [&](int k0) {
+    // the kept list through scalar loads (constant address space: written by an earlier
+    // launch), so that no vector load sits among the counted direct-to-LDS fetches
+    const cint32_p sel = (cint32_p)(a.idx + ((size_t)bh * a.nqb + qb) * a.top_k);
+    auto kept = [&](int e) { return min(max(sel[e], 0), a.nkb - 1); };
+    // subtiles: 2^lsh per kept block, minus the empty tail of a short last block (the list
+    // is ascending, so that block can only be the final entry)
+    const int nsub_blk = 1 << lsh;
+    int nsubt = a.top_k << lsh;
+    {
+        const int lastb = kept(a.top_k - 1);
+        if (lastb == a.nkb - 1 && a.bk >= 32) nsubt -= nsub_blk - (a.Nk - lastb * a.bk + 31) / 32;
+    }
+    auto key0_of = [&](int u) { return kept(u >> lsh) * a.bk + ((u & (nsub_blk - 1)) << 5); };
+    // this wave's load instructions jj: rows RPI j + lane / LPR of the subtile (j = w PW + jj),
+    // LDS slot lane % LPR holding chunk slot ^ swz_row(row)
+    uint32_t lo[PW];
 #pragma unroll
-        for (int e0 = 0; e0 < PR; ++e0) {
-            const int e = threadIdx.x + NTH * e0, rr = e / (D / 8), c8 = (e % (D / 8)) * 8;
-            pk[e0] = *reinterpret_cast<const u32x4 *>(krp + (size_t)(k0 + rr) * D + c8);
-            pv[e0] = *reinterpret_cast<const u32x4 *>(vrp + (size_t)(k0 + rr) * D + c8);
+    for (int jj = 0; jj < PW; ++jj) {
+        const int r = RPI * (w * PW + jj) + lane / LPR;
+        lo[jj] = (uint32_t)((r * D + 8 * ((lane % LPR) ^ swz_row<D>(r))) * 2);
+    }
+    // (the whole offset goes in the per-lane operand, which the buffer's range check covers)
+    auto fetch = [&](int u, DqStage<D> &st) {
+        const uint32_t base = (uint32_t)(key0_of(u) * D * 2);
+#pragma unroll
+        for (int jj = 0; jj < PW; ++jj) {
+            const int j = w * PW + jj;
+            dma16(rk, reinterpret_cast<unsigned char *>(st.k) + j * 1024, base + lo[jj]);
+            dma16(rv, reinterpret_cast<unsigned char *>(st.v) + j * 1024, base + lo[jj]);
         }
     };
-    load(k0_of(0, 0));
-    while (r < a.top_k) {
-        const int k0 = k0_of(r, su);
-        const int b = min(max(sel[r], 0), a.nkb - 1);
+    const int kr = perm32(n), ksw = swz_row<D>(kr);
+    auto step = [&](int u, DqStage<D> &cur, DqStage<D> &nxt) __attribute__((always_inline)) {
+        // this wave's loads of subtile u have landed, then everyone's, and everyone is done
+        // with the other stage, which takes subtile u + 1
+        wait_vm<0>();
+        lds_barrier();
+        if (u + 1 < nsubt) fetch(u + 1, nxt);
+        const int k0 = key0_of(u);
+        const int b = k0 / a.bk;
         const int nv = min(32, min(b * a.bk + a.bk, a.Nk) - k0);
-        __syncthreads();   // everyone is done with the previous subtile
-#pragma unroll
-        for (int e0 = 0; e0 < PR; ++e0) {
-            const int e = threadIdx.x + NTH * e0, rr = e / (D / 8), c8 = (e % (D / 8)) * 8;
-            *reinterpret_cast<u32x4 *>(&L.k[rr * D + (((c8 >> 3) ^ swz_row<D>(rr)) << 3)]) = pk[e0];
-            *reinterpret_cast<u32x4 *>(&L.v[rr][c8]) = pv[e0];
-        }
-        __syncthreads();
-        advance(r, su);
-        if (r < a.top_k) load(k0_of(r, su));
+        // S^T = K Q^T and dP^T = V dO^T: lane holds keys 16 g + i of the subtile for query n
         f32x16 s = {}, dp = {};
-        const int kr = perm32(n);
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.k[kr * D + (((2 * ks + g) ^ swz_row<D>(kr)) << 3)])),
-                       as_bf16x8(qf[ks]), s);
-            dp = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(&L.v[kr][16 * ks + 8 * g])), as_bf16x8(gf[ks]), dp);
+        for (int k0s = 0; k0s < D / 16; k0s += 2) {
+            uint32_t ad[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                ad[kk] = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t *)(
+                    cur.k + kr * D + (((2 * (k0s + kk) + g) ^ ksw) << 3));
+            u32x4 fk[2], fv[2];
+            dq_kv_reads<D>(ad, fk, fv);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                s = mfma32(as_bf16x8(fk[kk]), as_bf16x8(qf[k0s + kk]), s);
+                dp = mfma32(as_bf16x8(fv[kk]), as_bf16x8(gf[k0s + kk]), dp);
+            }
         }
-        // lane holds keys 16 g + i of the subtile for query n
         // (keys past the subtile's valid ones are masked; a full subtile has none)
         float gt[16];
         auto terms = [&](auto masked) __attribute__((always_inline)) {
@@ -617,14 +666,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
         for (int ks = 0; ks < 2; ++ks)
             gfr[ks] = u32x4{pack_bf16x2(gt[8 * ks], gt[8 * ks + 1]), pack_bf16x2(gt[8 * ks + 2], gt[8 * ks + 3]),
                             pack_bf16x2(gt[8 * ks + 4], gt[8 * ks + 5]), pack_bf16x2(gt[8 * ks + 6], gt[8 * ks + 7])};
+        // dq^T += K^T G^T: K^T rows 32 ft + perm32(n), keys 16 g + 8 ks .. + 8
 #pragma unroll
-        for (int ft = 0; ft < D / 32; ++ft) {
+        for (int ft = 0; ft < D / 32; ++ft)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)   // K^T rows 32 ft + perm32(n), keys 16 g + 8 ks .. + 8
-                acc[ft] = mfma32(as_bf16x8(xt_frag<D>(L.k, 16 * g + 8 * ks, ft, lane)), as_bf16x8(gfr[ks]),
-                                 acc[ft]);
-        }
+            for (int ks = 0; ks < 2; ++ks)
+                acc[ft] = mfma32(as_bf16x8(xt_frag<D, true>(cur.k, 16 * g + 8 * ks, ft, lane)), as_bf16x8(gfr[ks]), acc[ft]);
+    };
+    fetch(0, S0);
+    int u = 0;
+    for (; u + 1 < nsubt; u += 2) {
+        step(u, S0, S1);
+        step(u + 1, S1, S0);
     }
+    if (u < nsubt) step(u, S0, S1);
     if (valid) {
         float *dqp = a.dq + row * D + 16 * g;
 #pragma unroll
@@ -641,18 +696,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
 
 // ---------------------------------------------------------------- dk / dv pass
 
-constexpr int kBufDword3 = 0x00020000;        // raw buffer resource word 3 (gfx9 family)
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-typedef __attribute__((address_space(3))) void *LdsPtr;
-
-__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufDword3);
-}
-
-// 16 bytes per lane from the buffer into LDS at lds + 16 * lane.
-__device__ __forceinline__ void dma16(Rsrc r, unsigned char *lds, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 16, (int)voff, 0, 0, 0);
-}
 
 
 // One query block's operands, staged unpadded with swizzled chunks by direct-to-LDS loads:

@@ -321,7 +321,8 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
     const int bh = blockIdx.x / a.splits, sp = blockIdx.x % a.splits;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
     const int nchunks = (a.Nq + kQB - 1) / kQB;
-    const float *zp = a.z + (size_t)bh * D;
+    __shared__ __align__(16) float zp[D];     // z of the plane
+    for (int e = threadIdx.x; e < D; e += 128) zp[e] = a.z[(size_t)bh * D + e];
     {
         const uint16_t *sbg = a.sb + (size_t)bh * D * D;
         for (int e = threadIdx.x; e < D * D / 8; e += 128) {

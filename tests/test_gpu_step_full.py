@@ -143,12 +143,14 @@ FALLBACK = [(64, 32), (64, 64), (128, 32), (128, 64)]
 
 
 @pytest.mark.parametrize("D,bq", FALLBACK)
-def test_attention_online_fallback_on_large_logits(D, bq):
+@pytest.mark.parametrize("dt", [0, 16])
+def test_attention_online_fallback_on_large_logits(D, bq, dt):
     """Kept key blocks whose logits exceed the first subtile's maximum by about 30 (natural
     units) for some queries of every query block: in the 16-key tail of the last key block for
     query block 0, in a full subtile of a middle key block of its own for every other one.  The attention's
     fixed per-row reference then overflows its bound and the block is recomputed with the
-    online softmax; the result must still match the oracle."""
+    online softmax; the result must still match the oracle.  dt = 16: the same through the
+    instances with the relative temporal rotation (16 rotated features, offset cap 1)."""
     T, C, W, ncom, bk = 208, 1, 3, 2, 64        # window 624 keys: 9 full key blocks + 48 (32 + a 16-key tail)
     g = hf.Geometry(1, 2, D, T, C, W, bq, bk)
     Nq, Nk = C * T, (ncom + C) * T
@@ -156,8 +158,11 @@ def test_attention_online_fallback_on_large_logits(D, bq):
     rng = np.random.default_rng(D + bq)
     Q = rng.standard_normal((1, 2, Nq, D)).astype(np.float32)
     K = rng.standard_normal((1, 2, Nk, D)).astype(np.float32)
-    V = rng.standard_normal((1, 2, Nk, D)).astype(np.float32)
-    alpha = 30.0 / np.sqrt(D)          # planted key = alpha * query -> logit ~ 30
+    # values at half scale: the probabilities are bf16 matrix-core operands, so a weight near 1
+    # errs by up to 2^-9 of the value it multiplies, and the unplanted queries of block 0 meet
+    # the planted keys with logits spread by alpha
+    V = 0.5 * rng.standard_normal((1, 2, Nk, D)).astype(np.float32)
+    alpha = (30.0 if dt == 0 else 40.0) / np.sqrt(D)   # planted key = alpha * query -> logit ~ 30 (40)
     idx = np.zeros((1, 2, nqb, 3), dtype=np.int32)
     for i in range(nqb):
         q0, q1 = i * bq, min((i + 1) * bq, Nq)
@@ -172,13 +177,19 @@ def test_attention_online_fallback_on_large_logits(D, bq):
     qb, kb, vb = b(Q), b(K), b(V)
     Qd, Kd, Vd = f64(qb), f64(kb), f64(vb)
     # the inputs do what the test is about: for every query block, some query's best kept key
-    # lies >= 32 base-2 units above its best key of the first 32-key subtile
+    # lies >= 32 base-2 units above its best key of the first 32-key subtile (with the
+    # rotation: bounds from the unrotated features, the rotated pairs' part bounded by the
+    # product of their norms, which a rotation keeps)
+    c = np.log2(np.e) / np.sqrt(D)
     for p in range(2):
         for i in range(nqb):
             q0, q1 = i * bq, min((i + 1) * bq, Nq)
             keys = np.concatenate([np.arange(j * bk, min((j + 1) * bk, Nk)) for j in idx[0, p, i]])
-            lg = Qd[0, p, q0:q1] @ Kd[0, p, keys].T / np.sqrt(D) * np.log2(np.e)
-            assert (lg.max(axis=1) - lg[:, :32].max(axis=1)).max() >= 34.0
+            Qi, Kj = Qd[0, p, q0:q1], Kd[0, p, keys]
+            sp = Qi[:, dt:] @ Kj[:, dt:].T * c
+            tb = np.linalg.norm(Qi[:, :dt], axis=1)[:, None] * np.linalg.norm(Kj[:, :dt], axis=1)[None, :] * c
+            lo, hi = sp - tb, sp + tb
+            assert (lo.max(axis=1) - hi[:, :32].max(axis=1)).max() >= 34.0
     kev, vev = b(rng.standard_normal((1, 2, 300, D)).astype(np.float32)), b(rng.standard_normal((1, 2, 300, D)).astype(np.float32))
     ring = hf.Ring(g)
     fill_ring(ring, kb, vb, ncom + C, head=1)
@@ -188,14 +199,20 @@ def test_attention_online_fallback_on_large_logits(D, bq):
     z = torch.zeros((1, 2, D), dtype=torch.float32, device="cuda")
     hf.hf_linear_absorb(g, dev_bf16(kev), dev_bf16(vev), 300, S, z, ws)
     out = torch.empty((1, 2, Nq, D), dtype=torch.float32, device="cuda")
-    hf.hf_sparse_window_attn(g, dev_bf16(qb), ring, torch.from_numpy(idx).cuda(), 3, S, z, out, ws)
-    torch.cuda.synchronize()
+    idx_d = torch.from_numpy(idx).cuda()
     So, zo = oracle.absorb(f64(kev), f64(vev))
-    ref = oracle.sparse_attn(Qd, Kd, Vd, idx, bq, bk) + oracle.linear_readout(Qd, So, zo, bq)
+    if dt == 0:
+        hf.hf_sparse_window_attn(g, dev_bf16(qb), ring, idx_d, 3, S, z, out, ws)
+        ref = oracle.sparse_attn(Qd, Kd, Vd, idx, bq, bk)
+    else:
+        hf.hf_sparse_window_attn_rope(g, dev_bf16(qb), ring, idx_d, 3, S, z, out, ws, hf.Rope(dt, 1, 10000.0))
+        ref = oracle.sparse_attn_rope(Qd, Kd, Vd, idx, bq, bk, T, dt, 1, 10000.0)
+    torch.cuda.synchronize()
+    ref = ref + oracle.linear_readout(Qd, So, zo, bq)
     o = out.cpu().numpy()
     assert np.isfinite(o).all()
-    mx, mr = assert_close(o, ref, f"large logits D={D} bq={bq}")
-    print(f"large logits D={D} bq={bq}: max-abs {mx:.2e} mean-rel {mr:.2e}")
+    mx, mr = assert_close(o, ref, f"large logits D={D} bq={bq} dt={dt}")
+    print(f"large logits D={D} bq={bq} dt={dt}: max-abs {mx:.2e} mean-rel {mr:.2e}")
 
 
 def test_stream_on_chunk_aware_schedule():

@@ -54,6 +54,7 @@ __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
     constexpr int kVec = D / 8;              // 16-byte vectors per row
     constexpr int kRowsPerPass = 256 / kVec;
     __shared__ double red[kRowsPerPass][D];
+    __shared__ double red_hi[SPLIT ? kRowsPerPass : 1][D];   // the second frame part (hierarchical)
 
     const int per_plane = a.nqb + a.nkb;
     if ((int)blockIdx.x >= a.BH * per_plane) {
@@ -98,24 +99,29 @@ __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
             }
         }
     }
-    if (SPLIT && split) {
-        // the two frame parts of this key block, for the frame pooling (one LDS buffer,
-        // reduced twice)
-        double *pp = a.part + (((size_t)bh * a.nkb + b) * 2) * D;
+    if constexpr (SPLIT) {
+        if (split) {
+            // the two frame parts of this key block, for the frame pooling, reduced together;
+            // the block's sum is their sum (both exact, so it is the exact block sum)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) red[ro][v * 8 + e] = h == 0 ? acc[e] : acc2[e];
-            __syncthreads();
-            if (threadIdx.x < D) {
-                double s = 0.0;
-                for (int k = 0; k < kRowsPerPass; ++k) s += red[k][threadIdx.x];
-                pp[h * D + threadIdx.x] = s;
+            for (int e = 0; e < 8; ++e) {
+                red[ro][v * 8 + e] = acc[e];
+                red_hi[ro][v * 8 + e] = acc2[e];
             }
             __syncthreads();
+            if (threadIdx.x < D) {
+                double s0 = 0.0, s1 = 0.0;
+                for (int k = 0; k < kRowsPerPass; ++k) {
+                    s0 += red[k][threadIdx.x];
+                    s1 += red_hi[k][threadIdx.x];
+                }
+                double *pp = a.part + (((size_t)bh * a.nkb + b) * 2) * D;
+                pp[threadIdx.x] = s0;
+                pp[D + threadIdx.x] = s1;
+                a.kbar[((size_t)bh * a.nkb + b) * D + threadIdx.x] = (s0 + s1) / (double)(r1 - r0);
+            }
+            return;
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += acc2[e];
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[ro][v * 8 + e] = acc[e];

@@ -715,8 +715,13 @@ constexpr int kStagesKV = 4;   // query-block stages: up to three blocks ahead a
 // kStagesKV - 1 blocks ahead of their use; the products that contract over queries read
 // their Q^T / dO^T operands from the same rows with transposing LDS reads.  The two
 // query-tile halves of each key tile are added at the end.
-template <int D, int NKT, int NQT>
-__global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, float c_log2, float inv_sqrt_d) {
+// MODE 0 forms dv and dk together (one wave per SIMD: both accumulator sets and the key
+// tile's K and V fragments).  MODE 1 forms dv only and MODE 2 dk only, each with two
+// query-block stages (one block ahead), so that two workgroups -- two waves per SIMD --
+// share a CU; the pair recomputes S and fetches the Q and dO rows twice, and is still the
+// faster at 64 x 64 blocks.
+template <int D, int NKT, int NQT, int MODE = 0>
+__global__ __launch_bounds__(64 * NKT * NQT) __attribute__((amdgpu_waves_per_eu(MODE ? 2 : 1))) void dkdv_kernel(hf_bwd_args a, float c_log2, float inv_sqrt_d) {
     constexpr int NW = NKT * NQT;
     constexpr int NTF = D / 32;                    // 32-feature tiles of dk, dv
     constexpr int LPR = D / 8, RPI = 64 / LPR;    // chunks per row, rows per load instruction
@@ -726,7 +731,7 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
     // (even waves) or Delta (odd waves) row -- both when the workgroup has one wave
     constexpr int PER = 2 * (NI / NW) + (NW == 1 ? 2 : 1);
     // stages: one fewer when the loads of two blocks ahead would not fit the wait counter
-    constexpr int NS = 2 * PER < 64 ? kStagesKV : kStagesKV - 1;
+    constexpr int NS = MODE != 0 ? 2 : (2 * PER < 64 ? kStagesKV : kStagesKV - 1);
     static_assert(PER * (NS - 2) < 64, "vmcnt range");
     // one __shared__ object per stage, addressed only with compile-time stage numbers: the
     // compiler then tells each stage's direct-to-LDS writes from the reads of the others and
@@ -762,7 +767,7 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             kf[ks] = *reinterpret_cast<const u32x4 *>(a.kr + krow + 16 * ks);
-            vf[ks] = *reinterpret_cast<const u32x4 *>(a.vr + krow + 16 * ks);
+            if constexpr (MODE != 1) vf[ks] = *reinterpret_cast<const u32x4 *>(a.vr + krow + 16 * ks);
         }
     }
     const Rsrc rq = make_rsrc(a.q + (size_t)bh * a.Nq * D, (uint32_t)((size_t)a.Nq * D * 2));
@@ -801,7 +806,7 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
     // a branch makes it fall back to waiting for every load in flight).
     if (p0 < p1) {
         fetch(p0, stage(std::integral_constant<int, 0>{}));
-        fetch(min(p0 + 1, p1 - 1), stage(std::integral_constant<int, 1>{}));
+        if constexpr (NS > 2) fetch(min(p0 + 1, p1 - 1), stage(std::integral_constant<int, 1>{}));
         if constexpr (NS > 3) fetch(min(p0 + 2, p1 - 1), stage(std::integral_constant<int, 2>{}));
     }
     // block p (the ST-th of its group of NS) is in stage ST
@@ -850,7 +855,7 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 s = mfma32(as_bf16x8(fq[kk]), as_bf16x8(kf[k0 + kk]), s);
-                dp = mfma32(as_bf16x8(fg[kk]), as_bf16x8(vf[k0 + kk]), dp);
+                if constexpr (MODE != 1) dp = mfma32(as_bf16x8(fg[kk]), as_bf16x8(vf[k0 + kk]), dp);
             }
         }
         // lane (key n) holds queries 32 qt + 16 g + i.  Only query rows past the block's end
@@ -872,7 +877,7 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
                 float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i2], c_log2, -lv[i2]));
                 if constexpr (decltype(masked)::value) pr = qb0 + i2 < nqv ? pr : 0.f;
                 pv[i2] = pr;
-                gv[i2] = pr * (dp[i2] - dl[i2]);
+                if constexpr (MODE != 1) gv[i2] = pr * (dp[i2] - dl[i2]);
             }
         };
         if (32 * qt + 32 <= nqv) terms(std::false_type{});   // uniform per wave
@@ -882,6 +887,7 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
         for (int ks = 0; ks < 2; ++ks) {
             pf[ks] = u32x4{pack_bf16x2(pv[8 * ks], pv[8 * ks + 1]), pack_bf16x2(pv[8 * ks + 2], pv[8 * ks + 3]),
                            pack_bf16x2(pv[8 * ks + 4], pv[8 * ks + 5]), pack_bf16x2(pv[8 * ks + 6], pv[8 * ks + 7])};
+            if constexpr (MODE != 1)
             gfr[ks] = u32x4{pack_bf16x2(gv[8 * ks], gv[8 * ks + 1]), pack_bf16x2(gv[8 * ks + 2], gv[8 * ks + 3]),
                             pack_bf16x2(gv[8 * ks + 4], gv[8 * ks + 5]), pack_bf16x2(gv[8 * ks + 6], gv[8 * ks + 7])};
         }
@@ -890,6 +896,7 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
         // block's end repeat its last query and meet P = G = 0.
         // all transposed fragments of one operand are read before its products
         u32x4 xg[NTF][2];
+        if constexpr (MODE != 2) {
 #pragma unroll
         for (int fi = 0; fi < NTF; ++fi)
 #pragma unroll
@@ -898,6 +905,8 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
         for (int fi = 0; fi < NTF; ++fi)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) accV[fi] = mfma32(as_bf16x8(xg[fi][ks]), as_bf16x8(pf[ks]), accV[fi]);
+        }
+        if constexpr (MODE != 1) {
 #pragma unroll
         for (int fi = 0; fi < NTF; ++fi)
 #pragma unroll
@@ -906,12 +915,13 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
         for (int fi = 0; fi < NTF; ++fi)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) accK[fi] = mfma32(as_bf16x8(xg[fi][ks]), as_bf16x8(gfr[ks]), accK[fi]);
+        }
     };
     int p = p0;
     for (; p + NS <= p1; p += NS) {
         step(p, std::integral_constant<int, 0>{});
         step(p + 1, std::integral_constant<int, 1>{});
-        step(p + 2, std::integral_constant<int, 2>{});
+        if constexpr (NS > 2) step(p + 2, std::integral_constant<int, 2>{});
         if constexpr (NS > 3) step(p + 3, std::integral_constant<int, 3>{});
     }
     if (p < p1) step(p, std::integral_constant<int, 0>{});
@@ -929,8 +939,8 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
                 for (int fi = 0; fi < NTF; ++fi)
 #pragma unroll
                     for (int i2 = 0; i2 < 16; ++i2) {
-                        red[(0 * (D / 32) + fi) * 16 * 64 + i2 * 64 + lane] = accV[fi][i2];
-                        red[(1 * (D / 32) + fi) * 16 * 64 + i2 * 64 + lane] = accK[fi][i2];
+                        if constexpr (MODE != 2) red[(0 * (D / 32) + fi) * 16 * 64 + i2 * 64 + lane] = accV[fi][i2];
+                        if constexpr (MODE != 1) red[(1 * (D / 32) + fi) * 16 * 64 + i2 * 64 + lane] = accK[fi][i2];
                     }
             }
             __syncthreads();
@@ -939,8 +949,8 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
                 for (int fi = 0; fi < NTF; ++fi)
 #pragma unroll
                     for (int i2 = 0; i2 < 16; ++i2) {
-                        accV[fi][i2] += red[(0 * (D / 32) + fi) * 16 * 64 + i2 * 64 + lane];
-                        accK[fi][i2] += red[(1 * (D / 32) + fi) * 16 * 64 + i2 * 64 + lane];
+                        if constexpr (MODE != 2) accV[fi][i2] += red[(0 * (D / 32) + fi) * 16 * 64 + i2 * 64 + lane];
+                        if constexpr (MODE != 1) accK[fi][i2] += red[(1 * (D / 32) + fi) * 16 * 64 + i2 * 64 + lane];
                     }
             }
         }
@@ -954,8 +964,10 @@ __global__ __launch_bounds__(64 * NKT * NQT) void dkdv_kernel(hf_bwd_args a, flo
         for (int fi = 0; fi < NTF; ++fi) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
+                if constexpr (MODE != 2)
                 *reinterpret_cast<f32x4 *>(dvp + 32 * fi + 4 * v) =
                     f32x4{accV[fi][4 * v], accV[fi][4 * v + 1], accV[fi][4 * v + 2], accV[fi][4 * v + 3]};
+                if constexpr (MODE != 1)
                 *reinterpret_cast<f32x4 *>(dkp + 32 * fi + 4 * v) =
                     f32x4{accK[fi][4 * v] * inv_sqrt_d, accK[fi][4 * v + 1] * inv_sqrt_d,
                           accK[fi][4 * v + 2] * inv_sqrt_d, accK[fi][4 * v + 3] * inv_sqrt_d};
@@ -1044,13 +1056,13 @@ hipError_t launch_attn_backward(const hf_bwd_args &a, hipStream_t s) {
     else
         hipLaunchKernelGGL((dq_kernel<D, 1>), dim3((unsigned)(a.BH * a.nqb)), dim3(64), 0, s, a, c_log2, inv_sqrt_d, lsh);
     const dim3 gk((unsigned)((a.BH * a.nkb + 7) / 8 * 8));
-    // key tiles (bk / 32, at least 1) x query tiles (bq / 32, at least 1) waves; with 64 x 64
-    // blocks at D = 128 each of those is split over two waves by feature half (two waves per
-    // SIMD; their S and dP products repeat)
+    // key tiles (bk / 32, at least 1) x query tiles (bq / 32, at least 1) waves; 64 x 64
+    // blocks take the dv and dk launches apart
     if (a.bq > 32) {
         if (a.bk > 64) hipLaunchKernelGGL((dkdv_kernel<D, 4, 2>), gk, dim3(512), 0, s, a, c_log2, inv_sqrt_d);
         else if (a.bk > 32) {
-            hipLaunchKernelGGL((dkdv_kernel<D, 2, 2>), gk, dim3(256), 0, s, a, c_log2, inv_sqrt_d);
+            hipLaunchKernelGGL((dkdv_kernel<D, 2, 2, 1>), gk, dim3(256), 0, s, a, c_log2, inv_sqrt_d);
+            hipLaunchKernelGGL((dkdv_kernel<D, 2, 2, 2>), gk, dim3(256), 0, s, a, c_log2, inv_sqrt_d);
         } else hipLaunchKernelGGL((dkdv_kernel<D, 1, 2>), gk, dim3(128), 0, s, a, c_log2, inv_sqrt_d);
     } else {
         if (a.bk > 64) hipLaunchKernelGGL((dkdv_kernel<D, 4, 1>), gk, dim3(256), 0, s, a, c_log2, inv_sqrt_d);

@@ -13,18 +13,19 @@
 // gfx950 design.  A prep launch copies the window into logical order in bf16 -- K rows and
 // V rows -- and dO into bf16 rows, so that the passes below never touch the ring's frame
 // arithmetic.
-//   * readout pass: one workgroup per (plane, split of the queries), S and S^T staged in LDS
-//     once; the products S^T phi(q) and S dn on the matrix cores, per-query terms in fp32;
+//   * readout pass: one workgroup per (plane, split of the queries), S staged in LDS once;
+//     n = S^T phi(q) on the matrix cores, per-query terms in fp32 (Delta, 1 / den, dden);
 //     dS and dz as split partials (phi(q) and dn staged transposed in LDS), added in split
 //     order by a second launch.
 //   * dq pass: one workgroup per query block, one wave per 32-query tile, walking the kept
 //     key blocks in 32-key subtiles staged in LDS (two stages filled by direct-to-LDS
 //     loads, one subtile ahead): S^T = K Q^T, dP^T = V dO^T,
 //     G^T = P^T (dP^T - Delta) and dq^T += K^T G^T (K^T read from the staged K rows by
-//     transposing LDS reads).
+//     transposing LDS reads); then the readout's term S dn + z dden, times phi'(q), with S
+//     staged in the same LDS, and one store of dq.
 //   * dk/dv pass: one workgroup per key block, one wave per (32-key tile, 32-query tile),
 //     walking the query blocks that kept it (a per-plane transpose of the selection, in
-//     ascending order), their Q and dO rows fetched into LDS three blocks ahead:
+//     ascending order), their Q and dO rows fetched into LDS ahead of their use:
 //     S = Q K^T, dP = dO V^T, G = P (dP - Delta), dv^T += dO^T P, dk^T += Q^T G, the
 //     transposed operands read from the same rows by transposing LDS reads.
 //   Products in bf16 with fp32 accumulation; P and G rounded to bf16 as matrix-core
@@ -396,34 +397,12 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
             dnf[ks] = u32x4{pack_bf16x2(g0.x * inv_den, g0.y * inv_den), pack_bf16x2(g0.z * inv_den, g0.w * inv_den),
                             pack_bf16x2(g1.x * inv_den, g1.y * inv_den), pack_bf16x2(g1.z * inv_den, g1.w * inv_den)};
         }
-        // dphi^T = S dn^T + z dden; dq = dphi * phi'(q) (the first write of dq)
-#pragma unroll
-        for (int ft = 0; ft < NT; ++ft) {
-            f32x16 acc = {};
-            const int sr = 32 * ft + perm32(n);
-            const uint16_t *srow = s_sw + sr * D;
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
-                acc = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(srow + (((2 * ks + g) ^ swz_row<D>(sr)) << 3))),
-                             as_bf16x8(dnf[ks]), acc);
-            if (valid) {
-                const int a0 = 32 * ft + 16 * g;
-                const u32x4 q0 = *reinterpret_cast<const u32x4 *>(a.q + row * D + a0);
-                const u32x4 q1 = *reinterpret_cast<const u32x4 *>(a.q + row * D + a0 + 8);
-                const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-                float *dqp = a.dq + row * D + a0;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    float r[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 4 * v + e;
-                        const float qx = (i & 1) ? bf16_hi_to_f32(qw[i >> 1]) : bf16_lo_to_f32(qw[i >> 1]);
-                        r[e] = (acc[i] + zp[a0 + i] * dden) * phi_prime(qx);
-                    }
-                    *reinterpret_cast<f32x4 *>(dqp + 4 * v) = f32x4{r[0], r[1], r[2], r[3]};
-                }
-            }
+        // the readout's term of dq, (S dn + z dden) * phi'(q), is formed by the dq pass from
+        // these two per-query values
+        if (valid && g == 0) {
+            float *rp = a.rod + ((size_t)bh * a.NqP + t) * 2;
+            rp[0] = inv_den;
+            rp[1] = dden;
         }
         // stage phi(q) and dn transposed (zero for rows past the queries) for the partials
         const int col = 32 * w + n;
@@ -681,17 +660,68 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
         step(u + 1, S1, S0);
     }
     if (u < nsubt) step(u, S0, S1);
-    if (valid) {
-        float *dqp = a.dq + row * D + 16 * g;
+    // the readout's term, (S dn + z dden) * phi'(q) with dn = dO / den (the bf16 dO rows
+    // scaled, rounded to bf16 as the matrix-core operand) and 1 / den, dden from the readout
+    // pass; S (bf16 rows, chunk-swizzled like the K rows) is staged in the stages' LDS,
+    // 64 rows per stage object
+    lds_barrier();             // everyone is done with the last subtile (no load is in flight)
+    {
+        const Rsrc rs = make_rsrc(a.sb + (size_t)bh * D * D, (uint32_t)(D * D * 2));
+        constexpr int NIH = 64 * D * 2 / 1024;      // load instructions per 64 rows
+        static_assert(NIH % NW == 0 && sizeof(DqStage<D>) == 64 * D * 2, "S staging");
 #pragma unroll
-        for (int ft = 0; ft < D / 32; ++ft)
+        for (int h = 0; h < D / 64; ++h) {
+            unsigned char *dst = reinterpret_cast<unsigned char *>(h == 0 ? &S0 : &S1);
+#pragma unroll
+            for (int jj = 0; jj < NIH / NW; ++jj) {
+                const int j = w * (NIH / NW) + jj, r = RPI * j + lane / LPR;
+                dma16(rs, dst + j * 1024, (uint32_t)(((64 * h + r) * D + 8 * ((lane % LPR) ^ swz_row<D>(r))) * 2));
+            }
+        }
+    }
+    const float2 rd = *reinterpret_cast<const float2 *>(a.rod + ((size_t)bh * a.NqP + (valid ? t : q0)) * 2);
+    u32x4 dnf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const uint32_t wv[4] = {gf[ks].x, gf[ks].y, gf[ks].z, gf[ks].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(bf16_lo_to_f32(wv[e]) * rd.x, bf16_hi_to_f32(wv[e]) * rd.x);
+        dnf[ks] = u32x4{o[0], o[1], o[2], o[3]};
+    }
+    wait_vm<0>();
+    lds_barrier();
+#pragma unroll
+    for (int ft = 0; ft < D / 32; ++ft) {
+        // S rows 32 ft + perm32(n), features 16 ks + 8 g .. + 8: lane holds features 32 ft + 16 g + i
+        const int sr = 32 * ft + perm32(n), lr = sr % 64;
+        const unsigned char *sb = reinterpret_cast<const unsigned char *>(sr < 64 ? &S0 : &S1) + lr * D * 2;
+        f32x16 ro = {};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            ro = mfma32(as_bf16x8(*reinterpret_cast<const u32x4 *>(sb + (((2 * ks + g) ^ swz_row<D>(lr)) << 4))),
+                        as_bf16x8(dnf[ks]), ro);
+        if (valid) {
+            const int a0 = 32 * ft + 16 * g;
+            const u32x4 q0v = *reinterpret_cast<const u32x4 *>(a.q + row * D + a0);
+            const u32x4 q1v = *reinterpret_cast<const u32x4 *>(a.q + row * D + a0 + 8);
+            const uint32_t qw[8] = {q0v.x, q0v.y, q0v.z, q0v.w, q1v.x, q1v.y, q1v.z, q1v.w};
+            const float *zr = a.z + (size_t)bh * D + a0;
+            float *dqp = a.dq + row * D + a0;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                f32x4 *p4 = reinterpret_cast<f32x4 *>(dqp + 32 * ft + 4 * v);
-                const f32x4 o = *p4;
-                *p4 = f32x4{o.x + acc[ft][4 * v] * inv_sqrt_d, o.y + acc[ft][4 * v + 1] * inv_sqrt_d,
-                            o.z + acc[ft][4 * v + 2] * inv_sqrt_d, o.w + acc[ft][4 * v + 3] * inv_sqrt_d};
+                const f32x4 z4 = *reinterpret_cast<const f32x4 *>(zr + 4 * v);
+                const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
+                float r[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * v + e;
+                    const float qx = (i & 1) ? bf16_hi_to_f32(qw[i >> 1]) : bf16_lo_to_f32(qw[i >> 1]);
+                    r[e] = acc[ft][i] * inv_sqrt_d + (ro[i] + zz[e] * rd.y) * phi_prime(qx);
+                }
+                *reinterpret_cast<f32x4 *>(dqp + 4 * v) = f32x4{r[0], r[1], r[2], r[3]};
             }
+        }
     }
 }
 
@@ -1108,7 +1138,7 @@ static size_t bwd_layout(hf_bwd_args *a, int BH, int D, int Nq, int Nk, int bq, 
     char *kr = take((size_t)BH * NkP * D * 2), *vr = take((size_t)BH * NkP * D * 2);
     char *gr = take((size_t)BH * Nq * D * 2);
     char *sb = take((size_t)BH * D * D * 2), *stb = take((size_t)BH * D * D * 2);
-    char *delta = take((size_t)BH * NqP * 4);
+    char *delta = take((size_t)BH * NqP * 4), *rod = take((size_t)BH * NqP * 2 * 4);
     char *qoff = take((size_t)BH * (nkb + 1) * 4), *qlist = take((size_t)BH * nqb * top_k * 4);
     char *korder = take((size_t)BH * nkb * 4);
     char *dsp = take((size_t)BH * splits * D * D * 4), *dzp = take((size_t)BH * splits * D * 4);
@@ -1122,6 +1152,7 @@ static size_t bwd_layout(hf_bwd_args *a, int BH, int D, int Nq, int Nk, int bq, 
         a->sb = reinterpret_cast<uint16_t *>(sb);
         a->stb = reinterpret_cast<uint16_t *>(stb);
         a->delta = reinterpret_cast<float *>(delta);
+        a->rod = reinterpret_cast<float *>(rod);
         a->qoff = reinterpret_cast<int32_t *>(qoff);
         a->qlist = reinterpret_cast<int32_t *>(qlist);
         a->korder = reinterpret_cast<int32_t *>(korder);

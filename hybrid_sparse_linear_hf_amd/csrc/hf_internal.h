@@ -170,6 +170,7 @@ struct hf_bwd_args {
     uint16_t *gr;              // dO rows in bf16 [BH][NqP][D]
     uint16_t *sb, *stb;        // S and S^T in bf16 [BH][D][D]
     float *delta;              // [BH][NqP]: dO . (sparse part of out)
+    float *rod;                // [BH][NqP][2]: 1 / den and dden of each query (readout pass -> dq pass)
     int32_t *qoff, *qlist;     // per key block, the query blocks that kept it: [BH][nkb+1], [BH][nqb*top_k]
     int32_t *korder;           // [BH*nkb] key blocks (bh * nkb + j) by descending kept-by count
     float *dsp, *dzp;          // readout partials [BH][splits][D][D], [BH][splits][D]

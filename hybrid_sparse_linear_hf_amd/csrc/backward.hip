@@ -365,8 +365,9 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
         }
         den = pair_sum_b(den) + a.eps;
         const float inv_den = 1.f / den;
-        // n^T = S^T phi(q): lane holds n[c], c = 32 ft + 16 g + i
+        // n^T = S^T phi(q): lane holds n[c], c = 32 ft + 16 g + i, and reads dO[c] (kept for dn)
         float gn = 0.f, go = 0.f;
+        float gk[NT][16];
 #pragma unroll
         for (int ft = 0; ft < NT; ++ft) {
             f32x16 acc = {};
@@ -381,22 +382,13 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
                 const f32x4 ov = *reinterpret_cast<const f32x4 *>(op + 4 * v);
                 gn += gv.x * acc[4 * v] + gv.y * acc[4 * v + 1] + gv.z * acc[4 * v + 2] + gv.w * acc[4 * v + 3];
                 go += gv.x * ov.x + gv.y * ov.y + gv.z * ov.z + gv.w * ov.w;
+                gk[ft][4 * v] = gv.x, gk[ft][4 * v + 1] = gv.y, gk[ft][4 * v + 2] = gv.z, gk[ft][4 * v + 3] = gv.w;
             }
         }
         gn = pair_sum_b(gn);
         go = pair_sum_b(go);
         const float dden = -gn * inv_den * inv_den;
         if (valid && g == 0) a.delta[(size_t)bh * a.NqP + t] = go - gn * inv_den;
-        // dn = dO / den in the B layout
-        u32x4 dnf[D / 16];
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            const float *gp = a.dout + row * D + 16 * ks + 8 * g;
-            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(gp);
-            const f32x4 g1 = *reinterpret_cast<const f32x4 *>(gp + 4);
-            dnf[ks] = u32x4{pack_bf16x2(g0.x * inv_den, g0.y * inv_den), pack_bf16x2(g0.z * inv_den, g0.w * inv_den),
-                            pack_bf16x2(g1.x * inv_den, g1.y * inv_den), pack_bf16x2(g1.z * inv_den, g1.w * inv_den)};
-        }
         // the readout's term of dq, (S dn + z dden) * phi'(q), is formed by the dq pass from
         // these two per-query values
         if (valid && g == 0) {
@@ -404,19 +396,21 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
             rp[0] = inv_den;
             rp[1] = dden;
         }
-        // stage phi(q) and dn transposed (zero for rows past the queries) for the partials
+        // stage phi(q) and dn = dO / den (bf16) transposed, zero for rows past the queries, for
+        // the partials
         const int col = 32 * w + n;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             const uint32_t pw[4] = {pq[ks].x, pq[ks].y, pq[ks].z, pq[ks].w};
-            const uint32_t dw[4] = {dnf[ks].x, dnf[ks].y, dnf[ks].z, dnf[ks].w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int f = 16 * ks + 8 * g + e;
-                phT[f][col] = valid ? (uint16_t)((e & 1) ? (pw[e >> 1] >> 16) : (pw[e >> 1] & 0xFFFF)) : 0;
-                dnT[f][col] = valid ? (uint16_t)((e & 1) ? (dw[e >> 1] >> 16) : (dw[e >> 1] & 0xFFFF)) : 0;
-            }
+            for (int e = 0; e < 8; ++e)
+                phT[16 * ks + 8 * g + e][col] = valid ? (uint16_t)((e & 1) ? (pw[e >> 1] >> 16) : (pw[e >> 1] & 0xFFFF)) : 0;
         }
+#pragma unroll
+        for (int ft = 0; ft < NT; ++ft)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                dnT[32 * ft + 16 * g + i][col] = valid ? (uint16_t)f32_to_bf16_bits(gk[ft][i] * inv_den) : 0;
         if (g == 0) dden_s[col] = valid ? dden : 0.f;
         __syncthreads();
         // dS partial += phi^T dn over the chunk's 64 queries (4 contraction steps of 16)

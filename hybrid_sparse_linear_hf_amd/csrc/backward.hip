@@ -41,8 +41,6 @@ constexpr int kQB = 64;   // query-block stages hold 64 rows (a short block repe
 // constant address space so that uniform reads become scalar loads
 typedef const __attribute__((address_space(4))) int32_t *cint32_p;
 
-__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
-
 __device__ __forceinline__ u32x4 f32x8_to_bf16(const float *p) {
     const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
     const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
@@ -61,42 +59,60 @@ __device__ __forceinline__ float phi_prime(float x) {
 
 // ---------------------------------------------------------------- prep
 
-// One workgroup per (plane, 64-key tile of the logical window): K rows and V rows (V from
-// the ring's 8-token groups, transposed through LDS), rows past the window zeroed.  Keys
-// j0 .. j0 + 63 in aligned groups of 8 stay in one frame (T % 8 == 0).
+// One workgroup per (plane, 64-key tile of the logical window): K rows and V rows, rows
+// past the window zeroed.  Threads 0..127 turn V back from the ring's 8-token groups
+// ([D][8] per group) into rows: each owns 8 keys x 8 features, loads the 8 features' 16-byte
+// key runs (128 contiguous bytes), transposes the 8x8 block of 16-bit values in registers
+// (byte permutes) and stores 8 16-byte row pieces; threads 128..255 copy the K rows.  Keys
+// j0 .. j0 + 63 in aligned groups of 8 stay in one frame (T % 8 == 0).  Every load of a
+// thread is issued before its first store.
 template <int D>
 __global__ __launch_bounds__(256) void prep_keys_kernel(hf_bwd_args a) {
-    __shared__ __align__(16) uint16_t tv[D][64 + 8];
     const int tiles = a.NkP / 64;
     const int bh = blockIdx.x / tiles, j0 = (blockIdx.x % tiles) * 64;
-    auto slot_of = [&](int f) {
-        const int s = a.head + f;
-        return s >= a.W ? s - a.W : s;
+    auto ring_off = [&](int j) {     // element offset of window key j's row (K) or group (V)
+        const int f = j / a.T, t = j - f * a.T;
+        int s = a.head + f;
+        s = s >= a.W ? s - a.W : s;
+        return (((size_t)bh * a.W + s) * a.T + t) * D;
     };
-    for (int e = threadIdx.x; e < 64 * D / 8; e += 256) {
-        const int r = e / (D / 8), c8 = (e % (D / 8)) * 8, j = j0 + r;
-        u32x4 v = {0, 0, 0, 0};
+    const int tid = threadIdx.x;
+    if (tid < 128) {
+        const int fg = tid % 16, tg = tid / 16;             // feature octet, key group
+        if (fg >= D / 8) return;
+        const int j = j0 + 8 * tg;
+        u32x4 in[8];
         if (j < a.Nk) {
-            const int f = j / a.T, t = j - f * a.T;
-            v = *reinterpret_cast<const u32x4 *>(a.ring_k + (((size_t)bh * a.W + slot_of(f)) * a.T + t) * D + c8);
+            const uint16_t *src = a.ring_vg + ring_off(j) + 64 * fg;   // features 8 fg .. + 7, 8 keys each
+#pragma unroll
+            for (int i = 0; i < 8; ++i) in[i] = *reinterpret_cast<const u32x4 *>(src + 8 * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) in[i] = u32x4{0u, 0u, 0u, 0u};
         }
-        *reinterpret_cast<u32x4 *>(a.kr + ((size_t)bh * a.NkP + j) * D + c8) = v;
-    }
-    for (int e = threadIdx.x; e < D * 8; e += 256) {
-        const int d = e / 8, k8 = (e % 8) * 8, j = j0 + k8;
-        u32x4 v = {0, 0, 0, 0};
-        if (j < a.Nk) {
-            const int f = j / a.T, t = j - f * a.T;
-            v = *reinterpret_cast<const u32x4 *>(a.ring_vg + (((size_t)bh * a.W + slot_of(f)) * a.T + t) * D + 8 * d);
+        // out[k] = key k's features 8 fg .. + 7: word w takes feature 2w and 2w+1 of key k
+        uint16_t *dst = a.vr + ((size_t)bh * a.NkP + j) * D + 8 * fg;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+            uint32_t o[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(in[2 * w + 1][k >> 1], in[2 * w][k >> 1], sel);
+            *reinterpret_cast<u32x4 *>(dst + (size_t)k * D) = u32x4{o[0], o[1], o[2], o[3]};
         }
-        *reinterpret_cast<u32x4 *>(&tv[d][k8]) = v;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < 64 * D / 8; e += 256) {
-        const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
-        const u32x4 o = {pack2(tv[c8][r], tv[c8 + 1][r]), pack2(tv[c8 + 2][r], tv[c8 + 3][r]),
-                         pack2(tv[c8 + 4][r], tv[c8 + 5][r]), pack2(tv[c8 + 6][r], tv[c8 + 7][r])};
-        *reinterpret_cast<u32x4 *>(a.vr + ((size_t)bh * a.NkP + j0 + r) * D + c8) = o;
+    } else {
+        constexpr int kVecPerRow = D / 8, kIters = 64 * kVecPerRow / 128;
+        u32x4 kv[kIters];
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int e = tid - 128 + 128 * it, r = e / kVecPerRow, c8 = (e % kVecPerRow) * 8, j = j0 + r;
+            kv[it] = j < a.Nk ? *reinterpret_cast<const u32x4 *>(a.ring_k + ring_off(j) + c8) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int e = tid - 128 + 128 * it, r = e / kVecPerRow, c8 = (e % kVecPerRow) * 8;
+            *reinterpret_cast<u32x4 *>(a.kr + ((size_t)bh * a.NkP + j0 + r) * D + c8) = kv[it];
+        }
     }
 }
 

@@ -323,12 +323,25 @@ __device__ __forceinline__ u32x4 xt_frag(const uint16_t *X, int q0, int ft, int 
     return u32x4{h[0].x, h[0].y, h[1].x, h[1].y};
 }
 
+constexpr int kBufDword3 = 0x00020000;        // raw buffer resource word 3 (gfx9 family)
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef __attribute__((address_space(3))) void *LdsPtr;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufDword3);
+}
+
+// 16 bytes per lane from the buffer into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(Rsrc r, unsigned char *lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 16, (int)voff, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------- readout pass
 
 // One workgroup (two waves) per (plane, split); split s takes 64-query chunks
 // s, s + splits, ...  Each wave owns 32 queries of the chunk.
 template <int D>
-__global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) void readout_bwd_kernel(hf_bwd_args a) {
     __shared__ __align__(16) uint16_t phT[D][kQB + 8];
     __shared__ __align__(16) uint16_t dnT[D][kQB + 8];
     __shared__ __align__(16) float dden_s[kQB];
@@ -338,15 +351,25 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
     const int bh = blockIdx.x / a.splits, sp = blockIdx.x % a.splits;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31, g = lane >> 5;
     const int nchunks = (a.Nq + kQB - 1) / kQB;
-    __shared__ __align__(16) float zp[D];     // z of the plane
-    for (int e = threadIdx.x; e < D; e += 128) zp[e] = a.z[(size_t)bh * D + e];
+    // z at the features 16 ks + 8 g .. + 8 this lane's phi(q) holds, in registers for every chunk
+    f32x4 zr[D / 16][2];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) zr[ks][h] = *reinterpret_cast<const f32x4 *>(a.z + (size_t)bh * D + 16 * ks + 8 * g + 4 * h);
     {
-        const uint16_t *sbg = a.sb + (size_t)bh * D * D;
-        for (int e = threadIdx.x; e < D * D / 8; e += 128) {
-            const int r = e / (D / 8), c = e % (D / 8);
-            *reinterpret_cast<u32x4 *>(&s_sw[r * D + ((c ^ swz_row<D>(r)) << 3)]) =
-                *reinterpret_cast<const u32x4 *>(sbg + r * D + 8 * c);
+        // direct-to-LDS loads, 1 KB (RPI whole rows) per instruction, all issued before the
+        // first wait: lane l of instruction j fills slot l % LPR of row RPI j + l / LPR,
+        // which holds the row's chunk (l % LPR) ^ swz_row
+        constexpr int LPR = D / 8, RPI = 64 / LPR, NI = D * D * 2 / 1024;
+        const Rsrc rs = make_rsrc(a.sb + (size_t)__builtin_amdgcn_readfirstlane(bh) * D * D, (uint32_t)(D * D * 2));
+#pragma unroll
+        for (int jj = 0; jj < NI / 2; ++jj) {
+            const int j = 2 * jj + __builtin_amdgcn_readfirstlane(w), r = RPI * j + lane / LPR;
+            dma16(rs, reinterpret_cast<unsigned char *>(s_sw) + j * 1024,
+                  (uint32_t)(r * D * 2 + (((lane % LPR) ^ swz_row<D>(r)) << 4)));
         }
+        wait_vm<0>();
         __syncthreads();
     }
     // partial dS: wave w owns output tiles (a-tile XT w + x, c-tile y), x < XT = D/64,
@@ -363,42 +386,60 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
         const bool valid = t < a.Nq;
         const size_t row = (size_t)bh * a.Nq + (valid ? t : 0);
         // phi(q) in the B layout (features 16 ks + 8 g .. + 8) and the denominator
+        // every load of the chunk first (the LDS use holds this pass to one wave per SIMD, so
+        // the registers are there): q, and the dO and output features this lane meets below
         u32x4 pq[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) pq[ks] = *reinterpret_cast<const u32x4 *>(a.q + row * D + 16 * ks + 8 * g);
+        f32x4 gva[NT][4], ova[NT][4];
+#pragma unroll
+        for (int ft = 0; ft < NT; ++ft)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                gva[ft][v] = *reinterpret_cast<const f32x4 *>(a.dout + row * D + 32 * ft + 16 * g + 4 * v);
+                ova[ft][v] = *reinterpret_cast<const f32x4 *>(a.out + row * D + 32 * ft + 16 * g + 4 * v);
+            }
         float den = 0.f;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-            const u32x4 qv = *reinterpret_cast<const u32x4 *>(a.q + row * D + 16 * ks + 8 * g);
+            const u32x4 qv = pq[ks];
             const uint32_t wv[4] = {qv.x, qv.y, qv.z, qv.w};
             uint32_t o[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float f0 = phi_f32(bf16_lo_to_f32(wv[e])), f1 = phi_f32(bf16_hi_to_f32(wv[e]));
-                den = __builtin_fmaf(f0, zp[16 * ks + 8 * g + 2 * e], den);
-                den = __builtin_fmaf(f1, zp[16 * ks + 8 * g + 2 * e + 1], den);
+                den = __builtin_fmaf(f0, zr[ks][e >> 1][2 * (e & 1)], den);
+                den = __builtin_fmaf(f1, zr[ks][e >> 1][2 * (e & 1) + 1], den);
                 o[e] = pack_bf16x2(f0, f1);
             }
             pq[ks] = u32x4{o[0], o[1], o[2], o[3]};
         }
         den = pair_sum_b(den) + a.eps;
         const float inv_den = 1.f / den;
-        // n^T = S^T phi(q): lane holds n[c], c = 32 ft + 16 g + i, and reads dO[c] (kept for dn)
+        // n^T = S^T phi(q): lane holds n[c], c = 32 ft + 16 g + i, and reads dO[c], staging
+        // dn = dO / den (bf16) transposed, zero for rows past the queries, for the partials
+        // (the previous chunk's partials are done with dnT: the loop's closing barrier)
+        const int col = 32 * w + n;
         float gn = 0.f, go = 0.f;
-        float gk[NT][16];
 #pragma unroll
         for (int ft = 0; ft < NT; ++ft) {
+            // S^T rows 32 ft + perm32(n), features 16 ks + 8 g .. + 8: every fragment read
+            // before the first product
+            u32x4 sf[D / 16];
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) sf[ks] = xt_frag<D>(s_sw, 16 * ks + 8 * g, ft, lane);
             f32x16 acc = {};
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)   // S^T rows 32 ft + perm32(n), features 16 ks + 8 g .. + 8
-                acc = mfma32(as_bf16x8(xt_frag<D>(s_sw, 16 * ks + 8 * g, ft, lane)), as_bf16x8(pq[ks]), acc);
-            const float *gp = a.dout + row * D + 32 * ft + 16 * g;
-            const float *op = a.out + row * D + 32 * ft + 16 * g;
+            for (int ks = 0; ks < D / 16; ++ks) acc = mfma32(as_bf16x8(sf[ks]), as_bf16x8(pq[ks]), acc);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const f32x4 gv = *reinterpret_cast<const f32x4 *>(gp + 4 * v);
-                const f32x4 ov = *reinterpret_cast<const f32x4 *>(op + 4 * v);
+                const f32x4 gv = gva[ft][v], ov = ova[ft][v];
                 gn += gv.x * acc[4 * v] + gv.y * acc[4 * v + 1] + gv.z * acc[4 * v + 2] + gv.w * acc[4 * v + 3];
                 go += gv.x * ov.x + gv.y * ov.y + gv.z * ov.z + gv.w * ov.w;
-                gk[ft][4 * v] = gv.x, gk[ft][4 * v + 1] = gv.y, gk[ft][4 * v + 2] = gv.z, gk[ft][4 * v + 3] = gv.w;
+                const float gg[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dnT[32 * ft + 16 * g + 4 * v + e][col] = valid ? (uint16_t)f32_to_bf16_bits(gg[e] * inv_den) : 0;
             }
         }
         gn = pair_sum_b(gn);
@@ -412,9 +453,7 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
             rp[0] = inv_den;
             rp[1] = dden;
         }
-        // stage phi(q) and dn = dO / den (bf16) transposed, zero for rows past the queries, for
-        // the partials
-        const int col = 32 * w + n;
+        // stage phi(q) transposed, zero for rows past the queries, for the partials
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             const uint32_t pw[4] = {pq[ks].x, pq[ks].y, pq[ks].z, pq[ks].w};
@@ -422,11 +461,6 @@ __global__ __launch_bounds__(128) void readout_bwd_kernel(hf_bwd_args a) {
             for (int e = 0; e < 8; ++e)
                 phT[16 * ks + 8 * g + e][col] = valid ? (uint16_t)((e & 1) ? (pw[e >> 1] >> 16) : (pw[e >> 1] & 0xFFFF)) : 0;
         }
-#pragma unroll
-        for (int ft = 0; ft < NT; ++ft)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                dnT[32 * ft + 16 * g + i][col] = valid ? (uint16_t)f32_to_bf16_bits(gk[ft][i] * inv_den) : 0;
         if (g == 0) dden_s[col] = valid ? dden : 0.f;
         __syncthreads();
         // dS partial += phi^T dn over the chunk's 64 queries (4 contraction steps of 16)
@@ -510,19 +544,6 @@ __global__ __launch_bounds__(256) void reduce_readout_kernel(hf_bwd_args a) {
 }
 
 // ---------------------------------------------------------------- dq pass
-
-constexpr int kBufDword3 = 0x00020000;        // raw buffer resource word 3 (gfx9 family)
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-typedef __attribute__((address_space(3))) void *LdsPtr;
-
-__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufDword3);
-}
-
-// 16 bytes per lane from the buffer into LDS at lds + 16 * lane.
-__device__ __forceinline__ void dma16(Rsrc r, unsigned char *lds, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)lds, 16, (int)voff, 0, 0, 0);
-}
 
 // One workgroup per query block, one wave per 32-query tile, walking the kept key blocks in
 // 32-key subtiles.  Each subtile's K and V rows (both chunk-swizzled, swz_row) reach LDS by

@@ -188,10 +188,23 @@ __global__ __launch_bounds__(256) void prep_queries_kernel(hf_bwd_args a) {
     }
     const int bh = blockIdx.x / a.nqb, qb = blockIdx.x % a.nqb;
     const int q0 = qb * a.bq, nq = min(a.bq, a.Nq - q0);
-    for (int e = threadIdx.x; e < nq * D / 8; e += 256) {
-        const int r = e / (D / 8), c8 = (e % (D / 8)) * 8;
-        const size_t row = (size_t)bh * a.Nq + q0 + r;
-        *reinterpret_cast<u32x4 *>(a.gr + row * D + c8) = f32x8_to_bf16(a.dout + row * D + c8);
+    // every load of the block issued before the first conversion
+    constexpr int U = 64 * D / 8 / 256;       // 8-feature pieces per thread of a full block
+    f32x4 v[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int e = threadIdx.x + 256 * u, r = min(e / (D / 8), nq - 1), c8 = (e % (D / 8)) * 8;
+        const float *src = a.dout + ((size_t)bh * a.Nq + q0 + r) * D + c8;
+        v[u][0] = *reinterpret_cast<const f32x4 *>(src);
+        v[u][1] = *reinterpret_cast<const f32x4 *>(src + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int e = threadIdx.x + 256 * u, r = e / (D / 8), c8 = (e % (D / 8)) * 8;
+        if (r < nq)
+            *reinterpret_cast<u32x4 *>(a.gr + ((size_t)bh * a.Nq + q0 + r) * D + c8) =
+                u32x4{pack_bf16x2(v[u][0].x, v[u][0].y), pack_bf16x2(v[u][0].z, v[u][0].w),
+                      pack_bf16x2(v[u][1].x, v[u][1].y), pack_bf16x2(v[u][1].z, v[u][1].w)};
     }
 }
 
@@ -219,14 +232,23 @@ __global__ __launch_bounds__(256) void csr_kernel(hf_bwd_args a) {
     if (by_rank)
         for (int e = tid; e < a.nkb * words; e += 256) bits[e] = 0ull;
     __syncthreads();
-    for (int e = tid; e < total; e += 256) {
-        const int j = sel[e];
-        if (staged) sel_s[e] = j;
-        if (j >= 0 && j < a.nkb) {
-            atomicAdd(&cnt[j], 1);
-            if (by_rank) {
-                const int i = e / a.top_k;
-                atomicOr(&bits[j * words + (i >> 6)], 1ull << (i & 63));
+    // the kept entries, twelve loads per thread issued before the first is used
+    constexpr int U = 12;
+    for (int e0 = tid; e0 < total; e0 += 256 * U) {
+        int jv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) jv[u] = e0 + 256 * u < total ? sel[e0 + 256 * u] : -1;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = e0 + 256 * u, j = jv[u];
+            if (e >= total) break;
+            if (staged) sel_s[e] = j;
+            if (j >= 0 && j < a.nkb) {
+                atomicAdd(&cnt[j], 1);
+                if (by_rank) {
+                    const int i = e / a.top_k;
+                    atomicOr(&bits[j * words + (i >> 6)], 1ull << (i & 63));
+                }
             }
         }
     }

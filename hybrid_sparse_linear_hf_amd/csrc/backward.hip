@@ -11,12 +11,13 @@
 //   absorb       (S += phi(K)^T V, z += sum phi(K)):  dV = phi(K) dS, dK = (V dS^T + dz) * phi'(K).
 //
 // gfx950 design.  A prep launch copies the window into logical order in bf16 -- K rows and
-// V rows -- and dO into bf16 rows, so that the passes below never touch the ring's frame
-// arithmetic.
+// V rows -- so that the passes below never touch the ring's frame arithmetic, and S into
+// bf16 rows and transposed rows.
 //   * readout pass: one workgroup per (plane, split of the queries), S staged in LDS once;
 //     n = S^T phi(q) on the matrix cores, per-query terms in fp32 (Delta, 1 / den, dden);
 //     dS and dz as split partials (phi(q) and dn staged transposed in LDS), added in split
-//     order by a second launch.
+//     order by a second launch.  It reads every dO row and writes it back in bf16 for the
+//     passes below.
 //   * dq pass: one workgroup per query block, one wave per 32-query tile, walking the kept
 //     key blocks in 32-key subtiles staged in LDS (two stages filled by direct-to-LDS
 //     loads, one subtile ahead): S^T = K Q^T, dP^T = V dO^T,
@@ -41,12 +42,6 @@ constexpr int kQB = 64;   // query-block stages hold 64 rows (a short block repe
 // constant address space so that uniform reads become scalar loads
 typedef const __attribute__((address_space(4))) int32_t *cint32_p;
 
-__device__ __forceinline__ u32x4 f32x8_to_bf16(const float *p) {
-    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
-    return u32x4{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w)};
-}
-
 __device__ __forceinline__ float pair_sum_b(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -59,16 +54,42 @@ __device__ __forceinline__ float phi_prime(float x) {
 
 // ---------------------------------------------------------------- prep
 
+// A fp32 [BH][D][D] matrix into bf16 rows and bf16 transposed rows, one workgroup per
+// 32 x 32 tile.
+template <int D>
+__device__ void mat_copies(const float *M, uint16_t *mb, uint16_t *mtb, int tile, float (*t)[33]) {
+    constexpr int nt = D / 32;
+    const int bh = tile / (nt * nt), ti = (tile / nt) % nt, tj = tile % nt;
+    const float *src = M + (size_t)bh * D * D;
+    for (int e = threadIdx.x; e < 32 * 32; e += 256) {
+        const int r = e / 32, c = e % 32;
+        const float v = src[(size_t)(32 * ti + r) * D + 32 * tj + c];
+        t[r][c] = v;
+        mb[(size_t)bh * D * D + (size_t)(32 * ti + r) * D + 32 * tj + c] = (uint16_t)f32_to_bf16_bits(v);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 32 * 32; e += 256) {
+        const int r = e / 32, c = e % 32;   // transposed element (c, r) of the tile
+        mtb[(size_t)bh * D * D + (size_t)(32 * tj + r) * D + 32 * ti + c] = (uint16_t)f32_to_bf16_bits(t[c][r]);
+    }
+}
+
 // One workgroup per (plane, 64-key tile of the logical window): K rows and V rows, rows
 // past the window zeroed.  Threads 0..127 turn V back from the ring's 8-token groups
 // ([D][8] per group) into rows: each owns 8 keys x 8 features, loads the 8 features' 16-byte
 // key runs (128 contiguous bytes), transposes the 8x8 block of 16-bit values in registers
 // (byte permutes) and stores 8 16-byte row pieces; threads 128..255 copy the K rows.  Keys
 // j0 .. j0 + 63 in aligned groups of 8 stay in one frame (T % 8 == 0).  Every load of a
-// thread is issued before its first store.
+// thread is issued before its first store.  Extra workgroups copy S into bf16 rows and
+// transposed rows (mat_copies).
 template <int D>
 __global__ __launch_bounds__(256) void prep_keys_kernel(hf_bwd_args a) {
     const int tiles = a.NkP / 64;
+    if ((int)blockIdx.x >= a.BH * tiles) {
+        __shared__ float t[32][33];
+        mat_copies<D>(a.S, a.sb, a.stb, (int)blockIdx.x - a.BH * tiles, t);
+        return;
+    }
     const int bh = blockIdx.x / tiles, j0 = (blockIdx.x % tiles) * 64;
     auto ring_off = [&](int j) {     // element offset of window key j's row (K) or group (V)
         const int f = j / a.T, t = j - f * a.T;
@@ -154,58 +175,6 @@ __global__ __launch_bounds__(1024) void order_kernel(hf_bwd_args a) {
     start[2 * t + 1] = base + c0;
     __syncthreads();
     for (int it = lo + t; it < hi; it += 1024) a.korder[lo + atomicAdd(&start[bucket(it)], 1)] = it;
-}
-
-// A fp32 [BH][D][D] matrix into bf16 rows and bf16 transposed rows, one workgroup per
-// 32 x 32 tile.
-template <int D>
-__device__ void mat_copies(const float *M, uint16_t *mb, uint16_t *mtb, int tile, float (*t)[33]) {
-    constexpr int nt = D / 32;
-    const int bh = tile / (nt * nt), ti = (tile / nt) % nt, tj = tile % nt;
-    const float *src = M + (size_t)bh * D * D;
-    for (int e = threadIdx.x; e < 32 * 32; e += 256) {
-        const int r = e / 32, c = e % 32;
-        const float v = src[(size_t)(32 * ti + r) * D + 32 * tj + c];
-        t[r][c] = v;
-        mb[(size_t)bh * D * D + (size_t)(32 * ti + r) * D + 32 * tj + c] = (uint16_t)f32_to_bf16_bits(v);
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < 32 * 32; e += 256) {
-        const int r = e / 32, c = e % 32;   // transposed element (c, r) of the tile
-        mtb[(size_t)bh * D * D + (size_t)(32 * tj + r) * D + 32 * ti + c] = (uint16_t)f32_to_bf16_bits(t[c][r]);
-    }
-}
-
-// One workgroup per (plane, query block): dO rows in bf16; extra workgroups copy S into
-// bf16 rows and transposed rows.
-template <int D>
-__global__ __launch_bounds__(256) void prep_queries_kernel(hf_bwd_args a) {
-    __shared__ float t[32][33];
-    const int nblk = a.BH * a.nqb;
-    if ((int)blockIdx.x >= nblk) {
-        mat_copies<D>(a.S, a.sb, a.stb, (int)blockIdx.x - nblk, t);
-        return;
-    }
-    const int bh = blockIdx.x / a.nqb, qb = blockIdx.x % a.nqb;
-    const int q0 = qb * a.bq, nq = min(a.bq, a.Nq - q0);
-    // every load of the block issued before the first conversion
-    constexpr int U = 64 * D / 8 / 256;       // 8-feature pieces per thread of a full block
-    f32x4 v[U][2];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int e = threadIdx.x + 256 * u, r = min(e / (D / 8), nq - 1), c8 = (e % (D / 8)) * 8;
-        const float *src = a.dout + ((size_t)bh * a.Nq + q0 + r) * D + c8;
-        v[u][0] = *reinterpret_cast<const f32x4 *>(src);
-        v[u][1] = *reinterpret_cast<const f32x4 *>(src + 4);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int e = threadIdx.x + 256 * u, r = e / (D / 8), c8 = (e % (D / 8)) * 8;
-        if (r < nq)
-            *reinterpret_cast<u32x4 *>(a.gr + ((size_t)bh * a.Nq + q0 + r) * D + c8) =
-                u32x4{pack_bf16x2(v[u][0].x, v[u][0].y), pack_bf16x2(v[u][0].z, v[u][0].w),
-                      pack_bf16x2(v[u][1].x, v[u][1].y), pack_bf16x2(v[u][1].z, v[u][1].w)};
-    }
 }
 
 // Per plane, the query blocks that kept each key block, ascending: count (LDS atomics over
@@ -421,6 +390,17 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 gva[ft][v] = *reinterpret_cast<const f32x4 *>(a.dout + row * D + 32 * ft + 16 * g + 4 * v);
                 ova[ft][v] = *reinterpret_cast<const f32x4 *>(a.out + row * D + 32 * ft + 16 * g + 4 * v);
             }
+        // the dO row in bf16 (round to nearest even) for the dq and dk / dv passes
+        if (valid) {
+#pragma unroll
+            for (int ft = 0; ft < NT; ++ft)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const f32x4 x = gva[ft][2 * h], y = gva[ft][2 * h + 1];
+                    *reinterpret_cast<u32x4 *>(a.gr + row * D + 32 * ft + 16 * g + 8 * h) =
+                        u32x4{pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w), pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w)};
+                }
+        }
         float den = 0.f;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
@@ -1128,8 +1108,7 @@ hipError_t launch_attn_backward(const hf_bwd_args &a, hipStream_t s) {
     const float c_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const float inv_sqrt_d = (float)(1.0 / sqrt((double)D));
     const int lsh = a.bk >= 128 ? 2 : (a.bk >= 64 ? 1 : 0);
-    hipLaunchKernelGGL(prep_keys_kernel<D>, dim3((unsigned)(a.BH * (a.NkP / 64))), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(prep_queries_kernel<D>, dim3((unsigned)(a.BH * a.nqb + a.BH * nt * nt)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(prep_keys_kernel<D>, dim3((unsigned)(a.BH * (a.NkP / 64) + a.BH * nt * nt)), dim3(256), 0, s, a);
     hipLaunchKernelGGL(csr_kernel, dim3((unsigned)a.BH), dim3(256), 0, s, a);
     hipLaunchKernelGGL(order_kernel, dim3(8), dim3(1024), 0, s, a);
     hipLaunchKernelGGL(readout_bwd_kernel<D>, dim3((unsigned)(a.BH * a.splits)), dim3(128), 0, s, a);

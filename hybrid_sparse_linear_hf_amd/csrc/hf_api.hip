@@ -77,7 +77,7 @@ Geometry geometry(const hf_dims *d, const hf_kv_ring *r) {
 //   [frame-pooled keys fp64, up to kMaxHierFrames frames]  [frame scores fp64]
 //   [per key block frame parts fp64]
 struct WsLayout {
-    size_t absorb, qbar, kbar, sc, st, zc, fbar, fsc, part, total;
+    size_t absorb, qbar, kbar, st, zc, fbar, part, total;
 };
 
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -90,13 +90,11 @@ WsLayout ws_layout(const hf_dims *d) {
     w.absorb = 0;
     w.qbar = al(hf_absorb_workspace_bytes(BH, d->D));
     w.kbar = w.qbar + al((size_t)BH * nqb * d->D * sizeof(double));
-    w.sc = w.kbar + al((size_t)BH * nkb * d->D * sizeof(double));
-    w.st = w.sc + al((size_t)BH * nqb * nkb * sizeof(double));
+    w.st = w.kbar + al((size_t)BH * nkb * d->D * sizeof(double));
     w.zc = w.st + al((size_t)BH * d->D * d->D * sizeof(uint16_t));
     w.fbar = w.zc + al((size_t)BH * d->D * sizeof(float));
     const int frames = d->W < kMaxHierFrames ? d->W : kMaxHierFrames;
-    w.fsc = w.fbar + al((size_t)BH * frames * d->D * sizeof(double));
-    w.part = w.fsc + al((size_t)BH * nqb * frames * sizeof(double));
+    w.part = w.fbar + al((size_t)BH * frames * d->D * sizeof(double));
     w.total = w.part + al((size_t)BH * nkb * 2 * d->D * sizeof(double));
     return w;
 }
@@ -160,13 +158,11 @@ hipError_t enqueue_select(const hf_dims *d, const void *q, const hf_kv_ring *r, 
     a.ring_k = static_cast<const uint16_t *>(r->k_dev);
     a.qbar = reinterpret_cast<double *>(wsp(ws, L.qbar));
     a.kbar = reinterpret_cast<double *>(wsp(ws, L.kbar));
-    a.sc = reinterpret_cast<double *>(wsp(ws, L.sc));
     a.idx = idx;
     a.scores = scores;
     a.nfr = r->n_committed + d->C;
     a.top_frames = top_frames;
     a.fbar = reinterpret_cast<double *>(wsp(ws, L.fbar));
-    a.fsc = reinterpret_cast<double *>(wsp(ws, L.fsc));
     a.part = reinterpret_cast<double *>(wsp(ws, L.part));
     a.fidx = fidx;
     a.fscores = fscores;

@@ -109,13 +109,11 @@ struct hf_select_args {
     int BH, D, T, W, head, Nq, Nk, bq, bk, nqb, nkb, top_k;
     const uint16_t *q, *ring_k;
     double *qbar, *kbar;       // workspace: pooled blocks
-    double *sc;                // workspace: scores [BH][nqb][nkb]
     int32_t *idx;
     double *scores;            // may be null
     // hierarchical selection (top_frames > 0): frames of the window, pooled per frame
     int nfr, top_frames;
     double *fbar;              // workspace: frame-pooled keys [BH][nfr][D]
-    double *fsc;               // workspace: frame scores [BH][nqb][nfr]
     double *part;              // workspace: per key block, sums of its rows in its first frame
                                // and in the next one [BH][nkb][2][D] (needs bk <= T)
     // readout preparation run as extra workgroups of the pool launch (prep_tiles > 0)

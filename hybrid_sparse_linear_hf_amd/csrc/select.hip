@@ -12,7 +12,7 @@
 // pool kernel keeps each key block's rows of its two frames apart, frame_pool_kernel adds
 // those parts per frame.
 //
-// Flat selection, two launches:
+// Two launches (three for the hierarchical variant):
 //   pool_kernel        HBM-bound: one workgroup per query or key block sums its rows in
 //                      fp64 and stores the block mean.  The sums are exact while the
 //                      magnitudes in one feature span at most 2^39 over 64 rows (8 bits of
@@ -27,10 +27,9 @@
 //                      k-th largest (score, -index) key and an ascending emit of the kept
 //                      indices.  In a hybrid step the same launch carries the ring append of
 //                      the chunk as extra workgroups, whose copying overlaps the scoring.
-// The hierarchical variant pools per frame as well (frame_pool_kernel), scores with the
-// tiled score_kernel (16 x 16 tiles, one wave each, same summation order) over block pairs
-// and over (query block, frame) pairs, and lets topk_kernel select the frames before the
-// blocks.
+// The hierarchical variant pools per frame as well (frame_pool_kernel, between the two),
+// and its score_topk_kernel instance scores the frames first, through the same LDS path
+// and summation order, and selects them before the blocks.
 #include "append_tile.h"
 #include "state_tile.h"
 
@@ -54,7 +53,6 @@ __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
     constexpr int kVec = D / 8;              // 16-byte vectors per row
     constexpr int kRowsPerPass = 256 / kVec;
     __shared__ double red[kRowsPerPass][D];
-    __shared__ double red_hi[SPLIT ? kRowsPerPass : 1][D];   // the second frame part (hierarchical)
 
     const int per_plane = a.nqb + a.nkb;
     if ((int)blockIdx.x >= a.BH * per_plane) {
@@ -79,42 +77,41 @@ __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
     double acc[8], acc2[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = acc2[e] = 0.0;
+    // this thread's rows r0 + ro, r0 + ro + kRowsPerPass, ... below `end`, from `r` on
+    auto add_rows = [&](int r, int end, double (&s)[8]) __attribute__((always_inline)) {
 #pragma unroll 4
-    for (int r = r0 + ro; r < r1; r += kRowsPerPass) {
-        const uint16_t *row = is_q ? a.q + ((size_t)bh * a.Nq + r) * D : key_row(a, bh, r);
-        const u32x4 w = *reinterpret_cast<const u32x4 *>(row + v * 8);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        for (; r < end; r += kRowsPerPass) {
+            const uint16_t *row = is_q ? a.q + ((size_t)bh * a.Nq + r) * D : key_row(a, bh, r);
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(row + v * 8);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const double lo = bf16_to_f64(ws[e] & 0xFFFFu), hi = bf16_to_f64(ws[e] >> 16);
-            if constexpr (SPLIT) {
-                const bool first = r < fend;           // adding 0.0 leaves a sum unchanged
-                acc[2 * e] += first ? lo : 0.0;
-                acc[2 * e + 1] += first ? hi : 0.0;
-                acc2[2 * e] += first ? 0.0 : lo;
-                acc2[2 * e + 1] += first ? 0.0 : hi;
-            } else {
-                acc[2 * e] += lo;
-                acc[2 * e + 1] += hi;
+            for (int e = 0; e < 4; ++e) {
+                s[2 * e] += bf16_to_f64(ws[e] & 0xFFFFu);
+                s[2 * e + 1] += bf16_to_f64(ws[e] >> 16);
             }
         }
-    }
+        return r;
+    };
+    // the first frame's rows into acc, the second's (hierarchical key blocks) into acc2
+    const int r = add_rows(r0 + ro, min(fend, r1), acc);
+    if constexpr (SPLIT) add_rows(r, r1, acc2);
     if constexpr (SPLIT) {
         if (split) {
-            // the two frame parts of this key block, for the frame pooling, reduced together;
-            // the block's sum is their sum (both exact, so it is the exact block sum)
+            // the two frame parts of this key block, for the frame pooling, reduced one after
+            // the other through the same LDS (one array keeps the launch at eight workgroups
+            // per CU); the block's sum is their sum (both exact, so it is the exact block sum)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                red[ro][v * 8 + e] = acc[e];
-                red_hi[ro][v * 8 + e] = acc2[e];
-            }
+            for (int e = 0; e < 8; ++e) red[ro][v * 8 + e] = acc[e];
+            __syncthreads();
+            double s0 = 0.0, s1 = 0.0;
+            if (threadIdx.x < D)
+                for (int k = 0; k < kRowsPerPass; ++k) s0 += red[k][threadIdx.x];
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[ro][v * 8 + e] = acc2[e];
             __syncthreads();
             if (threadIdx.x < D) {
-                double s0 = 0.0, s1 = 0.0;
-                for (int k = 0; k < kRowsPerPass; ++k) {
-                    s0 += red[k][threadIdx.x];
-                    s1 += red_hi[k][threadIdx.x];
-                }
+                for (int k = 0; k < kRowsPerPass; ++k) s1 += red[k][threadIdx.x];
                 double *pp = a.part + (((size_t)bh * a.nkb + b) * 2) * D;
                 pp[threadIdx.x] = s0;
                 pp[D + threadIdx.x] = s1;
@@ -163,84 +160,6 @@ __global__ __launch_bounds__(D) void frame_pool_kernel(hf_select_args a) {
 __device__ __forceinline__ uint64_t order_key(double s) {
     const uint64_t u = (uint64_t)__double_as_longlong(s + 0.0);  // -0 -> +0
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-}
-
-constexpr int kTile = 16;   // score tile: 16 query blocks x 16 key blocks per workgroup
-
-// Scores of a 16 x 16 tile of (query block, key block) pairs, one wave per tile: both
-// pooled tiles are staged in LDS (every staging load issued before the first LDS write),
-// then each lane forms a 2 x 2 block of dot products, each a sequential sum in index
-// order, reading two features per 16-byte LDS load.
-template <int D>
-__global__ __launch_bounds__(64) void score_kernel(hf_select_args a, double scale) {
-    constexpr int P = D + 2;                 // row pitch in doubles (16-byte aligned rows)
-    __shared__ __align__(16) double qs[kTile][P];
-    __shared__ __align__(16) double ks[kTile][P];
-    typedef __attribute__((ext_vector_type(2))) double f64x2;
-    const int ti_n = (a.nqb + kTile - 1) / kTile, tj_n = (a.nkb + kTile - 1) / kTile;
-    const int bh = blockIdx.x / (ti_n * tj_n);
-    const int i0 = ((blockIdx.x / tj_n) % ti_n) * kTile, j0 = (blockIdx.x % tj_n) * kTile;
-    const int tid = threadIdx.x;
-    {
-        // rows past the end re-read the last row and are zeroed
-        constexpr int kPer = kTile * D / 2 / 64;        // 16-byte loads per lane per matrix
-        constexpr int kBatch = 8;
-#pragma unroll
-        for (int e0 = 0; e0 < kPer; e0 += kBatch) {
-            f64x2 qv[kBatch], kv[kBatch];
-#pragma unroll
-            for (int e = 0; e < kBatch; ++e) {
-                const int idx = tid + 64 * (e0 + e), r = idx / (D / 2), d = 2 * (idx % (D / 2));
-                qv[e] = *reinterpret_cast<const f64x2 *>(a.qbar + ((size_t)bh * a.nqb + min(i0 + r, a.nqb - 1)) * D + d);
-                kv[e] = *reinterpret_cast<const f64x2 *>(a.kbar + ((size_t)bh * a.nkb + min(j0 + r, a.nkb - 1)) * D + d);
-            }
-#pragma unroll
-            for (int e = 0; e < kBatch; ++e) {
-                const int idx = tid + 64 * (e0 + e), r = idx / (D / 2), d = 2 * (idx % (D / 2));
-                const f64x2 z = {0.0, 0.0};
-                *reinterpret_cast<f64x2 *>(&qs[r][d]) = i0 + r < a.nqb ? qv[e] : z;
-                *reinterpret_cast<f64x2 *>(&ks[r][d]) = j0 + r < a.nkb ? kv[e] : z;
-            }
-        }
-    }
-    __syncthreads();
-    const int ti = 2 * (tid / 8), tj = 2 * (tid % 8);
-    double acc[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
-    {
-        // products and sums rounded separately (no fused multiply-add), in index order
-#pragma clang fp contract(off)
-#pragma unroll 4
-        for (int d = 0; d < D; d += 2) {
-            const f64x2 q0 = *reinterpret_cast<const f64x2 *>(&qs[ti][d]);
-            const f64x2 q1 = *reinterpret_cast<const f64x2 *>(&qs[ti + 1][d]);
-            const f64x2 k0 = *reinterpret_cast<const f64x2 *>(&ks[tj][d]);
-            const f64x2 k1 = *reinterpret_cast<const f64x2 *>(&ks[tj + 1][d]);
-            acc[0][0] = acc[0][0] + q0.x * k0.x;
-            acc[0][1] = acc[0][1] + q0.x * k1.x;
-            acc[1][0] = acc[1][0] + q1.x * k0.x;
-            acc[1][1] = acc[1][1] + q1.x * k1.x;
-            acc[0][0] = acc[0][0] + q0.y * k0.y;
-            acc[0][1] = acc[0][1] + q0.y * k1.y;
-            acc[1][0] = acc[1][0] + q1.y * k0.y;
-            acc[1][1] = acc[1][1] + q1.y * k1.y;
-        }
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int y = 0; y < 2; ++y) acc[x][y] = acc[x][y] * scale;
-    }
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-        const int i = i0 + ti + x;
-        if (i >= a.nqb) continue;
-#pragma unroll
-        for (int y = 0; y < 2; ++y) {
-            const int j = j0 + tj + y;
-            if (j >= a.nkb) continue;
-            a.sc[((size_t)bh * a.nqb + i) * a.nkb + j] = acc[x][y];
-            if (a.scores) a.scores[((size_t)bh * a.nqb + i) * a.nkb + j] = acc[x][y];
-        }
-    }
 }
 
 // Radix select over one wave: the k-th largest of the keys held in registers (KPL per
@@ -295,52 +214,18 @@ __device__ __forceinline__ uint64_t emit_kept(const uint64_t (&key)[KPL], int n,
     return kept;
 }
 
-// One wave per (plane, query block): radix select of the k-th largest (score, -index)
-// key, then an ascending emit of the kept block indices.  Lane l holds keys of blocks
-// l, l + 64, ... in registers (KPL of them).  HIER: the candidates are first restricted
-// to the key blocks touching the query block's top_frames best window frames (lane f
-// holds frame f's score).
-template <int KPL, bool HIER>
-__global__ __launch_bounds__(256) void topk_kernel(hf_select_args a) {
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const int row = blockIdx.x * 4 + wave;                    // (bh, i) flattened
-    if (row >= a.BH * a.nqb) return;
-    uint64_t frames = ~0ull;                                  // kept frames (bit f)
-    if constexpr (HIER) {
-        const uint64_t fkey[1] = {lane < a.nfr ? order_key(a.fsc[(size_t)row * a.nfr + lane]) : 0};
-        int need_eq;
-        const uint64_t prefix = kth_key<1>(fkey, a.top_frames, need_eq);
-        frames = emit_kept<1>(fkey, a.nfr, prefix, need_eq,
-                              a.fidx ? a.fidx + (size_t)row * a.top_frames : nullptr, lane);
-    }
-    const double *src = a.sc + (size_t)row * a.nkb;
-    uint64_t key[KPL];
-#pragma unroll
-    for (int e = 0; e < KPL; ++e) {
-        const int j = lane + 64 * e;
-        bool ok = j < a.nkb;
-        if constexpr (HIER) {
-            if (ok) {
-                // frames touched by key block j: f0 .. f1 (at most 17 of them: bk <= 128, T >= 8)
-                const int f0 = j * a.bk / a.T, f1 = (min((j + 1) * a.bk, a.Nk) - 1) / a.T;
-                ok = ((frames >> f0) & ((2ull << (f1 - f0)) - 1)) != 0;
-            }
-        }
-        key[e] = ok ? order_key(src[j]) : 0;
-    }
-    int need_eq;
-    const uint64_t prefix = kth_key<KPL>(key, a.top_k, need_eq);
-    emit_kept<KPL>(key, a.nkb, prefix, need_eq, a.idx + (size_t)row * a.top_k, lane);
-}
-
 // Flat selection, scores and top-k in one launch: a workgroup takes kRows query blocks of
 // one plane (one wave each).  The plane's pooled key blocks pass through LDS in chunks of
 // 64 (the next chunk is loaded into registers while the current one is scored); lane l of
 // wave w scores query block w against key block (chunk start + l) as a sequential sum in
-// index order with separately rounded products and sums, exactly as the tiled kernel
-// does.  The row of scores stays in LDS for the wave's radix select.
+// index order with separately rounded products and sums, as the oracle does.  The row of
+// scores stays in LDS for the wave's radix select.  HIER (hierarchical selection): before
+// the key blocks the plane's frame-pooled keys pass through the same LDS (at most 64
+// frames), lane f scoring frame f the same way; each wave keeps its top_frames best frames
+// (radix select, ties to the lower frame), and only the key blocks touching a kept frame
+// enter the block select.
 constexpr int kRows = 4;
-template <int D, int KPL>
+template <int D, int KPL, bool HIER = false>
 __global__ __launch_bounds__(64 * kRows) void score_topk_kernel(hf_select_args a, double scale) {
     constexpr int P = D + 2;                  // row pitch in doubles (16-byte aligned rows)
     constexpr int CH = 64;                    // key blocks per chunk
@@ -367,24 +252,23 @@ __global__ __launch_bounds__(64 * kRows) void score_topk_kernel(hf_select_args a
     }
     const double *kb = a.kbar + (size_t)bh * a.nkb * D;
     f64x2 nxt[kPer];
-    auto load_chunk = [&](int c0) {
+    auto load_rows = [&](const double *base, int nrows, int c0) {
 #pragma unroll
         for (int e = 0; e < kPer; ++e) {
             const int t = tid + 64 * kRows * e, r = t / (D / 2), d = 2 * (t % (D / 2));
-            nxt[e] = *reinterpret_cast<const f64x2 *>(kb + (size_t)min(c0 + r, a.nkb - 1) * D + d);
+            nxt[e] = *reinterpret_cast<const f64x2 *>(base + (size_t)min(c0 + r, nrows - 1) * D + d);
         }
     };
-    load_chunk(0);
-    for (int c0 = 0; c0 < a.nkb; c0 += CH) {
-        __syncthreads();                      // everyone is done with the previous chunk
+    auto load_chunk = [&](int c0) { load_rows(kb, a.nkb, c0); };
+    auto stage = [&]() {
 #pragma unroll
         for (int e = 0; e < kPer; ++e) {
             const int t = tid + 64 * kRows * e, r = t / (D / 2), d = 2 * (t % (D / 2));
             *reinterpret_cast<f64x2 *>(&ks[r][d]) = nxt[e];
         }
-        __syncthreads();
-        if (c0 + CH < a.nkb) load_chunk(c0 + CH);
-        const int j = c0 + lane;
+    };
+    // score of query block w against staged row `lane`
+    auto row_score = [&]() -> double {
         double acc = 0.0;
         {
 #pragma clang fp contract(off)
@@ -397,6 +281,32 @@ __global__ __launch_bounds__(64 * kRows) void score_topk_kernel(hf_select_args a
             }
             acc = acc * scale;
         }
+        return acc;
+    };
+    uint64_t frames = ~0ull;                  // kept frames of this wave's query block (bit f)
+    if constexpr (HIER) {
+        load_rows(a.fbar + (size_t)bh * a.nfr * D, a.nfr, 0);
+        stage();
+        __syncthreads();                      // qs and the frame rows are in place
+        load_chunk(0);
+        const double sf = row_score();
+        const size_t row = (size_t)bh * a.nqb + i;
+        if (a.fscores && i < a.nqb && lane < a.nfr) a.fscores[row * a.nfr + lane] = sf;
+        const uint64_t fkey[1] = {lane < a.nfr ? order_key(sf) : 0};
+        int need_eq;
+        const uint64_t prefix = kth_key<1>(fkey, a.top_frames, need_eq);
+        frames = emit_kept<1>(fkey, a.nfr, prefix, need_eq,
+                              a.fidx && i < a.nqb ? a.fidx + row * a.top_frames : nullptr, lane);
+    } else {
+        load_chunk(0);
+    }
+    for (int c0 = 0; c0 < a.nkb; c0 += CH) {
+        __syncthreads();                      // everyone is done with the previous chunk
+        stage();
+        __syncthreads();
+        if (c0 + CH < a.nkb) load_chunk(c0 + CH);
+        const int j = c0 + lane;
+        const double acc = row_score();
         if (j < a.nkb) {
             srow[w][j] = acc;
             if (a.scores && i < a.nqb) a.scores[((size_t)bh * a.nqb + i) * a.nkb + j] = acc;
@@ -407,7 +317,15 @@ __global__ __launch_bounds__(64 * kRows) void score_topk_kernel(hf_select_args a
 #pragma unroll
     for (int e = 0; e < KPL; ++e) {
         const int j = lane + 64 * e;
-        key[e] = j < a.nkb ? order_key(srow[w][j]) : 0;
+        bool ok = j < a.nkb;
+        if constexpr (HIER) {
+            if (ok) {
+                // frames touched by key block j: f0 .. f1 (bk <= T: at most two)
+                const int f0 = j * a.bk / a.T, f1 = (min((j + 1) * a.bk, a.Nk) - 1) / a.T;
+                ok = ((frames >> f0) & ((2ull << (f1 - f0)) - 1)) != 0;
+            }
+        }
+        key[e] = ok ? order_key(srow[w][j]) : 0;
     }
     int need_eq;
     const uint64_t prefix = kth_key<KPL>(key, a.top_k, need_eq);
@@ -417,36 +335,23 @@ __global__ __launch_bounds__(64 * kRows) void score_topk_kernel(hf_select_args a
 }  // namespace
 }  // namespace hf
 
-static void launch_topk(int kpl, dim3 grid, const hf_select_args &a, hipStream_t s) {
-    if (kpl <= 1) hipLaunchKernelGGL((hf::topk_kernel<1, true>), grid, dim3(256), 0, s, a);
-    else if (kpl <= 2) hipLaunchKernelGGL((hf::topk_kernel<2, true>), grid, dim3(256), 0, s, a);
-    else if (kpl <= 3) hipLaunchKernelGGL((hf::topk_kernel<3, true>), grid, dim3(256), 0, s, a);
-    else if (kpl <= 4) hipLaunchKernelGGL((hf::topk_kernel<4, true>), grid, dim3(256), 0, s, a);
-    else if (kpl <= 8) hipLaunchKernelGGL((hf::topk_kernel<8, true>), grid, dim3(256), 0, s, a);
-    else if (kpl <= 16) hipLaunchKernelGGL((hf::topk_kernel<16, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((hf::topk_kernel<24, true>), grid, dim3(256), 0, s, a);
-}
-
-template <int D>
+template <int D, bool HIER = false>
 static void launch_score_topk(int kpl, const hf_select_args &a, double scale, hipStream_t s) {
     const dim3 grid((unsigned)(a.BH * ((a.nqb + hf::kRows - 1) / hf::kRows) + a.app_tiles));
     const dim3 block(64 * hf::kRows);
-    if (kpl <= 1) hipLaunchKernelGGL((hf::score_topk_kernel<D, 1>), grid, block, 0, s, a, scale);
-    else if (kpl <= 2) hipLaunchKernelGGL((hf::score_topk_kernel<D, 2>), grid, block, 0, s, a, scale);
-    else if (kpl <= 3) hipLaunchKernelGGL((hf::score_topk_kernel<D, 3>), grid, block, 0, s, a, scale);
-    else if (kpl <= 4) hipLaunchKernelGGL((hf::score_topk_kernel<D, 4>), grid, block, 0, s, a, scale);
-    else if (kpl <= 8) hipLaunchKernelGGL((hf::score_topk_kernel<D, 8>), grid, block, 0, s, a, scale);
-    else if (kpl <= 16) hipLaunchKernelGGL((hf::score_topk_kernel<D, 16>), grid, block, 0, s, a, scale);
-    else hipLaunchKernelGGL((hf::score_topk_kernel<D, 24>), grid, block, 0, s, a, scale);
+    if (kpl <= 1) hipLaunchKernelGGL((hf::score_topk_kernel<D, 1, HIER>), grid, block, 0, s, a, scale);
+    else if (kpl <= 2) hipLaunchKernelGGL((hf::score_topk_kernel<D, 2, HIER>), grid, block, 0, s, a, scale);
+    else if (kpl <= 3) hipLaunchKernelGGL((hf::score_topk_kernel<D, 3, HIER>), grid, block, 0, s, a, scale);
+    else if (kpl <= 4) hipLaunchKernelGGL((hf::score_topk_kernel<D, 4, HIER>), grid, block, 0, s, a, scale);
+    else if (kpl <= 8) hipLaunchKernelGGL((hf::score_topk_kernel<D, 8, HIER>), grid, block, 0, s, a, scale);
+    else if (kpl <= 16) hipLaunchKernelGGL((hf::score_topk_kernel<D, 16, HIER>), grid, block, 0, s, a, scale);
+    else hipLaunchKernelGGL((hf::score_topk_kernel<D, 24, HIER>), grid, block, 0, s, a, scale);
 }
 
 hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s) {
     // a step's ring append runs as extra workgroups of the score + top-k launch (flat
     // selection; the hierarchical path is never given one)
     const dim3 grid_pool((unsigned)(a.BH * (a.nqb + a.nkb) + a.prep_tiles));
-    const int ti_n = (a.nqb + hf::kTile - 1) / hf::kTile, tj_n = (a.nkb + hf::kTile - 1) / hf::kTile;
-    const dim3 grid_score((unsigned)(a.BH * ti_n * tj_n));
-    const dim3 grid_topk((unsigned)((a.BH * a.nqb + 3) / 4));
     const double scale = 1.0 / sqrt((double)a.D);
     const int kpl = (a.nkb + 63) / 64;
     if (a.top_frames == 0) {
@@ -460,31 +365,17 @@ hipError_t hf_launch_block_select(const hf_select_args &a, hipStream_t s) {
         }
         return hipGetLastError();
     }
-    // hierarchical: pool (keeping each key block's frame parts), frame means, block and
-    // frame scores, then the two-level top-k
+    // hierarchical: pool (keeping each key block's frame parts), frame means, then frame
+    // scores, frame top-k, block scores and the block top-k among the kept frames' blocks in
+    // one launch
     if (a.D == 64) {
         hipLaunchKernelGGL((hf::pool_kernel<64, true>), grid_pool, dim3(256), 0, s, a);
-        hipLaunchKernelGGL(hf::score_kernel<64>, grid_score, dim3(64), 0, s, a, scale);
+        hipLaunchKernelGGL(hf::frame_pool_kernel<64>, dim3((unsigned)(a.BH * a.nfr)), dim3(64), 0, s, a);
+        launch_score_topk<64, true>(kpl, a, scale, s);
     } else {
         hipLaunchKernelGGL((hf::pool_kernel<128, true>), grid_pool, dim3(256), 0, s, a);
-        hipLaunchKernelGGL(hf::score_kernel<128>, grid_score, dim3(64), 0, s, a, scale);
+        hipLaunchKernelGGL(hf::frame_pool_kernel<128>, dim3((unsigned)(a.BH * a.nfr)), dim3(128), 0, s, a);
+        launch_score_topk<128, true>(kpl, a, scale, s);
     }
-    const dim3 grid_fp((unsigned)(a.BH * a.nfr));
-    if (a.D == 64)
-        hipLaunchKernelGGL(hf::frame_pool_kernel<64>, grid_fp, dim3(64), 0, s, a);
-    else
-        hipLaunchKernelGGL(hf::frame_pool_kernel<128>, grid_fp, dim3(128), 0, s, a);
-    // frame scores: the score kernel over (query block, frame) pairs
-    hf_select_args f = a;
-    f.kbar = a.fbar;
-    f.nkb = a.nfr;
-    f.sc = a.fsc;
-    f.scores = a.fscores;
-    const dim3 grid_fs((unsigned)(a.BH * ti_n * ((a.nfr + hf::kTile - 1) / hf::kTile)));
-    if (a.D == 64)
-        hipLaunchKernelGGL(hf::score_kernel<64>, grid_fs, dim3(64), 0, s, f, scale);
-    else
-        hipLaunchKernelGGL(hf::score_kernel<128>, grid_fs, dim3(64), 0, s, f, scale);
-    launch_topk(kpl, grid_topk, a, s);
     return hipGetLastError();
 }

@@ -106,12 +106,15 @@ __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
             double s0 = 0.0, s1 = 0.0;
             if (threadIdx.x < D)
                 for (int k = 0; k < kRowsPerPass; ++k) s0 += red[k][threadIdx.x];
-            __syncthreads();
+            if (fend < r1) {                  // the block reaches into the next frame (uniform)
+                __syncthreads();
 #pragma unroll
-            for (int e = 0; e < 8; ++e) red[ro][v * 8 + e] = acc2[e];
-            __syncthreads();
+                for (int e = 0; e < 8; ++e) red[ro][v * 8 + e] = acc2[e];
+                __syncthreads();
+                if (threadIdx.x < D)
+                    for (int k = 0; k < kRowsPerPass; ++k) s1 += red[k][threadIdx.x];
+            }
             if (threadIdx.x < D) {
-                for (int k = 0; k < kRowsPerPass; ++k) s1 += red[k][threadIdx.x];
                 double *pp = a.part + (((size_t)bh * a.nkb + b) * 2) * D;
                 pp[threadIdx.x] = s0;
                 pp[D + threadIdx.x] = s1;

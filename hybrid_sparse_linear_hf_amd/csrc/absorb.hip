@@ -257,11 +257,12 @@ __global__ __launch_bounds__(256, 2) void absorb_rows_kernel(hf_absorb_args a, i
 
 // ------------------------------------------------------------------ host side
 
-// Splits per 64-row block aim at no more than ~256 workgroups (about one per CU) whatever
-// the number of planes, and never exceed the number of 64-token chunks.
+// Splits per 64-row block aim at about 512 workgroups (two per CU, the most the kernel's
+// two LDS stages allow, so that one workgroup's products overlap the other's staging)
+// whatever the number of planes, and never exceed the number of 64-token chunks.
 int hf_absorb_splits(int BH, int D, int64_t n_tok) {
     const int blocks = BH * (D / 64);
-    int P = 256 / blocks;
+    int P = 512 / blocks;
     P = P < 1 ? 1 : P;
     const int64_t nch = (n_tok + hf::kChunk - 1) / hf::kChunk;
     return nch < P ? (int)(nch > 0 ? nch : 1) : P;

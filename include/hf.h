@@ -268,7 +268,7 @@ hf_status hf_hybrid_step(const hf_dims *d, const void *q_dev, const void *k_cur_
  * or threads) race on that array; calls in one stream order are safe.  The stream's device
  * (the current device for the null stream) runs the work.  Errors: those of hf_hybrid_step,
  * HF_ERR_UNSUPPORTED when the step's transient data would exceed 32 MiB (the 832x480 layer
- * with 12 heads needs about 10.5 MiB, four such streams batched about 18 MiB), HF_ERR_HIP when
+ * with 12 heads needs about 19 MiB, four such streams batched about 27 MiB), HF_ERR_HIP when
  * the array's device address cannot be obtained. */
 hf_status hf_hybrid_step_noalloc(const hf_dims *d, const void *q_dev, const void *k_cur_dev, const void *v_cur_dev,
                                  hf_kv_ring *ring, int32_t top_k, uint32_t flags, float *S_dev, float *z_dev,

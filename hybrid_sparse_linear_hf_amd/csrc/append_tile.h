@@ -14,14 +14,15 @@ constexpr int kTileTok = 64;
 
 // One tile per (plane, chunk frame, 64 tokens), for a workgroup of 256 threads.  Threads
 // 0..127 regroup V: each owns an 8-token x 8-feature block, loads its 8 rows (16 bytes
-// each), transposes the 8x8 block of 16-bit values in registers (byte permutes) and stores
-// the 8 features' 16-byte token rows, 128 contiguous bytes of the group.  Lane t of the
-// regrouping threads takes feature group t % 16 and token group t / 16, so the 16 lanes of
-// a token group write one group's 2 KB (D = 128) and read whole V rows.  Threads
-// 128..255 copy the tile's K rows, 8 16-byte vectors each.  Every load of a thread is
-// issued before its first store.
+// each), transposes the 8x8 block of 16-bit values in registers (byte permutes) and puts
+// the 8 features' 16-byte token rows into `vbuf` (LDS, 64 / 8 * D pieces of 16 bytes) at
+// their positions in the tile's groups.  Lane t of the regrouping threads takes feature
+// group t % 16 and token group t / 16, so the 16 lanes of a token group read whole V
+// rows.  Threads 128..255 copy the tile's K rows, 8 16-byte vectors each, every load
+// issued before the first store.  Then all 256 threads store the tile's groups, one
+// contiguous run of the slot, from `vbuf`: every store instruction writes whole lines.
 template <int D>
-__device__ void append_tile(const hf_append_args &a, int tile) {
+__device__ void append_tile(const hf_append_args &a, int tile, u32x4 *vbuf) {
     const int tiles_per_frame = (a.T + kTileTok - 1) / kTileTok;
     const int tile_id = tile % tiles_per_frame;
     const int fc = (tile / tiles_per_frame) % a.C;   // frame within the chunk
@@ -40,8 +41,7 @@ __device__ void append_tile(const hf_append_args &a, int tile) {
             u32x4 in[8];
 #pragma unroll
             for (int r = 0; r < 8; ++r) in[r] = *reinterpret_cast<const u32x4 *>(src + (size_t)r * D);
-            // out[i] = feature 8fg + i over tokens 8tg .. 8tg + 7: row 8fg + i of the group
-            uint16_t *dst = a.ring_vg + (((size_t)bh * a.W + slot) * a.T + t0 + 8 * tg) * D + 64 * fg;
+            // piece i = feature 8fg + i over tokens 8tg .. 8tg + 7, at LDS position tg D + 8fg + i
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
@@ -51,7 +51,7 @@ __device__ void append_tile(const hf_append_args &a, int tile) {
                     const uint32_t wa = in[2 * j][i >> 1], wb = in[2 * j + 1][i >> 1];
                     o[j] = __builtin_amdgcn_perm(wb, wa, sel);
                 }
-                *reinterpret_cast<u32x4 *>(dst + 8 * i) = u32x4{o[0], o[1], o[2], o[3]};
+                vbuf[tg * D + 8 * fg + i] = u32x4{o[0], o[1], o[2], o[3]};
             }
         }
     } else {
@@ -73,6 +73,11 @@ __device__ void append_tile(const hf_append_args &a, int tile) {
             if (r < ntok) *reinterpret_cast<u32x4 *>(kdst + (size_t)r * D + c8) = kv[it];
         }
     }
+    __syncthreads();
+    // the tile's groups are one contiguous run of the slot: piece e of the run is LDS piece e
+    uint16_t *vdst = a.ring_vg + (((size_t)bh * a.W + slot) * a.T + t0) * D;
+    const int npieces = (ntok / 8) * D;
+    for (int e = tid; e < npieces; e += 256) *reinterpret_cast<u32x4 *>(vdst + 8 * e) = vbuf[e];
 }
 
 

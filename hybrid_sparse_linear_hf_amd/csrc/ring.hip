@@ -8,7 +8,8 @@ namespace {
 
 template <int D>
 __global__ __launch_bounds__(256) void ring_append_kernel(hf_append_args a) {
-    append_tile<D>(a, blockIdx.x);
+    __shared__ u32x4 vbuf[kTileTok / 8 * D];
+    append_tile<D>(a, blockIdx.x, vbuf);
 }
 
 }  // namespace

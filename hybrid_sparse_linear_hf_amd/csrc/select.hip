@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64 * kRows) void score_topk_kernel(hf_select_args a
         // a hybrid step's ring append: pure copying, which fills the slots this latency-bound
         // scoring leaves idle (nothing here reads the ring: the current chunk's keys were
         // pooled from the chunk input)
-        append_tile<D>(a.app, (int)blockIdx.x - a.BH * groups);
+        append_tile<D>(a.app, (int)blockIdx.x - a.BH * groups, reinterpret_cast<u32x4 *>(&ks[0][0]));
         return;
     }
     const int bh = blockIdx.x / groups, i0 = (blockIdx.x % groups) * kRows;

@@ -576,6 +576,75 @@ __device__ __forceinline__ void dq_kv_reads(const uint32_t (&ad)[2], u32x4 (&fk)
         : "memory");
 }
 
+// The K^T fragments of a staged 32-key subtile for the dq products -- xt_frag(X, 16 g +
+// 8 ks, ft) for every ft and ks = 0, 1 -- read in one asm block that waits once at its end
+// (left to itself the compiler waits for each fragment's pair of reads before its
+// product).  Per lane the reads of ks = 1 lie 8 rows (16 D bytes) past those of ks = 0:
+// the row swizzle ignores bit 3 of the row.
+template <int D>
+__device__ __forceinline__ void dq_kt_frags(const uint16_t *X, int g, int lane, u32x4 (&f)[D / 32][2]) {
+    static_assert(D == 64 || D == 128, "head dimension");
+    const int s = lane & 15, t = s & 3, G = (lane >> 4) & 1;
+    uint32_t ad[D / 32][2];
+#pragma unroll
+    for (int ft = 0; ft < D / 32; ++ft)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int r = 16 * g + 4 * hh + (s >> 2);
+            const int d = 32 * ft + 8 * G + 16 * (t & 1) + 4 * (t >> 1);
+            const int e = r * D + (((d >> 3) ^ swz_row<D>(r)) << 3) + (d & 7);
+            ad[ft][hh] = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t *)(X + e);
+        }
+    u32x2 h[D / 32][2][2];   // [ft][ks][hh]
+    if constexpr (D == 128) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %16\n\t"
+            "ds_read_b64_tr_b16 %1, %17\n\t"
+            "ds_read_b64_tr_b16 %2, %16 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %3, %17 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %4, %18\n\t"
+            "ds_read_b64_tr_b16 %5, %19\n\t"
+            "ds_read_b64_tr_b16 %6, %18 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %7, %19 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %8, %20\n\t"
+            "ds_read_b64_tr_b16 %9, %21\n\t"
+            "ds_read_b64_tr_b16 %10, %20 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %11, %21 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %12, %22\n\t"
+            "ds_read_b64_tr_b16 %13, %23\n\t"
+            "ds_read_b64_tr_b16 %14, %22 offset:%24\n\t"
+            "ds_read_b64_tr_b16 %15, %23 offset:%24\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(h[0][0][0]), "=&v"(h[0][0][1]), "=&v"(h[0][1][0]), "=&v"(h[0][1][1]),
+              "=&v"(h[1][0][0]), "=&v"(h[1][0][1]), "=&v"(h[1][1][0]), "=&v"(h[1][1][1]),
+              "=&v"(h[2][0][0]), "=&v"(h[2][0][1]), "=&v"(h[2][1][0]), "=&v"(h[2][1][1]),
+              "=&v"(h[3][0][0]), "=&v"(h[3][0][1]), "=&v"(h[3][1][0]), "=&v"(h[3][1][1])
+            : "v"(ad[0][0]), "v"(ad[0][1]), "v"(ad[1][0]), "v"(ad[1][1]), "v"(ad[2][0]), "v"(ad[2][1]),
+              "v"(ad[3][0]), "v"(ad[3][1]), "i"(16 * D)
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8\n\t"
+            "ds_read_b64_tr_b16 %1, %9\n\t"
+            "ds_read_b64_tr_b16 %2, %8 offset:%12\n\t"
+            "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
+            "ds_read_b64_tr_b16 %4, %10\n\t"
+            "ds_read_b64_tr_b16 %5, %11\n\t"
+            "ds_read_b64_tr_b16 %6, %10 offset:%12\n\t"
+            "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(h[0][0][0]), "=&v"(h[0][0][1]), "=&v"(h[0][1][0]), "=&v"(h[0][1][1]),
+              "=&v"(h[1][0][0]), "=&v"(h[1][0][1]), "=&v"(h[1][1][0]), "=&v"(h[1][1][1])
+            : "v"(ad[0][0]), "v"(ad[0][1]), "v"(ad[1][0]), "v"(ad[1][1]), "i"(16 * D)
+            : "memory");
+    }
+#pragma unroll
+    for (int ft = 0; ft < D / 32; ++ft)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            f[ft][ks] = u32x4{h[ft][ks][0].x, h[ft][ks][0].y, h[ft][ks][1].x, h[ft][ks][1].y};
+}
+
 template <int D, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW, 2))) void dq_kernel(hf_bwd_args a, float c_log2, float inv_sqrt_d, int lsh) {
     constexpr int LPR = D / 8, RPI = 64 / LPR;      // chunks per row, rows per load instruction
@@ -680,11 +749,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
             gfr[ks] = u32x4{pack_bf16x2(gt[8 * ks], gt[8 * ks + 1]), pack_bf16x2(gt[8 * ks + 2], gt[8 * ks + 3]),
                             pack_bf16x2(gt[8 * ks + 4], gt[8 * ks + 5]), pack_bf16x2(gt[8 * ks + 6], gt[8 * ks + 7])};
         // dq^T += K^T G^T: K^T rows 32 ft + perm32(n), keys 16 g + 8 ks .. + 8
+        u32x4 kt[D / 32][2];
+        dq_kt_frags<D>(cur.k, g, lane, kt);
 #pragma unroll
         for (int ft = 0; ft < D / 32; ++ft)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                acc[ft] = mfma32(as_bf16x8(xt_frag<D, true>(cur.k, 16 * g + 8 * ks, ft, lane)), as_bf16x8(gfr[ks]), acc[ft]);
+            for (int ks = 0; ks < 2; ++ks) acc[ft] = mfma32(as_bf16x8(kt[ft][ks]), as_bf16x8(gfr[ks]), acc[ft]);
     };
     fetch(0, S0);
     int u = 0;

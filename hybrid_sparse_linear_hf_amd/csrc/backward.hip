@@ -576,13 +576,13 @@ __device__ __forceinline__ void dq_kv_reads(const uint32_t (&ad)[2], u32x4 (&fk)
         : "memory");
 }
 
-// The K^T fragments of a staged 32-key subtile for the dq products -- xt_frag(X, 16 g +
-// 8 ks, ft) for every ft and ks = 0, 1 -- read in one asm block that waits once at its end
-// (left to itself the compiler waits for each fragment's pair of reads before its
-// product).  Per lane the reads of ks = 1 lie 8 rows (16 D bytes) past those of ks = 0:
-// the row swizzle ignores bit 3 of the row.
+// Every transposed fragment of 16 staged rows for one set of products -- xt_frag(X, r0 +
+// 8 ks, ft) for every ft and ks = 0, 1 (r0 a multiple of 16) -- read in one asm block that
+// waits once at its end (left to itself the compiler waits for each fragment's pair of
+// reads before its product).  Per lane the reads of ks = 1 lie 8 rows (16 D bytes) past
+// those of ks = 0: the row swizzle ignores bit 3 of the row.
 template <int D>
-__device__ __forceinline__ void dq_kt_frags(const uint16_t *X, int g, int lane, u32x4 (&f)[D / 32][2]) {
+__device__ __forceinline__ void xt_frags(const uint16_t *X, int r0, int lane, u32x4 (&f)[D / 32][2]) {
     static_assert(D == 64 || D == 128, "head dimension");
     const int s = lane & 15, t = s & 3, G = (lane >> 4) & 1;
     uint32_t ad[D / 32][2];
@@ -590,7 +590,7 @@ __device__ __forceinline__ void dq_kt_frags(const uint16_t *X, int g, int lane, 
     for (int ft = 0; ft < D / 32; ++ft)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const int r = 16 * g + 4 * hh + (s >> 2);
+            const int r = r0 + 4 * hh + (s >> 2);
             const int d = 32 * ft + 8 * G + 16 * (t & 1) + 4 * (t >> 1);
             const int e = r * D + (((d >> 3) ^ swz_row<D>(r)) << 3) + (d & 7);
             ad[ft][hh] = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t *)(X + e);
@@ -750,7 +750,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
                             pack_bf16x2(gt[8 * ks + 4], gt[8 * ks + 5]), pack_bf16x2(gt[8 * ks + 6], gt[8 * ks + 7])};
         // dq^T += K^T G^T: K^T rows 32 ft + perm32(n), keys 16 g + 8 ks .. + 8
         u32x4 kt[D / 32][2];
-        dq_kt_frags<D>(cur.k, g, lane, kt);
+        xt_frags<D>(cur.k, 16 * g, lane, kt);
 #pragma unroll
         for (int ft = 0; ft < D / 32; ++ft)
 #pragma unroll
@@ -1030,20 +1030,14 @@ __global__ __launch_bounds__(64 * NKT * NQT) __attribute__((amdgpu_waves_per_eu(
         // all transposed fragments of one operand are read before its products
         u32x4 xg[NTF][2];
         if constexpr (MODE != 2) {
-#pragma unroll
-        for (int fi = 0; fi < NTF; ++fi)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) xg[fi][ks] = xt_frag<D, true>(Lg, 32 * qt + 16 * g + 8 * ks, fi, lane);
+        xt_frags<D>(Lg, 32 * qt + 16 * g, lane, xg);
 #pragma unroll
         for (int fi = 0; fi < NTF; ++fi)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) accV[fi] = mfma32(as_bf16x8(xg[fi][ks]), as_bf16x8(pf[ks]), accV[fi]);
         }
         if constexpr (MODE != 1) {
-#pragma unroll
-        for (int fi = 0; fi < NTF; ++fi)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) xg[fi][ks] = xt_frag<D, true>(Lq, 32 * qt + 16 * g + 8 * ks, fi, lane);
+        xt_frags<D>(Lq, 32 * qt + 16 * g, lane, xg);
 #pragma unroll
         for (int fi = 0; fi < NTF; ++fi)
 #pragma unroll

@@ -295,7 +295,7 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t *p) {
 // as two transposing reads of four rows.  In a 16-lane group (n = 16 G + i) lane s points
 // at row q0 + 4 h + s / 4, features 32 ft + 8 G + 16 ((s % 4) & 1) + 4 ((s % 4) >> 1) .. + 3,
 // so that lane i receives feature 32 ft + perm32(16 G + i).
-template <int D, bool OPAQUE = false>
+template <int D>
 __device__ __forceinline__ u32x4 xt_frag(const uint16_t *X, int q0, int ft, int lane) {
     const int s = lane & 15, t = s & 3, G = (lane >> 4) & 1;
     const int d = 32 * ft + 8 * G + 16 * (t & 1) + 4 * (t >> 1);
@@ -303,12 +303,7 @@ __device__ __forceinline__ u32x4 xt_frag(const uint16_t *X, int q0, int ft, int 
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         const int r = q0 + 4 * hh + (s >> 2);
-        int e = r * D + (((d >> 3) ^ swz_row<D>(r)) << 3) + (d & 7);
-        // OPAQUE (tiles that direct-to-LDS fetches refill): the offset is hidden from the
-        // optimizer, which would otherwise rebuild the second row's address as "first + 1024
-        // bytes" outside the stage object's bounds; the compiler's wait tracking would then
-        // assume the read may touch any stage and wait for every fetch in flight
-        if constexpr (OPAQUE) asm volatile("" : "+v"(e));
+        const int e = r * D + (((d >> 3) ^ swz_row<D>(r)) << 3) + (d & 7);
         h[hh] = ds_read_tr16(X + e);
     }
     return u32x4{h[0].x, h[0].y, h[1].x, h[1].y};

@@ -73,9 +73,8 @@ Geometry geometry(const hf_dims *d, const hf_kv_ring *r) {
 }
 
 // Workspace layout (offsets 256-byte aligned):
-//   [absorb partials]  [qbar fp64]  [kbar fp64]  [scores fp64]  [S^T bf16]  [z copy fp32]
-//   [frame-pooled keys fp64, up to kMaxHierFrames frames]  [frame scores fp64]
-//   [per key block frame parts fp64]
+//   [absorb partials]  [qbar fp64]  [kbar fp64]  [S^T bf16]  [z copy fp32]
+//   [frame-pooled keys fp64, up to kMaxHierFrames frames]  [per key block frame parts fp64]
 struct WsLayout {
     size_t absorb, qbar, kbar, st, zc, fbar, part, total;
 };

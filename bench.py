@@ -389,7 +389,7 @@ def main():
     ms_step = wall * 1e3 / args.steps
     value = flops.sum() / wall / 1e12
     t_sel = phases[:, 1].mean() * 1e-3
-    t_prep = phases[:, 2].mean() * 1e-3
+    t_evpair = phases[:, 2].mean() * 1e-3   # ev2 -> ev3: nothing runs between them
     t_attn = phases[:, 3].mean() * 1e-3
     t_state = phases[:, 4].mean() * 1e-3   # the state pass adding the absorb partials
     t_abs = t_abs_wall   # what the absorb adds to a step
@@ -435,9 +435,13 @@ def main():
                                        "readout-operand launch",
                      "launch_note": "in a committed step the attention launch also forms the absorb partials"},
         "phases_us": {"select_append_prep": round(t_sel * 1e6, 2),
-                      "readout_prep": round(t_prep * 1e6, 2),
+                      "event_pair_only": round(t_evpair * 1e6, 2),
                       "sparse_attn_readout_and_absorb_partials": round(t_attn * 1e6, 2),
                       "state_pass": round(t_state * 1e6, 2)},
+        "phases_note": "HIP events recorded inside hf_hybrid_step on the step's stream: select = pool launch "
+                       "(with the readout operands) + score/top-k launch (with the ring append); "
+                       "event_pair_only = two events recorded back to back with no launch between them, "
+                       "the cost of one recorded event, which every other phase figure also carries",
         "absorb_roofline": {"bound": "hbm", "achieved": round(absorb_bytes / t_abs / 1e9, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(absorb_bytes / t_abs / 1e9 / PEAK_HBM_GBS, 4),
                             "bytes_per_launch": absorb_bytes, "added_us_per_step": round(t_abs * 1e6, 2),

@@ -71,16 +71,20 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// LDS swizzles (16-byte chunks), chosen so that the operand reads below touch 16 distinct
-// bank groups per 16 lanes.  K rows hold D/8 chunks, permuted per row.  A V group holds D
-// 16-byte feature rows; feature f sits at position vslot(f) (bit 3 ^= bit 4): the 16 lanes
-// of a read take features perm32(0 .. 15) = {0-3, 16-19, 4-7, 20-23} (+ 8 for the next 16).
+// LDS swizzles (16-byte chunks) of the operand reads below.  K rows hold D/8 chunks,
+// permuted per row, so that the 16 lanes of a read touch 16 distinct bank groups.  A V
+// group holds D 16-byte feature rows; feature f sits at position vslot(f), which flips bits
+// 2 and 3 where bit 4 is set (an involution that leaves bits 4 and up alone).  The lanes of
+// a read take features perm32(0 .. 31) = {0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31}
+// (+ 32 ft) of group ks and, lanes 32-63, of group 2 + ks.  Counted with SQ_LDS_BANK_CONFLICT
+// on gfx950 for these exact 64-lane patterns: no conflict cycles, where flipping bit 3 alone
+// cost one extra pass per read (2-way).
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
     if constexpr (D == 128) return ((r & 3) << 1) | ((r >> 2) & 1) | ((r >> 1) & 8);
     else return ((r >> 1) & 3) | ((r >> 2) & 4);
 }
-__device__ __forceinline__ int vslot(int f) { return f ^ ((f >> 1) & 8); }
+__device__ __forceinline__ int vslot(int f) { return f ^ (((f >> 4) & 1) * 12); }
 
 struct SmState {
     float m;     // reference maximum of s * c_log2 (base-2 logits)

@@ -21,6 +21,12 @@ constexpr int kTileTok = 64;
 // rows.  Threads 128..255 copy the tile's K rows, 8 16-byte vectors each, every load
 // issued before the first store.  Then all 256 threads store the tile's groups, one
 // contiguous run of the slot, from `vbuf`: every store instruction writes whole lines.
+// LDS position of value piece f (feature f of a token group) within its group's D pieces:
+// bits 4-6 of f XORed into bits 0-2, so that the 16 lanes of a piece write (features
+// 8 fg + i, fg = 0 .. 15) and of a piece read (16 consecutive features) each touch 16
+// distinct 16-byte bank groups
+__device__ __forceinline__ int vpos(int f) { return f ^ ((f >> 4) & 7); }
+
 template <int D>
 __device__ void append_tile(const hf_append_args &a, int tile, u32x4 *vbuf) {
     const int tiles_per_frame = (a.T + kTileTok - 1) / kTileTok;
@@ -51,7 +57,7 @@ __device__ void append_tile(const hf_append_args &a, int tile, u32x4 *vbuf) {
                     const uint32_t wa = in[2 * j][i >> 1], wb = in[2 * j + 1][i >> 1];
                     o[j] = __builtin_amdgcn_perm(wb, wa, sel);
                 }
-                vbuf[tg * D + 8 * fg + i] = u32x4{o[0], o[1], o[2], o[3]};
+                vbuf[tg * D + vpos(8 * fg + i)] = u32x4{o[0], o[1], o[2], o[3]};
             }
         }
     } else {
@@ -77,7 +83,7 @@ __device__ void append_tile(const hf_append_args &a, int tile, u32x4 *vbuf) {
     // the tile's groups are one contiguous run of the slot: piece e of the run is LDS piece e
     uint16_t *vdst = a.ring_vg + (((size_t)bh * a.W + slot) * a.T + t0) * D;
     const int npieces = (ntok / 8) * D;
-    for (int e = tid; e < npieces; e += 256) *reinterpret_cast<u32x4 *>(vdst + 8 * e) = vbuf[e];
+    for (int e = tid; e < npieces; e += 256) *reinterpret_cast<u32x4 *>(vdst + 8 * e) = vbuf[(e & ~(D - 1)) | vpos(e & (D - 1))];
 }
 
 

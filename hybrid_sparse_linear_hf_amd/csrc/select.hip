@@ -48,6 +48,12 @@ __device__ __forceinline__ const uint16_t *key_row(const hf_select_args &a, int 
     return a.ring_k + (((size_t)bh * a.W + slot) * a.T + t) * a.D;
 }
 
+// Position of feature d of row ro in the pool's fp64 reduction array: bits 5-6 of d and
+// bit 0 of ro XORed into bits 0-2, so that a write (lanes v = 0 .. 15 of two rows, features
+// 8 v + e) and a read (consecutive features of one row) touch distinct banks.  Values and
+// summation order are unchanged.
+__device__ __forceinline__ int rpos(int ro, int d) { return d ^ (((d >> 5) & 3) | ((ro & 1) << 2)); }
+
 template <int D, bool SPLIT>
 __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
     constexpr int kVec = D / 8;              // 16-byte vectors per row
@@ -101,18 +107,18 @@ __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
             // the other through the same LDS (one array keeps the launch at eight workgroups
             // per CU); the block's sum is their sum (both exact, so it is the exact block sum)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) red[ro][v * 8 + e] = acc[e];
+            for (int e = 0; e < 8; ++e) red[ro][rpos(ro, v * 8 + e)] = acc[e];
             __syncthreads();
             double s0 = 0.0, s1 = 0.0;
             if (threadIdx.x < D)
-                for (int k = 0; k < kRowsPerPass; ++k) s0 += red[k][threadIdx.x];
+                for (int k = 0; k < kRowsPerPass; ++k) s0 += red[k][rpos(k, threadIdx.x)];
             if (fend < r1) {                  // the block reaches into the next frame (uniform)
                 __syncthreads();
 #pragma unroll
-                for (int e = 0; e < 8; ++e) red[ro][v * 8 + e] = acc2[e];
+                for (int e = 0; e < 8; ++e) red[ro][rpos(ro, v * 8 + e)] = acc2[e];
                 __syncthreads();
                 if (threadIdx.x < D)
-                    for (int k = 0; k < kRowsPerPass; ++k) s1 += red[k][threadIdx.x];
+                    for (int k = 0; k < kRowsPerPass; ++k) s1 += red[k][rpos(k, threadIdx.x)];
             }
             if (threadIdx.x < D) {
                 double *pp = a.part + (((size_t)bh * a.nkb + b) * 2) * D;
@@ -124,11 +130,11 @@ __global__ __launch_bounds__(256) void pool_kernel(hf_select_args a) {
         }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[ro][v * 8 + e] = acc[e];
+    for (int e = 0; e < 8; ++e) red[ro][rpos(ro, v * 8 + e)] = acc[e];
     __syncthreads();
     if (threadIdx.x < D) {
         double s = 0.0;
-        for (int k = 0; k < kRowsPerPass; ++k) s += red[k][threadIdx.x];
+        for (int k = 0; k < kRowsPerPass; ++k) s += red[k][rpos(k, threadIdx.x)];
         double *dst = is_q ? a.qbar + ((size_t)bh * a.nqb + b) * D : a.kbar + ((size_t)bh * a.nkb + b) * D;
         dst[threadIdx.x] = s / (double)(r1 - r0);
     }
